@@ -1,0 +1,79 @@
+"""Seeded synthetic inputs for the cached causal Conv3D.
+
+Shared by the tests, the benchmark and the smoke check, and by both sides of
+every parity comparison (the GPU path and the CPU oracle read the very same
+buffers).  This module holds none of the convolution's arithmetic: it only
+draws random tensors and rounds them to the storage dtype.
+
+Value recipe (the decoder workloads of "Cache-Aware Conv3D Lowering Across
+Embedded World-Model Decoders" run on trained weights and real latents, which
+are not available; these seeded draws stand in for them):
+  * "uniform" (tiny fp32 case): x, cache, w ~ U(-1, 1); b ~ U(-0.1, 0.1).
+  * "normal" (every bf16 case): x, cache ~ N(0, 1); w ~ N(0, 1/fan_in) with
+    fan_in = C_in*Kt*Kh*Kw; b ~ N(0, 0.01) (variance 0.01, std 0.1).
+Draw order is w, b, cache, x from one torch.Generator seeded with ``seed`` on
+the device the tensors are made on; values are drawn in float32 and rounded
+once (round to nearest even) to the storage dtype.
+
+Layouts are the physical ones the library uses: activations
+[N][T][H][W][C] contiguous, weights [Cout][Kt][Kh][Kw][Cin] contiguous,
+bias [Cout].
+"""
+import torch
+
+__all__ = ["SEED_BASE", "draw", "conv_inputs", "replay_chunks"]
+
+SEED_BASE = 20261203
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def draw(shape, kind, g, device, dtype, scale=1.0):
+    """One tensor of ``shape``: kind 'normal' (N(0, scale^2)) or 'uniform'
+    (U(-scale, scale)), drawn in float32 then rounded to ``dtype``."""
+    if kind == "normal":
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            t.mul_(scale)
+    elif kind == "uniform":
+        t = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+        t.mul_(2.0 * scale).sub_(scale)
+    else:
+        raise ValueError(kind)
+    return t.to(dtype)
+
+
+def conv_inputs(n, cin, cout, h, w, tx, tc, k=(3, 3, 3), *, kind="normal",
+                dtype=torch.bfloat16, device="cpu", seed=SEED_BASE, has_bias=True):
+    """Seeded (x, cache, w, b) for one call.  cache is None when tc == 0."""
+    g = _gen(device, seed)
+    kt, kh, kw = k
+    if kind == "uniform":
+        wt = draw((cout, kt, kh, kw, cin), "uniform", g, device, dtype, 1.0)
+        bt = draw((cout,), "uniform", g, device, dtype, 0.1) if has_bias else None
+        ct = draw((n, tc, h, w, cin), "uniform", g, device, dtype, 1.0) if tc else None
+        xt = draw((n, tx, h, w, cin), "uniform", g, device, dtype, 1.0)
+    else:
+        fan_in = cin * kt * kh * kw
+        wt = draw((cout, kt, kh, kw, cin), "normal", g, device, dtype, fan_in ** -0.5)
+        bt = draw((cout,), "normal", g, device, dtype, 0.1) if has_bias else None
+        ct = draw((n, tc, h, w, cin), "normal", g, device, dtype, 1.0) if tc else None
+        xt = draw((n, tx, h, w, cin), "normal", g, device, dtype, 1.0)
+    return xt, ct, wt, bt
+
+
+def replay_chunks(n, cin, cout, h, w, frames, k=(3, 3, 3), *, dtype=torch.bfloat16,
+                  device="cpu", seed=SEED_BASE, has_bias=True):
+    """Seeded weights and a list of per-chunk inputs for a streaming replay:
+    w, b, then x for each chunk (frames[c] frames in chunk c), all 'normal'."""
+    g = _gen(device, seed)
+    kt, kh, kw = k
+    fan_in = cin * kt * kh * kw
+    wt = draw((cout, kt, kh, kw, cin), "normal", g, device, dtype, fan_in ** -0.5)
+    bt = draw((cout,), "normal", g, device, dtype, 0.1) if has_bias else None
+    xs = [draw((n, f, h, w, cin), "normal", g, device, dtype, 1.0) for f in frames]
+    return wt, bt, xs
