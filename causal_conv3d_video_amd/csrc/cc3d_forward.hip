@@ -1,0 +1,472 @@
+// Kernels and launcher of the cached causal Conv3D on gfx950 (MI355X).
+//
+// The operation ("Cache-Aware Conv3D Lowering Across Embedded World-Model
+// Decoders", lowering section): output frame o sums, over the active
+// temporal taps k, the bias-free spatial Conv2D of source frame o + delta_k of
+// Z = [C; X] with the weight slice W[:, :, k], and adds the bias once.  The
+// paper evaluates each active tap as its own batched Conv2D; here every
+// active tap, every spatial tap and every input channel is one K reduction of
+// an implicit GEMM held in MFMA accumulators, and Z is read in place from the
+// cache and input buffers (no concatenation, no per-tap weight copies).
+//
+//   GEMM view per output frame:  D[co][pixel] = sum_K  W[co][K] * Z[K][pixel]
+//   K = (active tap k, spatial tap (a, c), input channel ci)
+//
+// bf16 kernel (one workgroup = 4 waves = one output frame, one patch of
+// TH x 32 output pixels, BN output channels):
+//   * a pipeline stage is (active tap, chunk of CB input channels); its
+//     operands are the (TH+2) x 34 pixel halo of the source frame (zero
+//     outside the image) and the BN x 9 x CB weight slice, both staged through
+//     LDS, double-buffered, with the next stage's global loads in flight while
+//     the current stage's MFMAs run;
+//   * LDS rows are padded by 16 bytes so that the 16-byte operand reads of
+//     any 8 consecutive lanes fall in distinct banks;
+//   * v_mfma_f32_32x32x16_bf16: A = 32 output channels x 16 input channels of
+//     W, B = 16 input channels x 32 pixels (one patch row, shifted by the
+//     spatial tap) of the halo; fp32 accumulation in registers;
+//   * epilogue: fp32 bias added once, round to nearest even to bf16,
+//     channels-last stores of 4 channels per lane.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "cc3d_internal.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+struct ConvArgs {
+  const void* x;
+  const void* cache;
+  const void* w;
+  const void* b;
+  void* out;
+  int n, tx, tc, h, wd, cin, cout, to, ho, wo;
+  int kt, kh, kw, sh, sw, dh, dw, ph, pw;
+  int tz;
+  int delta[CC3D_MAX_KT];
+  int tiles_x, tiles_y, nblk_n;
+  int has_bias;
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8).  Renumber so that each XCD receives one contiguous range of
+// logical tiles: neighbouring patches and the output frames that share source
+// frames then meet in the same L2.
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+  const int q = grid >> 3, r = grid & 7;
+  const int xcd = bid & 7, j = bid >> 3;
+  return xcd * q + min(xcd, r) + j;
+}
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short h) {
+  return __uint_as_float(static_cast<unsigned>(h) << 16);
+}
+
+// Round to nearest, ties to even (hardware conversion on gfx950).
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ int tap_delta(const ConvArgs& a, int k) {
+  int d = 0;
+#pragma unroll
+  for (int q = 0; q < CC3D_MAX_KT; ++q)
+    if (q == k) d = a.delta[q];
+  return d;
+}
+
+template <int BN, int TH, int WM, int WN, int KS, int CB>
+__global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
+  constexpr int TW = 32;                       // patch width = MFMA pixel block
+  constexpr int PAD = (KS - 1) / 2;
+  constexpr int HP = TH + KS - 1, WP = TW + KS - 1, S = KS * KS;
+  constexpr int PZ = CB / 8;                   // 16-byte pieces per pixel per stage
+  constexpr int ZSTR = CB * 2 + 16;            // LDS bytes per halo pixel
+  constexpr int WSTR = S * CB * 2 + 16;        // LDS bytes per output channel
+  constexpr int ZBYTES = HP * WP * ZSTR;
+  constexpr int STAGE = ZBYTES + BN * WSTR;
+  constexpr int ZCH = HP * WP * PZ, WCH = BN * S * PZ;
+  constexpr int ZIT = (ZCH + 255) / 256, WIT = (WCH + 255) / 256;
+  constexpr int RW = TH / WM;                  // patch rows per wave
+  constexpr int CW = BN / (32 * WN);           // 32-channel blocks per wave
+  static_assert(WM * WN == 4 && TH % WM == 0 && BN % (32 * WN) == 0, "wave tiling");
+  static_assert(CB % 16 == 0, "stage channels");
+  static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int g = lane >> 5, l32 = lane & 31;
+
+  int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int o = bid % a.to;
+  bid /= a.to;
+  const int nb = bid % a.nblk_n;
+  bid /= a.nblk_n;
+  const int tile_x = bid % a.tiles_x;
+  bid /= a.tiles_x;
+  const int tile_y = bid % a.tiles_y;
+  const int nn = bid / a.tiles_y;
+  const int x0 = tile_x * TW, y0 = tile_y * TH, n0 = nb * BN;
+
+  // Active taps of this output frame (uniform over the workgroup).
+  unsigned mask = 0;
+  for (int k = 0; k < a.kt; ++k) {
+    const int z = o + tap_delta(a, k);
+    if (z >= 0 && z < a.tz) mask |= 1u << k;
+  }
+  const int nact = __builtin_popcount(mask);
+  const int nch = a.cin / CB;
+  const int nst = nact * nch;
+
+  const unsigned short* __restrict__ xs = static_cast<const unsigned short*>(a.x);
+  const unsigned short* __restrict__ cs = static_cast<const unsigned short*>(a.cache);
+  const unsigned short* __restrict__ ws = static_cast<const unsigned short*>(a.w);
+  const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
+
+  uint4 zreg[ZIT], wreg[WIT];
+
+  auto load_stage = [&](int st) {
+    int ti = st / nch;
+    const int ci0 = (st - ti * nch) * CB;
+    int k = 0;
+    for (; k < a.kt; ++k) {
+      if (mask & (1u << k)) {
+        if (ti == 0) break;
+        --ti;
+      }
+    }
+    const int z = o + tap_delta(a, k);
+    const unsigned short* fp = z < a.tc ? cs + (int64_t(nn) * a.tc + z) * frame_el
+                                        : xs + (int64_t(nn) * a.tx + (z - a.tc)) * frame_el;
+#pragma unroll
+    for (int it = 0; it < ZIT; ++it) {
+      const int id = tid + 256 * it;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ZCH % 256 == 0 || id < ZCH) {
+        const int pix = id / PZ, pc = id % PZ;
+        const int hr = pix / WP, hc = pix % WP;
+        const int y = y0 - PAD + hr, x = x0 - PAD + hc;
+        if (y >= 0 && y < a.h && x >= 0 && x < a.wd)
+          v = *reinterpret_cast<const uint4*>(fp + (int64_t(y) * a.wd + x) * a.cin + ci0 + pc * 8);
+      }
+      zreg[it] = v;
+    }
+#pragma unroll
+    for (int it = 0; it < WIT; ++it) {
+      const int id = tid + 256 * it;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (WCH % 256 == 0 || id < WCH) {
+        const int col = id / (S * PZ), rem = id % (S * PZ);
+        const int s = rem / PZ, pc = rem % PZ;
+        const int co = n0 + col;
+        if (co < a.cout)
+          v = *reinterpret_cast<const uint4*>(ws + ((int64_t(co) * a.kt + k) * S + s) * a.cin + ci0 + pc * 8);
+      }
+      wreg[it] = v;
+    }
+  };
+
+  auto store_stage = [&](int buf) {
+    unsigned char* base = lds + buf * STAGE;
+#pragma unroll
+    for (int it = 0; it < ZIT; ++it) {
+      const int id = tid + 256 * it;
+      if (ZCH % 256 == 0 || id < ZCH) {
+        const int pix = id / PZ, pc = id % PZ;
+        *reinterpret_cast<uint4*>(base + pix * ZSTR + pc * 16) = zreg[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < WIT; ++it) {
+      const int id = tid + 256 * it;
+      if (WCH % 256 == 0 || id < WCH) {
+        const int col = id / (S * PZ), rem = id % (S * PZ);
+        const int s = rem / PZ, pc = rem % PZ;
+        *reinterpret_cast<uint4*>(base + ZBYTES + col * WSTR + s * CB * 2 + pc * 16) = wreg[it];
+      }
+    }
+  };
+
+  f32x16_t acc[CW][RW];
+#pragma unroll
+  for (int q = 0; q < CW; ++q)
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[q][r][v] = 0.f;
+
+  auto compute = [&](int buf) {
+    const unsigned char* zb = lds + buf * STAGE;
+    const unsigned char* wb = zb + ZBYTES;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int ta = s / KS, tcol = s % KS;
+#pragma unroll
+      for (int kk = 0; kk < CB / 16; ++kk) {
+        bf16x8_t wf[CW], zf[RW];
+#pragma unroll
+        for (int q = 0; q < CW; ++q)
+          wf[q] = *reinterpret_cast<const bf16x8_t*>(
+              wb + ((wn * CW + q) * 32 + l32) * WSTR + s * CB * 2 + kk * 32 + g * 16);
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+          zf[r] = *reinterpret_cast<const bf16x8_t*>(
+              zb + ((wm * RW + r + ta) * WP + l32 + tcol) * ZSTR + kk * 32 + g * 16);
+#pragma unroll
+        for (int q = 0; q < CW; ++q)
+#pragma unroll
+          for (int r = 0; r < RW; ++r)
+            acc[q][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[q], zf[r], acc[q][r], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nst > 0) {
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+      const bool more = st + 1 < nst;
+      if (more) load_stage(st + 1);
+      compute(st & 1);
+      if (more) store_stage((st + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: lane holds, for pixel column l32 of each patch row, channels
+  // (v/4)*8 + g*4 + (v%4) of each 32-channel block.
+  const unsigned short* bs = static_cast<const unsigned short*>(a.b);
+  unsigned short* os = static_cast<unsigned short*>(a.out);
+  const bool vec_ok = (a.cout & 3) == 0;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int y = y0 + wm * RW + r, xo = x0 + l32;
+    if (y >= a.ho || xo >= a.wo) continue;
+    unsigned short* op = os + (((int64_t(nn) * a.to + o) * a.ho + y) * a.wo + xo) * a.cout;
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int co = n0 + (wn * CW + q) * 32 + v4 * 8 + g * 4;
+        if (co >= a.cout) continue;
+        float val[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float bias = (a.has_bias && co + e < a.cout) ? bf16_to_f32(bs[co + e]) : 0.f;
+          val[e] = acc[q][r][v4 * 4 + e] + bias;
+        }
+        if (vec_ok) {
+          uint2 pk;
+          pk.x = unsigned(f32_to_bf16(val[0])) | (unsigned(f32_to_bf16(val[1])) << 16);
+          pk.y = unsigned(f32_to_bf16(val[2])) | (unsigned(f32_to_bf16(val[3])) << 16);
+          *reinterpret_cast<uint2*>(op + co) = pk;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (co + e < a.cout) op[co + e] = f32_to_bf16(val[e]);
+        }
+      }
+    }
+  }
+}
+
+// fp32 path: one output element per thread, direct loops in the order of the
+// definition (taps, rows, columns, channels) with fp32 fused multiply-add.
+__global__ __launch_bounds__(256) void conv_f32_direct(ConvArgs a) {
+  const int64_t total = int64_t(a.n) * a.to * a.ho * a.wo * a.cout;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  int64_t r = idx;
+  const int co = int(r % a.cout);
+  r /= a.cout;
+  const int j = int(r % a.wo);
+  r /= a.wo;
+  const int i = int(r % a.ho);
+  r /= a.ho;
+  const int o = int(r % a.to);
+  const int nn = int(r / a.to);
+  const float* xs = static_cast<const float*>(a.x);
+  const float* cs = static_cast<const float*>(a.cache);
+  const float* ws = static_cast<const float*>(a.w);
+  const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
+  float acc = a.has_bias ? static_cast<const float*>(a.b)[co] : 0.f;
+  for (int k = 0; k < a.kt; ++k) {
+    const int t = o + tap_delta(a, k);
+    if (t < 0 || t >= a.tz) continue;
+    const float* fp = t < a.tc ? cs + (int64_t(nn) * a.tc + t) * frame_el
+                               : xs + (int64_t(nn) * a.tx + (t - a.tc)) * frame_el;
+    for (int ta = 0; ta < a.kh; ++ta) {
+      const int u = i * a.sh - a.ph + ta * a.dh;
+      if (u < 0 || u >= a.h) continue;
+      for (int tb = 0; tb < a.kw; ++tb) {
+        const int v = j * a.sw - a.pw + tb * a.dw;
+        if (v < 0 || v >= a.wd) continue;
+        const float* zp = fp + (int64_t(u) * a.wd + v) * a.cin;
+        const float* wp = ws + ((int64_t(co) * a.kt + k) * a.kh * a.kw + ta * a.kw + tb) * a.cin;
+        for (int ci = 0; ci < a.cin; ++ci) acc = fmaf(zp[ci], wp[ci], acc);
+      }
+    }
+  }
+  static_cast<float*>(a.out)[idx] = acc;
+}
+
+// Cache-out writer: copies the last L frames of Z = [C; X] of every batch
+// item into cache_out[n][0..L).  Frames are contiguous byte ranges.
+__global__ __launch_bounds__(256) void copy_tail_frames(const unsigned char* __restrict__ x,
+                                                        const unsigned char* __restrict__ cache,
+                                                        unsigned char* __restrict__ dst,
+                                                        int64_t frame_bytes, int n, int tx, int tc,
+                                                        int L, int vec16) {
+  const int tz = tx + tc;
+  for (int f = blockIdx.y; f < n * L; f += gridDim.y) {
+    const int nn = f / L, j = f - nn * L;
+    const int zf = tz - L + j;
+    const unsigned char* src = zf < tc ? cache + (int64_t(nn) * tc + zf) * frame_bytes
+                                       : x + (int64_t(nn) * tx + (zf - tc)) * frame_bytes;
+    unsigned char* d = dst + int64_t(f) * frame_bytes;
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    int64_t done = 0;
+    if (vec16) {
+      const int64_t n16 = frame_bytes / 16;
+      for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride)
+        reinterpret_cast<uint4*>(d)[i] = reinterpret_cast<const uint4*>(src)[i];
+      done = n16 * 16;
+    }
+    for (int64_t i = done + int64_t(blockIdx.x) * 256 + threadIdx.x; i < frame_bytes; i += stride)
+      d[i] = src[i];
+  }
+}
+
+bool overlaps(const void* p, int64_t pb, const void* q, int64_t qb) {
+  if (!p || !q || pb <= 0 || qb <= 0) return false;
+  const auto a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+  return a0 < b0 + uint64_t(qb) && b0 < a0 + uint64_t(pb);
+}
+
+bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) & (al - 1)) == 0; }
+
+cc3d_status_t invalid() {
+  cc3d::g_invalid.fetch_add(1, std::memory_order_relaxed);
+  return CC3D_ERR_INVALID_ARG;
+}
+
+hipError_t launch_conv(const void* kernel, const ConvArgs& a, int64_t grid, hipStream_t s) {
+  ConvArgs arg = a;
+  void* args[] = {&arg};
+  return hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(256), args, 0, s);
+}
+
+template <int BN, int TH, int WM, int WN, int KS, int CB>
+hipError_t launch_bf16(const ConvArgs& a, int64_t grid, hipStream_t s) {
+  return launch_conv(reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB>), a, grid, s);
+}
+
+}  // namespace
+
+extern "C" cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, const void* cache_in,
+                                               const void* w, const void* b, void* out, void* cache_out,
+                                               void* stream) {
+  if (!plan) return invalid();
+  const cc3d_desc_t& d = plan->d;
+  const cc3d_plan_info_t& in = plan->info;
+  if (d.t_cache == 0) cache_in = nullptr;
+  if (!x || !w || !out || (d.t_cache > 0 && !cache_in) || (d.has_bias && !b)) return invalid();
+  if (!d.has_bias) b = nullptr;
+  const uintptr_t al = d.dtype == CC3D_BF16 ? 16 : 4;
+  if (!aligned(x, al) || !aligned(cache_in, al) || !aligned(w, al) || !aligned(out, al) ||
+      !aligned(cache_out, al) || !aligned(b, uintptr_t(plan->elem)))
+    return invalid();
+  if (overlaps(out, plan->out_bytes, x, plan->x_bytes) ||
+      overlaps(out, plan->out_bytes, cache_in, plan->cache_bytes) ||
+      overlaps(out, plan->out_bytes, w, plan->w_bytes) || overlaps(out, plan->out_bytes, b, plan->b_bytes) ||
+      overlaps(out, plan->out_bytes, cache_out, plan->cache_out_bytes) ||
+      overlaps(cache_out, plan->cache_out_bytes, x, plan->x_bytes) ||
+      overlaps(cache_out, plan->cache_out_bytes, cache_in, plan->cache_bytes) ||
+      overlaps(cache_out, plan->cache_out_bytes, w, plan->w_bytes) ||
+      overlaps(cache_out, plan->cache_out_bytes, b, plan->b_bytes))
+    return invalid();
+
+  ConvArgs a{};
+  a.x = x;
+  a.cache = cache_in;
+  a.w = w;
+  a.b = b;
+  a.out = out;
+  a.n = d.n;
+  a.tx = d.t_x;
+  a.tc = d.t_cache;
+  a.h = d.h;
+  a.wd = d.w;
+  a.cin = d.c_in;
+  a.cout = d.c_out;
+  a.to = in.t_out;
+  a.ho = in.h_out;
+  a.wo = in.w_out;
+  a.kt = d.k_t;
+  a.kh = d.k_h;
+  a.kw = d.k_w;
+  a.sh = d.s_h;
+  a.sw = d.s_w;
+  a.dh = d.d_h;
+  a.dw = d.d_w;
+  a.ph = d.p_h;
+  a.pw = d.p_w;
+  a.tz = in.t_z;
+  for (int k = 0; k < CC3D_MAX_KT; ++k) a.delta[k] = k < d.k_t ? in.taps[k].delta : 0;
+  a.tiles_x = plan->tiles_x;
+  a.tiles_y = plan->tiles_y;
+  a.nblk_n = plan->nblk_n;
+  a.has_bias = d.has_bias;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  switch (in.kernel_id) {
+    case CC3D_K_F32_DIRECT:
+      e = launch_conv(reinterpret_cast<const void*>(&conv_f32_direct), a, in.grid, s);
+      break;
+    case CC3D_K_BF16_S3_N192: e = launch_bf16<192, 8, 2, 2, 3, 16>(a, in.grid, s); break;
+    case CC3D_K_BF16_S3_N96: e = launch_bf16<96, 16, 4, 1, 3, 16>(a, in.grid, s); break;
+    case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16>(a, in.grid, s); break;
+    case CC3D_K_BF16_S1_N192:
+      if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64>(a, in.grid, s);
+      else if (plan->cin_chunk == 32) e = launch_bf16<192, 8, 2, 2, 1, 32>(a, in.grid, s);
+      else e = launch_bf16<192, 8, 2, 2, 1, 16>(a, in.grid, s);
+      break;
+    case CC3D_K_BF16_S1_N32:
+      if (plan->cin_chunk == 64) e = launch_bf16<32, 8, 4, 1, 1, 64>(a, in.grid, s);
+      else if (plan->cin_chunk == 32) e = launch_bf16<32, 8, 4, 1, 1, 32>(a, in.grid, s);
+      else e = launch_bf16<32, 8, 4, 1, 1, 16>(a, in.grid, s);
+      break;
+    default:
+      return invalid();
+  }
+  if (e == hipSuccess && cache_out && in.t_cache_out > 0) {
+    const int64_t frame_bytes = int64_t(d.h) * d.w * d.c_in * plan->elem;
+    int vec16 = (frame_bytes % 16 == 0) && aligned(x, 16) && aligned(cache_in, 16) && aligned(cache_out, 16);
+    const int64_t units = vec16 ? frame_bytes / 16 : frame_bytes;
+    int n = d.n, tx = d.t_x, tc = d.t_cache, L = in.t_cache_out;
+    const int frames = n * L;
+    const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>((units + 1023) / 1024, 2048)));
+    const unsigned gy = unsigned(std::min(frames, 65535));
+    const unsigned char* xp = static_cast<const unsigned char*>(x);
+    const unsigned char* cp = static_cast<const unsigned char*>(cache_in);
+    unsigned char* dp = static_cast<unsigned char*>(cache_out);
+    int64_t fb = frame_bytes;
+    void* args[] = {&xp, &cp, &dp, &fb, &n, &tx, &tc, &L, &vec16};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&copy_tail_frames), dim3(gx, gy), dim3(256), args, 0, s);
+  }
+  if (e != hipSuccess) {
+    cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
+    return CC3D_ERR_DEVICE;
+  }
+  cc3d::g_fast_path.fetch_add(1, std::memory_order_relaxed);
+  return CC3D_OK;
+}

@@ -1,0 +1,32 @@
+// Internal plan representation shared by the planner and the launcher.
+#pragma once
+#include "cc3d.h"
+
+#include <atomic>
+#include <cstdint>
+
+// Kernel variants the planner can pick.  The bf16 ones are implicit-GEMM
+// MFMA kernels (block tile = block_m output pixels x block_n output channels).
+enum cc3d_kernel_id : int32_t {
+  CC3D_K_F32_DIRECT = 0,     // fp32, any spatial parameters, one output per thread
+  CC3D_K_BF16_S3_N192 = 1,   // 3x3 spatial, 256 px (8x32) x 192 channels
+  CC3D_K_BF16_S3_N96 = 2,    // 3x3 spatial, 512 px (16x32) x 96 channels
+  CC3D_K_BF16_S3_N32 = 3,    // 3x3 spatial, 256 px (8x32) x 32 channels, any C_out
+  CC3D_K_BF16_S1_N192 = 4,   // 1x1 spatial, 256 px (8x32) x 192 channels
+  CC3D_K_BF16_S1_N32 = 5,    // 1x1 spatial, 256 px (8x32) x 32 channels, any C_out
+};
+
+struct cc3d_plan {
+  cc3d_desc_t d;
+  cc3d_plan_info_t info;
+  int32_t tile_h;      // output rows per workgroup patch
+  int32_t tile_w;      // output columns per workgroup patch
+  int32_t tiles_y, tiles_x, nblk_n;
+  int32_t cin_chunk;   // input channels per pipeline stage
+  int64_t x_bytes, cache_bytes, w_bytes, b_bytes, out_bytes, cache_out_bytes;
+  int32_t elem;        // bytes per element
+};
+
+namespace cc3d {
+extern std::atomic<uint64_t> g_fast_path, g_unsupported, g_invalid, g_device_error;
+}

@@ -1,0 +1,205 @@
+// Host-side planner for the cached causal Conv3D: contract check, the
+// temporal tap intervals of the lowering (cache-augmented source Z = [C; X],
+// p_l = p_base - |C|, delta_k = k*d_t - p_l, equal-length output and source
+// intervals; "Cache-Aware Conv3D Lowering Across Embedded World-Model
+// Decoders", lowering section), and the kernel tile choice.  No device calls.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "cc3d_internal.h"
+
+namespace cc3d {
+std::atomic<uint64_t> g_fast_path{0}, g_unsupported{0}, g_invalid{0}, g_device_error{0};
+}
+
+namespace {
+
+int64_t floordiv(int64_t num, int64_t den) {
+  int64_t q = num / den;
+  if ((num % den != 0) && (num < 0)) q -= 1;
+  return q;
+}
+
+cc3d_status_t refuse(cc3d_status_t s) {
+  if (s == CC3D_ERR_UNSUPPORTED) cc3d::g_unsupported.fetch_add(1, std::memory_order_relaxed);
+  if (s == CC3D_ERR_INVALID_ARG) cc3d::g_invalid.fetch_add(1, std::memory_order_relaxed);
+  return s;
+}
+
+struct Variant {
+  cc3d_kernel_id id;
+  int tile_h, tile_w, block_n, cin_chunk;
+  const char* name;
+};
+
+// Tile choice for bf16.  The patch width is 32 output columns (one MFMA
+// operand block of pixels); rows and channel tiles trade accumulator
+// registers against LDS and L2 traffic per MFMA.
+Variant choose_bf16(const cc3d_desc_t& d) {
+  const bool s3 = d.k_h == 3;
+  if (s3) {
+    if (d.c_out % 192 == 0) return {CC3D_K_BF16_S3_N192, 8, 32, 192, 16, "bf16_s3_n192_p8x32"};
+    if (d.c_out % 96 == 0) return {CC3D_K_BF16_S3_N96, 16, 32, 96, 16, "bf16_s3_n96_p16x32"};
+    return {CC3D_K_BF16_S3_N32, 8, 32, 32, 16, "bf16_s3_n32_p8x32"};
+  }
+  const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
+  if (d.c_out % 192 == 0) return {CC3D_K_BF16_S1_N192, 8, 32, 192, cb, "bf16_s1_n192_p8x32"};
+  return {CC3D_K_BF16_S1_N32, 8, 32, 32, cb, "bf16_s1_n32_p8x32"};
+}
+
+}  // namespace
+
+extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out) {
+  if (out) *out = nullptr;
+  if (!desc || !out) return refuse(CC3D_ERR_INVALID_ARG);
+  const cc3d_desc_t d = *desc;
+  if (d.dtype != CC3D_F32 && d.dtype != CC3D_BF16) return refuse(CC3D_ERR_INVALID_ARG);
+  if (d.n < 1 || d.c_in < 1 || d.c_out < 1 || d.h < 1 || d.w < 1 || d.t_x < 1 || d.t_cache < 0 ||
+      d.k_t < 1 || d.k_h < 1 || d.k_w < 1 || d.s_t < 1 || d.s_h < 1 || d.s_w < 1 || d.d_t < 1 ||
+      d.d_h < 1 || d.d_w < 1 || d.p_h < 0 || d.p_w < 0 || d.p_base < 0 || d.groups < 1 ||
+      (d.has_bias != 0 && d.has_bias != 1))
+    return refuse(CC3D_ERR_INVALID_ARG);
+  // The lowering's contract: unit temporal stride, one group.
+  if (d.s_t != 1 || d.groups != 1 || d.k_t > CC3D_MAX_KT) return refuse(CC3D_ERR_UNSUPPORTED);
+
+  cc3d_plan_info_t in;
+  std::memset(&in, 0, sizeof in);
+  in.t_z = d.t_cache + d.t_x;
+  in.p_l = d.p_base - d.t_cache;
+  const int64_t t_out = floordiv(int64_t(in.t_z) + in.p_l - int64_t(d.d_t) * (d.k_t - 1) - 1, d.s_t) + 1;
+  const int64_t h_out = floordiv(int64_t(d.h) + 2 * d.p_h - int64_t(d.d_h) * (d.k_h - 1) - 1, d.s_h) + 1;
+  const int64_t w_out = floordiv(int64_t(d.w) + 2 * d.p_w - int64_t(d.d_w) * (d.k_w - 1) - 1, d.s_w) + 1;
+  if (t_out < 1 || h_out < 1 || w_out < 1) return refuse(CC3D_ERR_INVALID_ARG);
+  in.t_out = int32_t(t_out);
+  in.h_out = int32_t(h_out);
+  in.w_out = int32_t(w_out);
+  in.t_cache_out = std::min(d.p_base, in.t_z);
+
+  // Per-tap intervals: 0 <= o < T_o and 0 <= o + delta_k < |Z|.
+  int64_t active_pairs = 0;
+  int64_t read_frames = 0;  // frames of Z read by at least one active tap
+  for (int k = 0; k < d.k_t; ++k) {
+    cc3d_tap_t& tp = in.taps[k];
+    tp.delta = k * d.d_t - in.p_l;
+    tp.o_lo = std::max(0, -tp.delta);
+    tp.o_hi = std::min(in.t_out, in.t_z - tp.delta);
+    tp.active = tp.o_hi > tp.o_lo;
+    if (!tp.active) tp.o_hi = tp.o_lo;
+    tp.src_lo = tp.o_lo + tp.delta;
+    tp.src_hi = tp.o_hi + tp.delta;
+    if (tp.active) {
+      in.n_active_taps += 1;
+      active_pairs += tp.o_hi - tp.o_lo;
+    }
+  }
+  for (int32_t z = 0; z < in.t_z; ++z) {
+    bool read = false;
+    for (int k = 0; k < d.k_t; ++k)
+      read = read || (in.taps[k].active && z >= in.taps[k].src_lo && z < in.taps[k].src_hi);
+    read_frames += read;
+  }
+
+  const int elem = d.dtype == CC3D_BF16 ? 2 : 4;
+  const double spatial = double(h_out) * w_out;
+  const double mac_per_px = double(d.c_out) * d.c_in * d.k_h * d.k_w;
+  in.flops_nominal = 2.0 * d.n * double(t_out) * spatial * mac_per_px * d.k_t;
+  in.flops_active = 2.0 * d.n * double(active_pairs) * spatial * mac_per_px;
+  const double frame_in = double(d.h) * d.w * d.c_in * elem;
+  in.bytes_conv = d.n * double(read_frames) * frame_in +
+                  double(d.c_out) * d.k_t * d.k_h * d.k_w * d.c_in * elem +
+                  (d.has_bias ? double(d.c_out) * elem : 0.0) +
+                  double(d.n) * t_out * spatial * d.c_out * elem;
+  in.bytes_cache_out = 2.0 * d.n * in.t_cache_out * frame_in;
+
+  auto* p = new (std::nothrow) cc3d_plan;
+  if (!p) return CC3D_ERR_NO_MEMORY;
+  std::memset(p, 0, sizeof *p);
+  p->d = d;
+  p->elem = elem;
+  const int64_t frame_el_in = int64_t(d.h) * d.w * d.c_in;
+  p->x_bytes = int64_t(d.n) * d.t_x * frame_el_in * elem;
+  p->cache_bytes = int64_t(d.n) * d.t_cache * frame_el_in * elem;
+  p->w_bytes = int64_t(d.c_out) * d.k_t * d.k_h * d.k_w * d.c_in * elem;
+  p->b_bytes = d.has_bias ? int64_t(d.c_out) * elem : 0;
+  p->out_bytes = int64_t(d.n) * t_out * h_out * w_out * d.c_out * elem;
+  p->cache_out_bytes = int64_t(d.n) * in.t_cache_out * frame_el_in * elem;
+
+  if (d.dtype == CC3D_BF16) {
+    const bool spatial_ok = d.k_h == d.k_w && (d.k_h == 1 || d.k_h == 3) && d.s_h == 1 &&
+                            d.s_w == 1 && d.d_h == 1 && d.d_w == 1 &&
+                            d.p_h == (d.k_h - 1) / 2 && d.p_w == (d.k_w - 1) / 2;
+    const int64_t frame_el = int64_t(d.h) * d.w * std::max(d.c_in, d.c_out);
+    if (!spatial_ok || d.c_in % 16 != 0 || frame_el >= (int64_t(1) << 31)) {
+      delete p;
+      return refuse(CC3D_ERR_UNSUPPORTED);
+    }
+    const Variant v = choose_bf16(d);
+    in.kernel_id = v.id;
+    p->tile_h = v.tile_h;
+    p->tile_w = v.tile_w;
+    p->cin_chunk = v.cin_chunk;
+    p->tiles_y = int32_t((h_out + v.tile_h - 1) / v.tile_h);
+    p->tiles_x = int32_t((w_out + v.tile_w - 1) / v.tile_w);
+    p->nblk_n = (d.c_out + v.block_n - 1) / v.block_n;
+    in.block_m = v.tile_h * v.tile_w;
+    in.block_n = v.block_n;
+    in.grid = int64_t(d.n) * t_out * p->tiles_y * p->tiles_x * p->nblk_n;
+    std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);
+  } else {
+    const int64_t frame_el = int64_t(h_out) * w_out * d.c_out;
+    if (frame_el >= (int64_t(1) << 31) || int64_t(d.h) * d.w * d.c_in >= (int64_t(1) << 31)) {
+      delete p;
+      return refuse(CC3D_ERR_UNSUPPORTED);
+    }
+    in.kernel_id = CC3D_K_F32_DIRECT;
+    in.block_m = 256;
+    in.block_n = 1;
+    const int64_t total = int64_t(d.n) * t_out * h_out * w_out * d.c_out;
+    in.grid = (total + 255) / 256;
+    std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", "f32_direct");
+  }
+  if (in.grid >= (int64_t(1) << 31)) {
+    delete p;
+    return refuse(CC3D_ERR_UNSUPPORTED);
+  }
+  p->info = in;
+  *out = p;
+  return CC3D_OK;
+}
+
+extern "C" cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_info_t* info) {
+  if (!plan || !info) return refuse(CC3D_ERR_INVALID_ARG);
+  *info = plan->info;
+  return CC3D_OK;
+}
+
+extern "C" void causal_conv3d_plan_destroy(cc3d_plan_t plan) { delete plan; }
+
+extern "C" const char* causal_conv3d_status_string(cc3d_status_t s) {
+  switch (s) {
+    case CC3D_OK: return "ok";
+    case CC3D_ERR_INVALID_ARG: return "invalid argument";
+    case CC3D_ERR_UNSUPPORTED: return "unsupported by the cached causal Conv3D kernels";
+    case CC3D_ERR_DEVICE: return "HIP runtime rejected a launch";
+    case CC3D_ERR_NO_MEMORY: return "out of host memory";
+  }
+  return "unknown status";
+}
+
+extern "C" void causal_conv3d_counters(cc3d_counters_t* out, int reset) {
+  using namespace cc3d;
+  if (out) {
+    out->fast_path = g_fast_path.load();
+    out->unsupported = g_unsupported.load();
+    out->invalid = g_invalid.load();
+    out->device_error = g_device_error.load();
+  }
+  if (reset) {
+    g_fast_path = 0;
+    g_unsupported = 0;
+    g_invalid = 0;
+    g_device_error = 0;
+  }
+}

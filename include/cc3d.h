@@ -1,0 +1,176 @@
+/*
+ * cc3d.h -- cached causal Conv3D for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation is the cached causal 3-D convolution of world-model video
+ * VAE decoders, as stated in "Cache-Aware Conv3D Lowering Across Embedded
+ * World-Model Decoders", lowering section (the paper's Sec. 4, the paragraphs
+ * that define the cache-augmented source, the per-tap source time, the
+ * effective left padding and the output/source intervals):
+ *
+ *   Z = [C; X]  -- the temporal cache C (trailing frames of the previous
+ *                  chunk) joined ahead of the current input X along time;
+ *   p_l = p_base - |C|            effective causal left pad;
+ *   delta_k = k*d_t - p_l         offset of temporal tap k (unit stride);
+ *   tap k of output frame o reads source frame o + delta_k; frames outside
+ *   [0, |Z|) contribute zero, so tap k is evaluated only for o in
+ *   [o_lo, o_hi) = [max(0, -delta_k), min(T_o, |Z| - delta_k)), whose source
+ *   interval [o_lo + delta_k, o_hi + delta_k) has the same length;
+ *   y[o] = b + sum over active taps k of Conv2D(Z[o + delta_k], W[:, :, k])
+ *   with PyTorch's cross-correlation convention and the original spatial
+ *   stride, zero padding and dilation; the bias is added exactly once.
+ *   T_o = |Z| + p_l - d_t*(k_t - 1)  (T_o = |X| when p_base = d_t*(k_t - 1)).
+ *
+ * All active temporal taps, all spatial taps and all input channels form one
+ * K reduction accumulated in registers by one kernel (no per-tap Conv2D, no
+ * materialised [C; X], no per-tap weight copies).  The carried cache (the
+ * last min(p_base, |Z|) frames of Z) is written by a second small kernel.
+ *
+ * Layouts (dense, channels last; element type given by the descriptor):
+ *   x          [N][T_x][H][W][C_in]
+ *   cache_in   [N][T_cache][H][W][C_in]
+ *   w          [C_out][k_t][k_h][k_w][C_in]   (PyTorch OIDHW weight in
+ *                                              channels_last_3d memory format)
+ *   b          [C_out]
+ *   out        [N][T_o][H_o][W_o][C_out]
+ *   cache_out  [N][min(p_base, T_cache + T_x)][H][W][C_in]
+ *
+ * Ownership: every tensor is caller-owned device memory.  A plan owns only
+ * host metadata; it holds no device memory and no copy of any tensor.
+ * Threading: plans are immutable after creation and may be used from any
+ * thread and stream; counters are atomic.
+ * Errors: every check is synchronous and happens before any launch; a launch
+ * failure reported by the runtime returns CC3D_ERR_DEVICE; faults during
+ * execution surface at the caller's next synchronisation.  The library never
+ * falls back to another implementation: an unsupported call returns
+ * CC3D_ERR_UNSUPPORTED and the caller decides what to do.
+ */
+#ifndef CC3D_H
+#define CC3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CC3D_OK = 0,
+  CC3D_ERR_INVALID_ARG = 1,  /* NULL/misaligned/overlapping buffer, bad size, empty output */
+  CC3D_ERR_UNSUPPORTED = 2,  /* outside the supported contract (see causal_conv3d_plan) */
+  CC3D_ERR_DEVICE = 3,       /* the HIP runtime rejected a launch */
+  CC3D_ERR_NO_MEMORY = 4     /* host allocation failed */
+} cc3d_status_t;
+
+typedef enum {
+  CC3D_F32 = 0,   /* fp32 storage, fp32 arithmetic */
+  CC3D_BF16 = 1   /* bf16 storage, fp32 accumulation, RNE-rounded bf16 output */
+} cc3d_dtype_t;
+
+#define CC3D_MAX_KT 8
+
+/* Convolution descriptor: the shape of one call. */
+typedef struct cc3d_desc {
+  int32_t n, c_in, c_out, h, w;
+  int32_t t_x;      /* |X|, frames of the current input, >= 1 */
+  int32_t t_cache;  /* |C|, cached frames ahead of X, >= 0 */
+  int32_t k_t, k_h, k_w;
+  int32_t s_t, s_h, s_w;
+  int32_t d_t, d_h, d_w;
+  int32_t p_h, p_w;  /* symmetric spatial zero padding */
+  int32_t p_base;    /* base causal left pad (d_t*(k_t-1) keeps T_o = |X|) */
+  int32_t groups;
+  int32_t has_bias;
+  int32_t dtype;     /* cc3d_dtype_t */
+} cc3d_desc_t;
+
+/* One temporal tap of the plan. */
+typedef struct cc3d_tap {
+  int32_t delta;          /* k*d_t - p_l */
+  int32_t o_lo, o_hi;     /* output frames that read this tap: [o_lo, o_hi) */
+  int32_t src_lo, src_hi; /* frames of Z they read: [o_lo+delta, o_hi+delta) */
+  int32_t active;         /* o_hi > o_lo */
+} cc3d_tap_t;
+
+typedef struct cc3d_plan_info {
+  int32_t t_z;            /* |Z| = |C| + |X| */
+  int32_t p_l;            /* p_base - |C| (negative: leading cache frames unused) */
+  int32_t t_out, h_out, w_out;
+  int32_t t_cache_out;    /* frames written to cache_out: min(p_base, |Z|) */
+  int32_t n_active_taps;
+  cc3d_tap_t taps[CC3D_MAX_KT];
+  double flops_nominal;   /* 2*N*T_o*H_o*W_o*C_out*C_in*k_t*k_h*k_w */
+  double flops_active;    /* the same counted over active (o, k) pairs only */
+  double bytes_conv;      /* algorithmic HBM bytes of the conv kernel: each
+                             read source frame once, W, b, the output */
+  double bytes_cache_out; /* bytes read + written by the cache-out writer */
+  int32_t kernel_id;      /* which kernel variant forward launches */
+  int32_t block_m, block_n; /* output pixels x output channels per workgroup */
+  int64_t grid;           /* workgroups of the conv kernel */
+  char kernel_name[64];
+} cc3d_plan_info_t;
+
+typedef struct cc3d_plan* cc3d_plan_t;
+
+typedef struct cc3d_counters {
+  uint64_t fast_path;     /* forward calls that launched */
+  uint64_t unsupported;   /* plans refused as unsupported */
+  uint64_t invalid;       /* plans or forwards refused as invalid */
+  uint64_t device_error;  /* launches the runtime rejected */
+} cc3d_counters_t;
+
+/*
+ * Validate a call's shape and build its plan (host only; no device call).
+ *   desc  shape of the call; it is copied.
+ *   out   receives the plan; set to NULL on error.
+ * Contract (the paper's lowering covers 5-D tensors with unit temporal
+ * stride and one group; every call it observed has k_t = 3):
+ *   CC3D_ERR_UNSUPPORTED when s_t != 1, groups != 1, k_t > CC3D_MAX_KT, or,
+ *   for bf16: spatial stride or dilation != 1, k_h != k_w, k_h not in {1, 3},
+ *   padding other than (k_h-1)/2, C_in not a multiple of 16, or one frame of
+ *   H*W*max(C_in, C_out) elements reaching 2^31.
+ *   CC3D_ERR_INVALID_ARG for a NULL pointer, a size < 1 (t_cache < 0), an
+ *   unknown dtype, or an empty output (T_o, H_o or W_o < 1).
+ */
+cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
+
+/* Intervals, sizes, work and launch geometry of a plan (host only). */
+cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_info_t* info);
+
+/* Release a plan; NULL is ignored. */
+void causal_conv3d_plan_destroy(cc3d_plan_t plan);
+
+/*
+ * Run the cached causal Conv3D of `plan` asynchronously on `stream`.
+ *   x          device pointer, [N][T_x][H][W][C_in]; required.
+ *   cache_in   device pointer, [N][T_cache][H][W][C_in]; required when
+ *              T_cache > 0, ignored when T_cache = 0.
+ *   w          device pointer, [C_out][k_t][k_h][k_w][C_in]; required.
+ *   b          device pointer, [C_out]; required iff has_bias.
+ *   out        device pointer, [N][T_o][H_o][W_o][C_out]; required.
+ *   cache_out  device pointer, [N][t_cache_out][H][W][C_in], or NULL when no
+ *              carry is wanted.
+ *   stream     a hipStream_t (NULL: the null stream).
+ * Frames of Z outside every tap's source interval are never read (e.g. the
+ * leading |C| - p_base cache frames when |C| > p_base).
+ * Returns CC3D_ERR_INVALID_ARG (nothing launched) for a NULL required
+ * pointer, a bf16 buffer not 16-byte aligned (fp32: 4-byte), `out`
+ * overlapping any other buffer, or `cache_out` overlapping x, cache_in, w or
+ * b (in a streaming loop ping-pong two cache buffers).  Returns
+ * CC3D_ERR_DEVICE if the runtime rejects a launch.
+ */
+cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, const void* cache_in,
+                                    const void* w, const void* b, void* out, void* cache_out,
+                                    void* stream);
+
+/* Static description of a status code. */
+const char* causal_conv3d_status_string(cc3d_status_t status);
+
+/* Snapshot the route counters into *out (may be NULL); reset them if reset != 0. */
+void causal_conv3d_counters(cc3d_counters_t* out, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CC3D_H */

@@ -77,3 +77,40 @@ def replay_chunks(n, cin, cout, h, w, frames, k=(3, 3, 3), *, dtype=torch.bfloat
     bt = draw((cout,), "normal", g, device, dtype, 0.1) if has_bias else None
     xs = [draw((n, f, h, w, cin), "normal", g, device, dtype, 1.0) for f in frames]
     return wt, bt, xs
+
+
+# Workload shapes (N = 1, channels last).  Each entry: C_in, C_out, H, W,
+# frames of X per call, cached frames, kernel, temporal dilation, base pad.
+def _sig(name, cin, cout, h, w, tx, tc, k=(3, 3, 3), dt=1, p_base=None, kind="normal", dtype="bf16"):
+    pad = (1, 1) if k[1] == 3 else (0, 0)
+    return dict(name=name, n=1, cin=cin, cout=cout, h=h, w=w, tx=tx, tc=tc, k=k, pad=pad, dt=dt,
+                p_base=dt * (k[0] - 1) if p_base is None else p_base, kind=kind, dtype=dtype)
+
+
+# Tiny fp32 case: call A (no cache, 4 frames), then call B (the last 2 frames
+# of A's input as cache, 4 new frames).
+TINY = _sig("tiny_fp32", 8, 8, 16, 16, 4, 0, kind="uniform", dtype="f32")
+# Latent-resolution decoder conv: 2 cached frames + 1 new latent frame.
+LATENT = _sig("latent_384", 384, 384, 90, 160, 1, 2)
+# Mid resolution: 4 new frames + 2 cached.
+MID_192 = _sig("mid_192", 192, 192, 360, 640, 4, 2)
+MID_384_192 = _sig("mid_384_192", 384, 192, 360, 640, 4, 2)
+# Full resolution: 4 new frames + 2 cached.
+FULL_96 = _sig("full_96", 96, 96, 720, 1280, 4, 2)
+HEAD_96_3 = _sig("head_96_3", 96, 3, 720, 1280, 4, 2)
+
+SINGLE_CALLS = [LATENT, MID_192, MID_384_192, FULL_96, HEAD_96_3]
+
+# Streaming decoder replay: five chunks, chunk 0 causally zero-padded (no
+# cache), later chunks carry the previous chunk's trailing p_base source
+# frames.  tx is frames per chunk.
+REPLAY_CHUNKS = 5
+REPLAY_STACK = [
+    _sig("latent_384", 384, 384, 90, 160, 1, 0),
+    _sig("temporal_384_768", 384, 768, 90, 160, 1, 0, k=(3, 1, 1)),
+    _sig("mid_192", 192, 192, 360, 640, 4, 0),
+    _sig("full_96", 96, 96, 720, 1280, 4, 0),
+    _sig("head_96_3", 96, 3, 720, 1280, 4, 0),
+]
+# Temporal dilation 2 variant of the mid-resolution conv (carry depth 4).
+REPLAY_DILATED = _sig("mid_192_dt2", 192, 192, 360, 640, 4, 0, dt=2)

@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Tolerances: fp32 outputs within 1e-4 max-abs; bf16 outputs within
+2e-2 x RMS(oracle) max-abs, the oracle computed in fp64 from the very same
+bf16-rounded inputs.  The cache carry is compared byte for byte.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (assert_bf16_close, assert_f32_close, gather, metrics, plan_for, run,
+                      sample_points)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np(t):
+    return None if t is None else t.detach().cpu()
+
+
+def _oracle(x, cache, w, b, *, k=(3, 3, 3), pad=(1, 1), dt=1, p_base=2, points=None):
+    return oracle.conv3d(_np(x), _np(cache), _np(w), _np(b), dilation=(dt, 1, 1), padding=pad,
+                         pbase=p_base, points=points)
+
+
+def test_tiny_fp32_calls_a_then_b(cuda_device):
+    s = synth.TINY
+    g = torch.Generator(device=DEV).manual_seed(synth.SEED_BASE)
+    w = synth.draw((8, 3, 3, 3, 8), "uniform", g, DEV, torch.float32, 1.0)
+    b = synth.draw((8,), "uniform", g, DEV, torch.float32, 0.1)
+    xa = synth.draw((1, 4, 16, 16, 8), "uniform", g, DEV, torch.float32, 1.0)
+    xb = synth.draw((1, 4, 16, 16, 8), "uniform", g, DEV, torch.float32, 1.0)
+    # call A: no cache, p_l = 2
+    ya, ca, plan_a = run(xa, None, w, b, p_base=s["p_base"])
+    assert plan_a.info["p_l"] == 2 and plan_a.info["t_out"] == 4
+    torch.cuda.synchronize()
+    assert torch.equal(ca, xa[:, 2:4])
+    assert_f32_close(ya, _oracle(xa, None, w, b), "call A")
+    # call B: A's last two frames as cache, p_l = 0
+    yb, cb, plan_b = run(xb, ca, w, b, p_base=s["p_base"])
+    assert plan_b.info["p_l"] == 0 and plan_b.info["t_out"] == 4
+    torch.cuda.synchronize()
+    assert torch.equal(cb, xb[:, 2:4])
+    assert_f32_close(yb, _oracle(xb, ca, w, b), "call B")
+    # the two calls together equal one call over all eight frames
+    whole = _oracle(torch.cat([xa, xb], 1), None, w, b)
+    assert_f32_close(torch.cat([ya, yb], 1), whole, "A+B vs one shot")
+
+
+# (C_in, C_out, H, W, T_x, T_cache, k, d_t, p_base, N, bias): shapes that hit
+# every kernel variant with ragged tiles in both spatial directions.
+SMALL = [
+    (32, 192, 19, 45, 3, 2, (3, 3, 3), 1, 2, 1, True),    # 192-channel tile, ragged rows/cols
+    (48, 96, 21, 37, 2, 1, (3, 3, 3), 1, 2, 1, True),     # 96-channel tile
+    (16, 40, 9, 33, 1, 0, (3, 3, 3), 1, 2, 1, True),      # 32-channel tile, partial second block
+    (32, 3, 10, 70, 4, 2, (3, 3, 3), 1, 2, 1, True),      # 3 output channels
+    (64, 384, 11, 40, 1, 2, (3, 3, 3), 1, 2, 1, True),    # two 192-channel blocks
+    (64, 192, 9, 50, 1, 2, (3, 1, 1), 1, 2, 1, True),     # temporal-only conv, 64-channel stages
+    (48, 20, 5, 40, 2, 1, (3, 1, 1), 1, 2, 1, True),      # temporal-only, 16-channel stages
+    (32, 768, 7, 33, 1, 1, (3, 1, 1), 1, 2, 1, True),     # temporal-only, 4 channel blocks
+    (32, 96, 12, 34, 2, 2, (3, 3, 3), 1, 2, 2, True),     # batch of 2
+    (32, 192, 10, 40, 4, 4, (3, 3, 3), 2, 4, 1, True),    # temporal dilation 2, 4-frame carry
+    (32, 192, 10, 40, 4, 2, (3, 3, 3), 2, 4, 1, True),    # d_t = 2 behind a 2-frame cache
+    (32, 96, 8, 32, 3, 3, (3, 3, 3), 1, 2, 1, True),      # |C| > p_base: leading frame unused
+    (32, 96, 8, 32, 3, 1, (2, 3, 3), 1, 1, 1, True),      # k_t = 2
+    (32, 96, 8, 32, 3, 0, (1, 3, 3), 1, 0, 1, True),      # k_t = 1
+    (32, 192, 16, 64, 2, 2, (3, 3, 3), 1, 2, 1, False),   # no bias
+    (16, 32, 1, 1, 1, 0, (3, 3, 3), 1, 2, 1, True),       # 1x1 frame: halo all padding
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(i) for i in range(len(SMALL))])
+def test_bf16_small_shapes_full_compare(cuda_device, case):
+    cin, cout, h, w_, tx, tc, k, dt, p_base, n, bias = case
+    pad = (1, 1) if k[1] == 3 else (0, 0)
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
+                                   seed=synth.SEED_BASE + 100 + SMALL.index(case), has_bias=bias)
+    y, co, plan = run(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base)
+    torch.cuda.synchronize()
+    ref = _oracle(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base)
+    assert tuple(y.shape) == ref.shape
+    assert_bf16_close(y, ref, plan.info["kernel_name"])
+    z = x if c is None else torch.cat([c, x], 1)
+    keep = min(p_base, z.shape[1])
+    assert torch.equal(co, z[:, z.shape[1] - keep:])
+
+
+def test_latent_config_full_compare(cuda_device):
+    s = synth.LATENT
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
+                                   device=DEV, seed=synth.SEED_BASE + 1)
+    y, co, plan = run(x, c, w, b)
+    torch.cuda.synchronize()
+    ref = _oracle(x, c, w, b)
+    m = assert_bf16_close(y, ref, "latent")
+    assert m["cos"] > 0.9999
+    assert torch.equal(co, torch.cat([c, x], 1)[:, 1:])
+
+
+@pytest.mark.parametrize("sig", synth.SINGLE_CALLS[1:], ids=[s["name"] for s in synth.SINGLE_CALLS[1:]])
+def test_full_size_signatures_sampled(cuda_device, sig):
+    s = sig
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
+                                   device=DEV, seed=synth.SEED_BASE + 2 + synth.SINGLE_CALLS.index(s))
+    y, co, plan = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    torch.cuda.synchronize()
+    # properties over the whole output
+    assert bool(torch.isfinite(y).all())
+    assert torch.equal(co, x[:, 2:4])
+    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 600,
+                        seed=synth.SINGLE_CALLS.index(s), tile_h=max(plan.info["block_m"] // 32, 1))
+    ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], points=pts)
+    assert_bf16_close(gather(y, pts), ref, s["name"])
+
+
+def _replay(sig, frames, seed, device, h=None, w=None):
+    h = sig["h"] if h is None else h
+    w = sig["w"] if w is None else w
+    wt, bt, xs = synth.replay_chunks(1, sig["cin"], sig["cout"], h, w, frames, sig["k"], device=device, seed=seed)
+    outs, cache = [], None
+    for xc in xs:
+        y, cache_next, _ = run(xc, cache, wt, bt, k=sig["k"], pad=sig["pad"], dt=sig["dt"], p_base=sig["p_base"])
+        outs.append(y)
+        cache = cache_next
+    return wt, bt, xs, outs
+
+
+@pytest.mark.parametrize("sig", synth.REPLAY_STACK + [synth.REPLAY_DILATED],
+                         ids=[s["name"] for s in synth.REPLAY_STACK + [synth.REPLAY_DILATED]])
+def test_streaming_replay_reduced_spatial_full_compare(cuda_device, sig):
+    """Five chunks with cache carry at a reduced spatial size, every output
+    against one oracle call over the whole concatenated sequence."""
+    frames = [sig["tx"]] * synth.REPLAY_CHUNKS
+    wt, bt, xs, outs = _replay(sig, frames, synth.SEED_BASE + 40, DEV, h=13, w=41)
+    torch.cuda.synchronize()
+    whole = oracle.conv3d(torch.cat(xs, 1).cpu(), None, wt.cpu(), bt.cpu(), dilation=(sig["dt"], 1, 1),
+                          padding=sig["pad"], pbase=sig["p_base"])
+    assert_bf16_close(torch.cat(outs, 1), whole, sig["name"])
+
+
+@pytest.mark.parametrize("sig", synth.REPLAY_STACK + [synth.REPLAY_DILATED],
+                         ids=[s["name"] for s in synth.REPLAY_STACK + [synth.REPLAY_DILATED]])
+def test_streaming_replay_full_size_sampled(cuda_device, sig):
+    """The full-size five-chunk replay against the one-shot oracle over the
+    concatenated sequence, on sampled outputs of every chunk."""
+    frames = [sig["tx"]] * synth.REPLAY_CHUNKS
+    wt, bt, xs, outs = _replay(sig, frames, synth.SEED_BASE + 4, DEV)
+    torch.cuda.synchronize()
+    whole_x = torch.cat(xs, 1)
+    y = torch.cat(outs, 1)
+    assert bool(torch.isfinite(y).all())
+    pts = sample_points(1, y.shape[1], y.shape[2], y.shape[3], 400, seed=7)
+    ref = oracle.conv3d(whole_x.cpu(), None, wt.cpu(), bt.cpu(), dilation=(sig["dt"], 1, 1),
+                        padding=sig["pad"], pbase=sig["p_base"], points=pts)
+    assert_bf16_close(gather(y, pts), ref, sig["name"])
+
+
+def test_unread_frames_and_guard_bands_are_never_touched(cuda_device):
+    """Frames of Z outside every tap's source interval, and bytes just outside
+    each buffer, hold NaN; the output must be finite and bit-identical to the
+    run where they hold zeros, and guard bytes around the output must stay."""
+    cin, cout, h, w_ = 32, 96, 12, 40
+    # d_t = 2 behind a 4-frame cache with one new frame: taps read Z[0], Z[2], Z[4];
+    # Z[1] and Z[3] (cache frames 1 and 3) are never read.
+    x, c, w, b = synth.conv_inputs(1, cin, cout, h, w_, 1, 4, device=DEV, seed=synth.SEED_BASE + 60)
+    guard = 4096
+    def embed(t, fill):
+        buf = torch.full((t.numel() + 2 * guard,), fill, dtype=t.dtype, device=DEV)
+        v = buf[guard:guard + t.numel()].view(t.shape)
+        v.copy_(t)
+        return buf, v
+    results = []
+    for fill in (0.0, float("nan")):
+        cc = c.clone()
+        cc[:, 1] = fill
+        cc[:, 3] = fill
+        _, xv = embed(x, fill)
+        _, cv = embed(cc, fill)
+        _, wv = embed(w, fill)
+        plan = plan_for(xv, 4, wv, k=(3, 3, 3), pad=(1, 1), dt=2, p_base=4)
+        obuf = torch.full((int(np.prod(plan.shapes()["out"])) + 2 * guard,), 7.0, dtype=x.dtype, device=DEV)
+        ov = obuf[guard:guard + int(np.prod(plan.shapes()["out"]))].view(plan.shapes()["out"])
+        import causal_conv3d_video_amd as cc3d
+        cc3d.causal_conv3d_forward(plan, xv, cv, wv, b, ov, None)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(ov).all())
+        assert bool((obuf[:guard] == 7.0).all()) and bool((obuf[-guard:] == 7.0).all())
+        results.append(ov.clone())
+    assert torch.equal(results[0], results[1])
+    ref = _oracle(x, c, w, b, dt=2, p_base=4)
+    assert_bf16_close(results[0], ref, "poisoned")
+
+
+def test_repeated_runs_are_bitwise_identical(cuda_device):
+    s = synth.MID_192
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], 64, 128, 4, 2, device=DEV, seed=synth.SEED_BASE + 70)
+    y1, _, _ = run(x, c, w, b)
+    y2, _, _ = run(x, c, w, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_epilogue_rounds_to_nearest_even(cuda_device):
+    """With a single unit source value the fp32 sum is exactly w + b, so the
+    bf16 output must equal that exact value rounded to nearest even."""
+    cin, cout, h, w_ = 16, 192, 8, 32
+    g = torch.Generator(device=DEV).manual_seed(5)
+    w = torch.randn((cout, 3, 3, 3, cin), generator=g, device=DEV).to(torch.bfloat16)
+    b = (torch.randn((cout,), generator=g, device=DEV) * 3).to(torch.bfloat16)
+    x = torch.zeros((1, 1, h, w_, cin), dtype=torch.bfloat16, device=DEV)
+    c = torch.zeros((1, 2, h, w_, cin), dtype=torch.bfloat16, device=DEV)
+    c[0, 1, 3, 5, 7] = 1.0
+    y, _, _ = run(x, c, w, b)
+    torch.cuda.synchronize()
+    ref = _oracle(x, c, w, b)
+    ref_bf16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16)  # exact in fp32
+    assert torch.equal(y.cpu().view(torch.int16), ref_bf16.view(torch.int16))
+
+
+def test_counters_count_fast_path(cuda_device):
+    import causal_conv3d_video_amd as cc3d
+    x, c, w, b = synth.conv_inputs(1, 16, 32, 8, 32, 2, 2, device=DEV, seed=1)
+    cc3d.causal_conv3d_counters(reset=True)
+    for _ in range(3):
+        run(x, c, w, b)
+    torch.cuda.synchronize()
+    cnt = cc3d.causal_conv3d_counters()
+    assert cnt["fast_path"] == 3 and cnt["device_error"] == 0 and cnt["invalid"] == 0

@@ -1,0 +1,227 @@
+"""Host-side tests of the C ABI: the library loads and exports what
+include/cc3d.h declares, the planner's tap intervals match a brute-force
+enumeration of the lowering's source-time rule ("Cache-Aware Conv3D Lowering
+Across Embedded World-Model Decoders", lowering section), and the contract
+checks return the documented status codes.  No GPU is used: planning is
+host-only."""
+import ctypes
+import itertools
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _build_if_missing():
+    lib = os.path.join(ROOT, "causal_conv3d_video_amd", "libcc3d.so")
+    if not os.path.exists(lib):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("cc3d_build", os.path.join(ROOT, "causal_conv3d_video_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    return lib
+
+
+LIB = _build_if_missing()
+
+import causal_conv3d_video_amd as cc3d  # noqa: E402
+import oracle  # noqa: E402
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "cc3d.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(causal_conv3d_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert declared, "no declarations found"
+    assert set(declared) == set(cc3d.EXPORTED_SYMBOLS)
+    lib = ctypes.CDLL(LIB)
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)", nm))
+    for name in declared:
+        assert name in exported, name
+
+
+def test_library_has_gfx950_code_object():
+    # the embedded HIP fat binary names its one offload target
+    data = open(LIB, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def _desc(**kw):
+    base = dict(n=1, c_in=16, c_out=16, h=8, w=8, t_x=4, t_cache=0, k=(3, 3, 3), stride=(1, 1, 1),
+                dilation=(1, 1, 1), padding=(1, 1), p_base=2, dtype=torch.bfloat16)
+    base.update(kw)
+    return cc3d.make_desc(**base)
+
+
+def _brute_intervals(t_x, t_c, k_t, d_t, p_base, t_out):
+    """Active (o, k) pairs straight from the rule: tap k of output o reads
+    source frame o + k*d_t - (p_base - |C|), valid iff inside [0, |Z|)."""
+    tz = t_x + t_c
+    pl = p_base - t_c
+    res = []
+    for k in range(k_t):
+        outs = [o for o in range(t_out) if 0 <= o + k * d_t - pl < tz]
+        res.append(outs)
+    return res
+
+
+def test_tap_intervals_match_brute_force_enumeration():
+    n_checked = 0
+    for k_t, d_t in itertools.product((1, 2, 3), (1, 2, 3)):
+        for p_base in range(0, d_t * (k_t - 1) + 2):
+            for t_x in range(1, 9):
+                for t_c in range(0, p_base + 2):
+                    shp = oracle.out_shape(t_x, t_c, 8, 8, kt=k_t, kh=3, kw=3, dt=d_t, pbase=p_base)
+                    desc = _desc(t_x=t_x, t_cache=t_c, k=(k_t, 3, 3), dilation=(d_t, 1, 1), p_base=p_base)
+                    if shp is None:
+                        with pytest.raises(cc3d.CC3DError) as e:
+                            cc3d.causal_conv3d_plan(desc)
+                        assert e.value.status == cc3d.CC3D_ERR_INVALID_ARG
+                        continue
+                    plan = cc3d.causal_conv3d_plan(desc)
+                    info = plan.info
+                    assert (info["t_out"], info["h_out"], info["w_out"]) == shp
+                    assert info["t_z"] == t_x + t_c
+                    assert info["p_l"] == p_base - t_c
+                    assert info["t_cache_out"] == min(p_base, t_x + t_c)
+                    brute = _brute_intervals(t_x, t_c, k_t, d_t, p_base, info["t_out"])
+                    active = 0
+                    for k, tap in enumerate(info["taps"]):
+                        outs = brute[k]
+                        assert tap["delta"] == k * d_t - (p_base - t_c)
+                        # I3: the active outputs form exactly [o_lo, o_hi)
+                        assert list(range(tap["o_lo"], tap["o_hi"])) == outs
+                        assert bool(tap["active"]) == bool(outs)
+                        # I1: source interval has the output interval's length
+                        assert tap["src_hi"] - tap["src_lo"] == tap["o_hi"] - tap["o_lo"]
+                        if outs:
+                            active += 1
+                            # I2: source interval inside Z
+                            assert 0 <= tap["src_lo"] < tap["src_hi"] <= t_x + t_c
+                            assert tap["src_lo"] == outs[0] + tap["delta"]
+                    assert info["n_active_taps"] == active
+                    if p_base == d_t * (k_t - 1):
+                        # I4: output length equals input length
+                        assert info["t_out"] == t_x
+                        # I5: the last tap reads exactly X
+                        last = info["taps"][k_t - 1]
+                        assert (last["o_lo"], last["o_hi"]) == (0, t_x)
+                        assert (last["src_lo"], last["src_hi"]) == (t_c, t_c + t_x)
+                    n_checked += 1
+    assert n_checked > 500
+
+
+def test_tiny_workload_intervals():
+    # No cache, 4 frames, base pad 2: p_l = 2, four output frames; taps
+    # (delta, o_lo, o_hi) = (-2, 2, 4), (-1, 1, 4), (0, 0, 4).
+    a = cc3d.causal_conv3d_plan(_desc(c_in=8, c_out=8, t_x=4, t_cache=0, dtype=torch.float32)).info
+    assert a["p_l"] == 2 and a["t_out"] == 4
+    assert [(t["delta"], t["o_lo"], t["o_hi"]) for t in a["taps"]] == [(-2, 2, 4), (-1, 1, 4), (0, 0, 4)]
+    # Two cached frames ahead of four new ones: p_l = 0, every tap on every frame.
+    b = cc3d.causal_conv3d_plan(_desc(c_in=8, c_out=8, t_x=4, t_cache=2, dtype=torch.float32)).info
+    assert b["p_l"] == 0 and b["t_out"] == 4
+    assert [(t["delta"], t["o_lo"], t["o_hi"]) for t in b["taps"]] == [(0, 0, 4), (1, 0, 4), (2, 0, 4)]
+    # One latent frame, no cache: only the last tap is active.
+    c = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=0)).info
+    assert [t["active"] for t in c["taps"]] == [0, 0, 1]
+    # One latent frame behind a one-frame cache: taps 1 and 2.
+    d = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=1)).info
+    assert [t["active"] for t in d["taps"]] == [0, 1, 1] and d["p_l"] == 1
+
+
+def test_flops_and_bytes():
+    p = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2)).info
+    nominal = 2 * 1 * 4 * 360 * 640 * 192 * 192 * 27
+    assert p["flops_nominal"] == nominal
+    assert p["flops_active"] == nominal
+    frame = 360 * 640 * 192 * 2
+    assert p["bytes_conv"] == 6 * frame + 192 * 27 * 192 * 2 + 192 * 2 + 4 * frame
+    assert p["bytes_cache_out"] == 2 * 2 * frame
+    q = cc3d.causal_conv3d_plan(_desc(c_in=16, c_out=16, t_x=1, t_cache=0)).info
+    assert q["flops_active"] == q["flops_nominal"] / 3
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(stride=(2, 1, 1)), cc3d.CC3D_ERR_UNSUPPORTED),          # temporal stride 2
+    (dict(groups=2), cc3d.CC3D_ERR_UNSUPPORTED),
+    (dict(k=(9, 3, 3), p_base=8), cc3d.CC3D_ERR_UNSUPPORTED),      # k_t above the maximum
+    (dict(k=(3, 5, 5), padding=(2, 2)), cc3d.CC3D_ERR_UNSUPPORTED),  # bf16 spatial envelope
+    (dict(stride=(1, 2, 2)), cc3d.CC3D_ERR_UNSUPPORTED),
+    (dict(padding=(0, 0)), cc3d.CC3D_ERR_UNSUPPORTED),
+    (dict(c_in=24), cc3d.CC3D_ERR_UNSUPPORTED),                    # bf16 needs C_in % 16 == 0
+    (dict(n=0), cc3d.CC3D_ERR_INVALID_ARG),
+    (dict(t_x=0), cc3d.CC3D_ERR_INVALID_ARG),
+    (dict(t_cache=-1), cc3d.CC3D_ERR_INVALID_ARG),
+    (dict(t_x=1, p_base=0), cc3d.CC3D_ERR_INVALID_ARG),            # empty output
+    (dict(h=1, padding=(0, 0), k=(3, 3, 3), dtype=torch.float32), cc3d.CC3D_ERR_INVALID_ARG),
+])
+def test_refusals_and_counters(kw, status):
+    cc3d.causal_conv3d_counters(reset=True)
+    with pytest.raises(cc3d.CC3DError) as e:
+        cc3d.causal_conv3d_plan(_desc(**kw))
+    assert e.value.status == status
+    c = cc3d.causal_conv3d_counters()
+    key = "unsupported" if status == cc3d.CC3D_ERR_UNSUPPORTED else "invalid"
+    assert c[key] == 1 and c["fast_path"] == 0
+
+
+def test_fp32_accepts_general_spatial_parameters():
+    p = cc3d.causal_conv3d_plan(_desc(c_in=3, c_out=5, k=(3, 5, 5), stride=(1, 2, 2), dilation=(2, 2, 1),
+                                      padding=(2, 1), p_base=4, dtype=torch.float32))
+    assert p.info["kernel_name"] == "f32_direct"
+
+
+def test_forward_refuses_bad_pointers_without_launching():
+    lib = ctypes.CDLL(LIB)
+    lib.causal_conv3d_forward.argtypes = [ctypes.c_void_p] * 8
+    lib.causal_conv3d_forward.restype = ctypes.c_int
+    plan = cc3d.causal_conv3d_plan(_desc(t_cache=2))
+    cc3d.causal_conv3d_counters(reset=True)
+    base = 1 << 40  # never dereferenced: every call below is refused before any launch
+    mb = 1 << 20
+    x, c, w, b, out, co = base, base + mb, base + 2 * mb, base + 3 * mb, base + 4 * mb, base + 5 * mb
+    f = lib.causal_conv3d_forward
+    assert f(None, x, c, w, b, out, co, None) == cc3d.CC3D_ERR_INVALID_ARG      # no plan
+    assert f(plan.handle, None, c, w, b, out, co, None) == cc3d.CC3D_ERR_INVALID_ARG  # no x
+    assert f(plan.handle, x, None, w, b, out, co, None) == cc3d.CC3D_ERR_INVALID_ARG  # cache needed
+    assert f(plan.handle, x, c, w, None, out, co, None) == cc3d.CC3D_ERR_INVALID_ARG  # bias needed
+    assert f(plan.handle, x + 2, c, w, b, out, co, None) == cc3d.CC3D_ERR_INVALID_ARG  # misaligned
+    assert f(plan.handle, x, c, w, b, x + 16, co, None) == cc3d.CC3D_ERR_INVALID_ARG  # out overlaps x
+    assert f(plan.handle, x, c, w, b, out, c, None) == cc3d.CC3D_ERR_INVALID_ARG  # cache_out aliases cache_in
+    assert f(plan.handle, x, c, w, b, out, out, None) == cc3d.CC3D_ERR_INVALID_ARG  # cache_out aliases out
+    cnt = cc3d.causal_conv3d_counters()
+    assert cnt["invalid"] == 8 and cnt["fast_path"] == 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert cc3d.causal_conv3d_status_string(s)
+    assert "unknown" in cc3d.causal_conv3d_status_string(99)
+
+
+def test_workload_signatures_get_mfma_kernels():
+    sigs = [
+        (384, 384, 90, 160, 1, 2, (3, 3, 3)),
+        (384, 768, 90, 160, 1, 2, (3, 1, 1)),
+        (192, 192, 360, 640, 4, 2, (3, 3, 3)),
+        (384, 192, 360, 640, 4, 2, (3, 3, 3)),
+        (96, 96, 720, 1280, 4, 2, (3, 3, 3)),
+        (96, 3, 720, 1280, 4, 2, (3, 3, 3)),
+    ]
+    for cin, cout, h, w, tx, tc, k in sigs:
+        pad = (1, 1) if k[1] == 3 else (0, 0)
+        p = cc3d.causal_conv3d_plan(_desc(c_in=cin, c_out=cout, h=h, w=w, t_x=tx, t_cache=tc, k=k, padding=pad))
+        assert p.info["kernel_name"].startswith("bf16_"), p.info["kernel_name"]
+        assert p.info["grid"] > 0
