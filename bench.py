@@ -1,0 +1,290 @@
+"""Benchmark of the cached causal Conv3D on one MI355X.
+
+One step is the streaming decoder conv replay: five chunks, each running the
+signature stack 384->384 (3,3,3) at 90x160 on 1 frame, 384->768 (3,1,1) at
+90x160 on 1 frame, 192->192 (3,3,3) at 360x640 on 4 frames, 96->96 (3,3,3)
+at 720x1280 on 4 frames and 96->3 (3,3,3) at 720x1280 on 4 frames, plus a
+temporal-dilation-2 192->192 conv at 360x640 on 4 frames.  Chunk 0 is
+causally zero-padded; every later chunk carries the previous chunk's trailing
+source frames through cache_out -> cache_in.  Every call launches the conv
+kernel and the cache-out writer.  All inputs are seeded synthetic tensors
+already resident in HBM when timing starts.
+
+Prints one JSON line: whole-step bf16 TFLOP/s (active-tap FLOPs / time),
+per-signature kernel timings, the roofline of the dominant kernel (its
+average launch time measured with HIP events on its stream) and the CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "causal Conv3D BF16 TFLOP/s and % MFMA peak; 17-frame conv-replay ms"
+KERNEL_SRC = os.path.join(ROOT, "causal_conv3d_video_amd", "csrc", "cc3d_forward.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--kernel-launches", type=int, default=20,
+                   help="launches per signature for the per-kernel timing")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--only", default=None,
+                   help="profiling aid: run only this signature's conv kernel --kernel-launches times")
+    return p.parse_args()
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    with open(KERNEL_SRC, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def build_workload(device):
+    import torch
+
+    import causal_conv3d_video_amd as cc3d
+    import synth
+
+    sigs = synth.REPLAY_STACK + [synth.REPLAY_DILATED]
+    work = []
+    for si, s in enumerate(sigs):
+        frames = [s["tx"]] * synth.REPLAY_CHUNKS
+        w, b, xs = synth.replay_chunks(1, s["cin"], s["cout"], s["h"], s["w"], frames, s["k"],
+                                       device=device, seed=synth.SEED_BASE + 4 + 17 * si)
+        plans, outs = [], []
+        tc = 0
+        for c in range(synth.REPLAY_CHUNKS):
+            desc = cc3d.make_desc(1, s["cin"], s["cout"], s["h"], s["w"], frames[c], tc, k=s["k"],
+                                  dilation=(s["dt"], 1, 1), padding=s["pad"], p_base=s["p_base"])
+            plan = cc3d.causal_conv3d_plan(desc)
+            plans.append(plan)
+            outs.append(torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device))
+            tc = plan.info["t_cache_out"]
+        cache_shape = plans[-1].shapes()["cache_out"]
+        caches = [torch.empty(cache_shape, dtype=torch.bfloat16, device=device) for _ in range(2)]
+        work.append(dict(sig=s, w=w, b=b, xs=xs, plans=plans, outs=outs, caches=caches))
+    return work
+
+
+def run_step(work, stream):
+    import causal_conv3d_video_amd as cc3d
+
+    chunks = len(work[0]["xs"])
+    for c in range(chunks):
+        for wk in work:
+            plan = wk["plans"][c]
+            cin_buf = None if c == 0 else wk["caches"][(c - 1) % 2][:, :plan.desc.t_cache]
+            cout_buf = wk["caches"][c % 2][:, :plan.info["t_cache_out"]]
+            cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c],
+                                       cout_buf, stream)
+
+
+def time_kernels(work, launches, stream):
+    """Average conv-kernel launch time per signature at the steady-state chunk
+    (cache present), HIP events on the launch stream, no cache-out writer."""
+    import torch
+
+    import causal_conv3d_video_amd as cc3d
+
+    res = {}
+    for wk in work:
+        c = 2
+        plan = wk["plans"][c]
+        cin_buf = wk["caches"][(c - 1) % 2][:, :plan.desc.t_cache]
+        for _ in range(3):
+            cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c], None, stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c], None, stream)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        info = plan.info
+        res[wk["sig"]["name"]] = dict(
+            kernel=info["kernel_name"], us_per_launch=ms * 1e3,
+            tflops=info["flops_active"] / (ms * 1e-3) / 1e12,
+            frac_mfma_peak=info["flops_active"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
+            frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            flops=info["flops_active"], bytes=info["bytes_conv"], grid=info["grid"])
+    return res
+
+
+def cpu_baseline(work, target_seconds):
+    """The fp64 CPU oracle on a bounded sample of the same workload: random
+    output pixels (all output channels) of the steady-state chunk of every
+    signature, over that chunk's own [cache; x]."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(11)
+    per_sig = []
+    for wk in work:
+        s = wk["sig"]
+        c = 2
+        plan = wk["plans"][c]
+        tc = plan.desc.t_cache
+        # the steady-state chunk's cache is the trailing frames of chunks 0..1
+        prev = torch.cat([wk["xs"][0], wk["xs"][1]], 1)[:, -tc:].cpu()
+        x = wk["xs"][c].cpu()
+        info = plan.info
+        per_px = info["flops_active"] / (info["t_out"] * info["h_out"] * info["w_out"])
+        per_sig.append((s, plan, prev, x, per_px))
+    # calibrate the rate on a small sample, then size the timed sample
+    s0, p0, c0, x0, f0 = per_sig[2]
+    pts = np.stack([np.zeros(64, np.int64), rng.integers(0, p0.info["t_out"], 64),
+                    rng.integers(0, p0.info["h_out"], 64), rng.integers(0, p0.info["w_out"], 64)], 1)
+    t = time.perf_counter()
+    oracle.conv3d(x0, c0, work[2]["w"].cpu(), work[2]["b"].cpu(), dilation=(s0["dt"], 1, 1),
+                  padding=s0["pad"], pbase=s0["p_base"], points=pts, nthreads=threads)
+    rate = 64 * f0 / max(time.perf_counter() - t, 1e-6)
+    budget = rate * target_seconds / len(per_sig)   # flops per signature
+    total_flops, total_s, desc = 0.0, 0.0, []
+    for wk, (s, plan, prev, x, per_px) in zip(work, per_sig):
+        npx = int(max(16, min(budget / per_px, plan.info["t_out"] * plan.info["h_out"] * plan.info["w_out"])))
+        pts = np.stack([np.zeros(npx, np.int64), rng.integers(0, plan.info["t_out"], npx),
+                        rng.integers(0, plan.info["h_out"], npx), rng.integers(0, plan.info["w_out"], npx)], 1)
+        w, b = wk["w"].cpu(), wk["b"].cpu()
+        t = time.perf_counter()
+        oracle.conv3d(x, prev, w, b, dilation=(s["dt"], 1, 1), padding=s["pad"], pbase=s["p_base"],
+                      points=pts, nthreads=threads)
+        total_s += time.perf_counter() - t
+        total_flops += npx * per_px
+        desc.append("%s:%dpx" % (s["name"], npx))
+    return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle, random output pixels (all channels) of chunk 2 of each signature: "
+                      + ", ".join(desc) + "; %.1f s, %.1f GFLOP" % (total_s, total_flops / 1e9)}
+
+
+def traffic_for(kernel_name, launches_flops):
+    """HBM bytes per launch from the committed rocprofv3 counter record, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != _source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel_name)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import causal_conv3d_video_amd as cc3d  # noqa: F401  (fails loudly if the library is missing)
+
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    work = build_workload(device)
+    torch.cuda.synchronize()
+
+    if args.only:
+        wk = next(w for w in work if w["sig"]["name"] == args.only)
+        plan = wk["plans"][2]
+        cin_buf = wk["caches"][1][:, :plan.desc.t_cache]
+        for _ in range(args.kernel_launches):
+            cc3d.causal_conv3d_forward(plan, wk["xs"][2], cin_buf, wk["w"], wk["b"], wk["outs"][2], None, stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "kernel": plan.info["kernel_name"], "launches": args.kernel_launches}))
+        return
+
+    for _ in range(args.warmup):
+        run_step(work, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run_step(work, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    flops_step = sum(p.info["flops_active"] for wk in work for p in wk["plans"])
+    flops_nominal = sum(p.info["flops_nominal"] for wk in work for p in wk["plans"])
+    tflops = flops_step / (ms * 1e-3) / 1e12
+
+    kern = time_kernels(work, args.kernel_launches, stream)
+    # time share of each signature in a step: 5 chunk calls at the steady-state rate
+    share = {name: k["us_per_launch"] * len(work[0]["plans"]) for name, k in kern.items()}
+    dom = max(share, key=share.get)
+    kd = kern[dom]
+    mfma_bound = kd["flops"] / kd["bytes"] > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = traffic_for(kd["kernel"], kd["flops"])
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": kd["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": kd["frac_mfma_peak"], "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kd["frac_hbm_peak"], "traffic": traffic}
+    roof.update({"kernel": kd["kernel"], "signature": dom, "us_per_launch": kd["us_per_launch"],
+                 "algorithmic_flops_per_launch": kd["flops"], "algorithmic_bytes_per_launch": kd["bytes"]})
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(work, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, N(0,0.01) bias)",
+        "config": {
+            "workload": "streaming 17-frame decoder conv replay: 5 chunks x [384->384 (3,3,3) 90x160 1f; "
+                        "384->768 (3,1,1) 90x160 1f; 192->192 (3,3,3) 360x640 4f; 96->96 (3,3,3) 720x1280 4f; "
+                        "96->3 (3,3,3) 720x1280 4f] + 192->192 (3,3,3) d_t=2 360x640 4f; chunk 0 zero-padded, "
+                        "cache carry thereafter; 30 calls per step incl. cache-out writers",
+            "batch": 1, "calls_per_step": sum(len(wk["plans"]) for wk in work),
+        },
+        "mfma_peak_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+        "flops_active_per_step": flops_step,
+        "flops_nominal_per_step": flops_nominal,
+        "wall_s_timed": wall,
+        "signatures": kern,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+        "kernel_source_sha256": _source_hash(),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -72,7 +72,7 @@ class Counters(ctypes.Structure):
 def _load():
     if not os.path.exists(library_path):
         raise ImportError(
-            "libcc3d.so is not built (%s); run `python -m causal_conv3d_video_amd.build`" % library_path)
+            "libcc3d.so is not built (%s); run `python causal_conv3d_video_amd/build.py`" % library_path)
     lib = ctypes.CDLL(library_path)
     vp = ctypes.c_void_p
     lib.causal_conv3d_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(vp)]

@@ -2,7 +2,8 @@
 
 Compiles the planner (host C++) with g++ and the kernels and launcher with
 hipcc --offload-arch=gfx950, then links one shared library next to this file.
-Run as ``python -m causal_conv3d_video_amd.build``.
+Run as ``python causal_conv3d_video_amd/build.py`` (not with -m: importing
+the package loads the library this script builds).
 """
 import os
 import subprocess

@@ -56,18 +56,18 @@ struct ConvArgs {
 // XCD i % 8).  Renumber so that each XCD receives one contiguous range of
 // logical tiles: neighbouring patches and the output frames that share source
 // frames then meet in the same L2.
-__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+__device__ __forceinline__ __attribute__((unused)) int xcd_remap(int bid, int grid) {
   const int q = grid >> 3, r = grid & 7;
   const int xcd = bid & 7, j = bid >> 3;
   return xcd * q + min(xcd, r) + j;
 }
 
-__device__ __forceinline__ float bf16_to_f32(unsigned short h) {
+__device__ __forceinline__ __attribute__((unused)) float bf16_to_f32(unsigned short h) {
   return __uint_as_float(static_cast<unsigned>(h) << 16);
 }
 
 // Round to nearest, ties to even (hardware conversion on gfx950).
-__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+__device__ __forceinline__ __attribute__((unused)) unsigned short f32_to_bf16(float f) {
   return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
 
@@ -79,25 +79,35 @@ __device__ __forceinline__ int tap_delta(const ConvArgs& a, int k) {
   return d;
 }
 
+// XOR swizzle of the 16-byte pieces of one LDS row (a halo pixel, or one
+// output channel's weights): with PZ pieces per row, 8 consecutive rows read
+// at the same piece land in 8 distinct 16-byte slots of a 256-byte window,
+// which keeps the 16-byte operand reads of 8 consecutive lanes conflict-free.
+template <int PZ>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (PZ == 4) return (row >> 2) & 1;
+  else if constexpr (PZ == 8) return (row >> 1) & 3;
+  else return 0;
+}
+
 template <int BN, int TH, int WM, int WN, int KS, int CB>
 __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int TW = 32;                       // patch width = MFMA pixel block
   constexpr int PAD = (KS - 1) / 2;
   constexpr int HP = TH + KS - 1, WP = TW + KS - 1, S = KS * KS;
   constexpr int PZ = CB / 8;                   // 16-byte pieces per pixel per stage
-  constexpr int ZSTR = CB * 2 + 16;            // LDS bytes per halo pixel
-  constexpr int WSTR = S * CB * 2 + 16;        // LDS bytes per output channel
-  constexpr int ZBYTES = HP * WP * ZSTR;
-  constexpr int STAGE = ZBYTES + BN * WSTR;
   constexpr int ZCH = HP * WP * PZ, WCH = BN * S * PZ;
   constexpr int ZIT = (ZCH + 255) / 256, WIT = (WCH + 255) / 256;
+  constexpr int ZSLOTS = ZIT * 256, WSLOTS = WIT * 256;  // 16-byte LDS slots
+  constexpr int STAGE = ZSLOTS + WSLOTS;
   constexpr int RW = TH / WM;                  // patch rows per wave
   constexpr int CW = BN / (32 * WN);           // 32-channel blocks per wave
   static_assert(WM * WN == 4 && TH % WM == 0 && BN % (32 * WN) == 0, "wave tiling");
-  static_assert(CB % 16 == 0, "stage channels");
-  static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(PZ == 2 || PZ == 4 || PZ == 8, "stage channels");
+  static_assert(2 * STAGE * 16 <= 160 * 1024, "LDS budget");
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+  __shared__ uint4 lds[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -130,9 +140,41 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   const unsigned short* __restrict__ ws = static_cast<const unsigned short*>(a.w);
   const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
 
-  uint4 zreg[ZIT], wreg[WIT];
+  // Stage-invariant part of every slot this thread fills: the byte offset
+  // within a frame (halo) or within the weight tensor at tap 0, channel 0.
+  // Slots that must hold zeros (spatial padding, channels beyond C_out) get
+  // an offset past the buffer's record count: the range check of the buffer
+  // load then writes zeros into LDS.  Slot id = it*256 + tid.
+  constexpr int OOB = int(0x80000000u);
+  int zoff[ZIT], woff[WIT];
+#pragma unroll
+  for (int it = 0; it < ZIT; ++it) {
+    const int id = tid + 256 * it;
+    int off = OOB;
+    if (id < ZCH) {
+      const int pix = id / PZ;
+      const int q = (id % PZ) ^ swz<PZ>(pix);
+      const int y = y0 - PAD + pix / WP, x = x0 - PAD + pix % WP;
+      if (y >= 0 && y < a.h && x >= 0 && x < a.wd) off = ((y * a.wd + x) * a.cin + q * 8) * 2;
+    }
+    zoff[it] = off;
+  }
+#pragma unroll
+  for (int it = 0; it < WIT; ++it) {
+    const int id = tid + 256 * it;
+    int off = OOB;
+    if (id < WCH) {
+      const int row = id / PZ;               // (output channel, spatial tap) row
+      const int q = (id % PZ) ^ swz<PZ>(row);
+      const int col = row / S, s = row % S;
+      if (n0 + col < a.cout) off = (((n0 + col) * a.kt * S + s) * a.cin + q * 8) * 2;
+    }
+    woff[it] = off;
+  }
+  const int frame_bytes = int(frame_el * 2);
+  const int w_bytes = a.cout * a.kt * S * a.cin * 2;
 
-  auto load_stage = [&](int st) {
+  auto load_stage = [&](int st, int buf) {
     int ti = st / nch;
     const int ci0 = (st - ti * nch) * CB;
     int k = 0;
@@ -143,55 +185,19 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
       }
     }
     const int z = o + tap_delta(a, k);
-    const unsigned short* fp = z < a.tc ? cs + (int64_t(nn) * a.tc + z) * frame_el
-                                        : xs + (int64_t(nn) * a.tx + (z - a.tc)) * frame_el;
+    const unsigned short* fp = (z < a.tc ? cs + (int64_t(nn) * a.tc + z) * frame_el
+                                         : xs + (int64_t(nn) * a.tx + (z - a.tc)) * frame_el) + ci0;
+    const unsigned short* wp = ws + int64_t(k) * S * a.cin + ci0;
+    const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(wp), 0, w_bytes, 0x00020000);
+    uint4* zb = lds + buf * STAGE;
+    uint4* wb = zb + ZSLOTS;
 #pragma unroll
-    for (int it = 0; it < ZIT; ++it) {
-      const int id = tid + 256 * it;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (ZCH % 256 == 0 || id < ZCH) {
-        const int pix = id / PZ, pc = id % PZ;
-        const int hr = pix / WP, hc = pix % WP;
-        const int y = y0 - PAD + hr, x = x0 - PAD + hc;
-        if (y >= 0 && y < a.h && x >= 0 && x < a.wd)
-          v = *reinterpret_cast<const uint4*>(fp + (int64_t(y) * a.wd + x) * a.cin + ci0 + pc * 8);
-      }
-      zreg[it] = v;
-    }
+    for (int it = 0; it < ZIT; ++it)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (__attribute__((address_space(3))) void*)(zb + it * 256 + wave * 64), 16, zoff[it], 0, 0, 0);
 #pragma unroll
-    for (int it = 0; it < WIT; ++it) {
-      const int id = tid + 256 * it;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (WCH % 256 == 0 || id < WCH) {
-        const int col = id / (S * PZ), rem = id % (S * PZ);
-        const int s = rem / PZ, pc = rem % PZ;
-        const int co = n0 + col;
-        if (co < a.cout)
-          v = *reinterpret_cast<const uint4*>(ws + ((int64_t(co) * a.kt + k) * S + s) * a.cin + ci0 + pc * 8);
-      }
-      wreg[it] = v;
-    }
-  };
-
-  auto store_stage = [&](int buf) {
-    unsigned char* base = lds + buf * STAGE;
-#pragma unroll
-    for (int it = 0; it < ZIT; ++it) {
-      const int id = tid + 256 * it;
-      if (ZCH % 256 == 0 || id < ZCH) {
-        const int pix = id / PZ, pc = id % PZ;
-        *reinterpret_cast<uint4*>(base + pix * ZSTR + pc * 16) = zreg[it];
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < WIT; ++it) {
-      const int id = tid + 256 * it;
-      if (WCH % 256 == 0 || id < WCH) {
-        const int col = id / (S * PZ), rem = id % (S * PZ);
-        const int s = rem / PZ, pc = rem % PZ;
-        *reinterpret_cast<uint4*>(base + ZBYTES + col * WSTR + s * CB * 2 + pc * 16) = wreg[it];
-      }
-    }
+    for (int it = 0; it < WIT; ++it)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(wb + it * 256 + wave * 64), 16, woff[it], 0, 0, 0);
   };
 
   f32x16_t acc[CW][RW];
@@ -202,41 +208,65 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[q][r][v] = 0.f;
 
+  // One stage = (CB/16) x KS x KS steps; a step is one spatial tap (ta, tcol)
+  // of one 16-channel slice kk and issues CW x RW MFMAs.  Steps are grouped
+  // by (kk, tcol): the RW+KS-1 halo rows of a group serve all KS row taps ta.
+  // Operand fragments of step i+1 are read from LDS into a second register
+  // set before step i's MFMAs issue, so LDS latency hides behind MFMA work;
+  // sched_barrier keeps the compiler from sinking the reads to their uses.
+  constexpr int NG = (CB / 16) * KS;        // fragment groups per stage
+  constexpr int NSTEP = NG * KS;
+  constexpr int ZR = RW + KS - 1;           // halo rows per group
+  auto read_z = [&](const uint4* zb, int grp, bf16x8_t* zf) {
+    const int q = (grp / KS) * 2 + g, tcol = grp % KS;
+#pragma unroll
+    for (int r = 0; r < ZR; ++r) {
+      const int pix = (wm * RW + r) * WP + l32 + tcol;
+      zf[r] = __builtin_bit_cast(bf16x8_t, zb[pix * PZ + (q ^ swz<PZ>(pix))]);
+    }
+  };
+  auto read_w = [&](const uint4* wb, int step, bf16x8_t* wf) {
+    const int grp = step / KS, ta = step % KS;
+    const int q = (grp / KS) * 2 + g, s = ta * KS + grp % KS;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int row = ((wn * CW + c) * 32 + l32) * S + s;
+      wf[c] = __builtin_bit_cast(bf16x8_t, wb[row * PZ + (q ^ swz<PZ>(row))]);
+    }
+  };
   auto compute = [&](int buf) {
-    const unsigned char* zb = lds + buf * STAGE;
-    const unsigned char* wb = zb + ZBYTES;
+    const uint4* zb = lds + buf * STAGE;
+    const uint4* wb = zb + ZSLOTS;
+    bf16x8_t zf[2][ZR], wf[2][CW];
+    read_z(zb, 0, zf[0]);
+    read_w(wb, 0, wf[0]);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int ta = s / KS, tcol = s % KS;
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 1 < NSTEP) {
+        read_w(wb, i + 1, wf[(i + 1) & 1]);
+        if ((i + 1) % KS == 0) read_z(zb, (i + 1) / KS, zf[((i + 1) / KS) & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int ta = i % KS, zsel = (i / KS) & 1;
 #pragma unroll
-      for (int kk = 0; kk < CB / 16; ++kk) {
-        bf16x8_t wf[CW], zf[RW];
-#pragma unroll
-        for (int q = 0; q < CW; ++q)
-          wf[q] = *reinterpret_cast<const bf16x8_t*>(
-              wb + ((wn * CW + q) * 32 + l32) * WSTR + s * CB * 2 + kk * 32 + g * 16);
+      for (int c = 0; c < CW; ++c)
 #pragma unroll
         for (int r = 0; r < RW; ++r)
-          zf[r] = *reinterpret_cast<const bf16x8_t*>(
-              zb + ((wm * RW + r + ta) * WP + l32 + tcol) * ZSTR + kk * 32 + g * 16);
-#pragma unroll
-        for (int q = 0; q < CW; ++q)
-#pragma unroll
-          for (int r = 0; r < RW; ++r)
-            acc[q][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[q], zf[r], acc[q][r], 0, 0, 0);
-      }
+          acc[c][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i & 1][c], zf[zsel][r + ta], acc[c][r], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   if (nst > 0) {
-    load_stage(0);
-    store_stage(0);
+    load_stage(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
-      const bool more = st + 1 < nst;
-      if (more) load_stage(st + 1);
+      if (st + 1 < nst) load_stage(st + 1, (st + 1) & 1);
       compute(st & 1);
-      if (more) store_stage((st + 1) & 1);
+      // this thread's direct-to-LDS loads of the next stage have landed; the
+      // barrier then publishes everyone's and retires reads of this stage
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
   }
@@ -252,16 +282,16 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
     if (y >= a.ho || xo >= a.wo) continue;
     unsigned short* op = os + (((int64_t(nn) * a.to + o) * a.ho + y) * a.wo + xo) * a.cout;
 #pragma unroll
-    for (int q = 0; q < CW; ++q) {
+    for (int c = 0; c < CW; ++c) {
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const int co = n0 + (wn * CW + q) * 32 + v4 * 8 + g * 4;
+        const int co = n0 + (wn * CW + c) * 32 + v4 * 8 + g * 4;
         if (co >= a.cout) continue;
         float val[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float bias = (a.has_bias && co + e < a.cout) ? bf16_to_f32(bs[co + e]) : 0.f;
-          val[e] = acc[q][r][v4 * 4 + e] + bias;
+          val[e] = acc[c][r][v4 * 4 + e] + bias;
         }
         if (vec_ok) {
           uint2 pk;
@@ -276,6 +306,7 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
       }
     }
   }
+#endif
 }
 
 // fp32 path: one output element per thread, direct loops in the order of the

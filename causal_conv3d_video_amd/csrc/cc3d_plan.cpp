@@ -130,8 +130,11 @@ extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t
     const bool spatial_ok = d.k_h == d.k_w && (d.k_h == 1 || d.k_h == 3) && d.s_h == 1 &&
                             d.s_w == 1 && d.d_h == 1 && d.d_w == 1 &&
                             d.p_h == (d.k_h - 1) / 2 && d.p_w == (d.k_w - 1) / 2;
-    const int64_t frame_el = int64_t(d.h) * d.w * std::max(d.c_in, d.c_out);
-    if (!spatial_ok || d.c_in % 16 != 0 || frame_el >= (int64_t(1) << 31)) {
+    // buffer-load offsets are 32-bit byte offsets within one frame / the weights
+    const int64_t frame_bytes = int64_t(d.h) * d.w * std::max(d.c_in, d.c_out) * 2;
+    const int64_t w_bytes = int64_t(d.c_out) * d.k_t * d.k_h * d.k_w * d.c_in * 2;
+    if (!spatial_ok || d.c_in % 16 != 0 || frame_bytes >= (int64_t(1) << 31) ||
+        w_bytes >= (int64_t(1) << 31)) {
       delete p;
       return refuse(CC3D_ERR_UNSUPPORTED);
     }

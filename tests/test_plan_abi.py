@@ -52,6 +52,13 @@ def test_library_exports_every_declared_symbol():
         assert name in exported, name
 
 
+def test_library_has_no_undefined_internal_symbols():
+    # every kernel launch stub and helper must be defined inside the library
+    nm = subprocess.run(["nm", "-D", "--undefined-only", LIB], capture_output=True, text=True, check=True).stdout
+    bad = [l for l in nm.splitlines() if "_GLOBAL__N_" in l or "cc3d" in l or "conv_" in l]
+    assert not bad, bad
+
+
 def test_library_has_gfx950_code_object():
     # the embedded HIP fat binary names its one offload target
     data = open(LIB, "rb").read()
