@@ -123,7 +123,7 @@ def time_kernels(work, launches, stream):
             frac_mfma_peak=info["flops_active"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
             frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            flops=info["flops_active"], bytes=info["bytes_conv"], grid=info["grid"])
+            flops=info["flops_active"], bytes=info["bytes_conv"], tiles=info["tiles"])
     return res
 
 

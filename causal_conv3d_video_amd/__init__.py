@@ -60,7 +60,8 @@ class PlanInfo(ctypes.Structure):
         ("t_cache_out", _i32), ("n_active_taps", _i32), ("taps", Tap * CC3D_MAX_KT),
         ("flops_nominal", ctypes.c_double), ("flops_active", ctypes.c_double),
         ("bytes_conv", ctypes.c_double), ("bytes_cache_out", ctypes.c_double),
-        ("kernel_id", _i32), ("block_m", _i32), ("block_n", _i32), ("grid", ctypes.c_int64),
+        ("kernel_id", _i32), ("block_m", _i32), ("block_n", _i32), ("tiles", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
         ("kernel_name", ctypes.c_char * 64),
     ]
 

@@ -29,7 +29,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "cc3d_internal.h"
 
@@ -44,23 +46,14 @@ struct ConvArgs {
   const void* w;
   const void* b;
   void* out;
+  const void* wpk;  // bf16 kernels: weights repacked in stage order
   int n, tx, tc, h, wd, cin, cout, to, ho, wo;
   int kt, kh, kw, sh, sw, dh, dw, ph, pw;
   int tz;
   int delta[CC3D_MAX_KT];
-  int tiles_x, tiles_y, nblk_n;
+  int tiles_x, tiles_y, nblk_n, ntiles;
   int has_bias;
 };
-
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
-// XCD i % 8).  Renumber so that each XCD receives one contiguous range of
-// logical tiles: neighbouring patches and the output frames that share source
-// frames then meet in the same L2.
-__device__ __forceinline__ __attribute__((unused)) int xcd_remap(int bid, int grid) {
-  const int q = grid >> 3, r = grid & 7;
-  const int xcd = bid & 7, j = bid >> 3;
-  return xcd * q + min(xcd, r) + j;
-}
 
 __device__ __forceinline__ __attribute__((unused)) float bf16_to_f32(unsigned short h) {
   return __uint_as_float(static_cast<unsigned>(h) << 16);
@@ -80,26 +73,69 @@ __device__ __forceinline__ int tap_delta(const ConvArgs& a, int k) {
 }
 
 // XOR swizzle of the 16-byte pieces of one LDS row (a halo pixel, or one
-// output channel's weights): with PZ pieces per row, 8 consecutive rows read
-// at the same piece land in 8 distinct 16-byte slots of a 256-byte window,
-// which keeps the 16-byte operand reads of 8 consecutive lanes conflict-free.
+// (output channel, spatial tap) row of weights).  A 16-byte LDS read is
+// served 16 lanes at a time from a 256-byte window of banks, so the reads of
+// 16 consecutive rows at the same piece must land in 16 distinct 16-byte
+// slots: with PZ pieces per row, rows r and r + 16/PZ would collide, and
+// XOR-ing the piece index with bits of r above log2(16/PZ) separates them.
 template <int PZ>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (PZ == 4) return (row >> 2) & 1;
-  else if constexpr (PZ == 8) return (row >> 1) & 3;
-  else return 0;
+  if constexpr (PZ == 2) return (row >> 3) & 1;
+  else if constexpr (PZ == 4) return (row >> 2) & 3;
+  else return (row >> 1) & 7;
+}
+
+// Geometry shared by the MFMA kernel and the weight packer.
+template <int BN, int KS, int CB>
+struct WTile {
+  static constexpr int S = KS * KS;
+  static constexpr int PZ = CB / 8;                       // 16-byte pieces per row
+  static constexpr int WCH = BN * S * PZ;                 // used slots
+  static constexpr int WSLOTS = (WCH + 255) / 256 * 256;  // slots per stage tile
+};
+
+// Weight packer: writes, for every (tap k, input-channel chunk, output-channel
+// block), the exact 16-byte slot image of the LDS weight tile the MFMA kernel
+// consumes in that stage -- rows (output channel, spatial tap), CB channels,
+// pieces swizzled, zeros beyond C_out -- so a stage's weights are one
+// contiguous run that streams into LDS with fully used cache lines.
+template <int BN, int KS, int CB>
+__global__ __launch_bounds__(256) void pack_weights(const unsigned short* __restrict__ w,
+                                                    uint4* __restrict__ wpk, int cout, int kt, int cin,
+                                                    int nblk_n, int64_t total) {
+  using T = WTile<BN, KS, CB>;
+  const int nch = cin / CB;
+  for (int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x; idx < total; idx += int64_t(gridDim.x) * 256) {
+    const int id = int(idx % T::WSLOTS);
+    const int64_t tile = idx / T::WSLOTS;
+    const int nb = int(tile % nblk_n);
+    const int rest = int(tile / nblk_n);
+    const int cc = rest % nch, k = rest / nch;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (id < T::WCH) {
+      const int row = id / T::PZ;
+      const int q = (id % T::PZ) ^ swz<T::PZ>(row);
+      const int col = row / T::S, s = row % T::S;
+      const int co = nb * BN + col;
+      if (co < cout)
+        v = *reinterpret_cast<const uint4*>(w + ((int64_t(co) * kt + k) * T::S + s) * cin + cc * CB + q * 8);
+    }
+    wpk[idx] = v;
+  }
 }
 
 template <int BN, int TH, int WM, int WN, int KS, int CB>
 __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using WT = WTile<BN, KS, CB>;
   constexpr int TW = 32;                       // patch width = MFMA pixel block
   constexpr int PAD = (KS - 1) / 2;
   constexpr int HP = TH + KS - 1, WP = TW + KS - 1, S = KS * KS;
   constexpr int PZ = CB / 8;                   // 16-byte pieces per pixel per stage
-  constexpr int ZCH = HP * WP * PZ, WCH = BN * S * PZ;
-  constexpr int ZIT = (ZCH + 255) / 256, WIT = (WCH + 255) / 256;
-  constexpr int ZSLOTS = ZIT * 256, WSLOTS = WIT * 256;  // 16-byte LDS slots
+  constexpr int ZCH = HP * WP * PZ;
+  constexpr int ZIT = (ZCH + 255) / 256;
+  constexpr int ZSLOTS = ZIT * 256;            // 16-byte LDS slots of the halo tile
+  constexpr int WSLOTS = WT::WSLOTS, WIT = WSLOTS / 256;
   constexpr int STAGE = ZSLOTS + WSLOTS;
   constexpr int RW = TH / WM;                  // patch rows per wave
   constexpr int CW = BN / (32 * WN);           // 32-channel blocks per wave
@@ -114,99 +150,115 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   const int wm = wave / WN, wn = wave % WN;
   const int g = lane >> 5, l32 = lane & 31;
 
-  int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int o = bid % a.to;
-  bid /= a.to;
-  const int nb = bid % a.nblk_n;
-  bid /= a.nblk_n;
-  const int tile_x = bid % a.tiles_x;
-  bid /= a.tiles_x;
-  const int tile_y = bid % a.tiles_y;
-  const int nn = bid / a.tiles_y;
-  const int x0 = tile_x * TW, y0 = tile_y * TH, n0 = nb * BN;
+  // Persistent schedule.  Workgroups are dispatched round-robin over the 8
+  // XCDs (workgroup b runs on XCD b % 8); each XCD owns one contiguous range
+  // of tiles, which its workgroups walk together, so the tiles that run at
+  // the same time on one XCD are neighbours: adjacent patches, and the output
+  // frames of one patch that read the same source frames, meet in one L2.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nblk_here = (int(gridDim.x) >> 3) + (xcd < int(gridDim.x & 7) ? 1 : 0);
+  const int tq = a.ntiles >> 3, tr = a.ntiles & 7;
+  const int t_begin = xcd * tq + min(xcd, tr);
+  const int t_end = t_begin + tq + (xcd < tr ? 1 : 0);
+  int tile = t_begin + slot;
+  if (tile >= t_end) return;  // uniform over the workgroup
 
-  // Active taps of this output frame (uniform over the workgroup).
-  unsigned mask = 0;
-  for (int k = 0; k < a.kt; ++k) {
-    const int z = o + tap_delta(a, k);
-    if (z >= 0 && z < a.tz) mask |= 1u << k;
-  }
-  const int nact = __builtin_popcount(mask);
   const int nch = a.cin / CB;
-  const int nst = nact * nch;
-
+  const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
+  const int frame_bytes = int(frame_el * 2);
   const unsigned short* __restrict__ xs = static_cast<const unsigned short*>(a.x);
   const unsigned short* __restrict__ cs = static_cast<const unsigned short*>(a.cache);
-  const unsigned short* __restrict__ ws = static_cast<const unsigned short*>(a.w);
-  const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
+  const unsigned char* __restrict__ wpk = static_cast<const unsigned char*>(a.wpk);
+  const unsigned short* __restrict__ bs = static_cast<const unsigned short*>(a.b);
+  unsigned short* __restrict__ os = static_cast<unsigned short*>(a.out);
 
-  // Stage-invariant part of every slot this thread fills: the byte offset
-  // within a frame (halo) or within the weight tensor at tap 0, channel 0.
-  // Slots that must hold zeros (spatial padding, channels beyond C_out) get
-  // an offset past the buffer's record count: the range check of the buffer
-  // load then writes zeros into LDS.  Slot id = it*256 + tid.
+  struct Tile {
+    int o, nb, nn, x0, y0, n0;
+    unsigned mask;
+    int nst;
+  };
+  auto decode = [&](int t) {
+    Tile c;
+    c.o = t % a.to;
+    t /= a.to;
+    c.nb = t % a.nblk_n;
+    t /= a.nblk_n;
+    const int tile_x = t % a.tiles_x;
+    t /= a.tiles_x;
+    const int tile_y = t % a.tiles_y;
+    c.nn = t / a.tiles_y;
+    c.x0 = tile_x * TW;
+    c.y0 = tile_y * TH;
+    c.n0 = c.nb * BN;
+    c.mask = 0;
+    for (int k = 0; k < a.kt; ++k) {
+      const int z = c.o + tap_delta(a, k);
+      if (z >= 0 && z < a.tz) c.mask |= 1u << k;
+    }
+    c.nst = __builtin_popcount(c.mask) * nch;
+    return c;
+  };
+
+  // Byte offset, within a frame, of every halo slot this thread fills (slot
+  // id = it*256 + tid); slots in the spatial zero padding get an offset past
+  // the buffer's record count, and the range check of the buffer load then
+  // writes zeros into LDS.
   constexpr int OOB = int(0x80000000u);
-  int zoff[ZIT], woff[WIT];
+  int zoff[ZIT];
+  auto halo_offsets = [&](const Tile& c) {
 #pragma unroll
-  for (int it = 0; it < ZIT; ++it) {
-    const int id = tid + 256 * it;
-    int off = OOB;
-    if (id < ZCH) {
-      const int pix = id / PZ;
-      const int q = (id % PZ) ^ swz<PZ>(pix);
-      const int y = y0 - PAD + pix / WP, x = x0 - PAD + pix % WP;
-      if (y >= 0 && y < a.h && x >= 0 && x < a.wd) off = ((y * a.wd + x) * a.cin + q * 8) * 2;
+    for (int it = 0; it < ZIT; ++it) {
+      const int id = tid + 256 * it;
+      int off = OOB;
+      if (id < ZCH) {
+        const int pix = id / PZ;
+        const int q = (id % PZ) ^ swz<PZ>(pix);
+        const int y = c.y0 - PAD + pix / WP, x = c.x0 - PAD + pix % WP;
+        if (y >= 0 && y < a.h && x >= 0 && x < a.wd) off = ((y * a.wd + x) * a.cin + q * 8) * 2;
+      }
+      zoff[it] = off;
     }
-    zoff[it] = off;
-  }
-#pragma unroll
-  for (int it = 0; it < WIT; ++it) {
-    const int id = tid + 256 * it;
-    int off = OOB;
-    if (id < WCH) {
-      const int row = id / PZ;               // (output channel, spatial tap) row
-      const int q = (id % PZ) ^ swz<PZ>(row);
-      const int col = row / S, s = row % S;
-      if (n0 + col < a.cout) off = (((n0 + col) * a.kt * S + s) * a.cin + q * 8) * 2;
-    }
-    woff[it] = off;
-  }
-  const int frame_bytes = int(frame_el * 2);
-  const int w_bytes = a.cout * a.kt * S * a.cin * 2;
+  };
 
-  auto load_stage = [&](int st, int buf) {
+  auto load_stage = [&](const Tile& c, int st, int buf) {
     int ti = st / nch;
-    const int ci0 = (st - ti * nch) * CB;
+    const int cc = st - ti * nch;
     int k = 0;
     for (; k < a.kt; ++k) {
-      if (mask & (1u << k)) {
+      if (c.mask & (1u << k)) {
         if (ti == 0) break;
         --ti;
       }
     }
-    const int z = o + tap_delta(a, k);
-    const unsigned short* fp = (z < a.tc ? cs + (int64_t(nn) * a.tc + z) * frame_el
-                                         : xs + (int64_t(nn) * a.tx + (z - a.tc)) * frame_el) + ci0;
-    const unsigned short* wp = ws + int64_t(k) * S * a.cin + ci0;
-    const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(wp), 0, w_bytes, 0x00020000);
+    const int z = c.o + tap_delta(a, k);
+    const unsigned short* fp = (z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
+                                         : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el) + cc * CB;
+    const unsigned char* wp = wpk + ((int64_t(k) * nch + cc) * a.nblk_n + c.nb) * (WSLOTS * 16);
+    const __amdgpu_buffer_rsrc_t zr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(wp), 0, WSLOTS * 16, 0x00020000);
     uint4* zb = lds + buf * STAGE;
     uint4* wb = zb + ZSLOTS;
 #pragma unroll
     for (int it = 0; it < ZIT; ++it)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (__attribute__((address_space(3))) void*)(zb + it * 256 + wave * 64), 16, zoff[it], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (__attribute__((address_space(3))) void*)(zb + it * 256 + wave * 64),
+                                               16, zoff[it], 0, 0, 0);
 #pragma unroll
     for (int it = 0; it < WIT; ++it)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(wb + it * 256 + wave * 64), 16, woff[it], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(wb + it * 256 + wave * 64),
+                                               16, (it * 256 + tid) * 16, 0, 0, 0);
   };
 
   f32x16_t acc[CW][RW];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int q = 0; q < CW; ++q)
+    for (int q = 0; q < CW; ++q)
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+      for (int r = 0; r < RW; ++r)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[q][r][v] = 0.f;
+        for (int v = 0; v < 16; ++v) acc[q][r][v] = 0.f;
+  };
 
   // One stage = (CB/16) x KS x KS steps; a step is one spatial tap (ta, tcol)
   // of one 16-channel slice kk and issues CW x RW MFMAs.  Steps are grouped
@@ -214,8 +266,7 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   // Operand fragments of step i+1 are read from LDS into a second register
   // set before step i's MFMAs issue, so LDS latency hides behind MFMA work;
   // sched_barrier keeps the compiler from sinking the reads to their uses.
-  constexpr int NG = (CB / 16) * KS;        // fragment groups per stage
-  constexpr int NSTEP = NG * KS;
+  constexpr int NSTEP = (CB / 16) * KS * KS;
   constexpr int ZR = RW + KS - 1;           // halo rows per group
   auto read_z = [&](const uint4* zb, int grp, bf16x8_t* zf) {
     const int q = (grp / KS) * 2 + g, tcol = grp % KS;
@@ -257,54 +308,109 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
     }
   };
 
-  if (nst > 0) {
-    load_stage(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-      if (st + 1 < nst) load_stage(st + 1, (st + 1) & 1);
-      compute(st & 1);
+  // Bias of the channels this lane stores: channel n0 + (wn*CW + c)*32 +
+  // v4*8 + g*4 + e.  Loaded as 4-channel vectors when C_out % 4 == 0.
+  const bool vec_ok = (a.cout & 3) == 0;
+  float bias[CW][4][4];
+  auto load_bias = [&](const Tile& c) {
+#pragma unroll
+    for (int q = 0; q < CW; ++q)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int co = c.n0 + (wn * CW + q) * 32 + v4 * 8 + g * 4;
+        if (a.has_bias && vec_ok && co < a.cout) {
+          const uint2 u = *reinterpret_cast<const uint2*>(bs + co);
+          bias[q][v4][0] = __uint_as_float(u.x << 16);
+          bias[q][v4][1] = __uint_as_float(u.x & 0xffff0000u);
+          bias[q][v4][2] = __uint_as_float(u.y << 16);
+          bias[q][v4][3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bias[q][v4][e] = (a.has_bias && co + e < a.cout) ? bf16_to_f32(bs[co + e]) : 0.f;
+        }
+      }
+  };
+
+  // Epilogue: lane holds, for pixel column l32 of each patch row, channels
+  // (v/4)*8 + g*4 + (v%4) of each 32-channel block.  Bias added once in
+  // fp32, then one round-to-nearest-even to bf16.
+  auto epilogue = [&](const Tile& c) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int y = c.y0 + wm * RW + r, xo = c.x0 + l32;
+      if (y >= a.ho || xo >= a.wo) continue;
+      unsigned short* op = os + (((int64_t(c.nn) * a.to + c.o) * a.ho + y) * a.wo + xo) * a.cout;
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int co = c.n0 + (wn * CW + q) * 32 + v4 * 8 + g * 4;
+          if (co >= a.cout) continue;
+          float val[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = acc[q][r][v4 * 4 + e] + bias[q][v4][e];
+          if (vec_ok) {
+            uint2 pk;
+            pk.x = unsigned(f32_to_bf16(val[0])) | (unsigned(f32_to_bf16(val[1])) << 16);
+            pk.y = unsigned(f32_to_bf16(val[2])) | (unsigned(f32_to_bf16(val[3])) << 16);
+            *reinterpret_cast<uint2*>(op + co) = pk;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (co + e < a.cout) op[co + e] = f32_to_bf16(val[e]);
+          }
+        }
+      }
+    }
+  };
+
+  Tile cur = decode(tile);
+  halo_offsets(cur);
+  int buf = 0;
+  bool loaded = false;  // stage 0 of `cur` already sits in LDS buffer `buf`
+  for (;;) {
+    const int nxt_tile = tile + nblk_here < t_end ? tile + nblk_here : -1;
+    zero_acc();
+    if (cur.nst > 0 && !loaded) {
+      load_stage(cur, 0, buf);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    loaded = false;
+    Tile nxt = cur;
+    for (int st = 0; st < cur.nst; ++st) {
+      if (st + 1 < cur.nst) {
+        load_stage(cur, st + 1, buf ^ 1);
+      } else {
+        // last stage of this tile: start the next tile's first stage and
+        // this tile's bias while the MFMAs run
+        if (nxt_tile >= 0) {
+          nxt = decode(nxt_tile);
+          if (nxt.nst > 0) {
+            halo_offsets(nxt);
+            load_stage(nxt, 0, buf ^ 1);
+            loaded = true;
+          }
+        }
+        load_bias(cur);
+      }
+      compute(buf);
       // this thread's direct-to-LDS loads of the next stage have landed; the
       // barrier then publishes everyone's and retires reads of this stage
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      buf ^= 1;
     }
-  }
-
-  // Epilogue: lane holds, for pixel column l32 of each patch row, channels
-  // (v/4)*8 + g*4 + (v%4) of each 32-channel block.
-  const unsigned short* bs = static_cast<const unsigned short*>(a.b);
-  unsigned short* os = static_cast<unsigned short*>(a.out);
-  const bool vec_ok = (a.cout & 3) == 0;
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int y = y0 + wm * RW + r, xo = x0 + l32;
-    if (y >= a.ho || xo >= a.wo) continue;
-    unsigned short* op = os + (((int64_t(nn) * a.to + o) * a.ho + y) * a.wo + xo) * a.cout;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int co = n0 + (wn * CW + c) * 32 + v4 * 8 + g * 4;
-        if (co >= a.cout) continue;
-        float val[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float bias = (a.has_bias && co + e < a.cout) ? bf16_to_f32(bs[co + e]) : 0.f;
-          val[e] = acc[c][r][v4 * 4 + e] + bias;
-        }
-        if (vec_ok) {
-          uint2 pk;
-          pk.x = unsigned(f32_to_bf16(val[0])) | (unsigned(f32_to_bf16(val[1])) << 16);
-          pk.y = unsigned(f32_to_bf16(val[2])) | (unsigned(f32_to_bf16(val[3])) << 16);
-          *reinterpret_cast<uint2*>(op + co) = pk;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (co + e < a.cout) op[co + e] = f32_to_bf16(val[e]);
-        }
-      }
+    if (cur.nst == 0) load_bias(cur);
+    epilogue(cur);
+    if (nxt_tile < 0) break;
+    if (!loaded) {
+      nxt = decode(nxt_tile);
+      halo_offsets(nxt);
     }
+    cur = nxt;
+    tile = nxt_tile;
   }
 #endif
 }
@@ -395,9 +501,34 @@ hipError_t launch_conv(const void* kernel, const ConvArgs& a, int64_t grid, hipS
   return hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(256), args, 0, s);
 }
 
+// Compute units of the current device (cached per device).
+int device_cus(int dev) {
+  static std::atomic<int> cus[64];
+  if (dev < 0 || dev >= 64) return 256;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Repack the weights into the plan's workspace, then run the persistent
+// conv kernel: min(tiles, compute units) workgroups, one per compute unit.
 template <int BN, int TH, int WM, int WN, int KS, int CB>
-hipError_t launch_bf16(const ConvArgs& a, int64_t grid, hipStream_t s) {
-  return launch_conv(reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB>), a, grid, s);
+hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, hipStream_t s) {
+  using T = WTile<BN, KS, CB>;
+  const unsigned short* w = static_cast<const unsigned short*>(a.w);
+  uint4* wpk = static_cast<uint4*>(const_cast<void*>(a.wpk));
+  int cout = a.cout, kt = a.kt, cin = a.cin, nblk = a.nblk_n;
+  int64_t total = int64_t(kt) * (cin / CB) * nblk * T::WSLOTS;
+  const unsigned pgrid = unsigned(std::min<int64_t>((total + 255) / 256, 4096));
+  void* pargs[] = {&w, &wpk, &cout, &kt, &cin, &nblk, &total};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_weights<BN, KS, CB>), dim3(pgrid), dim3(256),
+                                 pargs, 0, s);
+  if (e != hipSuccess) return e;
+  return launch_conv(reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB>), a,
+                     std::min<int64_t>(tiles, cus), s);
 }
 
 }  // namespace
@@ -455,26 +586,49 @@ extern "C" cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, 
   a.tiles_x = plan->tiles_x;
   a.tiles_y = plan->tiles_y;
   a.nblk_n = plan->nblk_n;
+  a.ntiles = int(in.tiles);
   a.has_bias = d.has_bias;
+
+  int dev = 0;
+  int cus = 256;
+  if (d.dtype == CC3D_BF16) {
+    if (hipGetDevice(&dev) != hipSuccess) {
+      cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
+      return CC3D_ERR_DEVICE;
+    }
+    std::lock_guard<std::mutex> lock(plan->mu);
+    if (!plan->wpk) {
+      if (hipMalloc(&plan->wpk, size_t(plan->wpk_bytes)) != hipSuccess) {
+        plan->wpk = nullptr;
+        cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
+        return CC3D_ERR_DEVICE;
+      }
+      plan->wpk_device = dev;
+    } else if (plan->wpk_device != dev) {
+      return invalid();
+    }
+    a.wpk = plan->wpk;
+    cus = device_cus(dev);
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   switch (in.kernel_id) {
     case CC3D_K_F32_DIRECT:
-      e = launch_conv(reinterpret_cast<const void*>(&conv_f32_direct), a, in.grid, s);
+      e = launch_conv(reinterpret_cast<const void*>(&conv_f32_direct), a, in.tiles, s);
       break;
-    case CC3D_K_BF16_S3_N192: e = launch_bf16<192, 8, 2, 2, 3, 16>(a, in.grid, s); break;
-    case CC3D_K_BF16_S3_N96: e = launch_bf16<96, 16, 4, 1, 3, 16>(a, in.grid, s); break;
-    case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16>(a, in.grid, s); break;
+    case CC3D_K_BF16_S3_N192: e = launch_bf16<192, 8, 2, 2, 3, 16>(a, in.tiles, cus, s); break;
+    case CC3D_K_BF16_S3_N96: e = launch_bf16<96, 16, 4, 1, 3, 16>(a, in.tiles, cus, s); break;
+    case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16>(a, in.tiles, cus, s); break;
     case CC3D_K_BF16_S1_N192:
-      if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64>(a, in.grid, s);
-      else if (plan->cin_chunk == 32) e = launch_bf16<192, 8, 2, 2, 1, 32>(a, in.grid, s);
-      else e = launch_bf16<192, 8, 2, 2, 1, 16>(a, in.grid, s);
+      if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64>(a, in.tiles, cus, s);
+      else if (plan->cin_chunk == 32) e = launch_bf16<192, 8, 2, 2, 1, 32>(a, in.tiles, cus, s);
+      else e = launch_bf16<192, 8, 2, 2, 1, 16>(a, in.tiles, cus, s);
       break;
     case CC3D_K_BF16_S1_N32:
-      if (plan->cin_chunk == 64) e = launch_bf16<32, 8, 4, 1, 1, 64>(a, in.grid, s);
-      else if (plan->cin_chunk == 32) e = launch_bf16<32, 8, 4, 1, 1, 32>(a, in.grid, s);
-      else e = launch_bf16<32, 8, 4, 1, 1, 16>(a, in.grid, s);
+      if (plan->cin_chunk == 64) e = launch_bf16<32, 8, 4, 1, 1, 64>(a, in.tiles, cus, s);
+      else if (plan->cin_chunk == 32) e = launch_bf16<32, 8, 4, 1, 1, 32>(a, in.tiles, cus, s);
+      else e = launch_bf16<32, 8, 4, 1, 1, 16>(a, in.tiles, cus, s);
       break;
     default:
       return invalid();
@@ -500,4 +654,17 @@ extern "C" cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, 
   }
   cc3d::g_fast_path.fetch_add(1, std::memory_order_relaxed);
   return CC3D_OK;
+}
+
+// Frees a plan's device workspace (called by causal_conv3d_plan_destroy).
+void cc3d_release_workspace(cc3d_plan_t plan) {
+  std::lock_guard<std::mutex> lock(plan->mu);
+  if (plan->wpk) {
+    int cur = -1;
+    const bool switch_dev = hipGetDevice(&cur) == hipSuccess && cur != plan->wpk_device;
+    if (switch_dev) (void)hipSetDevice(plan->wpk_device);
+    (void)hipFree(plan->wpk);
+    if (switch_dev) (void)hipSetDevice(cur);
+    plan->wpk = nullptr;
+  }
 }

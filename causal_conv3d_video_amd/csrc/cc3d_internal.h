@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 // Kernel variants the planner can pick.  The bf16 ones are implicit-GEMM
 // MFMA kernels (block tile = block_m output pixels x block_n output channels).
@@ -17,14 +18,21 @@ enum cc3d_kernel_id : int32_t {
 };
 
 struct cc3d_plan {
-  cc3d_desc_t d;
-  cc3d_plan_info_t info;
-  int32_t tile_h;      // output rows per workgroup patch
-  int32_t tile_w;      // output columns per workgroup patch
-  int32_t tiles_y, tiles_x, nblk_n;
-  int32_t cin_chunk;   // input channels per pipeline stage
-  int64_t x_bytes, cache_bytes, w_bytes, b_bytes, out_bytes, cache_out_bytes;
-  int32_t elem;        // bytes per element
+  cc3d_desc_t d{};
+  cc3d_plan_info_t info{};
+  int32_t tile_h = 0;      // output rows per workgroup patch
+  int32_t tile_w = 0;      // output columns per workgroup patch
+  int32_t tiles_y = 0, tiles_x = 0, nblk_n = 0;
+  int32_t cin_chunk = 0;   // input channels per pipeline stage
+  int64_t x_bytes = 0, cache_bytes = 0, w_bytes = 0, b_bytes = 0, out_bytes = 0, cache_out_bytes = 0;
+  int32_t elem = 0;        // bytes per element
+  // Device workspace of the bf16 kernels: the weights repacked in stage
+  // order, rewritten by every forward call.  Allocated on first use on the
+  // device current at that time.
+  int64_t wpk_bytes = 0;
+  void* wpk = nullptr;
+  int wpk_device = -1;
+  std::mutex mu;
 };
 
 namespace cc3d {

@@ -115,7 +115,6 @@ extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t
 
   auto* p = new (std::nothrow) cc3d_plan;
   if (!p) return CC3D_ERR_NO_MEMORY;
-  std::memset(p, 0, sizeof *p);
   p->d = d;
   p->elem = elem;
   const int64_t frame_el_in = int64_t(d.h) * d.w * d.c_in;
@@ -148,7 +147,12 @@ extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t
     p->nblk_n = (d.c_out + v.block_n - 1) / v.block_n;
     in.block_m = v.tile_h * v.tile_w;
     in.block_n = v.block_n;
-    in.grid = int64_t(d.n) * t_out * p->tiles_y * p->tiles_x * p->nblk_n;
+    in.tiles = int64_t(d.n) * t_out * p->tiles_y * p->tiles_x * p->nblk_n;
+    // packed weights: one stage tile of 16-byte slots per (tap, channel chunk, channel block)
+    const int64_t ks = d.k_h;
+    const int64_t slots = (int64_t(v.block_n) * ks * ks * (v.cin_chunk / 8) + 255) / 256 * 256;
+    p->wpk_bytes = int64_t(d.k_t) * (d.c_in / v.cin_chunk) * p->nblk_n * slots * 16;
+    in.workspace_bytes = p->wpk_bytes;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);
   } else {
     const int64_t frame_el = int64_t(h_out) * w_out * d.c_out;
@@ -160,10 +164,10 @@ extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t
     in.block_m = 256;
     in.block_n = 1;
     const int64_t total = int64_t(d.n) * t_out * h_out * w_out * d.c_out;
-    in.grid = (total + 255) / 256;
+    in.tiles = (total + 255) / 256;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", "f32_direct");
   }
-  if (in.grid >= (int64_t(1) << 31)) {
+  if (in.tiles >= (int64_t(1) << 31)) {
     delete p;
     return refuse(CC3D_ERR_UNSUPPORTED);
   }
@@ -178,7 +182,13 @@ extern "C" cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_inf
   return CC3D_OK;
 }
 
-extern "C" void causal_conv3d_plan_destroy(cc3d_plan_t plan) { delete plan; }
+void cc3d_release_workspace(cc3d_plan_t plan);  // defined with the kernels
+
+extern "C" void causal_conv3d_plan_destroy(cc3d_plan_t plan) {
+  if (!plan) return;
+  cc3d_release_workspace(plan);
+  delete plan;
+}
 
 extern "C" const char* causal_conv3d_status_string(cc3d_status_t s) {
   switch (s) {

@@ -34,10 +34,15 @@
  *   out        [N][T_o][H_o][W_o][C_out]
  *   cache_out  [N][min(p_base, T_cache + T_x)][H][W][C_in]
  *
- * Ownership: every tensor is caller-owned device memory.  A plan owns only
- * host metadata; it holds no device memory and no copy of any tensor.
- * Threading: plans are immutable after creation and may be used from any
- * thread and stream; counters are atomic.
+ * Ownership: every tensor is caller-owned device memory.  A bf16 plan also
+ * owns one device workspace (workspace_bytes, allocated by its first forward
+ * call on the device current then, freed by causal_conv3d_plan_destroy): the
+ * weights repacked into the kernel's stage order, rewritten by every forward
+ * call before the convolution on the same stream.  Nothing else is kept.
+ * Threading: a plan's shape data is immutable and any thread may call
+ * forward; because the workspace is rewritten per call, forward calls that
+ * share one plan must be ordered on one stream (use one plan per stream for
+ * concurrent streams).  Counters are atomic.
  * Errors: every check is synchronous and happens before any launch; a launch
  * failure reported by the runtime returns CC3D_ERR_DEVICE; faults during
  * execution surface at the caller's next synchronisation.  The library never
@@ -105,8 +110,10 @@ typedef struct cc3d_plan_info {
                              read source frame once, W, b, the output */
   double bytes_cache_out; /* bytes read + written by the cache-out writer */
   int32_t kernel_id;      /* which kernel variant forward launches */
-  int32_t block_m, block_n; /* output pixels x output channels per workgroup */
-  int64_t grid;           /* workgroups of the conv kernel */
+  int32_t block_m, block_n; /* output pixels x output channels per tile */
+  int64_t tiles;          /* output tiles of the conv kernel (bf16: processed by
+                             min(tiles, compute units) persistent workgroups) */
+  int64_t workspace_bytes; /* device workspace the plan allocates on first use */
   char kernel_name[64];
 } cc3d_plan_info_t;
 
@@ -127,8 +134,8 @@ typedef struct cc3d_counters {
  * stride and one group; every call it observed has k_t = 3):
  *   CC3D_ERR_UNSUPPORTED when s_t != 1, groups != 1, k_t > CC3D_MAX_KT, or,
  *   for bf16: spatial stride or dilation != 1, k_h != k_w, k_h not in {1, 3},
- *   padding other than (k_h-1)/2, C_in not a multiple of 16, or one frame of
- *   H*W*max(C_in, C_out) elements reaching 2^31.
+ *   padding other than (k_h-1)/2, C_in not a multiple of 16, or one frame
+ *   (H*W*max(C_in, C_out) elements) or the weights reaching 2^31 bytes.
  *   CC3D_ERR_INVALID_ARG for a NULL pointer, a size < 1 (t_cache < 0), an
  *   unknown dtype, or an empty output (T_o, H_o or W_o < 1).
  */
@@ -137,7 +144,8 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
 /* Intervals, sizes, work and launch geometry of a plan (host only). */
 cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_info_t* info);
 
-/* Release a plan; NULL is ignored. */
+/* Release a plan and its device workspace; NULL is ignored.  The caller must
+ * make sure no forward call of this plan is still executing on the GPU. */
 void causal_conv3d_plan_destroy(cc3d_plan_t plan);
 
 /*
@@ -155,9 +163,10 @@ void causal_conv3d_plan_destroy(cc3d_plan_t plan);
  * leading |C| - p_base cache frames when |C| > p_base).
  * Returns CC3D_ERR_INVALID_ARG (nothing launched) for a NULL required
  * pointer, a bf16 buffer not 16-byte aligned (fp32: 4-byte), `out`
- * overlapping any other buffer, or `cache_out` overlapping x, cache_in, w or
- * b (in a streaming loop ping-pong two cache buffers).  Returns
- * CC3D_ERR_DEVICE if the runtime rejects a launch.
+ * overlapping any other buffer, `cache_out` overlapping x, cache_in, w or
+ * b (in a streaming loop ping-pong two cache buffers), or a bf16 plan used
+ * on another device than its first forward call.  Returns CC3D_ERR_DEVICE if
+ * the runtime rejects a launch or the workspace allocation.
  */
 cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, const void* cache_in,
                                     const void* w, const void* b, void* out, void* cache_out,

@@ -231,4 +231,4 @@ def test_workload_signatures_get_mfma_kernels():
         pad = (1, 1) if k[1] == 3 else (0, 0)
         p = cc3d.causal_conv3d_plan(_desc(c_in=cin, c_out=cout, h=h, w=w, t_x=tx, t_cache=tc, k=k, padding=pad))
         assert p.info["kernel_name"].startswith("bf16_"), p.info["kernel_name"]
-        assert p.info["grid"] > 0
+        assert p.info["tiles"] > 0 and p.info["workspace_bytes"] > 0
