@@ -30,7 +30,6 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 METRIC = "causal Conv3D BF16 TFLOP/s and % MFMA peak; 17-frame conv-replay ms"
 KERNEL_SRC = os.path.join(ROOT, "causal_conv3d_video_amd", "csrc", "cc3d_forward.hip")
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def _parse():
@@ -40,10 +39,12 @@ def _parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-launches", type=int, default=20,
                    help="launches per signature for the per-kernel timing")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
+    p.add_argument("--cpu-seconds", type=float, default=25.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
     p.add_argument("--only", default=None,
                    help="profiling aid: run only this signature's conv kernel --kernel-launches times")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="profiling aid: run only a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
 
 
@@ -81,7 +82,9 @@ def build_workload(device):
     return work
 
 
-def run_step(work, stream):
+def run_step(work, stream, packed=False):
+    """One pass of the replay: every chunk through every signature, carrying
+    each signature's cache through two ping-pong buffers."""
     import causal_conv3d_video_amd as cc3d
 
     chunks = len(work[0]["xs"])
@@ -90,13 +93,18 @@ def run_step(work, stream):
             plan = wk["plans"][c]
             cin_buf = None if c == 0 else wk["caches"][(c - 1) % 2][:, :plan.desc.t_cache]
             cout_buf = wk["caches"][c % 2][:, :plan.info["t_cache_out"]]
-            cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c],
-                                       cout_buf, stream)
+            if packed:
+                cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c],
+                                                  cout_buf, stream)
+            else:
+                cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c],
+                                           cout_buf, stream)
 
 
 def time_kernels(work, launches, stream):
     """Average conv-kernel launch time per signature at the steady-state chunk
-    (cache present), HIP events on the launch stream, no cache-out writer."""
+    (cache present): weights packed once, then causal_conv3d_forward_packed
+    launches only the conv kernel; HIP events on the launch stream."""
     import torch
 
     import causal_conv3d_video_amd as cc3d
@@ -106,13 +114,14 @@ def time_kernels(work, launches, stream):
         c = 2
         plan = wk["plans"][c]
         cin_buf = wk["caches"][(c - 1) % 2][:, :plan.desc.t_cache]
+        cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
         for _ in range(3):
-            cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c], None, stream)
+            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c], None, stream)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(launches):
-            cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c], None, stream)
+            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c], None, stream)
         e1.record(stream)
         e1.synchronize()
         ms = e0.elapsed_time(e1) / launches
@@ -150,14 +159,17 @@ def cpu_baseline(work, target_seconds):
         info = plan.info
         per_px = info["flops_active"] / (info["t_out"] * info["h_out"] * info["w_out"])
         per_sig.append((s, plan, prev, x, per_px))
-    # calibrate the rate on a small sample, then size the timed sample
+    # calibrate the rate on a first sample of the mid-resolution signature
+    # (large enough that per-call set-up is negligible), then size the timed
+    # samples so the whole baseline takes about target_seconds
     s0, p0, c0, x0, f0 = per_sig[2]
-    pts = np.stack([np.zeros(64, np.int64), rng.integers(0, p0.info["t_out"], 64),
-                    rng.integers(0, p0.info["h_out"], 64), rng.integers(0, p0.info["w_out"], 64)], 1)
+    ncal = 4096
+    pts = np.stack([np.zeros(ncal, np.int64), rng.integers(0, p0.info["t_out"], ncal),
+                    rng.integers(0, p0.info["h_out"], ncal), rng.integers(0, p0.info["w_out"], ncal)], 1)
     t = time.perf_counter()
     oracle.conv3d(x0, c0, work[2]["w"].cpu(), work[2]["b"].cpu(), dilation=(s0["dt"], 1, 1),
                   padding=s0["pad"], pbase=s0["p_base"], points=pts, nthreads=threads)
-    rate = 64 * f0 / max(time.perf_counter() - t, 1e-6)
+    rate = ncal * f0 / max(time.perf_counter() - t, 1e-6)
     budget = rate * target_seconds / len(per_sig)   # flops per signature
     total_flops, total_s, desc = 0.0, 0.0, []
     for wk, (s, plan, prev, x, per_px) in zip(work, per_sig):
@@ -176,18 +188,27 @@ def cpu_baseline(work, target_seconds):
                       + ", ".join(desc) + "; %.1f s, %.1f GFLOP" % (total_s, total_flops / 1e9)}
 
 
-def traffic_for(kernel_name, launches_flops):
-    """HBM bytes per launch from the committed rocprofv3 counter record, or
-    None when the kernel source changed since the counters were taken."""
+def traffic_for(kernel_name):
+    """HBM bytes per launch of ``kernel_name`` from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by the
+    counter's reading on a plain copy of known size), or None when there is
+    none for this kernel or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % kernel_name)
     try:
-        with open(TRAFFIC_RECORD) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+        rec = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    rec[key.strip()] = val.strip()
+    except OSError:
         return None
-    if rec.get("source_sha256") != _source_hash():
+    if rec.get("kernel_source_sha256") != _source_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel_name)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -206,12 +227,22 @@ def main():
     work = build_workload(device)
     torch.cuda.synchronize()
 
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 19, dtype=torch.bfloat16, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(args.kernel_launches):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 2, "launches": args.kernel_launches}))
+        return
     if args.only:
         wk = next(w for w in work if w["sig"]["name"] == args.only)
         plan = wk["plans"][2]
         cin_buf = wk["caches"][1][:, :plan.desc.t_cache]
+        cin_buf.copy_(torch.cat(wk["xs"][:2], 1)[:, -plan.desc.t_cache:])  # chunk 2's carried frames
+        cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
         for _ in range(args.kernel_launches):
-            cc3d.causal_conv3d_forward(plan, wk["xs"][2], cin_buf, wk["w"], wk["b"], wk["outs"][2], None, stream)
+            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][2], cin_buf, wk["b"], wk["outs"][2], None, stream)
         torch.cuda.synchronize()
         print(json.dumps({"only": args.only, "kernel": plan.info["kernel_name"], "launches": args.kernel_launches}))
         return
@@ -233,21 +264,45 @@ def main():
     flops_nominal = sum(p.info["flops_nominal"] for wk in work for p in wk["plans"])
     tflops = flops_step / (ms * 1e-3) / 1e12
 
+    # the same step with weights packed once beforehand (fixed decoder
+    # weights): conv kernels and cache-out writers only
+    for wk in work:
+        for plan in wk["plans"]:
+            cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
+    run_step(work, stream, packed=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run_step(work, stream, packed=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_packed = e0.elapsed_time(e1) / args.steps
+
     kern = time_kernels(work, args.kernel_launches, stream)
-    # time share of each signature in a step: 5 chunk calls at the steady-state rate
-    share = {name: k["us_per_launch"] * len(work[0]["plans"]) for name, k in kern.items()}
+    # dominant kernel: the variant with the largest share of a step (each
+    # signature makes 5 chunk calls; counted at the steady-state rate)
+    share = {}
+    for name, k in kern.items():
+        share[k["kernel"]] = share.get(k["kernel"], 0.0) + k["us_per_launch"] * len(work[0]["plans"])
     dom = max(share, key=share.get)
-    kd = kern[dom]
-    mfma_bound = kd["flops"] / kd["bytes"] > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    traffic = traffic_for(kd["kernel"], kd["flops"])
+    # the roofline is taken on that kernel's largest signature (first in step
+    # order among equals), whose steady-state launches are all alike
+    sig = max((n for n, k in kern.items() if k["kernel"] == dom), key=lambda n: kern[n]["flops"])
+    us = kern[sig]["us_per_launch"]                                    # average launch duration
+    flops = kern[sig]["flops"]                                         # algorithmic flops per launch
+    nbytes = kern[sig]["bytes"]                                        # algorithmic bytes per launch
+    mfma_bound = flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = traffic_for(dom)
     if mfma_bound:
-        roof = {"bound": "mfma", "achieved": kd["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": kd["frac_mfma_peak"], "traffic": traffic}
+        achieved = flops / (us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic}
     else:
-        roof = {"bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": kd["frac_hbm_peak"], "traffic": traffic}
-    roof.update({"kernel": kd["kernel"], "signature": dom, "us_per_launch": kd["us_per_launch"],
-                 "algorithmic_flops_per_launch": kd["flops"], "algorithmic_bytes_per_launch": kd["bytes"]})
+        achieved = nbytes / (us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+    roof.update({"kernel": dom, "signature": sig, "us_per_launch": us,
+                 "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -274,6 +329,8 @@ def main():
             "batch": 1, "calls_per_step": sum(len(wk["plans"]) for wk in work),
         },
         "mfma_peak_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+        "ms_per_step_weights_prepacked": ms_packed,
+        "tflops_weights_prepacked": flops_step / (ms_packed * 1e-3) / 1e12,
         "flops_active_per_step": flops_step,
         "flops_nominal_per_step": flops_nominal,
         "wall_s_timed": wall,

@@ -24,8 +24,8 @@ import torch
 __all__ = [
     "CC3DError", "Plan", "make_desc",
     "causal_conv3d_plan", "causal_conv3d_plan_info", "causal_conv3d_plan_destroy",
-    "causal_conv3d_forward", "causal_conv3d_status_string", "causal_conv3d_counters",
-    "library_path", "EXPORTED_SYMBOLS",
+    "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
+    "causal_conv3d_status_string", "causal_conv3d_counters", "library_path", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,8 @@ library_path = os.path.join(_HERE, "libcc3d.so")
 
 EXPORTED_SYMBOLS = (
     "causal_conv3d_plan", "causal_conv3d_plan_info", "causal_conv3d_plan_destroy",
-    "causal_conv3d_forward", "causal_conv3d_status_string", "causal_conv3d_counters",
+    "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
+    "causal_conv3d_status_string", "causal_conv3d_counters",
 )
 
 CC3D_OK, CC3D_ERR_INVALID_ARG, CC3D_ERR_UNSUPPORTED, CC3D_ERR_DEVICE, CC3D_ERR_NO_MEMORY = range(5)
@@ -84,6 +85,10 @@ def _load():
     lib.causal_conv3d_plan_destroy.restype = None
     lib.causal_conv3d_forward.argtypes = [vp] * 8
     lib.causal_conv3d_forward.restype = ctypes.c_int
+    lib.causal_conv3d_pack_weights.argtypes = [vp] * 3
+    lib.causal_conv3d_pack_weights.restype = ctypes.c_int
+    lib.causal_conv3d_forward_packed.argtypes = [vp] * 7
+    lib.causal_conv3d_forward_packed.restype = ctypes.c_int
     lib.causal_conv3d_status_string.argtypes = [ctypes.c_int]
     lib.causal_conv3d_status_string.restype = ctypes.c_char_p
     lib.causal_conv3d_counters.argtypes = [ctypes.POINTER(Counters), ctypes.c_int]
@@ -193,13 +198,8 @@ def _physical(t, shape, name):
                      % (name, tuple(shape), tuple(t.shape), tuple(t.stride())))
 
 
-def causal_conv3d_forward(plan, x, cache_in, w, b, out, cache_out=None, stream=None):
-    """Launch the plan's cached causal Conv3D on ``stream`` (default: the
-    current torch stream of x's device).  Asynchronous; raises CC3DError if
-    the library refuses the call."""
+def _marshal(plan, tensors):
     shapes = plan.shapes()
-    tensors = {"x": x, "cache_in": cache_in if plan.desc.t_cache > 0 else None, "w": w,
-               "b": b if plan.desc.has_bias else None, "out": out, "cache_out": cache_out}
     ptrs = {}
     for name, t in tensors.items():
         if t is None:
@@ -211,13 +211,44 @@ def causal_conv3d_forward(plan, x, cache_in, w, b, out, cache_out=None, stream=N
             raise TypeError("%s has dtype %s, the plan expects %s" % (name, t.dtype, plan.dtype))
         _physical(t, shapes[name], name)
         ptrs[name] = t.data_ptr()
+    return ptrs
+
+
+def _stream_handle(stream, like):
     if stream is None:
-        stream = torch.cuda.current_stream(x.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = _lib.causal_conv3d_forward(plan.handle, ptrs["x"], ptrs["cache_in"], ptrs["w"], ptrs["b"],
-                                    ptrs["out"], ptrs["cache_out"], handle)
+        stream = torch.cuda.current_stream(like.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def causal_conv3d_forward(plan, x, cache_in, w, b, out, cache_out=None, stream=None):
+    """Launch the plan's cached causal Conv3D on ``stream`` (default: the
+    current torch stream of x's device).  Asynchronous; raises CC3DError if
+    the library refuses the call."""
+    p = _marshal(plan, {"x": x, "cache_in": cache_in if plan.desc.t_cache > 0 else None, "w": w,
+                        "b": b if plan.desc.has_bias else None, "out": out, "cache_out": cache_out})
+    st = _lib.causal_conv3d_forward(plan.handle, p["x"], p["cache_in"], p["w"], p["b"], p["out"],
+                                    p["cache_out"], _stream_handle(stream, x))
     if st != CC3D_OK:
         raise CC3DError(st, "causal_conv3d_forward")
+
+
+def causal_conv3d_pack_weights(plan, w, stream=None):
+    """Repack ``w`` into the plan's workspace (bf16 plans), for
+    causal_conv3d_forward_packed."""
+    p = _marshal(plan, {"w": w})
+    st = _lib.causal_conv3d_pack_weights(plan.handle, p["w"], _stream_handle(stream, w))
+    if st != CC3D_OK:
+        raise CC3DError(st, "causal_conv3d_pack_weights")
+
+
+def causal_conv3d_forward_packed(plan, x, cache_in, b, out, cache_out=None, stream=None):
+    """The convolution with the weights last packed into ``plan``."""
+    p = _marshal(plan, {"x": x, "cache_in": cache_in if plan.desc.t_cache > 0 else None,
+                        "b": b if plan.desc.has_bias else None, "out": out, "cache_out": cache_out})
+    st = _lib.causal_conv3d_forward_packed(plan.handle, p["x"], p["cache_in"], p["b"], p["out"],
+                                           p["cache_out"], _stream_handle(stream, x))
+    if st != CC3D_OK:
+        raise CC3DError(st, "causal_conv3d_forward_packed")
 
 
 def causal_conv3d_counters(reset=False):

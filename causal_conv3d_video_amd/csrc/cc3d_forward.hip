@@ -94,11 +94,12 @@ struct WTile {
   static constexpr int WSLOTS = (WCH + 255) / 256 * 256;  // slots per stage tile
 };
 
-// Weight packer: writes, for every (tap k, input-channel chunk, output-channel
-// block), the exact 16-byte slot image of the LDS weight tile the MFMA kernel
-// consumes in that stage -- rows (output channel, spatial tap), CB channels,
-// pieces swizzled, zeros beyond C_out -- so a stage's weights are one
-// contiguous run that streams into LDS with fully used cache lines.
+// Weight packer: writes, for every (output-channel block nb, input-channel
+// chunk cc, tap k) in that order, the exact 16-byte slot image of the LDS
+// weight tile the MFMA kernel consumes in that stage -- rows (output
+// channel, spatial tap), CB channels, pieces swizzled, zeros beyond C_out --
+// so a stage's weights are one contiguous run that streams into LDS with
+// fully used cache lines.
 template <int BN, int KS, int CB>
 __global__ __launch_bounds__(256) void pack_weights(const unsigned short* __restrict__ w,
                                                     uint4* __restrict__ wpk, int cout, int kt, int cin,
@@ -108,9 +109,9 @@ __global__ __launch_bounds__(256) void pack_weights(const unsigned short* __rest
   for (int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x; idx < total; idx += int64_t(gridDim.x) * 256) {
     const int id = int(idx % T::WSLOTS);
     const int64_t tile = idx / T::WSLOTS;
-    const int nb = int(tile % nblk_n);
-    const int rest = int(tile / nblk_n);
-    const int cc = rest % nch, k = rest / nch;
+    const int k = int(tile % kt);
+    const int rest = int(tile / kt);
+    const int cc = rest % nch, nb = rest / nch;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (id < T::WCH) {
       const int row = id / T::PZ;
@@ -124,7 +125,9 @@ __global__ __launch_bounds__(256) void pack_weights(const unsigned short* __rest
   }
 }
 
-template <int BN, int TH, int WM, int WN, int KS, int CB>
+constexpr int kMaxTapsBf16 = 4;  // temporal taps the bf16 kernels track per tile
+
+template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF>
 __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using WT = WTile<BN, KS, CB>;
@@ -139,14 +142,18 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   constexpr int STAGE = ZSLOTS + WSLOTS;
   constexpr int RW = TH / WM;                  // patch rows per wave
   constexpr int CW = BN / (32 * WN);           // 32-channel blocks per wave
+  constexpr int LPS = ZIT + WIT;               // load instructions per stage per thread
   static_assert(WM * WN == 4 && TH % WM == 0 && BN % (32 * WN) == 0, "wave tiling");
   static_assert(PZ == 2 || PZ == 4 || PZ == 8, "stage channels");
-  static_assert(2 * STAGE * 16 <= 160 * 1024, "LDS budget");
+  static_assert(NBUF >= 2 && NBUF * STAGE * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
+  static_assert(LPS * (NBUF - 2) <= 63, "vmcnt range");
 
-  __shared__ uint4 lds[2 * STAGE];
+  __shared__ uint4 lds[NBUF * STAGE];
+  __shared__ float bias_lds[2][BN];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int g = lane >> 5, l32 = lane & 31;
 
@@ -160,8 +167,9 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   const int tq = a.ntiles >> 3, tr = a.ntiles & 7;
   const int t_begin = xcd * tq + min(xcd, tr);
   const int t_end = t_begin + tq + (xcd < tr ? 1 : 0);
-  int tile = t_begin + slot;
-  if (tile >= t_end) return;  // uniform over the workgroup
+  int ctile = t_begin + slot;
+  if (ctile >= t_end) return;  // uniform over the workgroup
+  auto next_tile = [&](int t) { return t + nblk_here < t_end ? t + nblk_here : -1; };
 
   const int nch = a.cin / CB;
   const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
@@ -172,10 +180,13 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   const unsigned short* __restrict__ bs = static_cast<const unsigned short*>(a.b);
   unsigned short* __restrict__ os = static_cast<unsigned short*>(a.out);
 
+  // A tile: one output frame o of batch item nn, a TH x 32 patch at (y0, x0),
+  // output channels [n0, n0 + BN); its active taps k[0..nact) read source
+  // frames z[i] = o + delta_k[i] of Z = [cache; x].
   struct Tile {
-    int o, nb, nn, x0, y0, n0;
-    unsigned mask;
-    int nst;
+    int o, nb, nn, x0, y0, n0, nact;
+    int k[kMaxTapsBf16];
+    int z[kMaxTapsBf16];
   };
   auto decode = [&](int t) {
     Tile c;
@@ -190,13 +201,33 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
     c.x0 = tile_x * TW;
     c.y0 = tile_y * TH;
     c.n0 = c.nb * BN;
-    c.mask = 0;
-    for (int k = 0; k < a.kt; ++k) {
-      const int z = c.o + tap_delta(a, k);
-      if (z >= 0 && z < a.tz) c.mask |= 1u << k;
+    c.nact = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxTapsBf16; ++k) {
+      c.k[k] = 0;
+      c.z[k] = 0;
     }
-    c.nst = __builtin_popcount(c.mask) * nch;
+#pragma unroll
+    for (int k = 0; k < kMaxTapsBf16; ++k) {
+      const int z = c.o + a.delta[k];
+      if (k < a.kt && z >= 0 && z < a.tz) {
+#pragma unroll
+        for (int i = 0; i < kMaxTapsBf16; ++i)
+          if (i == c.nact) {
+            c.k[i] = k;
+            c.z[i] = z;
+          }
+        ++c.nact;
+      }
+    }
     return c;
+  };
+  auto pick = [](const int* v, int i) {
+    int r = v[0];
+#pragma unroll
+    for (int j = 1; j < kMaxTapsBf16; ++j)
+      if (i == j) r = v[j];
+    return r;
   };
 
   // Byte offset, within a frame, of every halo slot this thread fills (slot
@@ -220,20 +251,15 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
     }
   };
 
-  auto load_stage = [&](const Tile& c, int st, int buf) {
-    int ti = st / nch;
-    const int cc = st - ti * nch;
-    int k = 0;
-    for (; k < a.kt; ++k) {
-      if (c.mask & (1u << k)) {
-        if (ti == 0) break;
-        --ti;
-      }
-    }
-    const int z = c.o + tap_delta(a, k);
+  // Stage (cc, ti) of a tile: input-channel chunk cc, active tap ti.  Stage
+  // order is tap major, chunk minor: consecutive stages read consecutive
+  // 32-byte pieces of the same halo pixels, so the 128-byte lines fetched
+  // for one stage serve the next stages from L2.
+  auto load_stage = [&](const Tile& c, int cc, int ti, int buf) {
+    const int z = pick(c.z, ti), k = pick(c.k, ti);
     const unsigned short* fp = (z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
                                          : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el) + cc * CB;
-    const unsigned char* wp = wpk + ((int64_t(k) * nch + cc) * a.nblk_n + c.nb) * (WSLOTS * 16);
+    const unsigned char* wp = wpk + ((int64_t(c.nb) * nch + cc) * a.kt + k) * (WSLOTS * 16);
     const __amdgpu_buffer_rsrc_t zr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t wr =
@@ -308,109 +334,137 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
     }
   };
 
-  // Bias of the channels this lane stores: channel n0 + (wn*CW + c)*32 +
-  // v4*8 + g*4 + e.  Loaded as 4-channel vectors when C_out % 4 == 0.
-  const bool vec_ok = (a.cout & 3) == 0;
-  float bias[CW][4][4];
-  auto load_bias = [&](const Tile& c) {
-#pragma unroll
-    for (int q = 0; q < CW; ++q)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int co = c.n0 + (wn * CW + q) * 32 + v4 * 8 + g * 4;
-        if (a.has_bias && vec_ok && co < a.cout) {
-          const uint2 u = *reinterpret_cast<const uint2*>(bs + co);
-          bias[q][v4][0] = __uint_as_float(u.x << 16);
-          bias[q][v4][1] = __uint_as_float(u.x & 0xffff0000u);
-          bias[q][v4][2] = __uint_as_float(u.y << 16);
-          bias[q][v4][3] = __uint_as_float(u.y & 0xffff0000u);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            bias[q][v4][e] = (a.has_bias && co + e < a.cout) ? bf16_to_f32(bs[co + e]) : 0.f;
-        }
-      }
-  };
-
-  // Epilogue: lane holds, for pixel column l32 of each patch row, channels
-  // (v/4)*8 + g*4 + (v%4) of each 32-channel block.  Bias added once in
-  // fp32, then one round-to-nearest-even to bf16.
-  auto epilogue = [&](const Tile& c) {
+  // Epilogue.  The lane holding pixel column l32 of a patch row has channels
+  // (v/4)*8 + g*4 + (v%4) of each 32-channel block.  The bias (fp32, from the
+  // tile's LDS slot) is added once, the sum rounded to nearest even to bf16,
+  // and each patch row of this wave -- 32 pixels x CW*32 channels -- goes
+  // through a private LDS region (the just-consumed stage buffer) so that
+  // global stores are whole 16-byte pieces of contiguous channel runs.
+  constexpr int EROW = CW * 32 * 2 + 16;         // LDS bytes per pixel (padded)
+  constexpr int EPIX = CW * 4;                   // 16-byte pieces per pixel
+  constexpr int EIT = (32 * EPIX + 63) / 64;     // store rounds per patch row
+  static_assert(4 * 32 * EROW <= STAGE * 16, "epilogue staging fits a stage buffer");
+  const bool vec_ok = (a.cout & 7) == 0;
+  auto epilogue = [&](const Tile& c, int par, int buf) {
+    unsigned char* eb = reinterpret_cast<unsigned char*>(lds + buf * STAGE) + wave * 32 * EROW;
+    const int cbase = c.n0 + wn * CW * 32;     // first channel of this wave
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      const int y = c.y0 + wm * RW + r, xo = c.x0 + l32;
-      if (y >= a.ho || xo >= a.wo) continue;
-      unsigned short* op = os + (((int64_t(c.nn) * a.to + c.o) * a.ho + y) * a.wo + xo) * a.cout;
+      const int y = c.y0 + wm * RW + r;
+      if (y >= a.ho) continue;                  // uniform over the wave
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
-          const int co = c.n0 + (wn * CW + q) * 32 + v4 * 8 + g * 4;
-          if (co >= a.cout) continue;
-          float val[4];
+          const int cl = q * 32 + v4 * 8 + g * 4;
+          const float4 bv = *reinterpret_cast<const float4*>(&bias_lds[par][wn * CW * 32 + cl]);
+          uint2 pk;
+          pk.x = unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 0] + bv.x)) |
+                 (unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 1] + bv.y)) << 16);
+          pk.y = unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 2] + bv.z)) |
+                 (unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 3] + bv.w)) << 16);
+          *reinterpret_cast<uint2*>(eb + l32 * EROW + cl * 2) = pk;
+        }
+      }
+      unsigned short* orow = os + ((int64_t(c.nn) * a.to + c.o) * a.ho + y) * int64_t(a.wo) * a.cout;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = acc[q][r][v4 * 4 + e] + bias[q][v4][e];
-          if (vec_ok) {
-            uint2 pk;
-            pk.x = unsigned(f32_to_bf16(val[0])) | (unsigned(f32_to_bf16(val[1])) << 16);
-            pk.y = unsigned(f32_to_bf16(val[2])) | (unsigned(f32_to_bf16(val[3])) << 16);
-            *reinterpret_cast<uint2*>(op + co) = pk;
-          } else {
+      for (int it = 0; it < EIT; ++it) {
+        const int piece = it * 64 + lane;
+        if (piece < 32 * EPIX) {
+          const int px = piece / EPIX, ch = (piece % EPIX) * 8;
+          const int xo = c.x0 + px, co = cbase + ch;
+          const uint4 v = *reinterpret_cast<const uint4*>(eb + px * EROW + ch * 2);
+          if (xo < a.wo && co < a.cout) {
+            unsigned short* op = orow + int64_t(xo) * a.cout + co;
+            if (vec_ok) {
+              *reinterpret_cast<uint4*>(op) = v;
+            } else {
+              const unsigned short* hv = reinterpret_cast<const unsigned short*>(&v);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (co + e < a.cout) op[co + e] = f32_to_bf16(val[e]);
+              for (int e = 0; e < 8; ++e)
+                if (co + e < a.cout) op[e] = hv[e];
+            }
           }
         }
       }
     }
   };
+  auto bias_value = [&](const Tile& c) {
+    return (a.has_bias && tid < BN && c.n0 + tid < a.cout) ? bs[c.n0 + tid] : (unsigned short)0;
+  };
 
-  Tile cur = decode(tile);
-  halo_offsets(cur);
-  int buf = 0;
-  bool loaded = false;  // stage 0 of `cur` already sits in LDS buffer `buf`
+  // Load cursor: runs NBUF-1 stages ahead of the compute cursor over the
+  // flattened (tile, stage) sequence, crossing tile boundaries, so a tile's
+  // first stages load while the previous tile finishes and writes its
+  // outputs.  Stage position p uses LDS buffer p % NBUF.
+  int ltile = ctile, lcc = 0, lti = 0;
+  Tile lt = decode(ltile);
+  auto lt_advance_tile = [&]() {
+    lcc = 0;
+    lti = 0;
+    for (;;) {
+      ltile = next_tile(ltile);
+      if (ltile < 0) return;
+      lt = decode(ltile);
+      if (lt.nact > 0) break;
+    }
+    halo_offsets(lt);
+  };
+  if (lt.nact > 0) halo_offsets(lt);
+  else lt_advance_tile();
+  auto issue = [&](int buf) {
+    if (ltile < 0) return false;
+    load_stage(lt, lcc, lti, buf);
+    if (++lcc == nch) {
+      lcc = 0;
+      if (++lti == lt.nact) lt_advance_tile();
+    }
+    return true;
+  };
+
+  int issued = 0;
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (issue(i)) ++issued;
+  if (NBUF > 2 && issued == NBUF - 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS * (NBUF - 2)) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  int pos = 0, par = 0;
+  Tile ct = decode(ctile);
   for (;;) {
-    const int nxt_tile = tile + nblk_here < t_end ? tile + nblk_here : -1;
     zero_acc();
-    if (cur.nst > 0 && !loaded) {
-      load_stage(cur, 0, buf);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int nst = ct.nact * nch;
+    if (nst == 0) {
+      // no active tap: the output is the bias alone
+      if (tid < BN) bias_lds[par][tid] = bf16_to_f32(bias_value(ct));
       __syncthreads();
-    }
-    loaded = false;
-    Tile nxt = cur;
-    for (int st = 0; st < cur.nst; ++st) {
-      if (st + 1 < cur.nst) {
-        load_stage(cur, st + 1, buf ^ 1);
-      } else {
-        // last stage of this tile: start the next tile's first stage and
-        // this tile's bias while the MFMAs run
-        if (nxt_tile >= 0) {
-          nxt = decode(nxt_tile);
-          if (nxt.nst > 0) {
-            halo_offsets(nxt);
-            load_stage(nxt, 0, buf ^ 1);
-            loaded = true;
-          }
-        }
-        load_bias(cur);
+      epilogue(ct, par, pos % NBUF);
+      __syncthreads();
+    } else {
+      for (int st = 0; st < nst; ++st, ++pos) {
+        unsigned short bval = 0;
+        if (st == 0) bval = bias_value(ct);  // issued before this stage's loads
+        const bool more = issue((pos + NBUF - 1) % NBUF);
+        compute(pos % NBUF);
+        if (st == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+        // wait until stage pos+1 has landed (the NBUF-2 newer stages may stay
+        // in flight); the barrier then publishes everyone's loads and the
+        // bias, and retires this stage's LDS reads
+        if (NBUF > 2 && more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS * (NBUF - 2)) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
       }
-      compute(buf);
-      // this thread's direct-to-LDS loads of the next stage have landed; the
-      // barrier then publishes everyone's and retires reads of this stage
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // the buffer of the last stage is idle until the next stage's loads are
+      // issued: stage the outputs through it, then make sure every wave is
+      // done with it before those loads go out
+      epilogue(ct, par, (pos - 1) % NBUF);
       __syncthreads();
-      buf ^= 1;
     }
-    if (cur.nst == 0) load_bias(cur);
-    epilogue(cur);
-    if (nxt_tile < 0) break;
-    if (!loaded) {
-      nxt = decode(nxt_tile);
-      halo_offsets(nxt);
-    }
-    cur = nxt;
-    tile = nxt_tile;
+    par ^= 1;
+    ctile = next_tile(ctile);
+    if (ctile < 0) break;
+    ct = decode(ctile);
   }
 #endif
 }
@@ -513,36 +567,61 @@ int device_cus(int dev) {
   return v;
 }
 
-// Repack the weights into the plan's workspace, then run the persistent
-// conv kernel: min(tiles, compute units) workgroups, one per compute unit.
-template <int BN, int TH, int WM, int WN, int KS, int CB>
-hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, hipStream_t s) {
+// bf16 path: optionally repack the weights into the plan's workspace, then
+// run the persistent conv kernel with min(tiles, compute units) workgroups,
+// one per compute unit.
+template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF>
+hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
   using T = WTile<BN, KS, CB>;
-  const unsigned short* w = static_cast<const unsigned short*>(a.w);
-  uint4* wpk = static_cast<uint4*>(const_cast<void*>(a.wpk));
-  int cout = a.cout, kt = a.kt, cin = a.cin, nblk = a.nblk_n;
-  int64_t total = int64_t(kt) * (cin / CB) * nblk * T::WSLOTS;
-  const unsigned pgrid = unsigned(std::min<int64_t>((total + 255) / 256, 4096));
-  void* pargs[] = {&w, &wpk, &cout, &kt, &cin, &nblk, &total};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_weights<BN, KS, CB>), dim3(pgrid), dim3(256),
-                                 pargs, 0, s);
-  if (e != hipSuccess) return e;
-  return launch_conv(reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB>), a,
-                     std::min<int64_t>(tiles, cus), s);
+  if (pack) {
+    const unsigned short* w = static_cast<const unsigned short*>(a.w);
+    uint4* wpk = static_cast<uint4*>(const_cast<void*>(a.wpk));
+    int cout = a.cout, kt = a.kt, cin = a.cin, nblk = a.nblk_n;
+    int64_t total = int64_t(kt) * (cin / CB) * nblk * T::WSLOTS;
+    const unsigned pgrid = unsigned(std::min<int64_t>((total + 255) / 256, 4096));
+    void* pargs[] = {&w, &wpk, &cout, &kt, &cin, &nblk, &total};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_weights<BN, KS, CB>), dim3(pgrid),
+                                         dim3(256), pargs, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!conv) return hipSuccess;
+  // as many persistent workgroups as fit on the device at once
+  const void* kernel = reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF>);
+  static std::atomic<int> per_cu{0};
+  int occ = per_cu.load(std::memory_order_relaxed);
+  if (occ <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess || occ <= 0) occ = 1;
+    per_cu.store(occ, std::memory_order_relaxed);
+  }
+  return launch_conv(kernel, a, std::min<int64_t>(tiles, int64_t(cus) * occ), s);
 }
 
 }  // namespace
 
-extern "C" cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, const void* cache_in,
-                                               const void* w, const void* b, void* out, void* cache_out,
-                                               void* stream) {
+namespace {
+
+enum RunMode { kPackAndRun, kPackOnly, kRunPacked };
+
+cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, const void* w, const void* b,
+                       void* out, void* cache_out, void* stream, RunMode mode) {
   if (!plan) return invalid();
   const cc3d_desc_t& d = plan->d;
   const cc3d_plan_info_t& in = plan->info;
+  const bool bf16 = d.dtype == CC3D_BF16;
+  const bool needs_w = mode != kRunPacked;
+  const bool runs = mode != kPackOnly;
+  if (!bf16 && mode != kPackAndRun) return invalid();
   if (d.t_cache == 0) cache_in = nullptr;
-  if (!x || !w || !out || (d.t_cache > 0 && !cache_in) || (d.has_bias && !b)) return invalid();
   if (!d.has_bias) b = nullptr;
-  const uintptr_t al = d.dtype == CC3D_BF16 ? 16 : 4;
+  if (!needs_w) w = nullptr;
+  if (!runs) {
+    x = cache_in = b = nullptr;
+    out = cache_out = nullptr;
+  }
+  if ((needs_w && !w) ||
+      (runs && (!x || !out || (d.t_cache > 0 && !cache_in) || (d.has_bias && !b))))
+    return invalid();
+  const uintptr_t al = bf16 ? 16 : 4;
   if (!aligned(x, al) || !aligned(cache_in, al) || !aligned(w, al) || !aligned(out, al) ||
       !aligned(cache_out, al) || !aligned(b, uintptr_t(plan->elem)))
     return invalid();
@@ -589,15 +668,16 @@ extern "C" cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, 
   a.ntiles = int(in.tiles);
   a.has_bias = d.has_bias;
 
-  int dev = 0;
   int cus = 256;
-  if (d.dtype == CC3D_BF16) {
+  if (bf16) {
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
       cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
       return CC3D_ERR_DEVICE;
     }
     std::lock_guard<std::mutex> lock(plan->mu);
     if (!plan->wpk) {
+      if (mode == kRunPacked) return invalid();  // nothing packed yet
       if (hipMalloc(&plan->wpk, size_t(plan->wpk_bytes)) != hipSuccess) {
         plan->wpk = nullptr;
         cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
@@ -613,27 +693,27 @@ extern "C" cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  const bool pack = mode != kRunPacked;
   switch (in.kernel_id) {
     case CC3D_K_F32_DIRECT:
       e = launch_conv(reinterpret_cast<const void*>(&conv_f32_direct), a, in.tiles, s);
       break;
-    case CC3D_K_BF16_S3_N192: e = launch_bf16<192, 8, 2, 2, 3, 16>(a, in.tiles, cus, s); break;
-    case CC3D_K_BF16_S3_N96: e = launch_bf16<96, 16, 4, 1, 3, 16>(a, in.tiles, cus, s); break;
-    case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16>(a, in.tiles, cus, s); break;
+    case CC3D_K_BF16_S3_N192: e = launch_bf16<192, 8, 2, 2, 3, 16, 2>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N96: e = launch_bf16<96, 16, 4, 1, 3, 16, 3>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16, 3>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S1_N192:
-      if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64>(a, in.tiles, cus, s);
-      else if (plan->cin_chunk == 32) e = launch_bf16<192, 8, 2, 2, 1, 32>(a, in.tiles, cus, s);
-      else e = launch_bf16<192, 8, 2, 2, 1, 16>(a, in.tiles, cus, s);
+      if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64, 2>(a, in.tiles, cus, pack, runs, s);
+      else e = launch_bf16<192, 8, 2, 2, 1, 32, 3>(a, in.tiles, cus, pack, runs, s);
       break;
     case CC3D_K_BF16_S1_N32:
-      if (plan->cin_chunk == 64) e = launch_bf16<32, 8, 4, 1, 1, 64>(a, in.tiles, cus, s);
-      else if (plan->cin_chunk == 32) e = launch_bf16<32, 8, 4, 1, 1, 32>(a, in.tiles, cus, s);
-      else e = launch_bf16<32, 8, 4, 1, 1, 16>(a, in.tiles, cus, s);
+      if (plan->cin_chunk == 64) e = launch_bf16<32, 8, 4, 1, 1, 64, 3>(a, in.tiles, cus, pack, runs, s);
+      else if (plan->cin_chunk == 32) e = launch_bf16<32, 8, 4, 1, 1, 32, 3>(a, in.tiles, cus, pack, runs, s);
+      else e = launch_bf16<32, 8, 4, 1, 1, 16, 3>(a, in.tiles, cus, pack, runs, s);
       break;
     default:
       return invalid();
   }
-  if (e == hipSuccess && cache_out && in.t_cache_out > 0) {
+  if (e == hipSuccess && runs && cache_out && in.t_cache_out > 0) {
     const int64_t frame_bytes = int64_t(d.h) * d.w * d.c_in * plan->elem;
     int vec16 = (frame_bytes % 16 == 0) && aligned(x, 16) && aligned(cache_in, 16) && aligned(cache_out, 16);
     const int64_t units = vec16 ? frame_bytes / 16 : frame_bytes;
@@ -652,8 +732,25 @@ extern "C" cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, 
     cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
     return CC3D_ERR_DEVICE;
   }
-  cc3d::g_fast_path.fetch_add(1, std::memory_order_relaxed);
+  if (runs) cc3d::g_fast_path.fetch_add(1, std::memory_order_relaxed);
   return CC3D_OK;
+}
+
+}  // namespace
+
+extern "C" cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, const void* cache_in,
+                                               const void* w, const void* b, void* out, void* cache_out,
+                                               void* stream) {
+  return run_plan(plan, x, cache_in, w, b, out, cache_out, stream, kPackAndRun);
+}
+
+extern "C" cc3d_status_t causal_conv3d_pack_weights(cc3d_plan_t plan, const void* w, void* stream) {
+  return run_plan(plan, nullptr, nullptr, w, nullptr, nullptr, nullptr, stream, kPackOnly);
+}
+
+extern "C" cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const void* x, const void* cache_in,
+                                                      const void* b, void* out, void* cache_out, void* stream) {
+  return run_plan(plan, x, cache_in, nullptr, b, out, cache_out, stream, kRunPacked);
 }
 
 // Frees a plan's device workspace (called by causal_conv3d_plan_destroy).

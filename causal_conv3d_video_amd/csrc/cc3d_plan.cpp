@@ -45,7 +45,9 @@ Variant choose_bf16(const cc3d_desc_t& d) {
     return {CC3D_K_BF16_S3_N32, 8, 32, 32, 16, "bf16_s3_n32_p8x32"};
   }
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
-  if (d.c_out % 192 == 0) return {CC3D_K_BF16_S1_N192, 8, 32, 192, cb, "bf16_s1_n192_p8x32"};
+  // the 192-channel tile stages at least 32 input channels (its stage buffer
+  // must also hold the epilogue's output staging)
+  if (d.c_out % 192 == 0 && cb >= 32) return {CC3D_K_BF16_S1_N192, 8, 32, 192, cb, "bf16_s1_n192_p8x32"};
   return {CC3D_K_BF16_S1_N32, 8, 32, 32, cb, "bf16_s1_n32_p8x32"};
 }
 
@@ -132,7 +134,7 @@ extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t
     // buffer-load offsets are 32-bit byte offsets within one frame / the weights
     const int64_t frame_bytes = int64_t(d.h) * d.w * std::max(d.c_in, d.c_out) * 2;
     const int64_t w_bytes = int64_t(d.c_out) * d.k_t * d.k_h * d.k_w * d.c_in * 2;
-    if (!spatial_ok || d.c_in % 16 != 0 || frame_bytes >= (int64_t(1) << 31) ||
+    if (!spatial_ok || d.c_in % 16 != 0 || d.k_t > 4 || frame_bytes >= (int64_t(1) << 31) ||
         w_bytes >= (int64_t(1) << 31)) {
       delete p;
       return refuse(CC3D_ERR_UNSUPPORTED);

@@ -133,7 +133,7 @@ typedef struct cc3d_counters {
  * Contract (the paper's lowering covers 5-D tensors with unit temporal
  * stride and one group; every call it observed has k_t = 3):
  *   CC3D_ERR_UNSUPPORTED when s_t != 1, groups != 1, k_t > CC3D_MAX_KT, or,
- *   for bf16: spatial stride or dilation != 1, k_h != k_w, k_h not in {1, 3},
+ *   for bf16: k_t > 4, spatial stride or dilation != 1, k_h != k_w, k_h not in {1, 3},
  *   padding other than (k_h-1)/2, C_in not a multiple of 16, or one frame
  *   (H*W*max(C_in, C_out) elements) or the weights reaching 2^31 bytes.
  *   CC3D_ERR_INVALID_ARG for a NULL pointer, a size < 1 (t_cache < 0), an
@@ -171,6 +171,23 @@ void causal_conv3d_plan_destroy(cc3d_plan_t plan);
 cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, const void* cache_in,
                                     const void* w, const void* b, void* out, void* cache_out,
                                     void* stream);
+
+/*
+ * Weights that do not change between calls (a decoder at inference) need not
+ * be repacked by every call.  causal_conv3d_pack_weights repacks w into the
+ * plan's workspace on `stream` (bf16 plans; allocates the workspace on first
+ * use); causal_conv3d_forward_packed then runs the convolution with the
+ * weights last packed into this plan -- by either causal_conv3d_pack_weights
+ * or causal_conv3d_forward -- and takes no weight pointer.  Both return
+ * CC3D_ERR_INVALID_ARG for an fp32 plan, a NULL required pointer, and
+ * (forward_packed) a plan whose weights were never packed; pointer and
+ * overlap rules are those of causal_conv3d_forward.  The packed weights are
+ * read by the convolution asynchronously: do not repack a plan while an
+ * earlier forward_packed of it may still run on another stream.
+ */
+cc3d_status_t causal_conv3d_pack_weights(cc3d_plan_t plan, const void* w, void* stream);
+cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const void* x, const void* cache_in,
+                                           const void* b, void* out, void* cache_out, void* stream);
 
 /* Static description of a status code. */
 const char* causal_conv3d_status_string(cc3d_status_t status);

@@ -230,3 +230,26 @@ def test_counters_count_fast_path(cuda_device):
     torch.cuda.synchronize()
     cnt = cc3d.causal_conv3d_counters()
     assert cnt["fast_path"] == 3 and cnt["device_error"] == 0 and cnt["invalid"] == 0
+
+
+def test_packed_weights_path_matches_forward_bitwise(cuda_device):
+    import causal_conv3d_video_amd as cc3d
+    x, c, w, b = synth.conv_inputs(1, 48, 96, 20, 70, 2, 2, device=DEV, seed=synth.SEED_BASE + 80)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1))
+    out_shape = plan.shapes()["out"]
+    # never packed: refused before any launch
+    fresh = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1))
+    y0 = torch.empty(out_shape, dtype=x.dtype, device=DEV)
+    with pytest.raises(cc3d.CC3DError) as e:
+        cc3d.causal_conv3d_forward_packed(fresh, x, c, b, y0, None)
+    assert e.value.status == cc3d.CC3D_ERR_INVALID_ARG
+    y1 = torch.empty(out_shape, dtype=x.dtype, device=DEV)
+    cc3d.causal_conv3d_forward(plan, x, c, w, b, y1, None)
+    cc3d.causal_conv3d_pack_weights(fresh, w)
+    y2 = torch.empty(out_shape, dtype=x.dtype, device=DEV)
+    y3 = torch.empty(out_shape, dtype=x.dtype, device=DEV)
+    cc3d.causal_conv3d_forward_packed(fresh, x, c, b, y2, None)
+    cc3d.causal_conv3d_forward_packed(plan, x, c, b, y3, None)  # weights packed by forward
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    assert_bf16_close(y2, _oracle(x, c, w, b), "packed")

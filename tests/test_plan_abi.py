@@ -232,3 +232,23 @@ def test_workload_signatures_get_mfma_kernels():
         p = cc3d.causal_conv3d_plan(_desc(c_in=cin, c_out=cout, h=h, w=w, t_x=tx, t_cache=tc, k=k, padding=pad))
         assert p.info["kernel_name"].startswith("bf16_"), p.info["kernel_name"]
         assert p.info["tiles"] > 0 and p.info["workspace_bytes"] > 0
+
+
+def test_packed_entry_points_refuse_fp32_plans_and_null_pointers():
+    lib = ctypes.CDLL(LIB)
+    lib.causal_conv3d_pack_weights.argtypes = [ctypes.c_void_p] * 3
+    lib.causal_conv3d_pack_weights.restype = ctypes.c_int
+    lib.causal_conv3d_forward_packed.argtypes = [ctypes.c_void_p] * 7
+    lib.causal_conv3d_forward_packed.restype = ctypes.c_int
+    f32 = cc3d.causal_conv3d_plan(_desc(dtype=torch.float32))
+    bf = cc3d.causal_conv3d_plan(_desc(t_cache=2))
+    base = 1 << 40  # never dereferenced: every call below is refused before any device call
+    mb = 1 << 20
+    assert lib.causal_conv3d_pack_weights(f32.handle, base, None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_forward_packed(f32.handle, base, base + mb, base + 2 * mb, base + 3 * mb, None,
+                                            None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_pack_weights(bf.handle, None, None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_forward_packed(bf.handle, None, base + mb, base + 2 * mb, base + 3 * mb, None,
+                                            None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_forward_packed(None, base, base + mb, base + 2 * mb, base + 3 * mb, None,
+                                            None) == cc3d.CC3D_ERR_INVALID_ARG
