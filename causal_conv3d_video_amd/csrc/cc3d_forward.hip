@@ -85,21 +85,26 @@ __device__ __forceinline__ int swz(int row) {
   else return (row >> 1) & 7;
 }
 
-// Geometry shared by the MFMA kernel and the weight packer.
+// Geometry shared by the MFMA kernel and the weight packer.  A stage's
+// weight tile is planar: 16-byte piece q (8 input channels) outermost, then
+// output channel, then spatial tap -- slot q*PLANE + col*S + s.  Lanes that
+// read consecutive output channels at one (q, s) then step S slots apart; S
+// (1 or 9) is odd, so any 16 consecutive lanes hit 16 distinct 16-byte slots
+// of a 256-byte bank window, and the slot is linear in the lane.
 template <int BN, int KS, int CB>
 struct WTile {
   static constexpr int S = KS * KS;
   static constexpr int PZ = CB / 8;                       // 16-byte pieces per row
-  static constexpr int WCH = BN * S * PZ;                 // used slots
-  static constexpr int WSLOTS = (WCH + 255) / 256 * 256;  // slots per stage tile
+  static constexpr int PLANE = BN * S;                    // slots per piece plane
+  static constexpr int WCH = PZ * PLANE;                  // used slots
+  static constexpr int WSLOTS = (WCH + 63) / 64 * 64;     // slots per stage tile (whole wave loads)
 };
 
 // Weight packer: writes, for every (output-channel block nb, input-channel
 // chunk cc, tap k) in that order, the exact 16-byte slot image of the LDS
-// weight tile the MFMA kernel consumes in that stage -- rows (output
-// channel, spatial tap), CB channels, pieces swizzled, zeros beyond C_out --
-// so a stage's weights are one contiguous run that streams into LDS with
-// fully used cache lines.
+// weight tile the MFMA kernel consumes in that stage (planar, zeros beyond
+// C_out), so a stage's weights are one contiguous run that streams into LDS
+// with fully used cache lines.
 template <int BN, int KS, int CB>
 __global__ __launch_bounds__(256) void pack_weights(const unsigned short* __restrict__ w,
                                                     uint4* __restrict__ wpk, int cout, int kt, int cin,
@@ -114,9 +119,8 @@ __global__ __launch_bounds__(256) void pack_weights(const unsigned short* __rest
     const int cc = rest % nch, nb = rest / nch;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (id < T::WCH) {
-      const int row = id / T::PZ;
-      const int q = (id % T::PZ) ^ swz<T::PZ>(row);
-      const int col = row / T::S, s = row % T::S;
+      const int q = id / T::PLANE, rem = id % T::PLANE;
+      const int col = rem / T::S, s = rem % T::S;
       const int co = nb * BN + col;
       if (co < cout)
         v = *reinterpret_cast<const uint4*>(w + ((int64_t(co) * kt + k) * T::S + s) * cin + cc * CB + q * 8);
@@ -127,8 +131,8 @@ __global__ __launch_bounds__(256) void pack_weights(const unsigned short* __rest
 
 constexpr int kMaxTapsBf16 = 4;  // temporal taps the bf16 kernels track per tile
 
-template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF>
-__global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
+template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void conv_bf16_mfma(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using WT = WTile<BN, KS, CB>;
   constexpr int TW = 32;                       // patch width = MFMA pixel block
@@ -136,16 +140,30 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   constexpr int HP = TH + KS - 1, WP = TW + KS - 1, S = KS * KS;
   constexpr int PZ = CB / 8;                   // 16-byte pieces per pixel per stage
   constexpr int ZCH = HP * WP * PZ;
-  constexpr int ZIT = (ZCH + 255) / 256;
-  constexpr int ZSLOTS = ZIT * 256;            // 16-byte LDS slots of the halo tile
-  constexpr int WSLOTS = WT::WSLOTS, WIT = WSLOTS / 256;
-  constexpr int STAGE = ZSLOTS + WSLOTS;
+  constexpr int ZSLOTS = (ZCH + 63) / 64 * 64; // 16-byte LDS slots of the halo tile
+  constexpr int NW = WM * WN, NT = NW * 64;    // waves, threads per workgroup
+  constexpr int ZIT = (ZSLOTS + NT - 1) / NT;
+  constexpr int WSLOTS = WT::WSLOTS, WIT = (WSLOTS + NT - 1) / NT;
   constexpr int RW = TH / WM;                  // patch rows per wave
   constexpr int CW = BN / (32 * WN);           // 32-channel blocks per wave
-  constexpr int LPS = ZIT + WIT;               // load instructions per stage per thread
-  static_assert(WM * WN == 4 && TH % WM == 0 && BN % (32 * WN) == 0, "wave tiling");
+  // each LDS buffer holds one stage (halo + weights), and at a tile's end the
+  // idle buffer stages the epilogue's output rows (4 waves x 32 pixels)
+  constexpr int EROW = CW * 32 * 2 + 16;       // epilogue LDS bytes per pixel (padded)
+  constexpr int STAGE = (ZSLOTS + WSLOTS) > (NW * 32 * EROW + 15) / 16 ? (ZSLOTS + WSLOTS)
+                                                                        : (NW * 32 * EROW + 15) / 16;
+  // load instructions one wave issues per stage (waves past a tile's last
+  // 64-slot block issue fewer)
+  constexpr auto lps_of = [](int w) {
+    int n = 0;
+    for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
+    for (int it = 0; it < WIT; ++it) n += it * NT + w * 64 < WSLOTS;
+    return n;
+  };
+  constexpr int LPS = ZIT + WIT;               // upper bound over the waves
+  static_assert((NW == 4 || NW == 8) && TH % WM == 0 && BN % (32 * WN) == 0, "wave tiling");
   static_assert(PZ == 2 || PZ == 4 || PZ == 8, "stage channels");
-  static_assert(NBUF >= 2 && NBUF * STAGE * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
+  constexpr int WG_PER_CU = OCC * 4 / NW > 0 ? OCC * 4 / NW : 1;  // OCC is waves per SIMD
+  static_assert(NBUF >= 2 && (NBUF * STAGE * 16 + 2 * BN * 4) * WG_PER_CU <= 160 * 1024, "LDS budget");
   static_assert(LPS * (NBUF - 2) <= 63, "vmcnt range");
 
   __shared__ uint4 lds[NBUF * STAGE];
@@ -185,8 +203,8 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   // frames z[i] = o + delta_k[i] of Z = [cache; x].
   struct Tile {
     int o, nb, nn, x0, y0, n0, nact;
-    int k[kMaxTapsBf16];
-    int z[kMaxTapsBf16];
+    int k0, k1, k2, k3;  // active taps, in order
+    int z0, z1, z2, z3;  // their source frames
   };
   auto decode = [&](int t) {
     Tile c;
@@ -202,32 +220,28 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
     c.y0 = tile_y * TH;
     c.n0 = c.nb * BN;
     c.nact = 0;
-#pragma unroll
-    for (int k = 0; k < kMaxTapsBf16; ++k) {
-      c.k[k] = 0;
-      c.z[k] = 0;
-    }
+    c.k0 = c.k1 = c.k2 = c.k3 = 0;
+    c.z0 = c.z1 = c.z2 = c.z3 = 0;
 #pragma unroll
     for (int k = 0; k < kMaxTapsBf16; ++k) {
       const int z = c.o + a.delta[k];
       if (k < a.kt && z >= 0 && z < a.tz) {
-#pragma unroll
-        for (int i = 0; i < kMaxTapsBf16; ++i)
-          if (i == c.nact) {
-            c.k[i] = k;
-            c.z[i] = z;
-          }
+        if (c.nact == 0) { c.k0 = k; c.z0 = z; }
+        else if (c.nact == 1) { c.k1 = k; c.z1 = z; }
+        else if (c.nact == 2) { c.k2 = k; c.z2 = z; }
+        else { c.k3 = k; c.z3 = z; }
         ++c.nact;
       }
     }
     return c;
   };
-  auto pick = [](const int* v, int i) {
-    int r = v[0];
-#pragma unroll
-    for (int j = 1; j < kMaxTapsBf16; ++j)
-      if (i == j) r = v[j];
-    return r;
+  auto pick = [](int i, int v0, int v1, int v2, int v3) { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; };
+  // wave-uniform copy of a pointer (kept in scalar registers)
+  auto uniform = [](const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v))));
+    const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v >> 32))));
+    return reinterpret_cast<const void*>((hi << 32) | lo);
   };
 
   // Byte offset, within a frame, of every halo slot this thread fills (slot
@@ -239,7 +253,7 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   auto halo_offsets = [&](const Tile& c) {
 #pragma unroll
     for (int it = 0; it < ZIT; ++it) {
-      const int id = tid + 256 * it;
+      const int id = tid + NT * it;
       int off = OOB;
       if (id < ZCH) {
         const int pix = id / PZ;
@@ -255,25 +269,52 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   // order is tap major, chunk minor: consecutive stages read consecutive
   // 32-byte pieces of the same halo pixels, so the 128-byte lines fetched
   // for one stage serve the next stages from L2.
+  // A stage's loads are prepared once (buffer descriptors, LDS targets) and
+  // then issued one 64-slot wave instruction at a time, spread over the first
+  // steps of the previous stage's MFMA loop: a burst of all of them would fill
+  // the vector-memory queue and stall the wave at issue instead of overlapping.
+  struct StageLoad {
+    const unsigned short* fp;  // halo source: frame base + chunk offset
+    const unsigned char* wp;   // packed weight tile
+    int buf;                   // LDS buffer
+  };
+  auto prep_stage = [&](const Tile& c, int cc, int ti, int buf) {
+    const int z = pick(ti, c.z0, c.z1, c.z2, c.z3), k = pick(ti, c.k0, c.k1, c.k2, c.k3);
+    StageLoad l;
+    l.fp = static_cast<const unsigned short*>(uniform((z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
+                                                                 : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el) +
+                                                      cc * CB));
+    l.wp = static_cast<const unsigned char*>(uniform(wpk + ((int64_t(c.nb) * nch + cc) * a.kt + k) * (WSLOTS * 16)));
+    l.buf = __builtin_amdgcn_readfirstlane(buf);
+    return l;
+  };
+  constexpr int NLOAD = ZIT + WIT;  // load instructions of one stage, per thread
+  // slots are filled 64 at a time (one wave instruction); a wave whose
+  // 64-slot block lies past the tile issues nothing
+  auto issue_piece = [&](const StageLoad& l, int j) {
+    uint4* zb = lds + l.buf * STAGE;
+    if (j < ZIT) {
+      if (ZSLOTS % NT == 0 || j * NT + wave * 64 < ZSLOTS) {
+        const __amdgpu_buffer_rsrc_t zr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(l.fp), 0, frame_bytes, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (__attribute__((address_space(3))) void*)(zb + j * NT + wave * 64),
+                                                 16, zoff[j], 0, 0, 0);
+      }
+    } else {
+      const int it = j - ZIT;
+      if (WSLOTS % NT == 0 || it * NT + wave * 64 < WSLOTS) {
+        const __amdgpu_buffer_rsrc_t wr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(l.wp), 0, WSLOTS * 16, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr,
+                                                 (__attribute__((address_space(3))) void*)(zb + ZSLOTS + it * NT + wave * 64),
+                                                 16, (it * NT + tid) * 16, 0, 0, 0);
+      }
+    }
+  };
   auto load_stage = [&](const Tile& c, int cc, int ti, int buf) {
-    const int z = pick(c.z, ti), k = pick(c.k, ti);
-    const unsigned short* fp = (z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
-                                         : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el) + cc * CB;
-    const unsigned char* wp = wpk + ((int64_t(c.nb) * nch + cc) * a.kt + k) * (WSLOTS * 16);
-    const __amdgpu_buffer_rsrc_t zr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t wr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(wp), 0, WSLOTS * 16, 0x00020000);
-    uint4* zb = lds + buf * STAGE;
-    uint4* wb = zb + ZSLOTS;
+    const StageLoad l = prep_stage(c, cc, ti, buf);
 #pragma unroll
-    for (int it = 0; it < ZIT; ++it)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (__attribute__((address_space(3))) void*)(zb + it * 256 + wave * 64),
-                                               16, zoff[it], 0, 0, 0);
-#pragma unroll
-    for (int it = 0; it < WIT; ++it)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(wb + it * 256 + wave * 64),
-                                               16, (it * 256 + tid) * 16, 0, 0, 0);
+    for (int j = 0; j < NLOAD; ++j) issue_piece(l, j);
   };
 
   f32x16_t acc[CW][RW];
@@ -306,12 +347,13 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
     const int grp = step / KS, ta = step % KS;
     const int q = (grp / KS) * 2 + g, s = ta * KS + grp % KS;
 #pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      const int row = ((wn * CW + c) * 32 + l32) * S + s;
-      wf[c] = __builtin_bit_cast(bf16x8_t, wb[row * PZ + (q ^ swz<PZ>(row))]);
-    }
+    for (int c = 0; c < CW; ++c)
+      wf[c] = __builtin_bit_cast(bf16x8_t, wb[q * WT::PLANE + ((wn * CW + c) * 32 + l32) * S + s]);
   };
-  auto compute = [&](int buf) {
+  // Steps over which the next stage's load instructions are spread: the first
+  // half of the stage, so they have the second half to land.
+  constexpr int ISSUE_STEPS = NSTEP > 1 ? (NSTEP + 1) / 2 : 1;
+  auto compute = [&](int buf, bool has_next, const StageLoad& next) {
     const uint4* zb = lds + buf * STAGE;
     const uint4* wb = zb + ZSLOTS;
     bf16x8_t zf[2][ZR], wf[2][CW];
@@ -331,6 +373,12 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
         for (int r = 0; r < RW; ++r)
           acc[c][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i & 1][c], zf[zsel][r + ta], acc[c][r], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      if (has_next && i < ISSUE_STEPS) {
+#pragma unroll
+        for (int j = 0; j < NLOAD; ++j)
+          if (j * ISSUE_STEPS / NLOAD == i) issue_piece(next, j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -340,10 +388,9 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   // and each patch row of this wave -- 32 pixels x CW*32 channels -- goes
   // through a private LDS region (the just-consumed stage buffer) so that
   // global stores are whole 16-byte pieces of contiguous channel runs.
-  constexpr int EROW = CW * 32 * 2 + 16;         // LDS bytes per pixel (padded)
   constexpr int EPIX = CW * 4;                   // 16-byte pieces per pixel
   constexpr int EIT = (32 * EPIX + 63) / 64;     // store rounds per patch row
-  static_assert(4 * 32 * EROW <= STAGE * 16, "epilogue staging fits a stage buffer");
+  static_assert(NW * 32 * EROW <= STAGE * 16, "epilogue staging fits a stage buffer");
   const bool vec_ok = (a.cout & 7) == 0;
   auto epilogue = [&](const Tile& c, int par, int buf) {
     unsigned char* eb = reinterpret_cast<unsigned char*>(lds + buf * STAGE) + wave * 32 * EROW;
@@ -412,21 +459,43 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
   };
   if (lt.nact > 0) halo_offsets(lt);
   else lt_advance_tile();
-  auto issue = [&](int buf) {
-    if (ltile < 0) return false;
-    load_stage(lt, lcc, lti, buf);
+  auto advance_load = [&]() {
     if (++lcc == nch) {
       lcc = 0;
       if (++lti == lt.nact) lt_advance_tile();
     }
+  };
+  auto issue = [&](int buf) {  // whole stage at once (pipeline prologue)
+    if (ltile < 0) return false;
+    load_stage(lt, lcc, lti, buf);
+    advance_load();
     return true;
+  };
+
+  // Wait until this wave's loads of all but the NBUF-2 newest stages have
+  // landed (vmcnt counts the wave's own outstanding loads, in issue order).
+  auto wait_newer_stages = [&]() {
+    if constexpr (NBUF > 2) {
+      switch (wave) {
+        case 0: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(0) * (NBUF - 2)) : "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(1) * (NBUF - 2)) : "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(2) * (NBUF - 2)) : "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(3) * (NBUF - 2)) : "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(4) * (NBUF - 2)) : "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(5) * (NBUF - 2)) : "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(6) * (NBUF - 2)) : "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(7) * (NBUF - 2)) : "memory"); break;
+      }
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
   };
 
   int issued = 0;
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i)
     if (issue(i)) ++issued;
-  if (NBUF > 2 && issued == NBUF - 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS * (NBUF - 2)) : "memory");
+  if (NBUF > 2 && issued == NBUF - 1) wait_newer_stages();
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -445,13 +514,15 @@ __global__ __launch_bounds__(256) void conv_bf16_mfma(ConvArgs a) {
       for (int st = 0; st < nst; ++st, ++pos) {
         unsigned short bval = 0;
         if (st == 0) bval = bias_value(ct);  // issued before this stage's loads
-        const bool more = issue((pos + NBUF - 1) % NBUF);
-        compute(pos % NBUF);
+        const bool more = ltile >= 0;
+        const StageLoad nl = prep_stage(lt, lcc, lti, (pos + NBUF - 1) % NBUF);
+        compute(pos % NBUF, more, nl);
+        if (more) advance_load();  // after the pieces: they read this tile's halo offsets
         if (st == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
         // wait until stage pos+1 has landed (the NBUF-2 newer stages may stay
         // in flight); the barrier then publishes everyone's loads and the
         // bias, and retires this stage's LDS reads
-        if (NBUF > 2 && more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS * (NBUF - 2)) : "memory");
+        if (NBUF > 2 && more) wait_newer_stages();
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
       }
@@ -549,10 +620,10 @@ cc3d_status_t invalid() {
   return CC3D_ERR_INVALID_ARG;
 }
 
-hipError_t launch_conv(const void* kernel, const ConvArgs& a, int64_t grid, hipStream_t s) {
+hipError_t launch_conv(const void* kernel, const ConvArgs& a, int64_t grid, hipStream_t s, int threads = 256) {
   ConvArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(256), args, 0, s);
+  return hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(unsigned(threads)), args, 0, s);
 }
 
 // Compute units of the current device (cached per device).
@@ -570,7 +641,7 @@ int device_cus(int dev) {
 // bf16 path: optionally repack the weights into the plan's workspace, then
 // run the persistent conv kernel with min(tiles, compute units) workgroups,
 // one per compute unit.
-template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF>
+template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
 hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
   using T = WTile<BN, KS, CB>;
   if (pack) {
@@ -586,14 +657,15 @@ hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv,
   }
   if (!conv) return hipSuccess;
   // as many persistent workgroups as fit on the device at once
-  const void* kernel = reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF>);
+  const void* kernel = reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF, OCC>);
   static std::atomic<int> per_cu{0};
   int occ = per_cu.load(std::memory_order_relaxed);
   if (occ <= 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess || occ <= 0) occ = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, WM * WN * 64, 0) != hipSuccess || occ <= 0)
+      occ = 1;
     per_cu.store(occ, std::memory_order_relaxed);
   }
-  return launch_conv(kernel, a, std::min<int64_t>(tiles, int64_t(cus) * occ), s);
+  return launch_conv(kernel, a, std::min<int64_t>(tiles, int64_t(cus) * occ), s, WM * WN * 64);
 }
 
 }  // namespace
@@ -698,17 +770,19 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     case CC3D_K_F32_DIRECT:
       e = launch_conv(reinterpret_cast<const void*>(&conv_f32_direct), a, in.tiles, s);
       break;
-    case CC3D_K_BF16_S3_N192: e = launch_bf16<192, 8, 2, 2, 3, 16, 2>(a, in.tiles, cus, pack, runs, s); break;
-    case CC3D_K_BF16_S3_N96: e = launch_bf16<96, 16, 4, 1, 3, 16, 3>(a, in.tiles, cus, pack, runs, s); break;
-    case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16, 3>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N96: e = launch_bf16<96, 16, 4, 1, 3, 16, 3, 1>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N96_X2: e = launch_bf16<96, 8, 4, 1, 3, 16, 2, 2>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N96_W8: e = launch_bf16<96, 16, 8, 1, 3, 16, 3, 2>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N192_W8: e = launch_bf16<192, 8, 4, 2, 3, 16, 2, 2>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16, 3, 2>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S1_N192:
-      if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64, 2>(a, in.tiles, cus, pack, runs, s);
-      else e = launch_bf16<192, 8, 2, 2, 1, 32, 3>(a, in.tiles, cus, pack, runs, s);
+      if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64, 2, 1>(a, in.tiles, cus, pack, runs, s);
+      else e = launch_bf16<192, 8, 2, 2, 1, 32, 3, 1>(a, in.tiles, cus, pack, runs, s);
       break;
     case CC3D_K_BF16_S1_N32:
-      if (plan->cin_chunk == 64) e = launch_bf16<32, 8, 4, 1, 1, 64, 3>(a, in.tiles, cus, pack, runs, s);
-      else if (plan->cin_chunk == 32) e = launch_bf16<32, 8, 4, 1, 1, 32, 3>(a, in.tiles, cus, pack, runs, s);
-      else e = launch_bf16<32, 8, 4, 1, 1, 16, 3>(a, in.tiles, cus, pack, runs, s);
+      if (plan->cin_chunk == 64) e = launch_bf16<32, 8, 4, 1, 1, 64, 3, 1>(a, in.tiles, cus, pack, runs, s);
+      else if (plan->cin_chunk == 32) e = launch_bf16<32, 8, 4, 1, 1, 32, 3, 2>(a, in.tiles, cus, pack, runs, s);
+      else e = launch_bf16<32, 8, 4, 1, 1, 16, 3, 2>(a, in.tiles, cus, pack, runs, s);
       break;
     default:
       return invalid();

@@ -40,8 +40,7 @@ struct Variant {
 Variant choose_bf16(const cc3d_desc_t& d) {
   const bool s3 = d.k_h == 3;
   if (s3) {
-    if (d.c_out % 192 == 0) return {CC3D_K_BF16_S3_N192, 8, 32, 192, 16, "bf16_s3_n192_p8x32"};
-    if (d.c_out % 96 == 0) return {CC3D_K_BF16_S3_N96, 16, 32, 96, 16, "bf16_s3_n96_p16x32"};
+    if (d.c_out % 96 == 0) return {CC3D_K_BF16_S3_N96_X2, 8, 32, 96, 16, "bf16_s3_n96_p8x32_x2"};
     return {CC3D_K_BF16_S3_N32, 8, 32, 32, 16, "bf16_s3_n32_p8x32"};
   }
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
