@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "CC3DError", "Plan", "make_desc",
-    "causal_conv3d_plan", "causal_conv3d_plan_info", "causal_conv3d_plan_destroy",
+    "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_info", "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
     "causal_conv3d_status_string", "causal_conv3d_counters", "library_path", "EXPORTED_SYMBOLS",
 ]
@@ -32,7 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libcc3d.so")
 
 EXPORTED_SYMBOLS = (
-    "causal_conv3d_plan", "causal_conv3d_plan_info", "causal_conv3d_plan_destroy",
+    "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_info", "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
     "causal_conv3d_status_string", "causal_conv3d_counters",
 )
@@ -79,6 +79,8 @@ def _load():
     vp = ctypes.c_void_p
     lib.causal_conv3d_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(vp)]
     lib.causal_conv3d_plan.restype = ctypes.c_int
+    lib.causal_conv3d_plan_variant.argtypes = [ctypes.POINTER(Desc), ctypes.c_char_p, ctypes.POINTER(vp)]
+    lib.causal_conv3d_plan_variant.restype = ctypes.c_int
     lib.causal_conv3d_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.causal_conv3d_plan_info.restype = ctypes.c_int
     lib.causal_conv3d_plan_destroy.argtypes = [vp]
@@ -166,6 +168,16 @@ def causal_conv3d_plan(desc):
     st = _lib.causal_conv3d_plan(ctypes.byref(desc), ctypes.byref(h))
     if st != CC3D_OK:
         raise CC3DError(st, "causal_conv3d_plan")
+    return Plan(h.value, desc)
+
+
+def causal_conv3d_plan_variant(desc, kernel_name):
+    """Plan ``desc`` on the named kernel variant; raises CC3DError if that
+    variant cannot run the call."""
+    h = ctypes.c_void_p()
+    st = _lib.causal_conv3d_plan_variant(ctypes.byref(desc), kernel_name.encode(), ctypes.byref(h))
+    if st != CC3D_OK:
+        raise CC3DError(st, "causal_conv3d_plan_variant")
     return Plan(h.value, desc)
 
 

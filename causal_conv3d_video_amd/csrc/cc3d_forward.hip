@@ -32,6 +32,7 @@
 #include <atomic>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "cc3d_internal.h"
 
@@ -39,6 +40,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 struct ConvArgs {
   const void* x;
@@ -540,6 +542,416 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
 #endif
 }
 
+// bf16 kernel for 3x3 spatial taps with the halo staged by 32-channel groups.
+//
+// The stage loads of the kernel above fetch 32 bytes (16 channels) of every
+// halo pixel per stage; the vector memory pipeline pays per 128-byte line
+// touched by a wave instruction, so three quarters of each halo line fetch are
+// wasted there and the halo stream alone keeps that pipeline about as busy as
+// the MFMAs keep the matrix cores.  This kernel stages the halo of a
+// (temporal tap, 32-channel group) once -- 64 bytes per pixel -- and runs the
+// group's two 16-channel weight sub-stages against it, and its tiles are
+// 16 x 32 output pixels, so each weight byte fetched feeds twice the MFMA work.
+// One workgroup per compute unit: WM = 4 waves (one per SIMD, each a 4-row x
+// 32-pixel x BN-channel register tile) or WM = 8 (two per SIMD, 2 rows each).
+//
+// LDS: two halo buffers (group g and g+1) and two weight buffers (sub-stages 0
+// and 1 of a group).  Schedule of group g (buffers H[g%2], W[0], W[1]):
+//   sub-stage 0: MFMAs on H[g%2] x W[0]; meanwhile load W[1] <- weights of
+//                (g, second 16 channels), then H[(g+1)%2] <- halo of g+1;
+//                wait for W[1] only; barrier.
+//   sub-stage 1: MFMAs on H[g%2] x W[1]; meanwhile load W[0] <- weights of
+//                (g+1, first 16 channels); wait for everything; barrier.
+// The group sequence runs across tile boundaries, so the next tile's first
+// loads overlap the current tile's last MFMAs and its epilogue.
+template <int BN, int TH, int WM>
+__global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4, WM / 4))) void conv_bf16_g32(ConvArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using WT = WTile<BN, 3, 16>;
+  constexpr int TW = 32, HP = TH + 2, WP = TW + 2, S = 9;
+  constexpr int PZ = 4;                          // 16-byte pieces per halo pixel
+  constexpr int ZCH = HP * WP * PZ;
+  constexpr int ZSLOTS = (ZCH + 63) / 64 * 64;
+  constexpr int NW = WM, NT = NW * 64;
+  constexpr int WSLOTS = WT::WSLOTS;
+  constexpr int ZIT = (ZSLOTS + NT - 1) / NT, WIT = (WSLOTS + NT - 1) / NT;
+  constexpr int RW = TH / WM, CW = BN / 32;
+  constexpr int ZR = RW + 2;                     // halo rows a wave reads per column tap
+  constexpr int EROW = CW * 32 * 2 + 16;         // epilogue LDS bytes per pixel (padded)
+  static_assert((WM == 4 || WM == 8) && TH % WM == 0 && BN % 32 == 0, "wave tiling");
+  // epilogue staging: waves 0-3 use the idle weight buffer, waves 4-7 the idle halo buffer
+  static_assert(4 * 32 * EROW <= WSLOTS * 16 && (NW - 4) * 32 * EROW <= ZSLOTS * 16, "epilogue staging");
+  static_assert((2 * (ZSLOTS + WSLOTS)) * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
+  constexpr auto zcnt = [](int w) {  // halo load instructions of wave w per group
+    int n = 0;
+    for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
+    return n;
+  };
+  static_assert(zcnt(0) + WIT <= 63, "vmcnt range");
+
+  __shared__ uint4 zl[2 * ZSLOTS];
+  __shared__ uint4 wl[2 * WSLOTS];
+  __shared__ float bias_lds[2][BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+
+  // persistent schedule: each XCD walks one contiguous range of tiles
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nblk_here = (int(gridDim.x) >> 3) + (xcd < int(gridDim.x & 7) ? 1 : 0);
+  const int tq = a.ntiles >> 3, tr = a.ntiles & 7;
+  const int t_begin = xcd * tq + min(xcd, tr);
+  const int t_end = t_begin + tq + (xcd < tr ? 1 : 0);
+  int ctile = t_begin + slot;
+  if (ctile >= t_end) return;
+  auto next_tile = [&](int t) { return t + nblk_here < t_end ? t + nblk_here : -1; };
+
+  const int ngrp = a.cin / 32;                   // 32-channel groups per tap
+  const int nch = a.cin / 16;                    // 16-channel weight sub-stages per tap
+  const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
+  const int frame_bytes = int(frame_el * 2);
+  const unsigned short* __restrict__ xs = static_cast<const unsigned short*>(a.x);
+  const unsigned short* __restrict__ cs = static_cast<const unsigned short*>(a.cache);
+  const unsigned char* __restrict__ wpk = static_cast<const unsigned char*>(a.wpk);
+  const unsigned short* __restrict__ bs = static_cast<const unsigned short*>(a.b);
+  unsigned short* __restrict__ os = static_cast<unsigned short*>(a.out);
+
+  struct Tile {
+    int o, nb, nn, x0, y0, n0, nact;
+    int k0, k1, k2, k3;
+    int z0, z1, z2, z3;
+  };
+  auto decode = [&](int t) {
+    Tile c;
+    c.o = t % a.to;
+    t /= a.to;
+    c.nb = t % a.nblk_n;
+    t /= a.nblk_n;
+    const int tile_x = t % a.tiles_x;
+    t /= a.tiles_x;
+    const int tile_y = t % a.tiles_y;
+    c.nn = t / a.tiles_y;
+    c.x0 = tile_x * TW;
+    c.y0 = tile_y * TH;
+    c.n0 = c.nb * BN;
+    c.nact = 0;
+    c.k0 = c.k1 = c.k2 = c.k3 = 0;
+    c.z0 = c.z1 = c.z2 = c.z3 = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxTapsBf16; ++k) {
+      const int z = c.o + a.delta[k];
+      if (k < a.kt && z >= 0 && z < a.tz) {
+        if (c.nact == 0) { c.k0 = k; c.z0 = z; }
+        else if (c.nact == 1) { c.k1 = k; c.z1 = z; }
+        else if (c.nact == 2) { c.k2 = k; c.z2 = z; }
+        else { c.k3 = k; c.z3 = z; }
+        ++c.nact;
+      }
+    }
+    return c;
+  };
+  auto pick = [](int i, int v0, int v1, int v2, int v3) { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; };
+  auto uniform = [](const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v))));
+    const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v >> 32))));
+    return reinterpret_cast<const void*>((hi << 32) | lo);
+  };
+
+  // Byte offsets within a frame of the halo slots this thread fills (slot id
+  // = it*NT + tid; 4 slots of 16 bytes per pixel, XOR-swizzled); slots in the
+  // spatial zero padding get an offset past the buffer's record count, and
+  // the buffer load's range check writes zeros for them.
+  constexpr int OOB = int(0x80000000u);
+  int zoff[ZIT];
+  auto halo_offsets = [&](const Tile& c) {
+#pragma unroll
+    for (int it = 0; it < ZIT; ++it) {
+      const int id = tid + NT * it;
+      int off = OOB;
+      if (id < ZCH) {
+        const int pix = id / PZ;
+        const int q = (id % PZ) ^ swz<PZ>(pix);
+        const int y = c.y0 - 1 + pix / WP, x = c.x0 - 1 + pix % WP;
+        if (y >= 0 && y < a.h && x >= 0 && x < a.wd) off = ((y * a.wd + x) * a.cin + q * 8) * 2;
+      }
+      zoff[it] = off;
+    }
+  };
+
+  // A group position: tile, active-tap index, 32-channel group.
+  struct Grp {
+    int t, ti, gz;
+  };
+  auto halo_src = [&](const Tile& c, int ti, int gz) {
+    const int z = pick(ti, c.z0, c.z1, c.z2, c.z3);
+    return static_cast<const unsigned short*>(uniform((z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
+                                                                : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el) +
+                                                     gz * 32));
+  };
+  auto wsrc = [&](const Tile& c, int ti, int cc) {
+    const int k = pick(ti, c.k0, c.k1, c.k2, c.k3);
+    return static_cast<const unsigned char*>(uniform(wpk + ((int64_t(c.nb) * nch + cc) * a.kt + k) * (WSLOTS * 16)));
+  };
+  auto issue_z = [&](const unsigned short* fp, int zb, int it) {
+    if (ZSLOTS % NT == 0 || it * NT + wave * 64 < ZSLOTS) {
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(zl + zb * ZSLOTS + it * NT + wave * 64), 16, zoff[it], 0, 0, 0);
+    }
+  };
+  auto issue_w = [&](const unsigned char* wp, int wb, int it) {
+    if (WSLOTS % NT == 0 || it * NT + wave * 64 < WSLOTS) {
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(wp), 0, WSLOTS * 16, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(wl + wb * WSLOTS + it * NT + wave * 64), 16, (it * NT + tid) * 16,
+          0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[CW][RW];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int q = 0; q < CW; ++q)
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[q][r][v] = 0.f;
+  };
+
+  // One sub-stage = 9 steps, one per spatial tap (ta, tcol), grouped by
+  // column tap: the RW+2 halo rows read for a column tap serve its 3 row
+  // taps.  Fragments of step i+1 are read before step i's MFMAs issue.
+  // Sub-stage J multiplies the 16 channels [16J, 16J+16) of the group.
+  constexpr int NSTEP = 9;
+  auto read_z = [&](const uint4* zb, int tcol, int J, bf16x8_t* zf) {
+    const int q = 2 * J + g;
+#pragma unroll
+    for (int r = 0; r < ZR; ++r) {
+      const int pix = (wave * RW + r) * WP + l32 + tcol;
+      zf[r] = __builtin_bit_cast(bf16x8_t, zb[pix * PZ + (q ^ swz<PZ>(pix))]);
+    }
+  };
+  auto read_w = [&](const uint4* wb, int step, bf16x8_t* wf) {
+    const int s = (step % 3) * 3 + step / 3;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) wf[c] = __builtin_bit_cast(bf16x8_t, wb[g * WT::PLANE + (c * 32 + l32) * S + s]);
+  };
+  // issue(k) is called once for k = 0..NL-1, spread over the first ISS steps
+  // A wave whose rows all lie below the image (the last patch row of a map
+  // whose height is not a multiple of TH) only issues its share of the loads.
+  auto compute = [&](const uint4* zb, const uint4* wb, bool rows_in, auto J, auto NLc, auto ISSc, auto&& issue) {
+    constexpr int NL = decltype(NLc)::value, ISS = decltype(ISSc)::value;
+    if (!rows_in) {
+#pragma unroll
+      for (int k = 0; k < NL; ++k) issue(k);
+      return;
+    }
+    bf16x8_t zf[2][ZR], wf[2][CW];
+    read_z(zb, 0, J, zf[0]);
+    read_w(wb, 0, wf[0]);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 1 < NSTEP) {
+        read_w(wb, i + 1, wf[(i + 1) & 1]);
+        if ((i + 1) % 3 == 0) read_z(zb, (i + 1) / 3, J, zf[((i + 1) / 3) & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int ta = i % 3, zsel = (i / 3) & 1;
+#pragma unroll
+      for (int c = 0; c < CW; ++c)
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+          acc[c][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i & 1][c], zf[zsel][r + ta], acc[c][r], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < NL; ++k)
+        if (k * ISS / NL == i) issue(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Epilogue (as in the kernel above): bias added once in fp32, round to
+  // nearest even, staged per wave through the idle weight buffer W[1] so
+  // global stores are whole 16-byte runs of channels.
+  constexpr int EPIX = CW * 4;
+  constexpr int EIT = (32 * EPIX + 63) / 64;
+  const bool vec_ok = (a.cout & 7) == 0;
+  auto epilogue = [&](const Tile& c, int par, int hidle) {
+    unsigned char* eb = wave < 4 ? reinterpret_cast<unsigned char*>(wl + WSLOTS) + wave * 32 * EROW
+                                 : reinterpret_cast<unsigned char*>(zl + hidle * ZSLOTS) + (wave - 4) * 32 * EROW;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int y = c.y0 + wave * RW + r;
+      if (y >= a.ho) continue;
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int cl = q * 32 + v4 * 8 + g * 4;
+          const float4 bv = *reinterpret_cast<const float4*>(&bias_lds[par][cl]);
+          uint2 pk;
+          pk.x = unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 0] + bv.x)) |
+                 (unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 1] + bv.y)) << 16);
+          pk.y = unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 2] + bv.z)) |
+                 (unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 3] + bv.w)) << 16);
+          *reinterpret_cast<uint2*>(eb + l32 * EROW + cl * 2) = pk;
+        }
+      }
+      unsigned short* orow = os + ((int64_t(c.nn) * a.to + c.o) * a.ho + y) * int64_t(a.wo) * a.cout;
+#pragma unroll
+      for (int it = 0; it < EIT; ++it) {
+        const int piece = it * 64 + lane;
+        if (piece < 32 * EPIX) {
+          const int px = piece / EPIX, ch = (piece % EPIX) * 8;
+          const int xo = c.x0 + px, co = c.n0 + ch;
+          const uint4 v = *reinterpret_cast<const uint4*>(eb + px * EROW + ch * 2);
+          if (xo < a.wo && co < a.cout) {
+            unsigned short* op = orow + int64_t(xo) * a.cout + co;
+            if (vec_ok) {
+              // streaming store: the output is not read again by this kernel
+              __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(op));
+            } else {
+              const unsigned short* hv = reinterpret_cast<const unsigned short*>(&v);
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (co + e < a.cout) op[e] = hv[e];
+            }
+          }
+        }
+      }
+    }
+  };
+  auto bias_value = [&](const Tile& c) {
+    return (a.has_bias && tid < BN && c.n0 + tid < a.cout) ? bs[c.n0 + tid] : (unsigned short)0;
+  };
+
+  // Load cursor: the group after the one being computed (tiles without an
+  // active tap are skipped: they load nothing).  zoff holds the halo offsets
+  // of its tile.
+  Grp nx{ctile, 0, 0};
+  Tile nt = decode(ctile);
+  bool nx_ok = true;
+  auto nx_seek_tile = [&]() {  // from nx.t (inclusive) to the first tile with an active tap
+    for (;;) {
+      if (nt.nact > 0) {
+        nx.ti = 0;
+        nx.gz = 0;
+        halo_offsets(nt);
+        return;
+      }
+      nx.t = next_tile(nx.t);
+      if (nx.t < 0) {
+        nx_ok = false;
+        return;
+      }
+      nt = decode(nx.t);
+    }
+  };
+  auto nx_advance = [&]() {
+    if (++nx.gz == ngrp) {
+      nx.gz = 0;
+      if (++nx.ti == nt.nact) {
+        nx.t = next_tile(nx.t);
+        if (nx.t < 0) {
+          nx_ok = false;
+          return;
+        }
+        nt = decode(nx.t);
+        nx_seek_tile();
+      }
+    }
+  };
+  nx_seek_tile();
+
+  auto wait_halo_in_flight = [&]() {  // all but this wave's halo loads of the last group
+    switch (wave) {
+      case 0: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(0)) : "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(1)) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(2)) : "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(3)) : "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(4 % NW)) : "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(5 % NW)) : "memory"); break;
+      case 6: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(6 % NW)) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(7 % NW)) : "memory"); break;
+    }
+  };
+
+  // prologue: the first group's halo and first weight sub-stage
+  int hpar = 0;
+  if (nx_ok) {
+    const unsigned short* fp = halo_src(nt, nx.ti, nx.gz);
+    const unsigned char* wp = wsrc(nt, nx.ti, nx.gz * 2);
+#pragma unroll
+    for (int it = 0; it < ZIT; ++it) issue_z(fp, 0, it);
+#pragma unroll
+    for (int it = 0; it < WIT; ++it) issue_w(wp, 0, it);
+    nx_advance();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  int par = 0;
+  Tile ct = decode(ctile);
+  for (;;) {
+    zero_acc();
+    if (ct.nact == 0) {
+      if (tid < BN) bias_lds[par][tid] = bf16_to_f32(bias_value(ct));
+      __syncthreads();
+      epilogue(ct, par, hpar ^ 1);
+      __syncthreads();
+    } else {
+      const int ngt = ct.nact * ngrp;
+      const bool rows_in = ct.y0 + wave * RW < a.ho;  // wave-uniform
+      for (int gi = 0; gi < ngt; ++gi) {
+        const int ti = gi / ngrp, gz = gi - ti * ngrp;
+        const uint4* zb = zl + hpar * ZSLOTS;
+        unsigned short bval = 0;
+        if (gi == 0) bval = bias_value(ct);
+        const bool more = nx_ok;
+        // sub-stage 0: load W[1] <- (this group, second half), H[next] <- next group
+        {
+          const unsigned char* wp1 = wsrc(ct, ti, gz * 2 + 1);
+          const unsigned short* fpn = more ? halo_src(nt, nx.ti, nx.gz) : xs;
+          const int hn = __builtin_amdgcn_readfirstlane(hpar ^ 1);
+          compute(zb, wl, rows_in, std::integral_constant<int, 0>{}, std::integral_constant<int, WIT + ZIT>{},
+                  std::integral_constant<int, NSTEP>{}, [&](int k) {
+                    if (k < WIT) issue_w(wp1, 1, k);
+                    else if (more) issue_z(fpn, hn, k - WIT);
+                  });
+        }
+        if (more) wait_halo_in_flight();
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+        __syncthreads();
+        // sub-stage 1: load W[0] <- next group, first half
+        {
+          const unsigned char* wpn = more ? wsrc(nt, nx.ti, nx.gz * 2) : wpk;
+          compute(zb, wl + WSLOTS, rows_in, std::integral_constant<int, 1>{}, std::integral_constant<int, WIT>{},
+                  std::integral_constant<int, (NSTEP + 1) / 2>{}, [&](int k) {
+                    if (more) issue_w(wpn, 0, k);
+                  });
+        }
+        if (more) nx_advance();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        hpar ^= 1;
+      }
+      epilogue(ct, par, hpar ^ 1);
+      __syncthreads();
+    }
+    par ^= 1;
+    ctile = next_tile(ctile);
+    if (ctile < 0) break;
+    ct = decode(ctile);
+  }
+#endif
+}
+
 // fp32 path: one output element per thread, direct loops in the order of the
 // definition (taps, rows, columns, channels) with fp32 fused multiply-add.
 __global__ __launch_bounds__(256) void conv_f32_direct(ConvArgs a) {
@@ -641,31 +1053,62 @@ int device_cus(int dev) {
 // bf16 path: optionally repack the weights into the plan's workspace, then
 // run the persistent conv kernel with min(tiles, compute units) workgroups,
 // one per compute unit.
-template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
-hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
+// Repack the weights into the stage-ordered layout of the bf16 kernels.
+template <int BN, int KS, int CB>
+hipError_t pack_bf16(const ConvArgs& a, hipStream_t s) {
   using T = WTile<BN, KS, CB>;
-  if (pack) {
-    const unsigned short* w = static_cast<const unsigned short*>(a.w);
-    uint4* wpk = static_cast<uint4*>(const_cast<void*>(a.wpk));
-    int cout = a.cout, kt = a.kt, cin = a.cin, nblk = a.nblk_n;
-    int64_t total = int64_t(kt) * (cin / CB) * nblk * T::WSLOTS;
-    const unsigned pgrid = unsigned(std::min<int64_t>((total + 255) / 256, 4096));
-    void* pargs[] = {&w, &wpk, &cout, &kt, &cin, &nblk, &total};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_weights<BN, KS, CB>), dim3(pgrid),
-                                         dim3(256), pargs, 0, s);
-    if (e != hipSuccess) return e;
-  }
-  if (!conv) return hipSuccess;
-  // as many persistent workgroups as fit on the device at once
-  const void* kernel = reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF, OCC>);
+  const unsigned short* w = static_cast<const unsigned short*>(a.w);
+  uint4* wpk = static_cast<uint4*>(const_cast<void*>(a.wpk));
+  int cout = a.cout, kt = a.kt, cin = a.cin, nblk = a.nblk_n;
+  int64_t total = int64_t(kt) * (cin / CB) * nblk * T::WSLOTS;
+  const unsigned pgrid = unsigned(std::min<int64_t>((total + 255) / 256, 4096));
+  void* pargs[] = {&w, &wpk, &cout, &kt, &cin, &nblk, &total};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&pack_weights<BN, KS, CB>), dim3(pgrid), dim3(256), pargs, 0,
+                         s);
+}
+
+// Launch a persistent bf16 kernel with as many workgroups as fit on the
+// device at once (the per-CU occupancy is queried once per kernel).
+template <const void* (*KernelOf)()>
+hipError_t launch_persistent(const ConvArgs& a, int64_t tiles, int cus, int threads, hipStream_t s) {
+  const void* kernel = KernelOf();
   static std::atomic<int> per_cu{0};
   int occ = per_cu.load(std::memory_order_relaxed);
   if (occ <= 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, WM * WN * 64, 0) != hipSuccess || occ <= 0)
-      occ = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess || occ <= 0) occ = 1;
     per_cu.store(occ, std::memory_order_relaxed);
   }
-  return launch_conv(kernel, a, std::min<int64_t>(tiles, int64_t(cus) * occ), s, WM * WN * 64);
+  return launch_conv(kernel, a, std::min<int64_t>(tiles, int64_t(cus) * occ), s, threads);
+}
+
+template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
+const void* mfma_kernel() {
+  return reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF, OCC>);
+}
+template <int BN, int TH, int WM>
+const void* g32_kernel() {
+  return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM>);
+}
+
+template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
+hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
+  if (pack) {
+    const hipError_t e = pack_bf16<BN, KS, CB>(a, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!conv) return hipSuccess;
+  return launch_persistent<&mfma_kernel<BN, TH, WM, WN, KS, CB, NBUF, OCC>>(a, tiles, cus, WM * WN * 64, s);
+}
+
+// The group-staged 3x3 kernel (16-channel weight sub-stages, same packing).
+template <int BN, int TH, int WM>
+hipError_t launch_g32(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
+  if (pack) {
+    const hipError_t e = pack_bf16<BN, 3, 16>(a, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!conv) return hipSuccess;
+  return launch_persistent<&g32_kernel<BN, TH, WM>>(a, tiles, cus, WM * 64, s);
 }
 
 }  // namespace
@@ -770,11 +1213,9 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     case CC3D_K_F32_DIRECT:
       e = launch_conv(reinterpret_cast<const void*>(&conv_f32_direct), a, in.tiles, s);
       break;
-    case CC3D_K_BF16_S3_N96: e = launch_bf16<96, 16, 4, 1, 3, 16, 3, 1>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S3_N96_X2: e = launch_bf16<96, 8, 4, 1, 3, 16, 2, 2>(a, in.tiles, cus, pack, runs, s); break;
-    case CC3D_K_BF16_S3_N96_W8: e = launch_bf16<96, 16, 8, 1, 3, 16, 3, 2>(a, in.tiles, cus, pack, runs, s); break;
-    case CC3D_K_BF16_S3_N192_W8: e = launch_bf16<192, 8, 4, 2, 3, 16, 2, 2>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16, 3, 2>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N96_G32W8: e = launch_g32<96, 16, 8>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S1_N192:
       if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64, 2, 1>(a, in.tiles, cus, pack, runs, s);
       else e = launch_bf16<192, 8, 2, 2, 1, 32, 3, 1>(a, in.tiles, cus, pack, runs, s);

@@ -10,14 +10,12 @@
 // MFMA kernels (block tile = block_m output pixels x block_n output channels).
 enum cc3d_kernel_id : int32_t {
   CC3D_K_F32_DIRECT = 0,     // fp32, any spatial parameters, one output per thread
-  CC3D_K_BF16_S3_N192 = 1,   // (retired) 3x3 spatial, 256 px (8x32) x 192 channels
-  CC3D_K_BF16_S3_N96 = 2,    // 3x3 spatial, 512 px (16x32) x 96 channels
   CC3D_K_BF16_S3_N32 = 3,    // 3x3 spatial, 256 px (8x32) x 32 channels, any C_out
   CC3D_K_BF16_S1_N192 = 4,   // 1x1 spatial, 256 px (8x32) x 192 channels
   CC3D_K_BF16_S1_N32 = 5,    // 1x1 spatial, 256 px (8x32) x 32 channels, any C_out
   CC3D_K_BF16_S3_N96_X2 = 6, // 3x3 spatial, 256 px (8x32) x 96 channels, two workgroups per CU
-  CC3D_K_BF16_S3_N96_W8 = 7, // 3x3 spatial, 512 px (16x32) x 96 channels, 8 waves (2 per SIMD)
-  CC3D_K_BF16_S3_N192_W8 = 8, // 3x3 spatial, 256 px (8x32) x 192 channels, 8 waves (2 per SIMD)
+  CC3D_K_BF16_S3_N96_G32W8 = 10, // 3x3 spatial, 512 px (16x32) x 96 channels, halo staged by 32
+                                 // channels, 8 waves (two per SIMD, 2 rows each)
 };
 
 struct cc3d_plan {

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <string>
 
 #include "cc3d_internal.h"
 
@@ -34,25 +35,62 @@ struct Variant {
   const char* name;
 };
 
-// Tile choice for bf16.  The patch width is 32 output columns (one MFMA
+// bf16 kernel variants.  The patch width is 32 output columns (one MFMA
 // operand block of pixels); rows and channel tiles trade accumulator
-// registers against LDS and L2 traffic per MFMA.
-Variant choose_bf16(const cc3d_desc_t& d) {
+// registers against LDS and L2 traffic per MFMA.  variant_for() gives the
+// named variant's geometry for a call, or nothing when it cannot run it.
+bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   const bool s3 = d.k_h == 3;
-  if (s3) {
-    if (d.c_out % 96 == 0) return {CC3D_K_BF16_S3_N96_X2, 8, 32, 96, 16, "bf16_s3_n96_p8x32_x2"};
-    return {CC3D_K_BF16_S3_N32, 8, 32, 32, 16, "bf16_s3_n32_p8x32"};
-  }
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
+  const std::string n(name);
+  if (n == "bf16_s3_n96_p16x32_g32") {
+    *v = {CC3D_K_BF16_S3_N96_G32W8, 16, 32, 96, 16, "bf16_s3_n96_p16x32_g32"};
+    return s3 && d.c_out % 96 == 0 && d.c_in % 32 == 0;
+  }
+  if (n == "bf16_s3_n96_p8x32_x2") {
+    *v = {CC3D_K_BF16_S3_N96_X2, 8, 32, 96, 16, "bf16_s3_n96_p8x32_x2"};
+    return s3 && d.c_out % 96 == 0;
+  }
+  if (n == "bf16_s3_n32_p8x32") {
+    *v = {CC3D_K_BF16_S3_N32, 8, 32, 32, 16, "bf16_s3_n32_p8x32"};
+    return s3;
+  }
   // the 192-channel tile stages at least 32 input channels (its stage buffer
   // must also hold the epilogue's output staging)
-  if (d.c_out % 192 == 0 && cb >= 32) return {CC3D_K_BF16_S1_N192, 8, 32, 192, cb, "bf16_s1_n192_p8x32"};
-  return {CC3D_K_BF16_S1_N32, 8, 32, 32, cb, "bf16_s1_n32_p8x32"};
+  if (n == "bf16_s1_n192_p8x32") {
+    *v = {CC3D_K_BF16_S1_N192, 8, 32, 192, cb, "bf16_s1_n192_p8x32"};
+    return !s3 && d.c_out % 192 == 0 && cb >= 32;
+  }
+  if (n == "bf16_s1_n32_p8x32") {
+    *v = {CC3D_K_BF16_S1_N32, 8, 32, 32, cb, "bf16_s1_n32_p8x32"};
+    return !s3;
+  }
+  return false;
+}
+
+// Default choice.  Large 3x3 maps take 16x32 patches with the halo staged by
+// 32 channels and one workgroup per compute unit; small ones keep two smaller
+// workgroups per compute unit so that every unit gets tiles.
+const char* default_variant(const cc3d_desc_t& d) {
+  if (d.k_h == 3) {
+    if (d.c_out % 96 == 0) {
+      const int64_t big_tiles = int64_t(d.n) * ((d.h + 15) / 16) * ((d.w + 31) / 32) * (d.c_out / 96) *
+                                std::max(1, d.t_x);
+      if (d.c_in % 32 == 0 && big_tiles >= 1024) return "bf16_s3_n96_p16x32_g32";
+      return "bf16_s3_n96_p8x32_x2";
+    }
+    return "bf16_s3_n32_p8x32";
+  }
+  const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
+  if (d.c_out % 192 == 0 && cb >= 32) return "bf16_s1_n192_p8x32";
+  return "bf16_s1_n32_p8x32";
 }
 
 }  // namespace
 
-extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out) {
+namespace {
+
+cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t* out) {
   if (out) *out = nullptr;
   if (!desc || !out) return refuse(CC3D_ERR_INVALID_ARG);
   const cc3d_desc_t d = *desc;
@@ -138,7 +176,11 @@ extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t
       delete p;
       return refuse(CC3D_ERR_UNSUPPORTED);
     }
-    const Variant v = choose_bf16(d);
+    Variant v{};
+    if (!variant_for(d, kernel ? kernel : default_variant(d), &v)) {
+      delete p;
+      return refuse(CC3D_ERR_UNSUPPORTED);
+    }
     in.kernel_id = v.id;
     p->tile_h = v.tile_h;
     p->tile_w = v.tile_w;
@@ -156,6 +198,10 @@ extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t
     in.workspace_bytes = p->wpk_bytes;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);
   } else {
+    if (kernel && std::strcmp(kernel, "f32_direct") != 0) {
+      delete p;
+      return refuse(CC3D_ERR_UNSUPPORTED);
+    }
     const int64_t frame_el = int64_t(h_out) * w_out * d.c_out;
     if (frame_el >= (int64_t(1) << 31) || int64_t(d.h) * d.w * d.c_in >= (int64_t(1) << 31)) {
       delete p;
@@ -175,6 +221,19 @@ extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t
   p->info = in;
   *out = p;
   return CC3D_OK;
+}
+
+}  // namespace
+
+extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out) {
+  return plan_impl(desc, nullptr, out);
+}
+
+extern "C" cc3d_status_t causal_conv3d_plan_variant(const cc3d_desc_t* desc, const char* kernel_name,
+                                                    cc3d_plan_t* out) {
+  if (out) *out = nullptr;
+  if (!kernel_name) return refuse(CC3D_ERR_INVALID_ARG);
+  return plan_impl(desc, kernel_name, out);
 }
 
 extern "C" cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_info_t* info) {

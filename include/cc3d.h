@@ -141,6 +141,25 @@ typedef struct cc3d_counters {
  */
 cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
 
+/*
+ * As causal_conv3d_plan, but run the call with the named kernel variant
+ * instead of the default choice (for tests that pin a variant and for
+ * tuning; the name is the one plan_info reports).  Variants:
+ *   "bf16_s3_n96_p16x32_g32"  3x3, C_out % 96 == 0, C_in % 32 == 0
+ *                              (default for large maps)
+ *   "bf16_s3_n96_p8x32_x2"    3x3, C_out % 96 == 0
+ *   "bf16_s3_n32_p8x32"       3x3, any C_out
+ *   "bf16_s1_n192_p8x32"      1x1, C_out % 192 == 0, C_in % 32 == 0
+ *   "bf16_s1_n32_p8x32"       1x1, any C_out
+ *   "f32_direct"              fp32
+ * Every variant computes the same operation; bf16 results of different
+ * variants may differ in the last bit (fp32 accumulation order).
+ * Returns CC3D_ERR_INVALID_ARG for a NULL name, CC3D_ERR_UNSUPPORTED for an
+ * unknown name or a variant that cannot run this call, and otherwise what
+ * causal_conv3d_plan returns.
+ */
+cc3d_status_t causal_conv3d_plan_variant(const cc3d_desc_t* desc, const char* kernel_name, cc3d_plan_t* out);
+
 /* Intervals, sizes, work and launch geometry of a plan (host only). */
 cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_info_t* info);
 

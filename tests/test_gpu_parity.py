@@ -89,6 +89,36 @@ def test_bf16_small_shapes_full_compare(cuda_device, case):
     assert torch.equal(co, z[:, z.shape[1] - keep:])
 
 
+# (C_in, C_out, H, W, T_x, T_cache, k, d_t, p_base, N, bias) run on the
+# group-staged 16x32 kernel (the default for large maps only), full compare.
+GROUP_STAGED = [
+    (32, 96, 20, 70, 2, 2, (3, 3, 3), 1, 2, 1, True),    # ragged rows (2nd patch row: 4 of 16) and columns
+    (64, 192, 17, 45, 3, 2, (3, 3, 3), 1, 2, 1, True),   # 2 channel groups, 2 channel blocks, 1-row tail
+    (96, 96, 33, 64, 4, 2, (3, 3, 3), 1, 2, 1, True),    # 3 channel groups, exact columns
+    (32, 96, 16, 32, 1, 0, (3, 3, 3), 1, 2, 2, True),    # batch 2, one active tap (p_l = 2)
+    (32, 96, 18, 40, 4, 2, (3, 3, 3), 2, 4, 1, True),    # temporal dilation 2
+    (32, 96, 16, 40, 3, 1, (2, 3, 3), 1, 1, 1, True),    # k_t = 2
+    (64, 96, 16, 33, 2, 0, (3, 3, 3), 1, 4, 1, True),    # p_base > (k_t-1)*d_t: bias-only frames
+    (32, 192, 24, 50, 2, 3, (3, 3, 3), 1, 2, 1, False),  # no bias, |C| > p_base
+]
+
+
+@pytest.mark.parametrize("variant", ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2"])
+@pytest.mark.parametrize("case", GROUP_STAGED, ids=[str(i) for i in range(len(GROUP_STAGED))])
+def test_bf16_pinned_variants_full_compare(cuda_device, case, variant):
+    cin, cout, h, w_, tx, tc, k, dt, p_base, n, bias = case
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
+                                   seed=synth.SEED_BASE + 300 + GROUP_STAGED.index(case), has_bias=bias)
+    y, co, plan = run(x, c, w, b, k=k, dt=dt, p_base=p_base, variant=variant)
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == variant
+    ref = _oracle(x, c, w, b, k=k, dt=dt, p_base=p_base)
+    assert tuple(y.shape) == ref.shape
+    assert_bf16_close(y, ref, variant)
+    z = x if c is None else torch.cat([c, x], 1)
+    assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
+
+
 def test_latent_config_full_compare(cuda_device):
     s = synth.LATENT
     x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],

@@ -252,3 +252,64 @@ def test_packed_entry_points_refuse_fp32_plans_and_null_pointers():
                                             None) == cc3d.CC3D_ERR_INVALID_ARG
     assert lib.causal_conv3d_forward_packed(None, base, base + mb, base + 2 * mb, base + 3 * mb, None,
                                             None) == cc3d.CC3D_ERR_INVALID_ARG
+
+
+def test_default_kernel_choice():
+    # large 3x3 maps with C_in % 32 == 0 and C_out % 96 == 0: the group-staged
+    # 16x32 kernel; small maps: the two-workgroup 8x32 kernel
+    big = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2))
+    assert big.info["kernel_name"] == "bf16_s3_n96_p16x32_g32"
+    assert big.info["block_m"] == 512 and big.info["block_n"] == 96
+    assert big.info["tiles"] == 23 * 20 * 2 * 4
+    lat = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2))
+    assert lat.info["kernel_name"] == "bf16_s3_n96_p8x32_x2"
+    odd = cc3d.causal_conv3d_plan(_desc(c_in=48, c_out=96, h=360, w=640, t_x=4, t_cache=2))
+    assert odd.info["kernel_name"] == "bf16_s3_n96_p8x32_x2"   # C_in % 32 != 0
+    head = cc3d.causal_conv3d_plan(_desc(c_in=96, c_out=3, h=720, w=1280, t_x=4, t_cache=2))
+    assert head.info["kernel_name"] == "bf16_s3_n32_p8x32"
+
+
+VARIANTS_3X3 = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32"]
+VARIANTS_1X1 = ["bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32"]
+
+
+def test_plan_variant_pins_the_kernel():
+    d3 = _desc(c_in=64, c_out=192, h=20, w=70, t_x=2, t_cache=2)
+    for name in VARIANTS_3X3:
+        p = cc3d.causal_conv3d_plan_variant(d3, name)
+        assert p.info["kernel_name"] == name
+        ref = cc3d.causal_conv3d_plan(d3)
+        for key in ("t_out", "h_out", "w_out", "t_cache_out", "flops_active", "bytes_conv"):
+            assert p.info[key] == ref.info[key], key
+    d1 = _desc(c_in=64, c_out=192, h=20, w=70, t_x=2, t_cache=2, k=(3, 1, 1), padding=(0, 0))
+    for name in VARIANTS_1X1:
+        assert cc3d.causal_conv3d_plan_variant(d1, name).info["kernel_name"] == name
+    f32 = _desc(dtype=torch.float32)
+    assert cc3d.causal_conv3d_plan_variant(f32, "f32_direct").info["kernel_name"] == "f32_direct"
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("bf16_s3_n96_p16x32_g32", dict(c_in=48, c_out=96)),      # C_in % 32 != 0
+    ("bf16_s3_n96_p16x32_g32", dict(c_in=32, c_out=64)),      # C_out % 96 != 0
+    ("bf16_s3_n96_p8x32_x2", dict(c_in=32, c_out=40)),
+    ("bf16_s1_n32_p8x32", dict(c_in=32, c_out=32)),           # 1x1 variant on a 3x3 call
+    ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, k=(3, 1, 1), padding=(0, 0))),
+    ("bf16_s1_n192_p8x32", dict(c_in=16, c_out=192, k=(3, 1, 1), padding=(0, 0))),  # C_in % 32 != 0
+    ("f32_direct", dict(c_in=32, c_out=32)),                  # fp32 kernel on a bf16 call
+    ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, dtype=torch.float32)),
+    ("no_such_kernel", dict(c_in=32, c_out=32)),
+])
+def test_plan_variant_refuses_what_it_cannot_run(name, kw):
+    with pytest.raises(cc3d.CC3DError) as e:
+        cc3d.causal_conv3d_plan_variant(_desc(**kw), name)
+    assert e.value.status == cc3d.CC3D_ERR_UNSUPPORTED
+
+
+def test_plan_variant_refuses_null_name():
+    lib = ctypes.CDLL(LIB)
+    lib.causal_conv3d_plan_variant.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p)]
+    lib.causal_conv3d_plan_variant.restype = ctypes.c_int
+    d = _desc()
+    h = ctypes.c_void_p(1)
+    assert lib.causal_conv3d_plan_variant(ctypes.addressof(d), None, ctypes.byref(h)) == cc3d.CC3D_ERR_INVALID_ARG
+    assert h.value is None
