@@ -881,6 +881,16 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     }
   };
 
+  // Workgroup barrier with explicit waits only: the caller has waited for
+  // the loads that must have landed; this waits for the wave's own LDS
+  // accesses.  (__syncthreads() would also drain every load in flight,
+  // including the next group's halo.)
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
   // prologue: the first group's halo and first weight sub-stage
   int hpar = 0;
   if (nx_ok) {
@@ -893,7 +903,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     nx_advance();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  barrier();
 
   int par = 0;
   Tile ct = decode(ctile);
@@ -901,9 +911,9 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     zero_acc();
     if (ct.nact == 0) {
       if (tid < BN) bias_lds[par][tid] = bf16_to_f32(bias_value(ct));
-      __syncthreads();
+      barrier();
       epilogue(ct, par, hpar ^ 1);
-      __syncthreads();
+      barrier();
     } else {
       const int ngt = ct.nact * ngrp;
       const bool rows_in = ct.y0 + wave * RW < a.ho;  // wave-uniform
@@ -927,7 +937,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
         if (more) wait_halo_in_flight();
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
-        __syncthreads();
+        barrier();
         // sub-stage 1: load W[0] <- next group, first half
         {
           const unsigned char* wpn = more ? wsrc(nt, nx.ti, nx.gz * 2) : wpk;
@@ -938,11 +948,12 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
         }
         if (more) nx_advance();
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        barrier();
         hpar ^= 1;
       }
+      // (the output stores may stay in flight across this barrier)
       epilogue(ct, par, hpar ^ 1);
-      __syncthreads();
+      barrier();
     }
     par ^= 1;
     ctile = next_tile(ctile);
