@@ -41,6 +41,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 struct ConvArgs {
   const void* x;
@@ -963,6 +964,256 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
 #endif
 }
 
+// bf16 kernel for few output channels (C_out <= 5; the decoder's RGB head):
+// 3x3 spatial taps, k_t = 3, unit temporal dilation, C_in = 32 * NCH.
+//
+// With three output channels a GEMM tile over output channels is almost all
+// padding, and the work is bound by reading the input once.  Each workgroup
+// owns a 16 x 32 output patch and walks the source frames z of Z = [C; X] in
+// time order, loading each frame's halo once (32 channels at a time, 64-byte
+// pixel pieces, through LDS).  One v_mfma_f32_16x16x32_bf16 multiplies 16
+// pixels x 32 channels of frame z by a 32 x 16 weight block whose 16 columns
+// are (temporal tap k, output channel co) pairs, so a single pass over frame z
+// produces its contributions to the three output frames o = z + p_l - k.  The
+// accumulator column for tap slot k holds output frame z + p_l - k: after
+// frame z the slot-2 columns hold a finished output frame, which is written
+// (bias added once, rounded to nearest even), and a lane shift by C_out
+// within each 16-lane row (DPP row_shr) moves slot k to slot k+1 for the next
+// frame.  Weights stay in registers for the whole kernel.
+template <int COUT, int NCH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv_bf16_few(ConvArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int TH = 16, TW = 32, HP = TH + 2, WP = TW + 2, PZ = 4;
+  constexpr int ZCH = HP * WP * PZ;
+  constexpr int ZSLOTS = (ZCH + 63) / 64 * 64;
+  constexpr int NT = 256, ZIT = (ZSLOTS + NT - 1) / NT;
+  constexpr int RW = 8;                     // output rows per wave (waves: 2 x 2 over the patch)
+  constexpr int NCOL = 3 * COUT;            // used accumulator columns
+  static_assert(NCOL <= 16 && NCH >= 1 && NCH <= 3, "few-channel kernel shape");
+  __shared__ uint4 zl[2 * ZSLOTS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int m = lane & 15, q = lane >> 4;   // A operand: pixel m, 8-channel piece q; D: column m
+
+  // persistent schedule over spatial patches, one contiguous range per XCD
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int nblk_here = (int(gridDim.x) >> 3) + (xcd < int(gridDim.x & 7) ? 1 : 0);
+  const int tq = a.ntiles >> 3, tr = a.ntiles & 7;
+  const int t_begin = xcd * tq + min(xcd, tr);
+  const int t_end = t_begin + tq + (xcd < tr ? 1 : 0);
+  int ctile = t_begin + slot;
+  if (ctile >= t_end) return;
+  auto next_tile = [&](int t) { return t + nblk_here < t_end ? t + nblk_here : -1; };
+
+  const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
+  const int frame_bytes = int(frame_el * 2);
+  const unsigned short* __restrict__ xs = static_cast<const unsigned short*>(a.x);
+  const unsigned short* __restrict__ cs = static_cast<const unsigned short*>(a.cache);
+  unsigned short* os = static_cast<unsigned short*>(a.out);
+  const int p_l = -a.delta[0];              // delta_0 = -p_l
+  const int z_lo = max(0, -p_l);            // first source frame any output reads
+  const int nst = (a.tz - z_lo) * NCH;      // stages per patch: (frame, 32-channel chunk)
+
+  // weights: B fragments [chunk][spatial tap], prepacked by the launcher
+  bf16x8_t wreg[NCH][9];
+  {
+    const uint4* wp = static_cast<const uint4*>(a.wpk);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int s = 0; s < 9; ++s) wreg[ch][s] = __builtin_bit_cast(bf16x8_t, wp[(ch * 9 + s) * 64 + lane]);
+  }
+  // bias of the output channel this lane emits (lanes of tap slot 2)
+  const int emit_co = m - 2 * COUT;
+  const bool emits = emit_co >= 0 && emit_co < COUT;
+  const float bias = (a.has_bias && emits) ? bf16_to_f32(static_cast<const unsigned short*>(a.b)[emit_co]) : 0.f;
+
+  auto uniform = [](const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v))));
+    const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v >> 32))));
+    return reinterpret_cast<const void*>((hi << 32) | lo);
+  };
+  struct Patch {
+    int nn, x0, y0;
+  };
+  auto decode = [&](int t) {
+    Patch p;
+    p.x0 = (t % a.tiles_x) * TW;
+    t /= a.tiles_x;
+    p.y0 = (t % a.tiles_y) * TH;
+    p.nn = t / a.tiles_y;
+    return p;
+  };
+  constexpr int OOB = int(0x80000000u);
+  int zoff[ZIT];
+  auto halo_offsets = [&](const Patch& c) {
+#pragma unroll
+    for (int it = 0; it < ZIT; ++it) {
+      const int id = tid + NT * it;
+      int off = OOB;
+      if (id < ZCH) {
+        const int pix = id / PZ;
+        const int qq = (id % PZ) ^ swz<PZ>(pix % WP);
+        const int y = c.y0 - 1 + pix / WP, x = c.x0 - 1 + pix % WP;
+        if (y >= 0 && y < a.h && x >= 0 && x < a.wd) off = ((y * a.wd + x) * a.cin + qq * 8) * 2;
+      }
+      zoff[it] = off;
+    }
+  };
+  auto issue_stage = [&](const Patch& c, int st, int buf) {
+    const int z = z_lo + st / NCH, ch = st % NCH;
+    const unsigned short* fp = static_cast<const unsigned short*>(
+        uniform((z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
+                          : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el) + ch * 32));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
+#pragma unroll
+    for (int it = 0; it < ZIT; ++it)
+      if (ZSLOTS % NT == 0 || it * NT + wave * 64 < ZSLOTS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(zl + buf * ZSLOTS + it * NT + wave * 64), 16, zoff[it], 0, 0, 0);
+  };
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  f32x4_t acc[RW];
+  // one stage: the 9 spatial taps of one 32-channel chunk.  Input row r of
+  // the wave's halo window, shifted by column tap c, feeds output rows r - ta
+  // for ta = 0..2; the 3 x (RW+2) operand reads are consumed in order from a
+  // ring of four registers, three reads ahead of their MFMAs.
+  constexpr int NRD = 3 * (RW + 2), AHEAD = 3;
+  // the swizzle depends on the column in the halo row only, so every row of
+  // one column tap is one per-lane slot plus a constant
+  int lane_slot[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int col = wc * 16 + m + c;
+    lane_slot[c] = (wr * RW * WP + col) * PZ + (q ^ swz<PZ>(col));
+  }
+  auto read_a = [&](const uint4* zb, int idx) {
+    const int c = idx / (RW + 2), r = idx % (RW + 2);
+    return __builtin_bit_cast(bf16x8_t, (zb + lane_slot[c])[r * WP * PZ]);
+  };
+  auto compute = [&](const uint4* zb, const bf16x8_t* wv) {
+    bf16x8_t ring[AHEAD + 1];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) ring[i] = read_a(zb, i);
+#pragma unroll
+    for (int idx = 0; idx < NRD; ++idx) {
+      if (idx + AHEAD < NRD) ring[(idx + AHEAD) % (AHEAD + 1)] = read_a(zb, idx + AHEAD);
+      __builtin_amdgcn_sched_barrier(0);
+      const int c = idx / (RW + 2), r = idx % (RW + 2);
+#pragma unroll
+      for (int ta = 0; ta < 3; ++ta)
+        if (r - ta >= 0 && r - ta < RW)
+          acc[r - ta] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[idx % (AHEAD + 1)], wv[ta * 3 + c], acc[r - ta], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Write output frame o from the tap-slot-2 columns (bias added once) with
+  // 16-bit buffer stores: a per-lane byte offset within the output row (out
+  // of range for lanes that hold no output), the row offset in a scalar.
+  int eoff[4];
+  auto emit_offsets = [&](const Patch& c) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int x = c.x0 + wc * 16 + q * 4 + v;
+      eoff[v] = (emits && x < a.wo) ? (x * COUT + emit_co) * 2 : OOB;
+    }
+  };
+  const int frame_out_bytes = a.ho * a.wo * COUT * 2;
+  auto emit = [&](const Patch& c, int o) {
+    if (o < 0 || o >= a.to) return;  // uniform
+    unsigned short* of = os + (int64_t(c.nn) * a.to + o) * a.ho * int64_t(a.wo) * COUT;
+    const __amdgpu_buffer_rsrc_t r_out =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(of)), 0, frame_out_bytes, 0x00020000);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int y = c.y0 + wr * RW + r;
+      if (y >= a.ho) break;  // uniform
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[r][v] + bias), r_out, eoff[v], y * a.wo * COUT * 2, 0);
+    }
+  };
+  auto rotate = [&]() {  // tap slot k -> k+1 (columns are lanes within 16-lane rows)
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        // (a vector element is copied to a scalar first: bit-casting the
+        // element expression itself does not read that element)
+        const float cur = acc[r][v];
+        acc[r][v] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(cur), 0x110 | COUT, 0xF, 0xF, true));
+      }
+  };
+
+  // load cursor: one stage ahead, across patch boundaries
+  int ltile = ctile, lst = 0;
+  Patch lp = decode(ltile);
+  halo_offsets(lp);
+  issue_stage(lp, 0, 0);
+  int pos = 0;
+  Patch cp = lp;
+  emit_offsets(cp);
+  for (;;) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // output frames no tap reaches (p_l > 2) are the bias alone
+    for (int o = 0; o < min(a.to, p_l - 2); ++o) emit(cp, o);
+    for (int zi = 0; zi < a.tz - z_lo; ++zi) {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch, ++pos) {
+        // next stage (possibly the next patch's first) into the other buffer
+        if (++lst == nst) {
+          lst = 0;
+          ltile = next_tile(ltile);
+          if (ltile >= 0) {
+            lp = decode(ltile);
+            halo_offsets(lp);
+          }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier();  // stage pos has landed everywhere; buffer (pos+1)%2 is free
+        if (ltile >= 0) issue_stage(lp, lst, (pos + 1) & 1);
+        compute(zl + (pos & 1) * ZSLOTS, wreg[ch]);
+      }
+      emit(cp, z_lo + zi + p_l - 2);
+      rotate();
+    }
+    ctile = next_tile(ctile);
+    if (ctile < 0) break;
+    cp = decode(ctile);
+    emit_offsets(cp);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
+// Packs the weights of the few-channel kernel into its B fragments: for
+// chunk ch, spatial tap s and lane l, the 8 weights of column n = l % 16
+// ((tap k, channel co) = (n / C_out, n % C_out), zero past 3 C_out) and
+// input channels ch*32 + (l/16)*8 + [0, 8).
+template <int COUT, int NCH>
+__global__ __launch_bounds__(64) void pack_weights_few(const unsigned short* __restrict__ w, uint4* __restrict__ wpk,
+                                                       int cin) {
+  const int ch = blockIdx.x / 9, s = blockIdx.x % 9, lane = threadIdx.x;
+  const int n = lane & 15, kq = lane >> 4;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (n < 3 * COUT) {
+    const int k = n / COUT, co = n % COUT;
+    v = *reinterpret_cast<const uint4*>(w + ((int64_t(co) * 3 + k) * 9 + s) * cin + ch * 32 + kq * 8);
+  }
+  wpk[(ch * 9 + s) * 64 + lane] = v;
+}
+
 // fp32 path: one output element per thread, direct loops in the order of the
 // definition (taps, rows, columns, channels) with fp32 fused multiply-add.
 __global__ __launch_bounds__(256) void conv_f32_direct(ConvArgs a) {
@@ -1100,6 +1351,34 @@ template <int BN, int TH, int WM>
 const void* g32_kernel() {
   return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM>);
 }
+template <int COUT, int NCH>
+const void* few_kernel() {
+  return reinterpret_cast<const void*>(&conv_bf16_few<COUT, NCH>);
+}
+
+// The few-output-channel kernel packs its weights as register fragments.
+template <int COUT, int NCH>
+hipError_t launch_few(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
+  if (pack) {
+    const unsigned short* w = static_cast<const unsigned short*>(a.w);
+    uint4* wpk = static_cast<uint4*>(const_cast<void*>(a.wpk));
+    int cin = a.cin;
+    void* pargs[] = {&w, &wpk, &cin};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&pack_weights_few<COUT, NCH>), dim3(NCH * 9),
+                                         dim3(64), pargs, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!conv) return hipSuccess;
+  return launch_persistent<&few_kernel<COUT, NCH>>(a, tiles, cus, 256, s);
+}
+template <int COUT>
+hipError_t launch_few_cin(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
+  switch (a.cin / 32) {
+    case 1: return launch_few<COUT, 1>(a, tiles, cus, pack, conv, s);
+    case 2: return launch_few<COUT, 2>(a, tiles, cus, pack, conv, s);
+    default: return launch_few<COUT, 3>(a, tiles, cus, pack, conv, s);
+  }
+}
 
 template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
 hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
@@ -1227,6 +1506,15 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     case CC3D_K_BF16_S3_N96_X2: e = launch_bf16<96, 8, 4, 1, 3, 16, 2, 2>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16, 3, 2>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S3_N96_G32W8: e = launch_g32<96, 16, 8>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_FEW:
+      switch (d.c_out) {
+        case 1: e = launch_few_cin<1>(a, in.tiles, cus, pack, runs, s); break;
+        case 2: e = launch_few_cin<2>(a, in.tiles, cus, pack, runs, s); break;
+        case 3: e = launch_few_cin<3>(a, in.tiles, cus, pack, runs, s); break;
+        case 4: e = launch_few_cin<4>(a, in.tiles, cus, pack, runs, s); break;
+        default: e = launch_few_cin<5>(a, in.tiles, cus, pack, runs, s); break;
+      }
+      break;
     case CC3D_K_BF16_S1_N192:
       if (plan->cin_chunk == 64) e = launch_bf16<192, 8, 2, 2, 1, 64, 2, 1>(a, in.tiles, cus, pack, runs, s);
       else e = launch_bf16<192, 8, 2, 2, 1, 32, 3, 1>(a, in.tiles, cus, pack, runs, s);

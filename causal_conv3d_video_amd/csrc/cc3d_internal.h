@@ -16,6 +16,8 @@ enum cc3d_kernel_id : int32_t {
   CC3D_K_BF16_S3_N96_X2 = 6, // 3x3 spatial, 256 px (8x32) x 96 channels, two workgroups per CU
   CC3D_K_BF16_S3_N96_G32W8 = 10, // 3x3 spatial, 512 px (16x32) x 96 channels, halo staged by 32
                                  // channels, 8 waves (two per SIMD, 2 rows each)
+  CC3D_K_BF16_S3_FEW = 11,   // 3x3 spatial, k_t = 3, d_t = 1, C_out <= 5, C_in in {32, 64, 96}:
+                             // 512 px (16x32) patches walked through time
 };
 
 struct cc3d_plan {

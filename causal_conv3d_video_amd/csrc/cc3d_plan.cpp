@@ -51,6 +51,10 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
     *v = {CC3D_K_BF16_S3_N96_X2, 8, 32, 96, 16, "bf16_s3_n96_p8x32_x2"};
     return s3 && d.c_out % 96 == 0;
   }
+  if (n == "bf16_s3_few_p16x32") {
+    *v = {CC3D_K_BF16_S3_FEW, 16, 32, d.c_out, 32, "bf16_s3_few_p16x32"};
+    return s3 && d.k_t == 3 && d.d_t == 1 && d.c_out <= 5 && d.c_in % 32 == 0 && d.c_in <= 96;
+  }
   if (n == "bf16_s3_n32_p8x32") {
     *v = {CC3D_K_BF16_S3_N32, 8, 32, 32, 16, "bf16_s3_n32_p8x32"};
     return s3;
@@ -79,6 +83,7 @@ const char* default_variant(const cc3d_desc_t& d) {
       if (d.c_in % 32 == 0 && big_tiles >= 1024) return "bf16_s3_n96_p16x32_g32";
       return "bf16_s3_n96_p8x32_x2";
     }
+    if (d.c_out <= 5 && d.k_t == 3 && d.d_t == 1 && d.c_in % 32 == 0 && d.c_in <= 96) return "bf16_s3_few_p16x32";
     return "bf16_s3_n32_p8x32";
   }
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
@@ -190,11 +195,13 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     p->nblk_n = (d.c_out + v.block_n - 1) / v.block_n;
     in.block_m = v.tile_h * v.tile_w;
     in.block_n = v.block_n;
-    in.tiles = int64_t(d.n) * t_out * p->tiles_y * p->tiles_x * p->nblk_n;
+    // the few-channel kernel's patches run through every output frame
+    in.tiles = int64_t(d.n) * (v.id == CC3D_K_BF16_S3_FEW ? 1 : t_out) * p->tiles_y * p->tiles_x * p->nblk_n;
     // packed weights: one stage tile of 16-byte slots per (tap, channel chunk, channel block)
     const int64_t ks = d.k_h;
     const int64_t slots = (int64_t(v.block_n) * ks * ks * (v.cin_chunk / 8) + 255) / 256 * 256;
     p->wpk_bytes = int64_t(d.k_t) * (d.c_in / v.cin_chunk) * p->nblk_n * slots * 16;
+    if (v.id == CC3D_K_BF16_S3_FEW) p->wpk_bytes = int64_t(d.c_in / 32) * 9 * 64 * 16;  // register fragments
     in.workspace_bytes = p->wpk_bytes;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);
   } else {

@@ -119,6 +119,33 @@ def test_bf16_pinned_variants_full_compare(cuda_device, case, variant):
     assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
 
 
+# (C_in, C_out, H, W, T_x, T_cache, p_base, N, bias) on the few-output-channel
+# kernel (frames walked in time order, tap slots rotated across lanes).
+FEW_CHANNELS = [
+    (96, 3, 20, 70, 4, 2, 2, 1, True),     # the RGB head's channels, ragged patches
+    (32, 1, 17, 33, 3, 0, 2, 1, True),     # one output channel, no cache (p_l = 2)
+    (64, 5, 16, 32, 2, 3, 2, 1, True),     # five channels, |C| > p_base (leading frame unused)
+    (96, 3, 18, 40, 2, 0, 4, 1, True),     # p_base = 4: two bias-only output frames
+    (32, 2, 9, 50, 5, 1, 2, 2, False),     # batch 2, no bias, p_l = 1
+    (64, 4, 33, 65, 1, 2, 2, 1, True),     # a single new frame behind a 2-frame cache
+]
+
+
+@pytest.mark.parametrize("case", FEW_CHANNELS, ids=[str(i) for i in range(len(FEW_CHANNELS))])
+def test_bf16_few_channel_kernel_full_compare(cuda_device, case):
+    cin, cout, h, w_, tx, tc, p_base, n, bias = case
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, device=DEV,
+                                   seed=synth.SEED_BASE + 400 + FEW_CHANNELS.index(case), has_bias=bias)
+    y, co, plan = run(x, c, w, b, p_base=p_base, variant="bf16_s3_few_p16x32")
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == "bf16_s3_few_p16x32"
+    ref = _oracle(x, c, w, b, p_base=p_base)
+    assert tuple(y.shape) == ref.shape
+    assert_bf16_close(y, ref, "few")
+    z = x if c is None else torch.cat([c, x], 1)
+    assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
+
+
 def test_latent_config_full_compare(cuda_device):
     s = synth.LATENT
     x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],

@@ -266,10 +266,17 @@ def test_default_kernel_choice():
     odd = cc3d.causal_conv3d_plan(_desc(c_in=48, c_out=96, h=360, w=640, t_x=4, t_cache=2))
     assert odd.info["kernel_name"] == "bf16_s3_n96_p8x32_x2"   # C_in % 32 != 0
     head = cc3d.causal_conv3d_plan(_desc(c_in=96, c_out=3, h=720, w=1280, t_x=4, t_cache=2))
-    assert head.info["kernel_name"] == "bf16_s3_n32_p8x32"
+    assert head.info["kernel_name"] == "bf16_s3_few_p16x32"
+    # one patch walks all output frames: tiles count patches only
+    assert head.info["tiles"] == 45 * 40 and head.info["block_n"] == 3
+    wide = cc3d.causal_conv3d_plan(_desc(c_in=128, c_out=3, h=64, w=64, t_x=4, t_cache=2))
+    assert wide.info["kernel_name"] == "bf16_s3_n32_p8x32"     # C_in > 96
+    dil = cc3d.causal_conv3d_plan(_desc(c_in=96, c_out=3, h=64, w=64, t_x=4, t_cache=4, dilation=(2, 1, 1), p_base=4))
+    assert dil.info["kernel_name"] == "bf16_s3_n32_p8x32"      # d_t = 2
 
 
 VARIANTS_3X3 = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32"]
+VARIANTS_FEW = ["bf16_s3_few_p16x32", "bf16_s3_n32_p8x32"]
 VARIANTS_1X1 = ["bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32"]
 
 
@@ -281,6 +288,9 @@ def test_plan_variant_pins_the_kernel():
         ref = cc3d.causal_conv3d_plan(d3)
         for key in ("t_out", "h_out", "w_out", "t_cache_out", "flops_active", "bytes_conv"):
             assert p.info[key] == ref.info[key], key
+    dfew = _desc(c_in=64, c_out=3, h=20, w=70, t_x=2, t_cache=2)
+    for name in VARIANTS_FEW:
+        assert cc3d.causal_conv3d_plan_variant(dfew, name).info["kernel_name"] == name
     d1 = _desc(c_in=64, c_out=192, h=20, w=70, t_x=2, t_cache=2, k=(3, 1, 1), padding=(0, 0))
     for name in VARIANTS_1X1:
         assert cc3d.causal_conv3d_plan_variant(d1, name).info["kernel_name"] == name
@@ -298,6 +308,11 @@ def test_plan_variant_pins_the_kernel():
     ("f32_direct", dict(c_in=32, c_out=32)),                  # fp32 kernel on a bf16 call
     ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, dtype=torch.float32)),
     ("no_such_kernel", dict(c_in=32, c_out=32)),
+    ("bf16_s3_few_p16x32", dict(c_in=32, c_out=6)),           # C_out > 5
+    ("bf16_s3_few_p16x32", dict(c_in=128, c_out=3)),          # C_in > 96
+    ("bf16_s3_few_p16x32", dict(c_in=48, c_out=3)),           # C_in % 32 != 0
+    ("bf16_s3_few_p16x32", dict(c_in=32, c_out=3, k=(2, 3, 3), p_base=1)),        # k_t != 3
+    ("bf16_s3_few_p16x32", dict(c_in=32, c_out=3, dilation=(2, 1, 1), p_base=4)),  # d_t != 1
 ])
 def test_plan_variant_refuses_what_it_cannot_run(name, kw):
     with pytest.raises(cc3d.CC3DError) as e:
