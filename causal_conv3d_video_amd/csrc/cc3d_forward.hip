@@ -854,9 +854,9 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     }
   };
   auto nx_advance = [&]() {
-    if (++nx.gz == ngrp) {
-      nx.gz = 0;
-      if (++nx.ti == nt.nact) {
+    if (++nx.ti == nt.nact) {
+      nx.ti = 0;
+      if (++nx.gz == ngrp) {
         nx.t = next_tile(nx.t);
         if (nx.t < 0) {
           nx_ok = false;
@@ -919,7 +919,10 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
       const int ngt = ct.nact * ngrp;
       const bool rows_in = ct.y0 + wave * RW < a.ho;  // wave-uniform
       for (int gi = 0; gi < ngt; ++gi) {
-        const int ti = gi / ngrp, gz = gi - ti * ngrp;
+        // group-major order: the active taps of one 32-channel group run back
+        // to back, so a source frame's group is reused by the output frames of
+        // the neighbouring tiles within a few groups, while it is still in L2
+        const int gz = gi / ct.nact, ti = gi - gz * ct.nact;
         const uint4* zb = zl + hpar * ZSLOTS;
         unsigned short bval = 0;
         if (gi == 0) bval = bias_value(ct);

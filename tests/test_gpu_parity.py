@@ -100,6 +100,8 @@ GROUP_STAGED = [
     (32, 96, 16, 40, 3, 1, (2, 3, 3), 1, 1, 1, True),    # k_t = 2
     (64, 96, 16, 33, 2, 0, (3, 3, 3), 1, 4, 1, True),    # p_base > (k_t-1)*d_t: bias-only frames
     (32, 192, 24, 50, 2, 3, (3, 3, 3), 1, 2, 1, False),  # no bias, |C| > p_base
+    (32, 96, 16, 40, 1, 4, (3, 3, 3), 2, 4, 1, True),    # d_t = 2, one new frame: some carried frames
+                                                          # are read by no tap (copied, not fused)
 ]
 
 
