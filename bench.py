@@ -36,7 +36,10 @@ def _parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=3,
+                   help="untimed warm-up steps (at least; warm-up also lasts at least --warm-seconds)")
+    p.add_argument("--warm-seconds", type=float, default=0.5,
+                   help="minimum warm-up time: the GPU clocks ramp up over the first ~0.2 s of load")
     p.add_argument("--kernel-launches", type=int, default=20,
                    help="launches per signature for the per-kernel timing")
     p.add_argument("--cpu-seconds", type=float, default=25.0,
@@ -101,10 +104,11 @@ def run_step(work, stream, packed=False):
                                            cout_buf, stream)
 
 
-def time_kernels(work, launches, stream):
+def time_kernels(work, launches, stream, warm_seconds=0.2):
     """Average conv-kernel launch time per signature at the steady-state chunk
     (cache present): weights packed once, then causal_conv3d_forward_packed
-    launches only the conv kernel; HIP events on the launch stream."""
+    launches only the conv kernel; HIP events on the launch stream.  Each
+    signature is first run untimed for warm_seconds (steady-state clocks)."""
     import torch
 
     import causal_conv3d_video_amd as cc3d
@@ -115,8 +119,13 @@ def time_kernels(work, launches, stream):
         plan = wk["plans"][c]
         cin_buf = wk["caches"][(c - 1) % 2][:, :plan.desc.t_cache]
         cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
-        for _ in range(3):
-            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c], None, stream)
+        t0 = time.perf_counter()
+        while True:
+            for _ in range(3):
+                cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c], None, stream)
+            stream.synchronize()
+            if time.perf_counter() - t0 >= warm_seconds:
+                break
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -247,9 +256,13 @@ def main():
         print(json.dumps({"only": args.only, "kernel": plan.info["kernel_name"], "launches": args.kernel_launches}))
         return
 
-    for _ in range(args.warmup):
+    # warm-up: at least args.warmup steps and at least args.warm_seconds
+    t0 = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t0 < args.warm_seconds:
         run_step(work, stream)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        done += 1
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -315,6 +328,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": done,   # at least --warmup, and at least --warm-seconds of load
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
