@@ -42,6 +42,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 struct ConvArgs {
   const void* x;
@@ -65,6 +67,13 @@ __device__ __forceinline__ __attribute__((unused)) float bf16_to_f32(unsigned sh
 // Round to nearest, ties to even (hardware conversion on gfx950).
 __device__ __forceinline__ __attribute__((unused)) unsigned short f32_to_bf16(float f) {
   return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
+}
+
+// Two fp32 values rounded to nearest even and packed as bf16, lo in bits
+// 0-15 (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ __attribute__((unused)) unsigned pack_bf16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2_t));
 }
 
 __device__ __forceinline__ int tap_delta(const ConvArgs& a, int k) {
@@ -776,15 +785,23 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     }
   };
 
-  // Epilogue (as in the kernel above): bias added once in fp32, round to
-  // nearest even, staged per wave through the idle weight buffer W[1] so
-  // global stores are whole 16-byte runs of channels.
+  // Epilogue: bias added once in fp32 (all of this lane's bias values are
+  // read before the first staging write), round to nearest even, staged per
+  // wave through the idle weight buffer W[1] (waves 0-3) or the idle halo
+  // buffer (waves 4-7) so global stores are whole 16-byte runs of channels.
+  // C_out is a multiple of BN here: every channel of the tile exists, and
+  // only the pixel column is range-checked.
   constexpr int EPIX = CW * 4;
   constexpr int EIT = (32 * EPIX + 63) / 64;
-  const bool vec_ok = (a.cout & 7) == 0;
   auto epilogue = [&](const Tile& c, int par, int hidle) {
     unsigned char* eb = wave < 4 ? reinterpret_cast<unsigned char*>(wl + WSLOTS) + wave * 32 * EROW
                                  : reinterpret_cast<unsigned char*>(zl + hidle * ZSLOTS) + (wave - 4) * 32 * EROW;
+    float4 bias[CW][4];
+#pragma unroll
+    for (int q = 0; q < CW; ++q)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        bias[q][v4] = *reinterpret_cast<const float4*>(&bias_lds[par][q * 32 + v4 * 8 + g * 4]);
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int y = c.y0 + wave * RW + r;
@@ -793,36 +810,26 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
       for (int q = 0; q < CW; ++q) {
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
-          const int cl = q * 32 + v4 * 8 + g * 4;
-          const float4 bv = *reinterpret_cast<const float4*>(&bias_lds[par][cl]);
+          const float4 bv = bias[q][v4];
+          const f32x16_t& v = acc[q][r];
           uint2 pk;
-          pk.x = unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 0] + bv.x)) |
-                 (unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 1] + bv.y)) << 16);
-          pk.y = unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 2] + bv.z)) |
-                 (unsigned(f32_to_bf16(acc[q][r][v4 * 4 + 3] + bv.w)) << 16);
-          *reinterpret_cast<uint2*>(eb + l32 * EROW + cl * 2) = pk;
+          pk.x = pack_bf16x2(v[v4 * 4 + 0] + bv.x, v[v4 * 4 + 1] + bv.y);
+          pk.y = pack_bf16x2(v[v4 * 4 + 2] + bv.z, v[v4 * 4 + 3] + bv.w);
+          *reinterpret_cast<uint2*>(eb + l32 * EROW + (q * 32 + v4 * 8 + g * 4) * 2) = pk;
         }
       }
-      unsigned short* orow = os + ((int64_t(c.nn) * a.to + c.o) * a.ho + y) * int64_t(a.wo) * a.cout;
+      unsigned short* orow = os + ((int64_t(c.nn) * a.to + c.o) * a.ho + y) * int64_t(a.wo) * a.cout + c.n0;
 #pragma unroll
       for (int it = 0; it < EIT; ++it) {
         const int piece = it * 64 + lane;
         if (piece < 32 * EPIX) {
           const int px = piece / EPIX, ch = (piece % EPIX) * 8;
-          const int xo = c.x0 + px, co = c.n0 + ch;
+          const int xo = c.x0 + px;
           const uint4 v = *reinterpret_cast<const uint4*>(eb + px * EROW + ch * 2);
-          if (xo < a.wo && co < a.cout) {
-            unsigned short* op = orow + int64_t(xo) * a.cout + co;
-            if (vec_ok) {
-              // streaming store: the output is not read again by this kernel
-              __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(op));
-            } else {
-              const unsigned short* hv = reinterpret_cast<const unsigned short*>(&v);
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (co + e < a.cout) op[e] = hv[e];
-            }
-          }
+          // streaming store: the output is not read again by this kernel
+          if (xo < a.wo)
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v),
+                                        reinterpret_cast<u32x4_t*>(orow + int64_t(xo) * a.cout + ch));
         }
       }
     }

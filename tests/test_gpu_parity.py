@@ -263,18 +263,27 @@ def test_repeated_runs_are_bitwise_identical(cuda_device):
     assert torch.equal(y1, y2)
 
 
-def test_epilogue_rounds_to_nearest_even(cuda_device):
+@pytest.mark.parametrize("cin,cout,variant", [
+    (16, 192, None),
+    (32, 96, "bf16_s3_n96_p16x32_g32"),
+    (16, 32, "bf16_s3_n32_p8x32"),
+    (32, 3, "bf16_s3_few_p16x32"),
+])
+def test_epilogue_rounds_to_nearest_even(cuda_device, cin, cout, variant):
     """With a single unit source value the fp32 sum is exactly w + b, so the
-    bf16 output must equal that exact value rounded to nearest even."""
-    cin, cout, h, w_ = 16, 192, 8, 32
+    bf16 output must equal that exact value rounded to nearest even (every
+    bf16 kernel's epilogue)."""
+    h, w_ = 8, 32
     g = torch.Generator(device=DEV).manual_seed(5)
     w = torch.randn((cout, 3, 3, 3, cin), generator=g, device=DEV).to(torch.bfloat16)
     b = (torch.randn((cout,), generator=g, device=DEV) * 3).to(torch.bfloat16)
     x = torch.zeros((1, 1, h, w_, cin), dtype=torch.bfloat16, device=DEV)
     c = torch.zeros((1, 2, h, w_, cin), dtype=torch.bfloat16, device=DEV)
     c[0, 1, 3, 5, 7] = 1.0
-    y, _, _ = run(x, c, w, b)
+    y, _, plan = run(x, c, w, b, variant=variant)
     torch.cuda.synchronize()
+    if variant is not None:
+        assert plan.info["kernel_name"] == variant
     ref = _oracle(x, c, w, b)
     ref_bf16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16)  # exact in fp32
     assert torch.equal(y.cpu().view(torch.int16), ref_bf16.view(torch.int16))
