@@ -45,7 +45,8 @@ def _parse():
     p.add_argument("--cpu-seconds", type=float, default=25.0,
                    help="target CPU time of the oracle baseline sample (0 disables it)")
     p.add_argument("--only", default=None,
-                   help="profiling aid: run only this signature's conv kernel --kernel-launches times")
+                   help="profiling aid: run only this signature's conv kernel, --warm-seconds of untimed "
+                        "launches and then --kernel-launches counted ones")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="profiling aid: run only a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -142,6 +143,52 @@ def time_kernels(work, launches, stream, warm_seconds=0.2):
             gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
             frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             flops=info["flops_active"], bytes=info["bytes_conv"], tiles=info["tiles"])
+    return res
+
+
+def time_single_calls(device, launches, stream, warm_seconds=0.2):
+    """Average conv-kernel launch time of each single-call configuration (the
+    latent, mid-resolution 192->192 and 384->192, full-resolution 96->96 and
+    96->3 calls, each with 2 cached frames), weights packed once; HIP events
+    on the launch stream after warm_seconds of untimed launches."""
+    import torch
+
+    import causal_conv3d_video_amd as cc3d
+    import synth
+
+    res = {}
+    for i, s in enumerate(synth.SINGLE_CALLS):
+        x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
+                                       device=device, seed=synth.SEED_BASE + 200 + i)
+        desc = cc3d.make_desc(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], k=s["k"],
+                              dilation=(s["dt"], 1, 1), padding=s["pad"], p_base=s["p_base"])
+        plan = cc3d.causal_conv3d_plan(desc)
+        out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
+        cc3d.causal_conv3d_pack_weights(plan, w, stream)
+        t0 = time.perf_counter()
+        while True:
+            for _ in range(3):
+                cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, None, stream)
+            stream.synchronize()
+            if time.perf_counter() - t0 >= warm_seconds:
+                break
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, None, stream)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        info = plan.info
+        res[s["name"]] = dict(
+            kernel=info["kernel_name"], us_per_launch=ms * 1e3,
+            tflops=info["flops_active"] / (ms * 1e-3) / 1e12,
+            frac_mfma_peak=info["flops_active"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
+            frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        del x, c, w, b, out, plan
+        torch.cuda.empty_cache()
     return res
 
 
@@ -250,10 +297,20 @@ def main():
         cin_buf = wk["caches"][1][:, :plan.desc.t_cache]
         cin_buf.copy_(torch.cat(wk["xs"][:2], 1)[:, -plan.desc.t_cache:])  # chunk 2's carried frames
         cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
+        # untimed launches for at least --warm-seconds, then the counted ones
+        # (a profile of this mode takes its statistics over the last
+        # --kernel-launches dispatches of the conv kernel)
+        warm, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.warm_seconds:
+            for _ in range(3):
+                cc3d.causal_conv3d_forward_packed(plan, wk["xs"][2], cin_buf, wk["b"], wk["outs"][2], None, stream)
+            stream.synchronize()
+            warm += 3
         for _ in range(args.kernel_launches):
             cc3d.causal_conv3d_forward_packed(plan, wk["xs"][2], cin_buf, wk["b"], wk["outs"][2], None, stream)
         torch.cuda.synchronize()
-        print(json.dumps({"only": args.only, "kernel": plan.info["kernel_name"], "launches": args.kernel_launches}))
+        print(json.dumps({"only": args.only, "kernel": plan.info["kernel_name"], "warm_launches": warm,
+                          "launches": args.kernel_launches}))
         return
 
     # warm-up: at least args.warmup steps and at least args.warm_seconds
@@ -317,6 +374,8 @@ def main():
     roof.update({"kernel": dom, "signature": sig, "us_per_launch": us,
                  "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
 
+    single = time_single_calls(device, args.kernel_launches, stream)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(work, args.cpu_seconds)
@@ -349,6 +408,7 @@ def main():
         "flops_nominal_per_step": flops_nominal,
         "wall_s_timed": wall,
         "signatures": kern,
+        "single_calls": single,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
