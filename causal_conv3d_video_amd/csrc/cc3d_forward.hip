@@ -33,6 +33,7 @@
 #include <cstdint>
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "cc3d_internal.h"
 
@@ -44,6 +45,8 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxFrameIv = 4;  // active-frame intervals (one per temporal tap, k_t <= 4)
 
 struct ConvArgs {
   const void* x;
@@ -58,6 +61,15 @@ struct ConvArgs {
   int delta[CC3D_MAX_KT];
   int tiles_x, tiles_y, nblk_n, ntiles;
   int has_bias;
+  // Group-staged kernel.  Output frames with at least one active tap, as
+  // disjoint intervals [act_lo, act_lo + act_n) (its tiles enumerate only
+  // these, ta_n frames in all, nat tiles), the other frames (output = bias),
+  // and this launch's scheduler counters: a tile counter per XCD and a count
+  // of finished workgroups, all zero at launch.
+  int act_lo[kMaxFrameIv], act_n[kMaxFrameIv], nact_iv, ta_n;
+  int ina_lo[kMaxFrameIv + 1], ina_n[kMaxFrameIv + 1], nina_iv;
+  int nat;
+  int* sched;
 };
 
 __device__ __forceinline__ __attribute__((unused)) float bf16_to_f32(unsigned short h) {
@@ -608,15 +620,30 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
 
-  // persistent schedule: each XCD walks one contiguous range of tiles
+  // Persistent schedule over the tiles of the output frames with an active
+  // tap.  Each XCD owns one contiguous range of them (neighbouring tiles
+  // share source frames in its L2).  A workgroup's first two tiles are
+  // fixed; it claims each later one while the tile before it runs, from its
+  // XCD's counter and, once that range is used up, from the other XCDs'
+  // counters, so XCDs that run at different clocks still finish together.
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int nblk_here = (int(gridDim.x) >> 3) + (xcd < int(gridDim.x & 7) ? 1 : 0);
-  const int tq = a.ntiles >> 3, tr = a.ntiles & 7;
-  const int t_begin = xcd * tq + min(xcd, tr);
-  const int t_end = t_begin + tq + (xcd < tr ? 1 : 0);
-  int ctile = t_begin + slot;
-  if (ctile >= t_end) return;
-  auto next_tile = [&](int t) { return t + nblk_here < t_end ? t + nblk_here : -1; };
+  auto xcd_wgs = [&](int x) { return (int(gridDim.x) >> 3) + (x < int(gridDim.x & 7) ? 1 : 0); };
+  auto xcd_begin = [&](int x) { return x * (a.nat >> 3) + min(x, a.nat & 7); };
+  auto xcd_len = [&](int x) { return (a.nat >> 3) + (x < (a.nat & 7) ? 1 : 0); };
+  auto fixed_tile = [&](int k) {  // k-th fixed tile (k = 0, 1) of this workgroup, or -1
+    const int r = slot + k * xcd_wgs(xcd);
+    return r < xcd_len(xcd) ? xcd_begin(xcd) + r : -1;
+  };
+  auto claim = [&](int x) {  // next claim number on XCD x's counter
+    return __hip_atomic_fetch_add(a.sched + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto claimed = [&](int x, int v) {  // the tile of claim v on XCD x, or -1 once its range is used up
+    const int r = 2 * xcd_wgs(x) + v;
+    return r < xcd_len(x) ? xcd_begin(x) + r : -1;
+  };
+  int ctile = fixed_tile(0), tnext = fixed_tile(1), tnn = -1;  // this tile, the next two
+  int steal = 0;  // (thread 0) offset of the XCD whose counter it claims from
+  __shared__ int claim_lds;
 
   const int ngrp = a.cin / 32;                   // 32-channel groups per tap
   const int nch = a.cin / 16;                    // 16-channel weight sub-stages per tap
@@ -633,10 +660,20 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     int k0, k1, k2, k3;
     int z0, z1, z2, z3;
   };
+  auto act_frame = [&](int j) {  // the j-th output frame with an active tap
+    int o = a.act_lo[0] + j;
+#pragma unroll
+    for (int i = 0; i + 1 < kMaxFrameIv; ++i)
+      if (i + 1 < a.nact_iv && j >= a.act_n[i]) {
+        j -= a.act_n[i];
+        o = a.act_lo[i + 1] + j;
+      }
+    return o;
+  };
   auto decode = [&](int t) {
     Tile c;
-    c.o = t % a.to;
-    t /= a.to;
+    c.o = act_frame(t % a.ta_n);
+    t /= a.ta_n;
     c.nb = t % a.nblk_n;
     t /= a.nblk_n;
     const int tile_x = t % a.tiles_x;
@@ -838,43 +875,31 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     return (a.has_bias && tid < BN && c.n0 + tid < a.cout) ? bs[c.n0 + tid] : (unsigned short)0;
   };
 
-  // Load cursor: the group after the one being computed (tiles without an
-  // active tap are skipped: they load nothing).  zoff holds the halo offsets
-  // of its tile.
+  // Load cursor: the group after the one being computed.  It enters the next
+  // tile during the current tile's last group, when that tile (tnext) is
+  // already known.  zoff holds the halo offsets of its tile.
   Grp nx{ctile, 0, 0};
-  Tile nt = decode(ctile);
-  bool nx_ok = true;
-  auto nx_seek_tile = [&]() {  // from nx.t (inclusive) to the first tile with an active tap
-    for (;;) {
-      if (nt.nact > 0) {
-        nx.ti = 0;
-        nx.gz = 0;
-        halo_offsets(nt);
-        return;
-      }
-      nx.t = next_tile(nx.t);
-      if (nx.t < 0) {
-        nx_ok = false;
-        return;
-      }
-      nt = decode(nx.t);
-    }
-  };
+  Tile nt{};
+  bool nx_ok = ctile >= 0;
+  if (nx_ok) {
+    nt = decode(ctile);
+    halo_offsets(nt);
+  }
   auto nx_advance = [&]() {
     if (++nx.ti == nt.nact) {
       nx.ti = 0;
       if (++nx.gz == ngrp) {
-        nx.t = next_tile(nx.t);
+        nx.gz = 0;
+        nx.t = tnext;
         if (nx.t < 0) {
           nx_ok = false;
           return;
         }
         nt = decode(nx.t);
-        nx_seek_tile();
+        halo_offsets(nt);
       }
     }
   };
-  nx_seek_tile();
 
   auto wait_halo_in_flight = [&]() {  // all but this wave's halo loads of the last group
     switch (wave) {
@@ -909,21 +934,17 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
 #pragma unroll
     for (int it = 0; it < WIT; ++it) issue_w(wp, 0, it);
     nx_advance();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  barrier();
 
   int par = 0;
-  Tile ct = decode(ctile);
-  for (;;) {
-    zero_acc();
-    if (ct.nact == 0) {
-      if (tid < BN) bias_lds[par][tid] = bf16_to_f32(bias_value(ct));
-      barrier();
-      epilogue(ct, par, hpar ^ 1);
-      barrier();
-    } else {
-      const int ngt = ct.nact * ngrp;
+  if (ctile >= 0) {
+    Tile ct = decode(ctile);
+    for (;;) {
+      zero_acc();
+      const bool claims = tnext >= 0;  // claim the tile after tnext while this one runs
+      const int ngt = ct.nact * ngrp;  // >= 1: only frames with an active tap have tiles
       const bool rows_in = ct.y0 + wave * RW < a.ho;  // wave-uniform
       for (int gi = 0; gi < ngt; ++gi) {
         // group-major order: the active taps of one 32-channel group run back
@@ -949,7 +970,12 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
         barrier();
-        // sub-stage 1: load W[0] <- next group, first half
+        // sub-stage 1: load W[0] <- next group, first half.  In the first
+        // group, thread 0 also claims a tile (the atomic's latency hides
+        // behind the sub-stage; the claim is published at its barrier).
+        const int cx = (xcd + steal) & 7;
+        int v = 0;
+        if (gi == 0 && claims && tid == 0) v = claim(cx);
         {
           const unsigned char* wpn = more ? wsrc(nt, nx.ti, nx.gz * 2) : wpk;
           compute(zb, wl + WSLOTS, rows_in, std::integral_constant<int, 1>{}, std::integral_constant<int, WIT>{},
@@ -957,19 +983,62 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
                     if (more) issue_w(wpn, 0, k);
                   });
         }
+        if (gi == 0 && claims && tid == 0) {
+          int t = claimed(cx, v);
+          while (t < 0 && steal < 7) {
+            ++steal;
+            const int x = (xcd + steal) & 7;
+            t = claimed(x, claim(x));
+          }
+          claim_lds = t;
+        }
         if (more) nx_advance();
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         barrier();
+        if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
         hpar ^= 1;
       }
       // (the output stores may stay in flight across this barrier)
       epilogue(ct, par, hpar ^ 1);
       barrier();
+      par ^= 1;
+      ctile = tnext;
+      tnext = tnn;
+      tnn = -1;
+      if (ctile < 0) break;
+      ct = decode(ctile);
     }
-    par ^= 1;
-    ctile = next_tile(ctile);
-    if (ctile < 0) break;
-    ct = decode(ctile);
+  }
+
+  // Output frames without an active tap hold the bias: every workgroup
+  // writes a strided share of them (C_out % 8 == 0: 16-byte runs).
+  {
+    const int64_t fpx = int64_t(a.ho) * a.wo;
+    const int cpp = a.cout >> 3;
+#pragma unroll 1
+    for (int i = 0; i < a.nina_iv; ++i) {
+      const int64_t per_n = int64_t(a.ina_n[i]) * fpx * cpp;
+      for (int64_t e = int64_t(blockIdx.x) * NT + tid; e < per_n * a.n; e += int64_t(gridDim.x) * NT) {
+        const int nn = int(e / per_n);
+        const int64_t r = e - nn * per_n;
+        const int cc = int(r % cpp);
+        unsigned short v8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v8[q] = a.has_bias ? bs[cc * 8 + q] : (unsigned short)0;
+        uint4 val;
+        __builtin_memcpy(&val, v8, 16);
+        *reinterpret_cast<uint4*>(os + ((int64_t(nn) * a.to + a.ina_lo[i]) * fpx + r / cpp) * a.cout + cc * 8) = val;
+      }
+    }
+  }
+
+  // The last workgroup to finish clears the counters for the next launch
+  // that uses them (its claims and every other workgroup's are done: each
+  // workgroup counts itself after its last claim).
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(a.sched + 8, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == int(gridDim.x) - 1)
+      for (int x = 0; x < 9; ++x) __hip_atomic_store(a.sched + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #endif
 }
@@ -1417,6 +1486,49 @@ namespace {
 
 enum RunMode { kPackAndRun, kPackOnly, kRunPacked };
 
+// The output frames with at least one active tap (the union of the taps'
+// output intervals [o_lo, o_hi)) as sorted disjoint intervals, their
+// complement in [0, T_o), and the number of tiles over the active frames.
+bool frame_intervals(const cc3d_plan* plan, ConvArgs& a) {
+  const cc3d_plan_info_t& in = plan->info;
+  std::pair<int, int> iv[CC3D_MAX_KT];
+  int n = 0;
+  for (int k = 0; k < plan->d.k_t; ++k)
+    if (in.taps[k].active) iv[n++] = {in.taps[k].o_lo, in.taps[k].o_hi};
+  std::sort(iv, iv + n);
+  a.nact_iv = 0;
+  a.ta_n = 0;
+  for (int i = 0; i < n; ++i) {
+    if (a.nact_iv > 0 && iv[i].first <= a.act_lo[a.nact_iv - 1] + a.act_n[a.nact_iv - 1]) {
+      const int hi = std::max(a.act_lo[a.nact_iv - 1] + a.act_n[a.nact_iv - 1], iv[i].second);
+      a.act_n[a.nact_iv - 1] = hi - a.act_lo[a.nact_iv - 1];
+    } else {
+      if (a.nact_iv == kMaxFrameIv) return false;
+      a.act_lo[a.nact_iv] = iv[i].first;
+      a.act_n[a.nact_iv] = iv[i].second - iv[i].first;
+      ++a.nact_iv;
+    }
+  }
+  a.nina_iv = 0;
+  int prev = 0;
+  for (int i = 0; i <= a.nact_iv; ++i) {
+    const int lo = i < a.nact_iv ? a.act_lo[i] : in.t_out;
+    if (lo > prev) {
+      a.ina_lo[a.nina_iv] = prev;
+      a.ina_n[a.nina_iv] = lo - prev;
+      ++a.nina_iv;
+    }
+    if (i < a.nact_iv) {
+      prev = a.act_lo[i] + a.act_n[i];
+      a.ta_n += a.act_n[i];
+    }
+  }
+  const int64_t nat = int64_t(a.n) * a.ta_n * a.tiles_y * a.tiles_x * a.nblk_n;
+  if (nat > INT32_MAX) return false;
+  a.nat = int(nat);
+  return true;
+}
+
 cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, const void* w, const void* b,
                        void* out, void* cache_out, void* stream, RunMode mode) {
   if (!plan) return invalid();
@@ -1482,6 +1594,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   a.nblk_n = plan->nblk_n;
   a.ntiles = int(in.tiles);
   a.has_bias = d.has_bias;
+  if (in.kernel_id == CC3D_K_BF16_S3_N96_G32W8 && !frame_intervals(plan, a)) return invalid();
 
   int cus = 256;
   if (bf16) {
@@ -1493,7 +1606,16 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     std::lock_guard<std::mutex> lock(plan->mu);
     if (!plan->wpk) {
       if (mode == kRunPacked) return invalid();  // nothing packed yet
-      if (hipMalloc(&plan->wpk, size_t(plan->wpk_bytes)) != hipSuccess) {
+      if (hipMalloc(&plan->wpk, size_t(in.workspace_bytes)) != hipSuccess) {
+        plan->wpk = nullptr;
+        cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
+        return CC3D_ERR_DEVICE;
+      }
+      // the scheduler counters start at zero (each launch leaves its slot so)
+      if (hipMemset(static_cast<char*>(plan->wpk) + plan->sched_off, 0,
+                    size_t(in.workspace_bytes - plan->sched_off)) != hipSuccess ||
+          hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(plan->wpk);
         plan->wpk = nullptr;
         cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
         return CC3D_ERR_DEVICE;
@@ -1503,6 +1625,8 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
       return invalid();
     }
     a.wpk = plan->wpk;
+    a.sched = reinterpret_cast<int*>(static_cast<char*>(plan->wpk) + plan->sched_off) +
+              int64_t(plan->sched_seq.fetch_add(1, std::memory_order_relaxed) % kSchedSlots) * kSchedInts;
     cus = device_cus(dev);
   }
 
@@ -1515,7 +1639,9 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
       break;
     case CC3D_K_BF16_S3_N96_X2: e = launch_bf16<96, 8, 4, 1, 3, 16, 2, 2>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16, 3, 2>(a, in.tiles, cus, pack, runs, s); break;
-    case CC3D_K_BF16_S3_N96_G32W8: e = launch_g32<96, 16, 8>(a, in.tiles, cus, pack, runs, s); break;
+    case CC3D_K_BF16_S3_N96_G32W8:
+      e = launch_g32<96, 16, 8>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
+      break;
     case CC3D_K_BF16_S3_FEW:
       switch (d.c_out) {
         case 1: e = launch_few_cin<1>(a, in.tiles, cus, pack, runs, s); break;

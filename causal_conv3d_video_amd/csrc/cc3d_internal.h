@@ -20,6 +20,13 @@ enum cc3d_kernel_id : int32_t {
                              // 512 px (16x32) patches walked through time
 };
 
+// Scheduler counters of the group-staged kernel, kept after the packed
+// weights in the plan's workspace: kSchedSlots slots of kSchedInts ints (a
+// tile counter per XCD and a finished-workgroup count).  Each launch takes
+// the next slot; the kernel leaves its slot zeroed when it finishes.
+constexpr int kSchedInts = 16;
+constexpr int kSchedSlots = 64;
+
 struct cc3d_plan {
   cc3d_desc_t d{};
   cc3d_plan_info_t info{};
@@ -33,8 +40,10 @@ struct cc3d_plan {
   // order, rewritten by every forward call.  Allocated on first use on the
   // device current at that time.
   int64_t wpk_bytes = 0;
+  int64_t sched_off = 0;   // byte offset of the scheduler counters in the workspace
   void* wpk = nullptr;
   int wpk_device = -1;
+  std::atomic<uint32_t> sched_seq{0};
   std::mutex mu;
 };
 

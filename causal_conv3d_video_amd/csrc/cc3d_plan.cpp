@@ -202,7 +202,8 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     const int64_t slots = (int64_t(v.block_n) * ks * ks * (v.cin_chunk / 8) + 255) / 256 * 256;
     p->wpk_bytes = int64_t(d.k_t) * (d.c_in / v.cin_chunk) * p->nblk_n * slots * 16;
     if (v.id == CC3D_K_BF16_S3_FEW) p->wpk_bytes = int64_t(d.c_in / 32) * 9 * 64 * 16;  // register fragments
-    in.workspace_bytes = p->wpk_bytes;
+    p->sched_off = (p->wpk_bytes + 255) / 256 * 256;
+    in.workspace_bytes = p->sched_off + int64_t(kSchedSlots) * kSchedInts * 4;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);
   } else {
     if (kernel && std::strcmp(kernel, "f32_direct") != 0) {

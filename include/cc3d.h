@@ -38,7 +38,10 @@
  * owns one device workspace (workspace_bytes, allocated by its first forward
  * call on the device current then, freed by causal_conv3d_plan_destroy): the
  * weights repacked into the kernel's stage order, rewritten by every forward
- * call before the convolution on the same stream.  Nothing else is kept.
+ * call before the convolution on the same stream, and 64 slots of tile
+ * counters for the group-staged kernel's dynamic schedule (each launch takes
+ * the next slot and leaves it zeroed when it completes, so at most 64
+ * convolutions of one plan may be in flight at once).  Nothing else is kept.
  * Threading: a plan's shape data is immutable and any thread may call
  * forward; because the workspace is rewritten per call, forward calls that
  * share one plan must be ordered on one stream (use one plan per stream for

@@ -254,6 +254,36 @@ def test_unread_frames_and_guard_bands_are_never_touched(cuda_device):
     assert_bf16_close(results[0], ref, "poisoned")
 
 
+def test_group_staged_schedule_writes_every_tile_across_launches(cuda_device):
+    """640 tiles on at most 256 workgroups: two fixed tiles each, the rest
+    claimed from per-XCD counters (and stolen across XCDs).  Every launch
+    takes the next of the plan's 64 counter slots, and the kernel leaves its
+    slot zeroed, so 130 launches reuse every slot twice.  The output is
+    poisoned with NaN before each launch: every tile must be written every
+    time, bitwise equal to the first launch and within tolerance of the oracle."""
+    import causal_conv3d_video_amd as cc3d
+    x, c, w, b = synth.conv_inputs(1, 32, 96, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 90)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant="bf16_s3_n96_p16x32_g32")
+    assert plan.info["tiles"] == 640
+    cc3d.causal_conv3d_pack_weights(plan, w)
+    first = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=DEV)
+    first.fill_(float("nan"))
+    cc3d.causal_conv3d_forward_packed(plan, x, c, b, first, None)
+    y = torch.empty_like(first)
+    bad = []
+    for i in range(130):
+        y.fill_(float("nan"))
+        cc3d.causal_conv3d_forward_packed(plan, x, c, b, y, None)
+        if not torch.equal(y, first):
+            bad.append(i)
+    torch.cuda.synchronize()
+    assert not bad, "launches with unwritten or different tiles: %s" % bad[:10]
+    assert bool(torch.isfinite(first).all())
+    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=90, tile_h=16)
+    ref = _oracle(x, c, w, b, points=pts)
+    assert_bf16_close(gather(first, pts), ref, "dynamic schedule")
+
+
 def test_repeated_runs_are_bitwise_identical(cuda_device):
     s = synth.MID_192
     x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], 64, 128, 4, 2, device=DEV, seed=synth.SEED_BASE + 70)
