@@ -914,6 +914,15 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     }
   };
 
+  // Wait for every vector memory operation.  The inline-asm waits are
+  // invisible to the compiler's own wait-count tracking; the builtin after
+  // it tells the compiler they have completed, so it does not drain loads
+  // again where it reuses the register of an earlier load or atomic.
+  auto vm_drain = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0), other counters unconstrained
+  };
+
   // Workgroup barrier with explicit waits only: the caller has waited for
   // the loads that must have landed; this waits for the wave's own LDS
   // accesses.  (__syncthreads() would also drain every load in flight,
@@ -934,7 +943,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
 #pragma unroll
     for (int it = 0; it < WIT; ++it) issue_w(wp, 0, it);
     nx_advance();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vm_drain();
     barrier();
   }
 
@@ -967,7 +976,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
                   });
         }
         if (more) wait_halo_in_flight();
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else vm_drain();
         if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
         barrier();
         // sub-stage 1: load W[0] <- next group, first half.  In the first
@@ -983,6 +992,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
                     if (more) issue_w(wpn, 0, k);
                   });
         }
+        asm volatile("" ::: "memory");  // the claim is read only after the sub-stage
         if (gi == 0 && claims && tid == 0) {
           int t = claimed(cx, v);
           while (t < 0 && steal < 7) {
@@ -993,7 +1003,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
           claim_lds = t;
         }
         if (more) nx_advance();
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        vm_drain();
         barrier();
         if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
         hpar ^= 1;
