@@ -192,6 +192,53 @@ def time_single_calls(device, launches, stream, warm_seconds=0.2):
     return res
 
 
+def time_decoder_signatures(device, launches, stream, warm_seconds=0.2):
+    """Every causal Conv3D signature of the 17-frame decoder at full size
+    (steady-state chunk: its frames plus a 2-frame cache): the default
+    kernel's average launch time (weights packed once, HIP events), and the
+    variant causal_conv3d_plan_autotune picks with its own timing."""
+    import torch
+
+    import causal_conv3d_video_amd as cc3d
+    import synth
+
+    res = {}
+    for i, s in enumerate(synth.DECODER_SIGNATURES):
+        x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
+                                       device=device, seed=synth.SEED_BASE + 400 + i)
+        desc = cc3d.make_desc(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], k=s["k"],
+                              dilation=(s["dt"], 1, 1), padding=s["pad"], p_base=s["p_base"])
+        plan = cc3d.causal_conv3d_plan(desc)
+        out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
+        cc3d.causal_conv3d_pack_weights(plan, w, stream)
+        t0 = time.perf_counter()
+        while True:
+            for _ in range(3):
+                cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, None, stream)
+            stream.synchronize()
+            if time.perf_counter() - t0 >= warm_seconds:
+                break
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, None, stream)
+        e1.record(stream)
+        e1.synchronize()
+        us = e0.elapsed_time(e1) / launches * 1e3
+        tuned, tuned_ms = cc3d.causal_conv3d_plan_autotune(desc, x, c, w, b, out, launches=5, stream=stream)
+        flops = plan.info["flops_active"]
+        res[s["name"]] = dict(kernel=plan.info["kernel_name"], us_per_launch=us,
+                              frac_mfma_peak=flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                              autotuned_kernel=tuned.info["kernel_name"], autotuned_us=tuned_ms * 1e3,
+                              flops=flops)
+        tuned.close()
+        plan.close()
+        del x, c, w, b, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(work, target_seconds):
     """The fp64 CPU oracle on a bounded sample of the same workload: random
     output pixels (all output channels) of the steady-state chunk of every
@@ -375,6 +422,7 @@ def main():
                  "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
 
     single = time_single_calls(device, args.kernel_launches, stream)
+    decoder = time_decoder_signatures(device, args.kernel_launches, stream)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -409,6 +457,7 @@ def main():
         "wall_s_timed": wall,
         "signatures": kern,
         "single_calls": single,
+        "decoder_signatures": decoder,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),

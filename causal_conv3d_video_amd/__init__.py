@@ -23,7 +23,8 @@ import torch
 
 __all__ = [
     "CC3DError", "Plan", "make_desc",
-    "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_info", "causal_conv3d_plan_destroy",
+    "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_autotune", "causal_conv3d_plan_info",
+    "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
     "causal_conv3d_status_string", "causal_conv3d_counters", "library_path", "EXPORTED_SYMBOLS",
 ]
@@ -32,7 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libcc3d.so")
 
 EXPORTED_SYMBOLS = (
-    "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_info", "causal_conv3d_plan_destroy",
+    "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_autotune", "causal_conv3d_plan_info",
+    "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
     "causal_conv3d_status_string", "causal_conv3d_counters",
 )
@@ -81,6 +83,9 @@ def _load():
     lib.causal_conv3d_plan.restype = ctypes.c_int
     lib.causal_conv3d_plan_variant.argtypes = [ctypes.POINTER(Desc), ctypes.c_char_p, ctypes.POINTER(vp)]
     lib.causal_conv3d_plan_variant.restype = ctypes.c_int
+    lib.causal_conv3d_plan_autotune.argtypes = [ctypes.POINTER(Desc)] + [vp] * 5 + [
+        ctypes.c_int, vp, ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_float)]
+    lib.causal_conv3d_plan_autotune.restype = ctypes.c_int
     lib.causal_conv3d_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.causal_conv3d_plan_info.restype = ctypes.c_int
     lib.causal_conv3d_plan_destroy.argtypes = [vp]
@@ -179,6 +184,26 @@ def causal_conv3d_plan_variant(desc, kernel_name):
     if st != CC3D_OK:
         raise CC3DError(st, "causal_conv3d_plan_variant")
     return Plan(h.value, desc)
+
+
+def causal_conv3d_plan_autotune(desc, x, cache_in, w, b, out, launches=5, stream=None):
+    """Time every bf16 variant that can run ``desc`` on these buffers and
+    return (plan of the fastest, with its weights packed; its ms per call).
+    Blocking; overwrites ``out``."""
+    probe = causal_conv3d_plan(desc)  # validates desc and gives the buffer shapes
+    try:
+        p = _marshal(probe, {"x": x, "cache_in": cache_in if desc.t_cache > 0 else None, "w": w,
+                             "b": b if desc.has_bias else None, "out": out})
+    finally:
+        probe.close()
+    h = ctypes.c_void_p()
+    ms = ctypes.c_float()
+    st = _lib.causal_conv3d_plan_autotune(ctypes.byref(desc), p["x"], p["cache_in"], p["w"], p["b"], p["out"],
+                                          int(launches), _stream_handle(stream, x), ctypes.byref(h),
+                                          ctypes.byref(ms))
+    if st != CC3D_OK:
+        raise CC3DError(st, "causal_conv3d_plan_autotune")
+    return Plan(h.value, desc), ms.value
 
 
 def causal_conv3d_plan_info(plan):

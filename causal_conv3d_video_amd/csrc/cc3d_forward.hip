@@ -1713,6 +1713,72 @@ extern "C" cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const vo
   return run_plan(plan, x, cache_in, nullptr, b, out, cache_out, stream, kRunPacked);
 }
 
+// Per-signature variant choice: every bf16 variant that can run the call is
+// timed on the caller's buffers and the fastest is kept.
+extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, const void* x, const void* cache_in,
+                                                     const void* w, const void* b, void* out, int launches,
+                                                     void* stream, cc3d_plan_t* out_plan, float* best_ms) {
+  static const char* const kCandidates[] = {"bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32",
+                                            "bf16_s3_few_p16x32",     "bf16_s1_n192_p8x32",   "bf16_s1_n32_p8x32"};
+  if (!out_plan) return invalid();
+  *out_plan = nullptr;
+  if (best_ms) *best_ms = 0.f;
+  if (!desc || launches < 1) return invalid();
+  if (desc->dtype != CC3D_BF16) return causal_conv3d_plan(desc, out_plan);  // one fp32 kernel
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    cc3d::g_device_error.fetch_add(1, std::memory_order_relaxed);
+    return CC3D_ERR_DEVICE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  cc3d_plan_t best = nullptr;
+  float best_t = 0.f;
+  cc3d_status_t st = CC3D_ERR_UNSUPPORTED;
+  for (const char* name : kCandidates) {
+    cc3d_plan_t p = nullptr;
+    const cc3d_status_t ps = causal_conv3d_plan_variant(desc, name, &p);
+    if (ps == CC3D_ERR_UNSUPPORTED) continue;
+    if (ps != CC3D_OK) {
+      st = ps;
+      break;
+    }
+    // first call packs the weights and warms up; then time the conv alone
+    cc3d_status_t rs = causal_conv3d_forward(p, x, cache_in, w, b, out, nullptr, stream);
+    if (rs == CC3D_OK && hipEventRecord(e0, s) != hipSuccess) rs = CC3D_ERR_DEVICE;
+    for (int i = 0; i < launches && rs == CC3D_OK; ++i)
+      rs = causal_conv3d_forward_packed(p, x, cache_in, b, out, nullptr, stream);
+    float ms = 0.f;
+    if (rs == CC3D_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                          hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+      rs = CC3D_ERR_DEVICE;
+    if (rs != CC3D_OK) {
+      (void)hipStreamSynchronize(s);
+      causal_conv3d_plan_destroy(p);
+      st = rs;
+      break;
+    }
+    ms /= float(launches);
+    if (!best || ms < best_t) {
+      if (best) causal_conv3d_plan_destroy(best);
+      best = p;
+      best_t = ms;
+    } else {
+      causal_conv3d_plan_destroy(p);
+    }
+    st = CC3D_OK;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != CC3D_OK || !best) {
+    if (best) causal_conv3d_plan_destroy(best);
+    return st == CC3D_OK ? CC3D_ERR_UNSUPPORTED : st;
+  }
+  *out_plan = best;
+  if (best_ms) *best_ms = best_t;
+  return CC3D_OK;
+}
+
 // Frees a plan's device workspace (called by causal_conv3d_plan_destroy).
 void cc3d_release_workspace(cc3d_plan_t plan) {
   std::lock_guard<std::mutex> lock(plan->mu);

@@ -73,14 +73,16 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
 }
 
 // Default choice.  Large 3x3 maps take 16x32 patches with the halo staged by
-// 32 channels and one workgroup per compute unit; small ones keep two smaller
-// workgroups per compute unit so that every unit gets tiles.
+// 32 channels and one workgroup per compute unit (from three rounds of 256
+// tiles: 384->384 at 180x320 with 2 frames, 960 tiles, runs 8% faster so);
+// small ones keep two smaller workgroups per compute unit so that every
+// unit gets tiles.  causal_conv3d_plan_autotune times the alternatives.
 const char* default_variant(const cc3d_desc_t& d) {
   if (d.k_h == 3) {
     if (d.c_out % 96 == 0) {
       const int64_t big_tiles = int64_t(d.n) * ((d.h + 15) / 16) * ((d.w + 31) / 32) * (d.c_out / 96) *
                                 std::max(1, d.t_x);
-      if (d.c_in % 32 == 0 && big_tiles >= 1024) return "bf16_s3_n96_p16x32_g32";
+      if (d.c_in % 32 == 0 && big_tiles >= 768) return "bf16_s3_n96_p16x32_g32";
       return "bf16_s3_n96_p8x32_x2";
     }
     if (d.c_out <= 5 && d.k_t == 3 && d.d_t == 1 && d.c_in % 32 == 0 && d.c_in <= 96) return "bf16_s3_few_p16x32";

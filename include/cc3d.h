@@ -152,6 +152,8 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *                              (default for large maps)
  *   "bf16_s3_n96_p8x32_x2"    3x3, C_out % 96 == 0
  *   "bf16_s3_n32_p8x32"       3x3, any C_out
+ *   "bf16_s3_few_p16x32"      3x3, k_t = 3, d_t = 1, C_out <= 5, C_in in {32, 64, 96}
+ *                              (default for the RGB head)
  *   "bf16_s1_n192_p8x32"      1x1, C_out % 192 == 0, C_in % 32 == 0
  *   "bf16_s1_n32_p8x32"       1x1, any C_out
  *   "f32_direct"              fp32
@@ -162,6 +164,27 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  * causal_conv3d_plan returns.
  */
 cc3d_status_t causal_conv3d_plan_variant(const cc3d_desc_t* desc, const char* kernel_name, cc3d_plan_t* out);
+
+/*
+ * Per-signature tuning (the pages time every runtime signature of a decoder;
+ * the variant that suits one shape need not suit another).  Plans desc on
+ * every bf16 variant that can run it, runs each once on the caller's
+ * buffers (which packs its weights), times `launches` further convolutions
+ * of it with HIP events on `stream`, and returns in *out the plan of the
+ * fastest, its weights packed, with its average time in *best_ms (may be
+ * NULL).  fp32 descriptors get causal_conv3d_plan's plan without timing.
+ *   x, cache_in, w, b, out  as for causal_conv3d_forward (out is
+ *                           overwritten; cache_out is not written)
+ *   launches                timed convolutions per variant, >= 1
+ * Blocking: it waits for its own launches.  Every launch counts in the
+ * fast-path counter.  Returns what causal_conv3d_plan returns for a refused
+ * descriptor, CC3D_ERR_INVALID_ARG for a NULL out or launches < 1 or a
+ * buffer the forward call rejects, and CC3D_ERR_DEVICE when a launch or an
+ * event fails; *out is NULL on error.
+ */
+cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, const void* x, const void* cache_in,
+                                          const void* w, const void* b, void* out, int launches, void* stream,
+                                          cc3d_plan_t* out_plan, float* best_ms);
 
 /* Intervals, sizes, work and launch geometry of a plan (host only). */
 cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_info_t* info);

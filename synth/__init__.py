@@ -114,3 +114,32 @@ REPLAY_STACK = [
 ]
 # Temporal dilation 2 variant of the mid-resolution conv (carry depth 4).
 REPLAY_DILATED = _sig("mid_192_dt2", 192, 192, 360, 640, 4, 0, dt=2)
+
+# Causal Conv3D signatures of a whole decoder at 720x1280 output, derived
+# from the workloads above: their resolution stages (latent 90x160, 360x640,
+# 720x1280) and channel widths (384, 192, 96), plus what a decoder built of
+# such stages implies between them -- the latent input conv (16 latent
+# channels for the Wan2.1-family decoder, 48 for the Wan2.2 one, as the
+# pages' latents have), a 180x320 stage at 384 channels with its own
+# temporal (3,1,1) upsampling conv, and the 192->96 channel change at full
+# resolution.  Every call has k_t = 3, as every observed call has.  Frames
+# per steady-state chunk follow the 1 + 4*4 schedule: one latent frame per
+# chunk, two frames after the first temporal upsampling, four after the
+# second.  The cache is the previous chunk's last two frames.
+DECODER_SIGNATURES = [
+    _sig("conv_in_16_384", 16, 384, 90, 160, 1, 2),
+    _sig("conv_in_48_384", 48, 384, 90, 160, 1, 2),
+    _sig("latent_384", 384, 384, 90, 160, 1, 2),
+    _sig("temporal_384_768", 384, 768, 90, 160, 1, 2, k=(3, 1, 1)),
+    _sig("stage_180x320_384", 384, 384, 180, 320, 2, 2),
+    _sig("temporal_384_768_180x320", 384, 768, 180, 320, 2, 2, k=(3, 1, 1)),
+    _sig("mid_384_192", 384, 192, 360, 640, 4, 2),
+    _sig("mid_192", 192, 192, 360, 640, 4, 2),
+    _sig("full_192_96", 192, 96, 720, 1280, 4, 2),
+    _sig("full_96", 96, 96, 720, 1280, 4, 2),
+    _sig("head_96_3", 96, 3, 720, 1280, 4, 2),
+]
+# Frames per chunk of the streaming 17-frame decode at the 360x640 and
+# 720x1280 stages: the first chunk decodes one frame, the next four decode
+# four each.
+SCHEDULE_17 = [1, 4, 4, 4, 4]

@@ -218,6 +218,69 @@ def test_streaming_replay_full_size_sampled(cuda_device, sig):
     assert_bf16_close(gather(y, pts), ref, sig["name"])
 
 
+@pytest.mark.parametrize("sig", synth.DECODER_SIGNATURES, ids=[s["name"] for s in synth.DECODER_SIGNATURES])
+def test_decoder_signatures_reduced_spatial_full_compare(cuda_device, sig):
+    """Every decoder signature at a reduced spatial size (several patches and
+    ragged edges) with its steady-state frames and 2-frame cache, through the
+    default kernel choice, against the oracle everywhere."""
+    s = sig
+    i = synth.DECODER_SIGNATURES.index(s)
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], 40, 72, s["tx"], s["tc"], s["k"], device=DEV,
+                                   seed=synth.SEED_BASE + 300 + i)
+    y, co, plan = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"].startswith("bf16_")
+    ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    assert_bf16_close(y, ref, s["name"] + "/" + plan.info["kernel_name"])
+    assert torch.equal(co, torch.cat([c, x], 1)[:, -2:])
+
+
+@pytest.mark.parametrize("name", ["mid_192", "head_96_3", "temporal_384_768", "conv_in_48_384"])
+def test_autotune_returns_the_fastest_runnable_variant(cuda_device, name):
+    """causal_conv3d_plan_autotune times every variant that can run the call
+    and returns one of them, with its weights packed: its output matches the
+    oracle and the default plan's within tolerance."""
+    import causal_conv3d_video_amd as cc3d
+    s = next(v for v in synth.DECODER_SIGNATURES if v["name"] == name)
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], 40, 72, s["tx"], s["tc"], s["k"], device=DEV,
+                                   seed=synth.SEED_BASE + 320)
+    desc = cc3d.make_desc(1, s["cin"], s["cout"], 40, 72, s["tx"], s["tc"], k=s["k"], padding=s["pad"],
+                          p_base=s["p_base"])
+    runnable = []
+    for v in ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32", "bf16_s3_few_p16x32",
+              "bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32"]:
+        try:
+            cc3d.causal_conv3d_plan_variant(desc, v).close()
+            runnable.append(v)
+        except cc3d.CC3DError as e:
+            assert e.status == cc3d.CC3D_ERR_UNSUPPORTED
+    scratch = torch.empty(cc3d.causal_conv3d_plan(desc).shapes()["out"], dtype=torch.bfloat16, device=DEV)
+    plan, ms = cc3d.causal_conv3d_plan_autotune(desc, x, c, w, b, scratch, launches=3)
+    assert plan.info["kernel_name"] in runnable and ms > 0
+    y = torch.full_like(scratch, float("nan"))
+    cc3d.causal_conv3d_forward_packed(plan, x, c, b, y, None)  # weights packed by the autotuner
+    y_def, _, _ = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    torch.cuda.synchronize()
+    ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    assert_bf16_close(y, ref, name + "/" + plan.info["kernel_name"])
+    assert_bf16_close(y_def, ref, name + "/default")
+
+
+@pytest.mark.parametrize("name", ["mid_192", "full_96", "head_96_3"])
+def test_streaming_17_frame_schedule_full_compare(cuda_device, name):
+    """The 1 + 4*4 frame schedule of a 17-frame decode at the 360x640 and
+    720x1280 stages (reduced spatial size): the first chunk decodes one frame
+    with no cache, each later one four frames with the carried cache; all 17
+    output frames against one oracle call over the whole sequence."""
+    s = next(v for v in synth.DECODER_SIGNATURES if v["name"] == name)
+    wt, bt, xs, outs = _replay(s, synth.SCHEDULE_17, synth.SEED_BASE + 330, DEV, h=21, w=40)
+    torch.cuda.synchronize()
+    assert sum(o.shape[1] for o in outs) == 17
+    whole = oracle.conv3d(torch.cat(xs, 1).cpu(), None, wt.cpu(), bt.cpu(), dilation=(s["dt"], 1, 1),
+                          padding=s["pad"], pbase=s["p_base"])
+    assert_bf16_close(torch.cat(outs, 1), whole, name)
+
+
 def test_unread_frames_and_guard_bands_are_never_touched(cuda_device):
     """Frames of Z outside every tap's source interval, and bytes just outside
     each buffer, hold NaN; the output must be finite and bit-identical to the

@@ -275,6 +275,22 @@ def test_default_kernel_choice():
     assert dil.info["kernel_name"] == "bf16_s3_n32_p8x32"      # d_t = 2
 
 
+def test_every_decoder_signature_takes_a_bf16_fast_path():
+    """Every call of the 17-frame streaming decode (first chunk: one frame,
+    no cache; later chunks: the steady-state frames and a 2-frame cache)
+    plans onto a bf16 kernel at full size: none is refused."""
+    import synth
+    calls = 0
+    for s in synth.DECODER_SIGNATURES:
+        for t_x, t_cache in [(1, 0)] + [(s["tx"], s["tc"])] * 4:
+            p = cc3d.causal_conv3d_plan(_desc(c_in=s["cin"], c_out=s["cout"], h=s["h"], w=s["w"], t_x=t_x,
+                                              t_cache=t_cache, k=s["k"], padding=s["pad"], p_base=s["p_base"]))
+            assert p.info["kernel_name"].startswith("bf16_"), (s["name"], p.info["kernel_name"])
+            assert p.info["t_out"] == t_x and p.info["t_cache_out"] == min(2, t_x + t_cache)
+            calls += 1
+    assert calls == 5 * len(synth.DECODER_SIGNATURES)
+
+
 VARIANTS_3X3 = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32"]
 VARIANTS_FEW = ["bf16_s3_few_p16x32", "bf16_s3_n32_p8x32"]
 VARIANTS_1X1 = ["bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32"]
