@@ -187,6 +187,22 @@ def time_single_calls(device, launches, stream, warm_seconds=0.2):
             frac_mfma_peak=info["flops_active"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
             frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        if info["kernel_name"] == "bf16_s3_few_p16x32":
+            # the head with 8-bit pixel output fused (one byte per channel)
+            o8 = torch.empty(plan.shapes()["out"], dtype=torch.uint8, device=device)
+            for _ in range(3):
+                cc3d.causal_conv3d_forward_u8(plan, x, c, None, b, o8, None, stream=stream)
+            e0.record(stream)
+            for _ in range(launches):
+                cc3d.causal_conv3d_forward_u8(plan, x, c, None, b, o8, None, stream=stream)
+            e1.record(stream)
+            e1.synchronize()
+            ms8 = e0.elapsed_time(e1) / launches
+            nbytes = info["bytes_conv"] - o8.numel()   # half the bf16 output bytes
+            res[s["name"] + "_u8"] = dict(kernel=info["kernel_name"] + "+u8", us_per_launch=ms8 * 1e3,
+                                          gbs=nbytes / (ms8 * 1e-3) / 1e9,
+                                          frac_hbm_peak=nbytes / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            del o8
         del x, c, w, b, out, plan
         torch.cuda.empty_cache()
     return res

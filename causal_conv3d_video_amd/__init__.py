@@ -26,7 +26,8 @@ __all__ = [
     "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_autotune", "causal_conv3d_plan_info",
     "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
-    "causal_conv3d_status_string", "causal_conv3d_counters", "library_path", "EXPORTED_SYMBOLS",
+    "causal_conv3d_forward_u8", "causal_conv3d_status_string", "causal_conv3d_counters", "library_path",
+    "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_autotune", "causal_conv3d_plan_info",
     "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
-    "causal_conv3d_status_string", "causal_conv3d_counters",
+    "causal_conv3d_forward_u8", "causal_conv3d_status_string", "causal_conv3d_counters",
 )
 
 CC3D_OK, CC3D_ERR_INVALID_ARG, CC3D_ERR_UNSUPPORTED, CC3D_ERR_DEVICE, CC3D_ERR_NO_MEMORY = range(5)
@@ -96,6 +97,8 @@ def _load():
     lib.causal_conv3d_pack_weights.restype = ctypes.c_int
     lib.causal_conv3d_forward_packed.argtypes = [vp] * 7
     lib.causal_conv3d_forward_packed.restype = ctypes.c_int
+    lib.causal_conv3d_forward_u8.argtypes = [vp] * 7 + [ctypes.c_float, ctypes.c_float, vp]
+    lib.causal_conv3d_forward_u8.restype = ctypes.c_int
     lib.causal_conv3d_status_string.argtypes = [ctypes.c_int]
     lib.causal_conv3d_status_string.restype = ctypes.c_char_p
     lib.causal_conv3d_counters.argtypes = [ctypes.POINTER(Counters), ctypes.c_int]
@@ -286,6 +289,21 @@ def causal_conv3d_forward_packed(plan, x, cache_in, b, out, cache_out=None, stre
                                            p["cache_out"], _stream_handle(stream, x))
     if st != CC3D_OK:
         raise CC3DError(st, "causal_conv3d_forward_packed")
+
+
+def causal_conv3d_forward_u8(plan, x, cache_in, w, b, out, cache_out=None, scale=0.5, offset=0.5, stream=None):
+    """The RGB head with 8-bit pixel output: ``out`` is a uint8 CUDA tensor of
+    the plan's output shape, code = trunc(clamp(fma(y, scale, offset) * 255,
+    0, 255)) in fp32.  ``w`` None runs with the weights last packed."""
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or out.dtype != torch.uint8:
+        raise TypeError("out must be a uint8 CUDA (HIP) tensor")
+    _physical(out, plan.shapes()["out"], "out")
+    p = _marshal(plan, {"x": x, "cache_in": cache_in if plan.desc.t_cache > 0 else None, "w": w,
+                        "b": b if plan.desc.has_bias else None, "cache_out": cache_out})
+    st = _lib.causal_conv3d_forward_u8(plan.handle, p["x"], p["cache_in"], p["w"], p["b"], out.data_ptr(),
+                                       p["cache_out"], float(scale), float(offset), _stream_handle(stream, x))
+    if st != CC3D_OK:
+        raise CC3DError(st, "causal_conv3d_forward_u8")
 
 
 def causal_conv3d_counters(reset=False):

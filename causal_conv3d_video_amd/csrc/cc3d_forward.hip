@@ -70,6 +70,10 @@ struct ConvArgs {
   int ina_lo[kMaxFrameIv + 1], ina_n[kMaxFrameIv + 1], nina_iv;
   int nat;
   int* sched;
+  // Few-output-channel kernel: write 8-bit pixel codes instead of bf16,
+  // code = trunc(clamp(fma(y, px_scale, px_offset) * 255, 0, 255)) in fp32.
+  int out_u8;
+  float px_scale, px_offset;
 };
 
 __device__ __forceinline__ __attribute__((unused)) float bf16_to_f32(unsigned short h) {
@@ -1100,7 +1104,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int frame_bytes = int(frame_el * 2);
   const unsigned short* __restrict__ xs = static_cast<const unsigned short*>(a.x);
   const unsigned short* __restrict__ cs = static_cast<const unsigned short*>(a.cache);
-  unsigned short* os = static_cast<unsigned short*>(a.out);
   const int p_l = -a.delta[0];              // delta_0 = -p_l
   const int z_lo = max(0, -p_l);            // first source frame any output reads
   const int nst = (a.tz - z_lo) * NCH;      // stages per patch: (frame, 32-channel chunk)
@@ -1209,20 +1212,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Write output frame o from the tap-slot-2 columns (bias added once) with
   // 16-bit buffer stores: a per-lane byte offset within the output row (out
   // of range for lanes that hold no output), the row offset in a scalar.
+  //
+  // With out_u8 the frame is written as 8-bit pixel codes (one byte per
+  // channel, same layout): the step after the head, on the device, before
+  // any copy to the host.  The code is decided in fp32 from the unrounded
+  // sum: trunc(clamp(fma(y, scale, offset) * 255, 0, 255)).
+  const int esz = a.out_u8 ? 1 : 2;  // bytes per output element
   int eoff[4];
   auto emit_offsets = [&](const Patch& c) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int x = c.x0 + wc * 16 + q * 4 + v;
-      eoff[v] = (emits && x < a.wo) ? (x * COUT + emit_co) * 2 : OOB;
+      eoff[v] = (emits && x < a.wo) ? (x * COUT + emit_co) * esz : OOB;
     }
   };
-  const int frame_out_bytes = a.ho * a.wo * COUT * 2;
+  const int frame_out_bytes = a.ho * a.wo * COUT * esz;
   auto emit = [&](const Patch& c, int o) {
     if (o < 0 || o >= a.to) return;  // uniform
-    unsigned short* of = os + (int64_t(c.nn) * a.to + o) * a.ho * int64_t(a.wo) * COUT;
+    unsigned char* of = static_cast<unsigned char*>(a.out) + ((int64_t(c.nn) * a.to + o) * a.ho * int64_t(a.wo) * COUT) * esz;
     const __amdgpu_buffer_rsrc_t r_out =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(of)), 0, frame_out_bytes, 0x00020000);
+    if (a.out_u8) {  // uniform
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const int y = c.y0 + wr * RW + r;
+        if (y >= a.ho) break;  // uniform
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p = __builtin_fmaf(acc[r][v] + bias, a.px_scale, a.px_offset) * 255.f;
+          const unsigned code = unsigned(fminf(fmaxf(p, 0.f), 255.f));  // truncates
+          __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, r_out, eoff[v], y * a.wo * COUT, 0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int y = c.y0 + wr * RW + r;
@@ -1539,11 +1562,21 @@ bool frame_intervals(const cc3d_plan* plan, ConvArgs& a) {
   return true;
 }
 
+// Pixel output of the head: 8-bit codes instead of bf16 (see ConvArgs).
+struct PixelOut {
+  float scale, offset;
+};
+
 cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, const void* w, const void* b,
-                       void* out, void* cache_out, void* stream, RunMode mode) {
+                       void* out, void* cache_out, void* stream, RunMode mode, const PixelOut* px = nullptr) {
   if (!plan) return invalid();
   const cc3d_desc_t& d = plan->d;
   const cc3d_plan_info_t& in = plan->info;
+  if (px && in.kernel_id != CC3D_K_BF16_S3_FEW) {
+    cc3d::g_unsupported.fetch_add(1, std::memory_order_relaxed);
+    return CC3D_ERR_UNSUPPORTED;
+  }
+  const int64_t out_bytes = px ? plan->out_bytes / plan->elem : plan->out_bytes;
   const bool bf16 = d.dtype == CC3D_BF16;
   const bool needs_w = mode != kRunPacked;
   const bool runs = mode != kPackOnly;
@@ -1559,13 +1592,12 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
       (runs && (!x || !out || (d.t_cache > 0 && !cache_in) || (d.has_bias && !b))))
     return invalid();
   const uintptr_t al = bf16 ? 16 : 4;
-  if (!aligned(x, al) || !aligned(cache_in, al) || !aligned(w, al) || !aligned(out, al) ||
+  if (!aligned(x, al) || !aligned(cache_in, al) || !aligned(w, al) || (!px && !aligned(out, al)) ||
       !aligned(cache_out, al) || !aligned(b, uintptr_t(plan->elem)))
     return invalid();
-  if (overlaps(out, plan->out_bytes, x, plan->x_bytes) ||
-      overlaps(out, plan->out_bytes, cache_in, plan->cache_bytes) ||
-      overlaps(out, plan->out_bytes, w, plan->w_bytes) || overlaps(out, plan->out_bytes, b, plan->b_bytes) ||
-      overlaps(out, plan->out_bytes, cache_out, plan->cache_out_bytes) ||
+  if (overlaps(out, out_bytes, x, plan->x_bytes) || overlaps(out, out_bytes, cache_in, plan->cache_bytes) ||
+      overlaps(out, out_bytes, w, plan->w_bytes) || overlaps(out, out_bytes, b, plan->b_bytes) ||
+      overlaps(out, out_bytes, cache_out, plan->cache_out_bytes) ||
       overlaps(cache_out, plan->cache_out_bytes, x, plan->x_bytes) ||
       overlaps(cache_out, plan->cache_out_bytes, cache_in, plan->cache_bytes) ||
       overlaps(cache_out, plan->cache_out_bytes, w, plan->w_bytes) ||
@@ -1604,6 +1636,11 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   a.nblk_n = plan->nblk_n;
   a.ntiles = int(in.tiles);
   a.has_bias = d.has_bias;
+  if (px) {
+    a.out_u8 = 1;
+    a.px_scale = px->scale;
+    a.px_offset = px->offset;
+  }
   if (in.kernel_id == CC3D_K_BF16_S3_N96_G32W8 && !frame_intervals(plan, a)) return invalid();
 
   int cus = 256;
@@ -1711,6 +1748,14 @@ extern "C" cc3d_status_t causal_conv3d_pack_weights(cc3d_plan_t plan, const void
 extern "C" cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const void* x, const void* cache_in,
                                                       const void* b, void* out, void* cache_out, void* stream) {
   return run_plan(plan, x, cache_in, nullptr, b, out, cache_out, stream, kRunPacked);
+}
+
+extern "C" cc3d_status_t causal_conv3d_forward_u8(cc3d_plan_t plan, const void* x, const void* cache_in,
+                                                  const void* w, const void* b, void* out, void* cache_out,
+                                                  float scale, float offset, void* stream) {
+  if (!(scale == scale) || !(offset == offset)) return invalid();  // NaN
+  const PixelOut px{scale, offset};
+  return run_plan(plan, x, cache_in, w, b, out, cache_out, stream, w ? kPackAndRun : kRunPacked, &px);
 }
 
 // Per-signature variant choice: every bf16 variant that can run the call is

@@ -234,6 +234,29 @@ cc3d_status_t causal_conv3d_pack_weights(cc3d_plan_t plan, const void* w, void* 
 cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const void* x, const void* cache_in,
                                            const void* b, void* out, void* cache_out, void* stream);
 
+/*
+ * The RGB head with its pixel quantisation fused in (FastVideo pull request
+ * "[perf] Quantize frames to uint8 on-device before the post-decode D->H
+ * copy": the decoded frames are scaled by 255, clamped to [0, 255] and cast
+ * to uint8 on the device, so the copy to the host is of bytes).  Runs the
+ * plan's convolution and writes out as 8-bit codes, one byte per channel in
+ * the layout of out ([N][T_o][H_o][W_o][C_out]):
+ *   code = trunc(clamp(fma(y, scale, offset) * 255, 0, 255))
+ * decided in fp32 from the unrounded fp32 sum y (bias included).  scale =
+ * offset = 0.5 maps a head output in [-1, 1] to [0, 1] first (that mapping is
+ * not on the pages; it is the usual video-decoder convention).  A NaN sum
+ * gives code 0.  w NULL runs with the weights last packed into the plan (as
+ * causal_conv3d_forward_packed); otherwise w is packed first (as
+ * causal_conv3d_forward).  cache_out is written as by causal_conv3d_forward.
+ * out needs no alignment.  Returns CC3D_ERR_UNSUPPORTED unless the plan runs
+ * on the few-output-channel kernel ("bf16_s3_few_p16x32"),
+ * CC3D_ERR_INVALID_ARG for a NaN scale or offset and as
+ * causal_conv3d_forward otherwise.
+ */
+cc3d_status_t causal_conv3d_forward_u8(cc3d_plan_t plan, const void* x, const void* cache_in, const void* w,
+                                       const void* b, void* out, void* cache_out, float scale, float offset,
+                                       void* stream);
+
 /* Static description of a status code. */
 const char* causal_conv3d_status_string(cc3d_status_t status);
 

@@ -29,7 +29,7 @@ _SRC = os.path.join(_HERE, "cc3d_oracle.c")
 _LIB = os.path.join(_HERE, "libcc3d_oracle.so")
 _lib = None
 
-__all__ = ["build", "out_shape", "conv3d", "cache_out", "default_threads"]
+__all__ = ["build", "out_shape", "conv3d", "cache_out", "pixels_u8", "default_threads"]
 
 
 def build(force=True):
@@ -167,3 +167,22 @@ def cache_out(x, cache, pbase):
     z = xa if ca is None or ca.shape[1] == 0 else np.concatenate([ca, xa], axis=1)
     keep = min(pbase, z.shape[1])
     return z[:, z.shape[1] - keep:].copy()
+
+
+def pixels_u8(y, scale=0.5, offset=0.5):
+    """8-bit pixel codes of decoded frames, following the FastVideo pull
+    request "[perf] Quantize frames to uint8 on-device before the post-decode
+    D->H copy" (Summary and Correctness sections): the frames are scaled by
+    255, clamped to [0, 255] and cast to uint8, and the cast truncates.  The
+    page starts from frames in [0, 1]; the head output y is mapped there first
+    by y*scale + offset (0.5, 0.5 maps [-1, 1] to [0, 1]; the usual decoder
+    convention, not on the pages).
+
+    The decision is taken in fp32, the precision of the frames on that page:
+    y is rounded to fp32, y*scale + offset is rounded once to fp32 (a fused
+    multiply-add), and the product by 255 is rounded to fp32.  NaN gives 0."""
+    y32 = np.asarray(y, dtype=np.float64).astype(np.float32)
+    v = (y32.astype(np.float64) * np.float64(np.float32(scale)) + np.float64(np.float32(offset))).astype(np.float32)
+    p = v * np.float32(255)
+    p = np.where(np.isnan(p), np.float32(0), p)
+    return np.trunc(np.clip(p, np.float32(0), np.float32(255))).astype(np.uint8)

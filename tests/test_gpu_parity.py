@@ -414,3 +414,79 @@ def test_packed_weights_path_matches_forward_bitwise(cuda_device):
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(y1, y3)
     assert_bf16_close(y2, _oracle(x, c, w, b), "packed")
+
+
+def _u8_compare(got_u8, y_ref, what, margin=0.01):
+    """8-bit pixel codes against the oracle's: equal wherever the oracle's
+    pre-truncation value (y*0.5 + 0.5)*255 is farther than ``margin`` from
+    an integer (the fp32 sum and the fp64 one differ by far less); within
+    that band the code may be either neighbour."""
+    got = np.asarray(got_u8).astype(np.int64)
+    ref = oracle.pixels_u8(y_ref).astype(np.int64)
+    p = np.clip((np.asarray(y_ref, dtype=np.float64) * 0.5 + 0.5) * 255, 0, 255)
+    near = np.abs(p - np.round(p)) < margin
+    far_bad = (got != ref) & ~near
+    assert not far_bad.any(), (what, int(far_bad.sum()), got[far_bad][:8], ref[far_bad][:8])
+    assert np.all(np.abs(got - ref)[near] <= 1), what
+    return int((got != ref).sum())
+
+
+def test_head_u8_codes_match_oracle(cuda_device):
+    """The RGB head with the pixel quantisation fused: every code against the
+    oracle's quantisation of its fp64 output; codes span the clamps; the
+    cache carry is that of the plain forward; the packed-weights call
+    (w = None) gives the same bytes."""
+    import causal_conv3d_video_amd as cc3d
+    s = synth.HEAD_96_3
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], 40, 72, s["tx"], s["tc"], device=DEV,
+                                   seed=synth.SEED_BASE + 340)
+    plan = plan_for(x, s["tc"], w, k=(3, 3, 3), pad=(1, 1))
+    assert plan.info["kernel_name"] == "bf16_s3_few_p16x32"
+    out = torch.zeros(plan.shapes()["out"], dtype=torch.uint8, device=DEV)
+    co = torch.empty(plan.shapes()["cache_out"], dtype=x.dtype, device=DEV)
+    cc3d.causal_conv3d_forward_u8(plan, x, c, w, b, out, co)
+    out2 = torch.zeros_like(out)
+    cc3d.causal_conv3d_forward_u8(plan, x, c, None, b, out2, None)
+    torch.cuda.synchronize()
+    ref = _oracle(x, c, w, b)
+    _u8_compare(out.cpu().numpy(), ref, "head u8")
+    got = out.cpu().numpy()
+    assert got.min() == 0 and got.max() == 255
+    assert torch.equal(out, out2)
+    assert torch.equal(co, torch.cat([c, x], 1)[:, -2:])
+
+
+def test_head_u8_full_size_sampled(cuda_device):
+    """At 720x1280 with the packed weights (the steady-state call): sampled
+    codes against the oracle; bias-only frames (p_base = 4) go through the
+    same quantisation."""
+    import causal_conv3d_video_amd as cc3d
+    s = synth.HEAD_96_3
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], device=DEV,
+                                   seed=synth.SEED_BASE + 341)
+    plan = plan_for(x, s["tc"], w, k=(3, 3, 3), pad=(1, 1))
+    cc3d.causal_conv3d_pack_weights(plan, w)
+    out = torch.zeros(plan.shapes()["out"], dtype=torch.uint8, device=DEV)
+    cc3d.causal_conv3d_forward_u8(plan, x, c, None, b, out, None)
+    torch.cuda.synchronize()
+    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 600, seed=34, tile_h=16)
+    ref = _oracle(x, c, w, b, points=pts)
+    _u8_compare(gather(out, pts), ref, "head u8 full size")
+    # bias-only leading frames
+    x2, _, w2, b2 = synth.conv_inputs(1, 64, 3, 18, 40, 2, 0, device=DEV, seed=synth.SEED_BASE + 342)
+    p2 = plan_for(x2, 0, w2, k=(3, 3, 3), pad=(1, 1), p_base=4)
+    assert p2.info["kernel_name"] == "bf16_s3_few_p16x32" and p2.info["t_out"] == 4
+    o2 = torch.zeros(p2.shapes()["out"], dtype=torch.uint8, device=DEV)
+    cc3d.causal_conv3d_forward_u8(p2, x2, None, w2, b2, o2, None)
+    torch.cuda.synchronize()
+    _u8_compare(o2.cpu().numpy(), _oracle(x2, None, w2, b2, p_base=4), "head u8 bias-only frames")
+
+
+def test_u8_output_refused_off_the_head_kernel(cuda_device):
+    import causal_conv3d_video_amd as cc3d
+    x, c, w, b = synth.conv_inputs(1, 32, 96, 16, 32, 2, 2, device=DEV, seed=synth.SEED_BASE + 343)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1))
+    out = torch.zeros(plan.shapes()["out"], dtype=torch.uint8, device=DEV)
+    with pytest.raises(cc3d.CC3DError) as e:
+        cc3d.causal_conv3d_forward_u8(plan, x, c, w, b, out, None)
+    assert e.value.status == cc3d.CC3D_ERR_UNSUPPORTED

@@ -280,3 +280,33 @@ def test_output_length_rule():
     assert oracle.out_shape(4, 4, 8, 8, dt=2, pbase=4) == (4, 8, 8)
     assert oracle.out_shape(4, 2, 8, 8, dt=2, pbase=4) == (4, 8, 8)
     assert oracle.out_shape(1, 0, 8, 8, pbase=0) is None
+
+
+# --- pixel quantisation of the head output (FastVideo pull request "[perf]
+# Quantize frames to uint8 on-device before the post-decode D->H copy",
+# Summary and Correctness: scale by 255, clamp to [0, 255], truncating uint8
+# cast; y mapped to [0, 1] by y*0.5 + 0.5 first) ---
+
+def test_pixel_codes_at_exact_points():
+    """Points where every fp32 step is exact: truncation, not rounding
+    (0 -> 127.5 -> 127), both clamps, and the affine map's offset and scale."""
+    y = np.array([-3.0, -1.0, -0.5, 0.0, 0.5, 1.0, 3.0])
+    assert oracle.pixels_u8(y).tolist() == [0, 0, 63, 127, 191, 255, 255]
+    # another affine map: y already in [0, 1]
+    assert oracle.pixels_u8(np.array([0.0, 0.25, 1.0, 1.5]), scale=1.0, offset=0.0).tolist() == [0, 63, 255, 255]
+    assert oracle.pixels_u8(np.array([np.nan])).tolist() == [0]
+
+
+def test_pixel_codes_match_torch_float32_pipeline():
+    """With scale 0.5 the product y*0.5 is exact, so the fused map equals the
+    plain torch float32 pipeline (y*0.5 + 0.5) * 255, clamp, uint8 cast."""
+    rng = np.random.default_rng(3)
+    y = np.concatenate([rng.normal(0, 1.2, 200000), np.linspace(-1.1, 1.1, 50001)])
+    t = torch.from_numpy(y).to(torch.float32)
+    ref = ((t * 0.5 + 0.5) * 255).clamp(0, 255).to(torch.uint8).numpy()
+    got = oracle.pixels_u8(y)
+    assert np.array_equal(got, ref)
+    # monotone in y, and every code is reached
+    order = np.argsort(y, kind="stable")
+    assert np.all(np.diff(got[order].astype(int)) >= 0)
+    assert set(np.unique(got).tolist()) == set(range(256))
