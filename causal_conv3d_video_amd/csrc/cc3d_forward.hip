@@ -58,6 +58,7 @@ struct ConvArgs {
   int n, tx, tc, h, wd, cin, cout, to, ho, wo;
   int kt, kh, kw, sh, sw, dh, dw, ph, pw;
   int tz;
+  int st;  // temporal stride: output frame o reads source frame o*st + delta[k]
   int delta[CC3D_MAX_KT];
   int tiles_x, tiles_y, nblk_n, ntiles;
   int has_bias;
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
     c.z0 = c.z1 = c.z2 = c.z3 = 0;
 #pragma unroll
     for (int k = 0; k < kMaxTapsBf16; ++k) {
-      const int z = c.o + a.delta[k];
+      const int z = c.o * a.st + a.delta[k];
       if (k < a.kt && z >= 0 && z < a.tz) {
         if (c.nact == 0) { c.k0 = k; c.z0 = z; }
         else if (c.nact == 1) { c.k1 = k; c.z1 = z; }
@@ -692,7 +693,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     c.z0 = c.z1 = c.z2 = c.z3 = 0;
 #pragma unroll
     for (int k = 0; k < kMaxTapsBf16; ++k) {
-      const int z = c.o + a.delta[k];
+      const int z = c.o * a.st + a.delta[k];
       if (k < a.kt && z >= 0 && z < a.tz) {
         if (c.nact == 0) { c.k0 = k; c.z0 = z; }
         else if (c.nact == 1) { c.k1 = k; c.z1 = z; }
@@ -1347,7 +1348,7 @@ __global__ __launch_bounds__(256) void conv_f32_direct(ConvArgs a) {
   const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
   float acc = a.has_bias ? static_cast<const float*>(a.b)[co] : 0.f;
   for (int k = 0; k < a.kt; ++k) {
-    const int t = o + tap_delta(a, k);
+    const int t = o * a.st + tap_delta(a, k);
     if (t < 0 || t >= a.tz) continue;
     const float* fp = t < a.tc ? cs + (int64_t(nn) * a.tc + t) * frame_el
                                : xs + (int64_t(nn) * a.tx + (t - a.tc)) * frame_el;
@@ -1631,6 +1632,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   a.pw = d.p_w;
   a.tz = in.t_z;
   for (int k = 0; k < CC3D_MAX_KT; ++k) a.delta[k] = k < d.k_t ? in.taps[k].delta : 0;
+  a.st = d.s_t;
   a.tiles_x = plan->tiles_x;
   a.tiles_y = plan->tiles_y;
   a.nblk_n = plan->nblk_n;

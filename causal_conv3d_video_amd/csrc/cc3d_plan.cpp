@@ -22,6 +22,7 @@ int64_t floordiv(int64_t num, int64_t den) {
   if ((num % den != 0) && (num < 0)) q -= 1;
   return q;
 }
+int64_t ceildiv(int64_t num, int64_t den) { return -floordiv(-num, den); }
 
 cc3d_status_t refuse(cc3d_status_t s) {
   if (s == CC3D_ERR_UNSUPPORTED) cc3d::g_unsupported.fetch_add(1, std::memory_order_relaxed);
@@ -53,7 +54,7 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   }
   if (n == "bf16_s3_few_p16x32") {
     *v = {CC3D_K_BF16_S3_FEW, 16, 32, d.c_out, 32, "bf16_s3_few_p16x32"};
-    return s3 && d.k_t == 3 && d.d_t == 1 && d.c_out <= 5 && d.c_in % 32 == 0 && d.c_in <= 96;
+    return s3 && d.k_t == 3 && d.d_t == 1 && d.s_t == 1 && d.c_out <= 5 && d.c_in % 32 == 0 && d.c_in <= 96;
   }
   if (n == "bf16_s3_n32_p8x32") {
     *v = {CC3D_K_BF16_S3_N32, 8, 32, 32, 16, "bf16_s3_n32_p8x32"};
@@ -85,7 +86,8 @@ const char* default_variant(const cc3d_desc_t& d) {
       if (d.c_in % 32 == 0 && big_tiles >= 768) return "bf16_s3_n96_p16x32_g32";
       return "bf16_s3_n96_p8x32_x2";
     }
-    if (d.c_out <= 5 && d.k_t == 3 && d.d_t == 1 && d.c_in % 32 == 0 && d.c_in <= 96) return "bf16_s3_few_p16x32";
+    if (d.c_out <= 5 && d.k_t == 3 && d.d_t == 1 && d.s_t == 1 && d.c_in % 32 == 0 && d.c_in <= 96)
+      return "bf16_s3_few_p16x32";
     return "bf16_s3_n32_p8x32";
   }
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
@@ -107,8 +109,10 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
       d.d_h < 1 || d.d_w < 1 || d.p_h < 0 || d.p_w < 0 || d.p_base < 0 || d.groups < 1 ||
       (d.has_bias != 0 && d.has_bias != 1))
     return refuse(CC3D_ERR_INVALID_ARG);
-  // The lowering's contract: unit temporal stride, one group.
-  if (d.s_t != 1 || d.groups != 1 || d.k_t > CC3D_MAX_KT) return refuse(CC3D_ERR_UNSUPPORTED);
+  // One group, as in the lowering's contract.  Temporal stride > 1 (the
+  // encoder's downsampling convs, outside that contract) is supported: output
+  // frame o reads source frame o*s_t + delta_k.
+  if (d.groups != 1 || d.k_t > CC3D_MAX_KT) return refuse(CC3D_ERR_UNSUPPORTED);
 
   cc3d_plan_info_t in;
   std::memset(&in, 0, sizeof in);
@@ -123,18 +127,21 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
   in.w_out = int32_t(w_out);
   in.t_cache_out = std::min(d.p_base, in.t_z);
 
-  // Per-tap intervals: 0 <= o < T_o and 0 <= o + delta_k < |Z|.
+  // Per-tap intervals: 0 <= o < T_o and 0 <= o*s_t + delta_k < |Z|.  With
+  // unit stride the source frames are the interval [o_lo, o_hi) + delta_k,
+  // of the same length; with s_t > 1 they are every s_t-th frame of
+  // [src_lo, src_hi).
   int64_t active_pairs = 0;
   int64_t read_frames = 0;  // frames of Z read by at least one active tap
   for (int k = 0; k < d.k_t; ++k) {
     cc3d_tap_t& tp = in.taps[k];
     tp.delta = k * d.d_t - in.p_l;
-    tp.o_lo = std::max(0, -tp.delta);
-    tp.o_hi = std::min(in.t_out, in.t_z - tp.delta);
+    tp.o_lo = int32_t(std::max<int64_t>(0, ceildiv(-int64_t(tp.delta), d.s_t)));
+    tp.o_hi = int32_t(std::min<int64_t>(in.t_out, ceildiv(int64_t(in.t_z) - tp.delta, d.s_t)));
     tp.active = tp.o_hi > tp.o_lo;
     if (!tp.active) tp.o_hi = tp.o_lo;
-    tp.src_lo = tp.o_lo + tp.delta;
-    tp.src_hi = tp.o_hi + tp.delta;
+    tp.src_lo = tp.o_lo * d.s_t + tp.delta;
+    tp.src_hi = tp.active ? (tp.o_hi - 1) * d.s_t + tp.delta + 1 : tp.src_lo;
     if (tp.active) {
       in.n_active_taps += 1;
       active_pairs += tp.o_hi - tp.o_lo;
@@ -142,8 +149,10 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
   }
   for (int32_t z = 0; z < in.t_z; ++z) {
     bool read = false;
-    for (int k = 0; k < d.k_t; ++k)
-      read = read || (in.taps[k].active && z >= in.taps[k].src_lo && z < in.taps[k].src_hi);
+    for (int k = 0; k < d.k_t; ++k) {
+      const cc3d_tap_t& tp = in.taps[k];
+      read = read || (tp.active && z >= tp.src_lo && z < tp.src_hi && (z - tp.src_lo) % d.s_t == 0);
+    }
     read_frames += read;
   }
 

@@ -81,9 +81,9 @@ def replay_chunks(n, cin, cout, h, w, frames, k=(3, 3, 3), *, dtype=torch.bfloat
 
 # Workload shapes (N = 1, channels last).  Each entry: C_in, C_out, H, W,
 # frames of X per call, cached frames, kernel, temporal dilation, base pad.
-def _sig(name, cin, cout, h, w, tx, tc, k=(3, 3, 3), dt=1, p_base=None, kind="normal", dtype="bf16"):
+def _sig(name, cin, cout, h, w, tx, tc, k=(3, 3, 3), dt=1, p_base=None, kind="normal", dtype="bf16", st=1):
     pad = (1, 1) if k[1] == 3 else (0, 0)
-    return dict(name=name, n=1, cin=cin, cout=cout, h=h, w=w, tx=tx, tc=tc, k=k, pad=pad, dt=dt,
+    return dict(name=name, n=1, cin=cin, cout=cout, h=h, w=w, tx=tx, tc=tc, k=k, pad=pad, dt=dt, st=st,
                 p_base=dt * (k[0] - 1) if p_base is None else p_base, kind=kind, dtype=dtype)
 
 
@@ -138,6 +138,14 @@ DECODER_SIGNATURES = [
     _sig("full_192_96", 192, 96, 720, 1280, 4, 2),
     _sig("full_96", 96, 96, 720, 1280, 4, 2),
     _sig("head_96_3", 96, 3, 720, 1280, 4, 2),
+]
+# The encoder's stride-2 temporal downsampling convs (the pages' only
+# fallbacks: outside the unit-stride contract), as temporal-only (3,1,1)
+# convs at the two coarsest stages of a 720x1280 encoder, four new frames
+# and the 2-frame carry per call (two output frames).
+ENCODER_DOWNSAMPLE = [
+    _sig("enc_tdown_384_180x320", 384, 384, 180, 320, 4, 2, k=(3, 1, 1), st=2),
+    _sig("enc_tdown_384_90x160", 384, 384, 90, 160, 4, 2, k=(3, 1, 1), st=2),
 ]
 # Frames per chunk of the streaming 17-frame decode at the 360x640 and
 # 720x1280 stages: the first chunk decodes one frame, the next four decode

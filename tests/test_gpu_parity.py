@@ -22,8 +22,8 @@ def _np(t):
     return None if t is None else t.detach().cpu()
 
 
-def _oracle(x, cache, w, b, *, k=(3, 3, 3), pad=(1, 1), dt=1, p_base=2, points=None):
-    return oracle.conv3d(_np(x), _np(cache), _np(w), _np(b), dilation=(dt, 1, 1), padding=pad,
+def _oracle(x, cache, w, b, *, k=(3, 3, 3), pad=(1, 1), dt=1, p_base=2, points=None, st=1):
+    return oracle.conv3d(_np(x), _np(cache), _np(w), _np(b), stride=(st, 1, 1), dilation=(dt, 1, 1), padding=pad,
                          pbase=p_base, points=points)
 
 
@@ -490,3 +490,70 @@ def test_u8_output_refused_off_the_head_kernel(cuda_device):
     with pytest.raises(cc3d.CC3DError) as e:
         cc3d.causal_conv3d_forward_u8(plan, x, c, w, b, out, None)
     assert e.value.status == cc3d.CC3D_ERR_UNSUPPORTED
+
+
+# Temporal stride (the encoder's downsampling convs): (C_in, C_out, H, W,
+# T_x, T_cache, k, s_t, variant) on every kernel that runs it.
+STRIDED = [
+    (32, 96, 20, 70, 4, 2, (3, 3, 3), 2, "bf16_s3_n96_p16x32_g32"),
+    (64, 192, 17, 45, 6, 2, (3, 3, 3), 2, "bf16_s3_n96_p8x32_x2"),
+    (32, 40, 13, 41, 5, 0, (3, 3, 3), 2, "bf16_s3_n32_p8x32"),       # chunk 0: odd length, no cache
+    (64, 192, 16, 40, 4, 2, (3, 1, 1), 2, "bf16_s1_n192_p8x32"),
+    (48, 40, 9, 33, 6, 2, (3, 1, 1), 3, "bf16_s1_n32_p8x32"),
+    (96, 3, 16, 32, 4, 2, (3, 3, 3), 2, "bf16_s3_n32_p8x32"),         # head shape: not the few kernel
+]
+
+
+@pytest.mark.parametrize("case", STRIDED)
+def test_temporal_stride_full_compare(cuda_device, case):
+    cin, cout, h, w_, tx, tc, k, st, variant = case
+    pad = (1, 1) if k[1] == 3 else (0, 0)
+    x, c, w, b = synth.conv_inputs(1, cin, cout, h, w_, tx, tc, k, device=DEV, seed=synth.SEED_BASE + 350 + h)
+    y, co, plan = run(x, c, w, b, k=k, pad=pad, st=st, variant=variant)
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == variant
+    ref = _oracle(x, c, w, b, k=k, pad=pad, st=st)
+    assert_bf16_close(y, ref, variant)
+    z = x if c is None else torch.cat([c, x], 1)
+    assert torch.equal(co, z[:, -min(2, z.shape[1]):])
+
+
+def test_temporal_stride_fp32_direct(cuda_device):
+    x, c, w, b = synth.conv_inputs(1, 8, 8, 16, 16, 4, 2, kind="uniform", dtype=torch.float32, device=DEV,
+                                   seed=synth.SEED_BASE + 360)
+    y, _, plan = run(x, c, w, b, st=2)
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == "f32_direct" and plan.info["t_out"] == 2  # floor((6 - 3) / 2) + 1
+    assert_f32_close(y, _oracle(x, c, w, b, st=2), "f32 s_t=2")
+
+
+@pytest.mark.parametrize("k", [(3, 3, 3), (3, 1, 1)])
+def test_temporal_stride_streaming_equals_one_shot(cuda_device, k):
+    """Stride-2 streaming with chunks of even length and the 2-frame carry:
+    every output against one oracle call over the whole sequence."""
+    cin, cout = (64, 96) if k[1] == 3 else (64, 192)
+    pad = (1, 1) if k[1] == 3 else (0, 0)
+    wt, bt, xs = synth.replay_chunks(1, cin, cout, 21, 40, [2, 4, 4, 6], k, device=DEV, seed=synth.SEED_BASE + 361)
+    outs, cache = [], None
+    for xc in xs:
+        y, cache, _ = run(xc, cache, wt, bt, k=k, pad=pad, st=2)
+        outs.append(y)
+    torch.cuda.synchronize()
+    whole = oracle.conv3d(torch.cat(xs, 1).cpu(), None, wt.cpu(), bt.cpu(), stride=(2, 1, 1), padding=pad, pbase=2)
+    got = torch.cat(outs, 1)
+    assert got.shape[1] == 8
+    assert_bf16_close(got, whole, "stride-2 streaming %s" % (k,))
+
+
+@pytest.mark.parametrize("sig", synth.ENCODER_DOWNSAMPLE, ids=[s["name"] for s in synth.ENCODER_DOWNSAMPLE])
+def test_encoder_downsample_full_size_sampled(cuda_device, sig):
+    """The encoder's stride-2 temporal downsampling convs at full size."""
+    s = sig
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"], device=DEV,
+                                   seed=synth.SEED_BASE + 370)
+    y, co, plan = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], st=s["st"])
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"].startswith("bf16_") and plan.info["t_out"] == s["tx"] // s["st"]
+    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=37)
+    ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], st=s["st"], points=pts)
+    assert_bf16_close(gather(y, pts), ref, s["name"])

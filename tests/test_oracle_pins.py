@@ -228,6 +228,32 @@ def test_streaming_with_cache_carry_equals_one_shot_bitwise(frames, dt, pbase, k
     assert np.array_equal(chunked, whole)
 
 
+@pytest.mark.parametrize("frames,st,k", [
+    ([4, 4, 4], 2, (3, 3, 3)),
+    ([2, 4, 2, 6], 2, (3, 3, 3)),
+    ([4, 2, 4], 2, (3, 1, 1)),   # the encoder's temporal downsampling conv
+    ([3, 6, 3], 3, (3, 3, 3)),
+])
+def test_strided_streaming_with_cache_carry_equals_one_shot_bitwise(frames, st, k):
+    """Temporal stride s_t with p_base = d_t*(k_t-1): when every chunk's
+    length is a multiple of s_t, chunked calls carrying the last p_base
+    frames of Z equal one call over the whole sequence (chunk c's first
+    output is whole-sequence output sum(frames[:c]) / s_t)."""
+    rng = np.random.default_rng(40 + sum(frames) + st)
+    h, wd, cin, cout = 5, 4, 3, 2
+    pad = (1, 1) if k[1] == 3 else (0, 0)
+    xs = [_rand((1, f, h, wd, cin), rng) for f in frames]
+    wt = _rand((cout,) + k + (cin,), rng)
+    b = _rand((cout,), rng)
+    whole = _call(np.concatenate(xs, axis=1), None, wt, b, stride=(st, 1, 1), padding=pad, pbase=2)
+    assert whole.shape[1] == sum(frames) // st
+    cache, outs = None, []
+    for xc in xs:
+        outs.append(_call(xc, cache, wt, b, stride=(st, 1, 1), padding=pad, pbase=2))
+        cache = oracle.cache_out(xc, cache, 2)
+    assert np.array_equal(np.concatenate(outs, axis=1), whole)
+
+
 def test_points_mode_equals_full_and_thread_count_does_not_matter():
     rng = np.random.default_rng(13)
     x = _rand((2, 4, 7, 9, 5), rng)

@@ -148,6 +148,49 @@ def test_tiny_workload_intervals():
     assert [t["active"] for t in d["taps"]] == [0, 1, 1] and d["p_l"] == 1
 
 
+def test_strided_tap_intervals_match_brute_force_enumeration():
+    """Temporal stride s_t > 1: tap k of output o reads source frame
+    o*s_t + k*d_t - p_l; the outputs reading a tap are still one interval
+    [o_lo, o_hi), their source frames every s_t-th one of [src_lo, src_hi)."""
+    checked = 0
+    for s_t, k_t, d_t in itertools.product((2, 3), (1, 2, 3), (1, 2)):
+        for p_base in range(0, d_t * (k_t - 1) + 2):
+            for t_x in range(1, 10):
+                for t_c in range(0, p_base + 2):
+                    shp = oracle.out_shape(t_x, t_c, 8, 8, kt=k_t, st=s_t, dt=d_t, pbase=p_base)
+                    desc = _desc(t_x=t_x, t_cache=t_c, k=(k_t, 3, 3), stride=(s_t, 1, 1), dilation=(d_t, 1, 1),
+                                 p_base=p_base)
+                    if shp is None:
+                        with pytest.raises(cc3d.CC3DError) as e:
+                            cc3d.causal_conv3d_plan(desc)
+                        assert e.value.status == cc3d.CC3D_ERR_INVALID_ARG
+                        continue
+                    info = cc3d.causal_conv3d_plan(desc).info
+                    assert (info["t_out"], info["h_out"], info["w_out"]) == shp
+                    pl, tz = p_base - t_c, t_x + t_c
+                    pairs = 0
+                    for k, tap in enumerate(info["taps"]):
+                        outs = [o for o in range(info["t_out"]) if 0 <= o * s_t + k * d_t - pl < tz]
+                        assert list(range(tap["o_lo"], tap["o_hi"])) == outs
+                        if outs:
+                            assert tap["src_lo"] == outs[0] * s_t + tap["delta"]
+                            assert tap["src_hi"] == outs[-1] * s_t + tap["delta"] + 1
+                            assert 0 <= tap["src_lo"] < tap["src_hi"] <= tz
+                        pairs += len(outs)
+                    per = 2 * 8 * 8 * 16 * 16 * 9
+                    assert info["flops_active"] == pairs * per
+                    checked += 1
+    assert checked > 300
+
+
+def test_strided_calls_never_take_the_head_kernel():
+    d = _desc(c_in=96, c_out=3, h=64, w=64, t_x=4, t_cache=2, stride=(2, 1, 1))
+    assert cc3d.causal_conv3d_plan(d).info["kernel_name"] == "bf16_s3_n32_p8x32"
+    with pytest.raises(cc3d.CC3DError) as e:
+        cc3d.causal_conv3d_plan_variant(d, "bf16_s3_few_p16x32")
+    assert e.value.status == cc3d.CC3D_ERR_UNSUPPORTED
+
+
 def test_flops_and_bytes():
     p = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2)).info
     nominal = 2 * 1 * 4 * 360 * 640 * 192 * 192 * 27
@@ -161,7 +204,6 @@ def test_flops_and_bytes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(stride=(2, 1, 1)), cc3d.CC3D_ERR_UNSUPPORTED),          # temporal stride 2
     (dict(groups=2), cc3d.CC3D_ERR_UNSUPPORTED),
     (dict(k=(9, 3, 3), p_base=8), cc3d.CC3D_ERR_UNSUPPORTED),      # k_t above the maximum
     (dict(k=(3, 5, 5), padding=(2, 2)), cc3d.CC3D_ERR_UNSUPPORTED),  # bf16 spatial envelope
