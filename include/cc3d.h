@@ -19,6 +19,13 @@
  *   with PyTorch's cross-correlation convention and the original spatial
  *   stride, zero padding and dilation; the bias is added exactly once.
  *   T_o = |Z| + p_l - d_t*(k_t - 1)  (T_o = |X| when p_base = d_t*(k_t - 1)).
+ * Temporal stride s_t > 1 (the encoder's downsampling convs, which the paper
+ * leaves outside its unit-stride contract) generalises this: tap k of output
+ * frame o reads source frame o*s_t + delta_k, tap k is evaluated for o in
+ * [ceil(-delta_k / s_t), min(T_o, ceil((|Z| - delta_k) / s_t))), and
+ * T_o = floor((|Z| + p_l - d_t*(k_t - 1) - 1) / s_t) + 1.  Chunked calls
+ * carrying the last p_base frames equal one call over the whole sequence
+ * when every chunk's length is a multiple of s_t.
  *
  * All active temporal taps, all spatial taps and all input channels form one
  * K reduction accumulated in registers by one kernel (no per-tap Conv2D, no
@@ -96,7 +103,8 @@ typedef struct cc3d_desc {
 typedef struct cc3d_tap {
   int32_t delta;          /* k*d_t - p_l */
   int32_t o_lo, o_hi;     /* output frames that read this tap: [o_lo, o_hi) */
-  int32_t src_lo, src_hi; /* frames of Z they read: [o_lo+delta, o_hi+delta) */
+  int32_t src_lo, src_hi; /* frames of Z they read: [o_lo+delta, o_hi+delta) at
+                             unit stride; every s_t-th frame of [src_lo, src_hi) */
   int32_t active;         /* o_hi > o_lo */
 } cc3d_tap_t;
 
@@ -134,8 +142,9 @@ typedef struct cc3d_counters {
  *   desc  shape of the call; it is copied.
  *   out   receives the plan; set to NULL on error.
  * Contract (the paper's lowering covers 5-D tensors with unit temporal
- * stride and one group; every call it observed has k_t = 3):
- *   CC3D_ERR_UNSUPPORTED when s_t != 1, groups != 1, k_t > CC3D_MAX_KT, or,
+ * stride and one group; every call it observed has k_t = 3; temporal stride
+ * > 1 is supported here as well):
+ *   CC3D_ERR_UNSUPPORTED when groups != 1, k_t > CC3D_MAX_KT, or,
  *   for bf16: k_t > 4, spatial stride or dilation != 1, k_h != k_w, k_h not in {1, 3},
  *   padding other than (k_h-1)/2, C_in not a multiple of 16, or one frame
  *   (H*W*max(C_in, C_out) elements) or the weights reaching 2^31 bytes.
