@@ -149,20 +149,21 @@ def time_kernels(work, launches, stream, warm_seconds=0.2):
 def time_single_calls(device, launches, stream, warm_seconds=0.2):
     """Average conv-kernel launch time of each single-call configuration (the
     latent, mid-resolution 192->192 and 384->192, full-resolution 96->96 and
-    96->3 calls, each with 2 cached frames, and the encoder's stride-2
-    temporal downsampling convs), weights packed once; HIP events on the
-    launch stream after warm_seconds of untimed launches."""
+    96->3 calls, each with 2 cached frames, the encoder's stride-2 temporal
+    downsampling convs, and two convs with spatial stride or dilation 2),
+    weights packed once; HIP events on the launch stream after warm_seconds
+    of untimed launches."""
     import torch
 
     import causal_conv3d_video_amd as cc3d
     import synth
 
     res = {}
-    for i, s in enumerate(synth.SINGLE_CALLS + synth.ENCODER_DOWNSAMPLE):
+    for i, s in enumerate(synth.SINGLE_CALLS + synth.ENCODER_DOWNSAMPLE + synth.GENERAL_SPATIAL):
         x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
                                        device=device, seed=synth.SEED_BASE + 200 + i)
         desc = cc3d.make_desc(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], k=s["k"],
-                              stride=(s["st"], 1, 1), dilation=(s["dt"], 1, 1), padding=s["pad"],
+                              stride=(s["st"],) + s["sst"], dilation=(s["dt"],) + s["sdil"], padding=s["pad"],
                               p_base=s["p_base"])
         plan = cc3d.causal_conv3d_plan(desc)
         out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)

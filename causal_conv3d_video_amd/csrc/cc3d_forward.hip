@@ -1310,6 +1310,158 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #endif
 }
 
+// bf16 kernel for any spatial kernel size, stride, dilation and padding
+// (k_t <= 4, C_in % 16 == 0): an implicit GEMM over stages (active temporal
+// tap, spatial tap, 32-channel chunk).  A stage gathers, for every output
+// pixel of the tile, the 16-byte channel pieces of the input pixel that tap
+// reads, straight into LDS (the buffer range check writes zeros for the
+// padding and for channels past C_in), and the 32 x 32 weight block from the
+// copy of W in the workspace ([C_out][k_t][k_h][k_w][C_in] as it is).  No
+// halo is shared between spatial taps, so the input is read k_h * k_w times
+// from L2: the kernel covers the shapes the halo-staged ones do not.
+// Tile: 8 x 32 output pixels x 32 output channels; wave w owns rows 2w and
+// 2w + 1 (two 32 x 32 accumulators); double-buffered stages.
+__global__ __launch_bounds__(256) void conv_bf16_gen(ConvArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int TH = 8, TW = 32, BN = 32, NT = 256, PPX = 4;  // 16-byte pieces per pixel: 32 channels
+  constexpr int ASL = TH * TW * PPX, BSL = BN * PPX;           // LDS slots per stage
+  __shared__ uint4 al[2 * ASL];
+  __shared__ uint4 bl[2 * BSL];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+
+  int t = blockIdx.x;
+  const int o = t % a.to;
+  t /= a.to;
+  const int nb = t % a.nblk_n;
+  t /= a.nblk_n;
+  const int x0 = (t % a.tiles_x) * TW;
+  t /= a.tiles_x;
+  const int y0 = (t % a.tiles_y) * TH;
+  const int nn = t / a.tiles_y;
+  const int n0 = nb * BN;
+
+  // active temporal taps of output frame o
+  int ktap[kMaxTapsBf16], ztap[kMaxTapsBf16], nact = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxTapsBf16; ++k) {
+    ktap[k] = ztap[k] = 0;
+    const int z = o * a.st + a.delta[k];
+    if (k < a.kt && z >= 0 && z < a.tz) {
+#pragma unroll
+      for (int i = 0; i < kMaxTapsBf16; ++i)
+        if (i == nact) {
+          ktap[i] = k;
+          ztap[i] = z;
+        }
+      ++nact;
+    }
+  }
+  const int nchk = (a.cin + 31) / 32, nsp = a.kh * a.kw;
+  const int nst = nact * nsp * nchk;
+  const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
+  const int frame_bytes = int(frame_el * 2);
+  const int w_bytes = a.cout * a.kt * nsp * a.cin * 2;
+  const unsigned short* __restrict__ xs = static_cast<const unsigned short*>(a.x);
+  const unsigned short* __restrict__ cs = static_cast<const unsigned short*>(a.cache);
+  unsigned short* __restrict__ os = static_cast<unsigned short*>(a.out);
+  const __amdgpu_buffer_rsrc_t r_w =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.wpk), 0, w_bytes, 0x00020000);
+  constexpr int OOB = int(0x80000000u);
+  auto pick = [](const int* v, int i) {
+    int r = v[0];
+#pragma unroll
+    for (int j = 1; j < kMaxTapsBf16; ++j)
+      if (j == i) r = v[j];
+    return r;
+  };
+
+  // Slot s of a stage buffer holds piece q of pixel px with s = px*4 + (q ^ (px & 3))
+  // (the XOR spreads the 32 pixels one fragment read touches over the banks);
+  // the direct-to-LDS load writes lane i's 16 bytes at slot base + i, so the
+  // thread owning slot s loads that pixel's piece.
+  auto issue = [&](int st, int buf) {
+    const int cc = st % nchk, sp = (st / nchk) % nsp, ti = st / (nchk * nsp);
+    const int ta = sp / a.kw, tcol = sp % a.kw;
+    const int k = pick(ktap, ti), z = pick(ztap, ti);
+    const unsigned short* fp =
+        z < a.tc ? cs + (int64_t(nn) * a.tc + z) * frame_el : xs + (int64_t(nn) * a.tx + (z - a.tc)) * frame_el;
+    const __amdgpu_buffer_rsrc_t r_z =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
+#pragma unroll
+    for (int it = 0; it < ASL / NT; ++it) {
+      const int sl = it * NT + tid, px = sl >> 2, q = (sl & 3) ^ (px & 3);
+      const int oy = y0 + (px >> 5), ox = x0 + (px & 31);
+      const int iy = oy * a.sh - a.ph + ta * a.dh, ix = ox * a.sw - a.pw + tcol * a.dw, ch = cc * 32 + q * 8;
+      const bool in = oy < a.ho && ox < a.wo && iy >= 0 && iy < a.h && ix >= 0 && ix < a.wd && ch < a.cin;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r_z, (__attribute__((address_space(3))) void*)(al + buf * ASL + it * NT + wave * 64), 16,
+          in ? ((iy * a.wd + ix) * a.cin + ch) * 2 : OOB, 0, 0, 0);
+    }
+    if (wave < BSL / 64) {
+      const int co = tid >> 2, q = (tid & 3) ^ (co & 3), ch = cc * 32 + q * 8;
+      const bool in = n0 + co < a.cout && ch < a.cin;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r_w, (__attribute__((address_space(3))) void*)(bl + buf * BSL + wave * 64), 16,
+          in ? ((((n0 + co) * a.kt + k) * nsp + sp) * a.cin + ch) * 2 : OOB, 0, 0, 0);
+    }
+  };
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[r][v] = 0.f;
+  if (nst > 0) issue(0, 0);
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) {
+      issue(st + 1, buf ^ 1);
+      // stage st has landed once only stage st + 1's loads are in flight
+      if (wave < BSL / 64) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ASL / NT + 1) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ASL / NT) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    barrier();
+    const uint4* ab = al + buf * ASL;
+    const uint4* bb = bl + buf * BSL;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int q = kk * 2 + g;  // 8-channel piece of this lane's k range
+      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, bb[l32 * 4 + (q ^ (l32 & 3))]);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int px = (wave * 2 + r) * 32 + l32;
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, ab[px * 4 + (q ^ (px & 3))]);
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, pf, acc[r], 0, 0, 0);
+      }
+    }
+    barrier();  // before stage st + 2 overwrites this buffer
+  }
+
+  // epilogue: bias once in fp32, round to nearest even, channels-last stores
+  const unsigned short* __restrict__ bs = static_cast<const unsigned short*>(a.b);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int oy = y0 + wave * 2 + r, ox = x0 + l32;
+    if (oy >= a.ho || ox >= a.wo) continue;
+    unsigned short* op = os + (((int64_t(nn) * a.to + o) * a.ho + oy) * a.wo + ox) * a.cout;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int co = n0 + (v >> 2) * 8 + g * 4 + (v & 3);
+      if (co < a.cout) op[co] = f32_to_bf16(acc[r][v] + (a.has_bias ? bf16_to_f32(bs[co]) : 0.f));
+    }
+  }
+#endif
+}
+
 // Packs the weights of the few-channel kernel into its B fragments: for
 // chunk ch, spatial tap s and lane l, the 8 weights of column n = l % 16
 // ((tap k, channel co) = (n / C_out, n % C_out), zero past 3 C_out) and
@@ -1503,6 +1655,18 @@ hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv,
   return launch_persistent<&mfma_kernel<BN, TH, WM, WN, KS, CB, NBUF, OCC>>(a, tiles, cus, WM * WN * 64, s);
 }
 
+// The general-spatial kernel reads W as it is, from a copy in the workspace
+// (so the packed-weights path works the same way); one workgroup per tile.
+hipError_t launch_gen(ConvArgs a, int64_t tiles, bool pack, bool conv, hipStream_t s) {
+  if (pack) {
+    const size_t w_bytes = size_t(a.cout) * a.kt * a.kh * a.kw * a.cin * 2;
+    const hipError_t e = hipMemcpyAsync(const_cast<void*>(a.wpk), a.w, w_bytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!conv) return hipSuccess;
+  return launch_conv(reinterpret_cast<const void*>(&conv_bf16_gen), a, tiles, s, 256);
+}
+
 // The group-staged 3x3 kernel (16-channel weight sub-stages, same packing).
 template <int BN, int TH, int WM>
 hipError_t launch_g32(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
@@ -1691,6 +1855,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     case CC3D_K_BF16_S3_N96_G32W8:
       e = launch_g32<96, 16, 8>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
       break;
+    case CC3D_K_BF16_GEN_N32: e = launch_gen(a, in.tiles, pack, runs, s); break;
     case CC3D_K_BF16_S3_FEW:
       switch (d.c_out) {
         case 1: e = launch_few_cin<1>(a, in.tiles, cus, pack, runs, s); break;

@@ -40,10 +40,22 @@ struct Variant {
 // operand block of pixels); rows and channel tiles trade accumulator
 // registers against LDS and L2 traffic per MFMA.  variant_for() gives the
 // named variant's geometry for a call, or nothing when it cannot run it.
+// The halo-staged kernels' spatial envelope: 3x3 "same" or 1x1, stride and
+// dilation 1.
+bool same_spatial(const cc3d_desc_t& d) {
+  return d.k_h == d.k_w && (d.k_h == 1 || d.k_h == 3) && d.s_h == 1 && d.s_w == 1 && d.d_h == 1 && d.d_w == 1 &&
+         d.p_h == (d.k_h - 1) / 2 && d.p_w == (d.k_w - 1) / 2;
+}
+
 bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
+  const std::string n(name);
+  if (n == "bf16_gen_n32_p8x32") {  // any spatial parameters
+    *v = {CC3D_K_BF16_GEN_N32, 8, 32, 32, 32, "bf16_gen_n32_p8x32"};
+    return true;
+  }
+  if (!same_spatial(d)) return false;
   const bool s3 = d.k_h == 3;
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
-  const std::string n(name);
   if (n == "bf16_s3_n96_p16x32_g32") {
     *v = {CC3D_K_BF16_S3_N96_G32W8, 16, 32, 96, 16, "bf16_s3_n96_p16x32_g32"};
     return s3 && d.c_out % 96 == 0 && d.c_in % 32 == 0;
@@ -79,6 +91,7 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
 // small ones keep two smaller workgroups per compute unit so that every
 // unit gets tiles.  causal_conv3d_plan_autotune times the alternatives.
 const char* default_variant(const cc3d_desc_t& d) {
+  if (!same_spatial(d)) return "bf16_gen_n32_p8x32";
   if (d.k_h == 3) {
     if (d.c_out % 96 == 0) {
       const int64_t big_tiles = int64_t(d.n) * ((d.h + 15) / 16) * ((d.w + 31) / 32) * (d.c_out / 96) *
@@ -181,14 +194,11 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
   p->cache_out_bytes = int64_t(d.n) * in.t_cache_out * frame_el_in * elem;
 
   if (d.dtype == CC3D_BF16) {
-    const bool spatial_ok = d.k_h == d.k_w && (d.k_h == 1 || d.k_h == 3) && d.s_h == 1 &&
-                            d.s_w == 1 && d.d_h == 1 && d.d_w == 1 &&
-                            d.p_h == (d.k_h - 1) / 2 && d.p_w == (d.k_w - 1) / 2;
     // buffer-load offsets are 32-bit byte offsets within one frame / the weights
-    const int64_t frame_bytes = int64_t(d.h) * d.w * std::max(d.c_in, d.c_out) * 2;
+    const int64_t frame_bytes =
+        std::max(int64_t(d.h) * d.w * std::max(d.c_in, d.c_out), h_out * w_out * d.c_out) * 2;
     const int64_t w_bytes = int64_t(d.c_out) * d.k_t * d.k_h * d.k_w * d.c_in * 2;
-    if (!spatial_ok || d.c_in % 16 != 0 || d.k_t > 4 || frame_bytes >= (int64_t(1) << 31) ||
-        w_bytes >= (int64_t(1) << 31)) {
+    if (d.c_in % 16 != 0 || d.k_t > 4 || frame_bytes >= (int64_t(1) << 31) || w_bytes >= (int64_t(1) << 31)) {
       delete p;
       return refuse(CC3D_ERR_UNSUPPORTED);
     }
@@ -213,6 +223,7 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     const int64_t slots = (int64_t(v.block_n) * ks * ks * (v.cin_chunk / 8) + 255) / 256 * 256;
     p->wpk_bytes = int64_t(d.k_t) * (d.c_in / v.cin_chunk) * p->nblk_n * slots * 16;
     if (v.id == CC3D_K_BF16_S3_FEW) p->wpk_bytes = int64_t(d.c_in / 32) * 9 * 64 * 16;  // register fragments
+    if (v.id == CC3D_K_BF16_GEN_N32) p->wpk_bytes = w_bytes;  // a copy of W, read as it is
     p->sched_off = (p->wpk_bytes + 255) / 256 * 256;
     in.workspace_bytes = p->sched_off + int64_t(kSchedSlots) * kSchedInts * 4;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);

@@ -81,10 +81,12 @@ def replay_chunks(n, cin, cout, h, w, frames, k=(3, 3, 3), *, dtype=torch.bfloat
 
 # Workload shapes (N = 1, channels last).  Each entry: C_in, C_out, H, W,
 # frames of X per call, cached frames, kernel, temporal dilation, base pad.
-def _sig(name, cin, cout, h, w, tx, tc, k=(3, 3, 3), dt=1, p_base=None, kind="normal", dtype="bf16", st=1):
-    pad = (1, 1) if k[1] == 3 else (0, 0)
+def _sig(name, cin, cout, h, w, tx, tc, k=(3, 3, 3), dt=1, p_base=None, kind="normal", dtype="bf16", st=1,
+         pad=None, sst=(1, 1), sdil=(1, 1)):
+    if pad is None:
+        pad = (1, 1) if k[1] == 3 else (0, 0)
     return dict(name=name, n=1, cin=cin, cout=cout, h=h, w=w, tx=tx, tc=tc, k=k, pad=pad, dt=dt, st=st,
-                p_base=dt * (k[0] - 1) if p_base is None else p_base, kind=kind, dtype=dtype)
+                sst=sst, sdil=sdil, p_base=dt * (k[0] - 1) if p_base is None else p_base, kind=kind, dtype=dtype)
 
 
 # Tiny fp32 case: call A (no cache, 4 frames), then call B (the last 2 frames
@@ -146,6 +148,13 @@ DECODER_SIGNATURES = [
 ENCODER_DOWNSAMPLE = [
     _sig("enc_tdown_384_180x320", 384, 384, 180, 320, 4, 2, k=(3, 1, 1), st=2),
     _sig("enc_tdown_384_90x160", 384, 384, 90, 160, 4, 2, k=(3, 1, 1), st=2),
+]
+# Spatial parameters outside the halo-staged kernels' envelope (they run on
+# the gather kernel): a stride-2 3x3 conv taking 720x1280 to 360x640 with a
+# channel doubling, and a dilation-2 3x3 conv at 360x640.
+GENERAL_SPATIAL = [
+    _sig("gen_s2_96_192_720x1280", 96, 192, 720, 1280, 4, 2, sst=(2, 2)),
+    _sig("gen_d2_192_360x640", 192, 192, 360, 640, 4, 2, pad=(2, 2), sdil=(2, 2)),
 ]
 # Frames per chunk of the streaming 17-frame decode at the 360x640 and
 # 720x1280 stages: the first chunk decodes one frame, the next four decode

@@ -9,22 +9,24 @@ BF16_REL_TOL = 2e-2   # max |gpu - oracle| <= 2e-2 * RMS(oracle) for bf16 output
 F32_ABS_TOL = 1e-4    # max |gpu - oracle| <= 1e-4 for fp32 outputs
 
 
-def plan_for(x, tc, w, *, k, pad, dt=1, p_base=2, has_bias=True, dtype=torch.bfloat16, variant=None, st=1):
+def plan_for(x, tc, w, *, k, pad, dt=1, p_base=2, has_bias=True, dtype=torch.bfloat16, variant=None, st=1,
+             sst=(1, 1), sdil=(1, 1)):
     n, tx, h, wd, cin = x.shape
     cout = w.shape[0]
-    desc = cc3d.make_desc(n, cin, cout, h, wd, tx, tc, k=k, stride=(st, 1, 1), dilation=(dt, 1, 1), padding=pad,
-                          p_base=p_base, has_bias=has_bias, dtype=dtype)
+    desc = cc3d.make_desc(n, cin, cout, h, wd, tx, tc, k=k, stride=(st,) + tuple(sst), dilation=(dt,) + tuple(sdil),
+                          padding=pad, p_base=p_base, has_bias=has_bias, dtype=dtype)
     if variant is not None:
         return cc3d.causal_conv3d_plan_variant(desc, variant)
     return cc3d.causal_conv3d_plan(desc)
 
 
-def run(x, cache, w, b, *, k=(3, 3, 3), pad=(1, 1), dt=1, p_base=2, want_cache=True, out=None, variant=None, st=1):
+def run(x, cache, w, b, *, k=(3, 3, 3), pad=(1, 1), dt=1, p_base=2, want_cache=True, out=None, variant=None, st=1,
+        sst=(1, 1), sdil=(1, 1)):
     """GPU forward through the C ABI; returns (out, cache_out, plan).  variant
     pins a kernel variant by name (default: the library's choice)."""
     tc = 0 if cache is None else cache.shape[1]
     plan = plan_for(x, tc, w, k=k, pad=pad, dt=dt, p_base=p_base, has_bias=b is not None, dtype=x.dtype,
-                    variant=variant, st=st)
+                    variant=variant, st=st, sst=sst, sdil=sdil)
     sh = plan.shapes()
     if out is None:
         out = torch.empty(sh["out"], dtype=x.dtype, device=x.device)

@@ -22,9 +22,10 @@ def _np(t):
     return None if t is None else t.detach().cpu()
 
 
-def _oracle(x, cache, w, b, *, k=(3, 3, 3), pad=(1, 1), dt=1, p_base=2, points=None, st=1):
-    return oracle.conv3d(_np(x), _np(cache), _np(w), _np(b), stride=(st, 1, 1), dilation=(dt, 1, 1), padding=pad,
-                         pbase=p_base, points=points)
+def _oracle(x, cache, w, b, *, k=(3, 3, 3), pad=(1, 1), dt=1, p_base=2, points=None, st=1, sst=(1, 1),
+            sdil=(1, 1)):
+    return oracle.conv3d(_np(x), _np(cache), _np(w), _np(b), stride=(st,) + tuple(sst), dilation=(dt,) + tuple(sdil),
+                         padding=pad, pbase=p_base, points=points)
 
 
 def test_tiny_fp32_calls_a_then_b(cuda_device):
@@ -556,4 +557,59 @@ def test_encoder_downsample_full_size_sampled(cuda_device, sig):
     assert plan.info["kernel_name"].startswith("bf16_") and plan.info["t_out"] == s["tx"] // s["st"]
     pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=37)
     ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], st=s["st"], points=pts)
+    assert_bf16_close(gather(y, pts), ref, s["name"])
+
+
+# General spatial parameters on the gather kernel: (C_in, C_out, H, W, T_x,
+# T_cache, k, pad, spatial stride, spatial dilation, s_t, d_t, p_base, N, bias)
+GENERAL = [
+    (32, 40, 20, 36, 4, 2, (3, 5, 5), (2, 2), (1, 1), (1, 1), 1, 1, 2, 1, True),   # 5x5 "same"
+    (32, 96, 21, 37, 4, 2, (3, 3, 3), (1, 1), (2, 2), (1, 1), 1, 1, 2, 1, True),   # spatial stride 2
+    (48, 40, 16, 40, 3, 2, (3, 3, 3), (2, 2), (1, 1), (2, 2), 1, 1, 2, 1, True),   # spatial dilation 2
+    (64, 64, 15, 33, 2, 2, (3, 1, 3), (0, 1), (1, 1), (1, 1), 1, 1, 2, 1, True),   # 1x3
+    (32, 70, 24, 50, 4, 2, (3, 3, 3), (0, 0), (1, 1), (1, 1), 1, 1, 2, 1, True),   # "valid", ragged C_out
+    (32, 96, 18, 34, 4, 2, (3, 3, 3), (1, 1), (2, 2), (1, 1), 2, 1, 2, 1, True),   # stride 2 in t, h, w
+    (32, 40, 12, 20, 2, 2, (3, 3, 3), (1, 1), (2, 1), (1, 1), 1, 1, 2, 2, True),   # batch 2, stride (2, 1)
+    (16, 32, 14, 30, 4, 4, (3, 3, 3), (2, 1), (1, 1), (2, 1), 1, 2, 4, 1, False),  # d_t 2, d_h 2, no bias
+    (48, 33, 9, 70, 1, 0, (3, 3, 3), (1, 1), (1, 2), (1, 1), 1, 1, 2, 1, True),    # one frame, no cache
+]
+
+
+@pytest.mark.parametrize("case", GENERAL)
+def test_general_spatial_parameters_full_compare(cuda_device, case):
+    cin, cout, h, w_, tx, tc, k, pad, sst, sdil, st, dt, p_base, n, bias = case
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV, seed=synth.SEED_BASE + 380 + h,
+                                   has_bias=bias)
+    y, co, plan = run(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, st=st, sst=sst, sdil=sdil)
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == "bf16_gen_n32_p8x32"
+    ref = _oracle(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, st=st, sst=sst, sdil=sdil)
+    assert_bf16_close(y, ref, "general %s" % (case,))
+    z = x if c is None else torch.cat([c, x], 1)
+    assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
+
+
+@pytest.mark.parametrize("case", GROUP_STAGED[:4])
+def test_gather_kernel_on_same_convs_full_compare(cuda_device, case):
+    """The gather kernel pinned on the 3x3 "same" shapes the halo-staged
+    kernels run, against the oracle."""
+    cin, cout, h, w_, tx, tc, k, dt, p_base, n, bias = case
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV, seed=synth.SEED_BASE + 390 + h,
+                                   has_bias=bias)
+    y, _, plan = run(x, c, w, b, k=k, dt=dt, p_base=p_base, variant="bf16_gen_n32_p8x32")
+    torch.cuda.synchronize()
+    assert_bf16_close(y, _oracle(x, c, w, b, k=k, dt=dt, p_base=p_base), "gather kernel")
+
+
+@pytest.mark.parametrize("sig", synth.GENERAL_SPATIAL, ids=[s["name"] for s in synth.GENERAL_SPATIAL])
+def test_general_spatial_full_size_sampled(cuda_device, sig):
+    s = sig
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"], device=DEV,
+                                   seed=synth.SEED_BASE + 395)
+    y, _, plan = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"])
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == "bf16_gen_n32_p8x32"
+    assert bool(torch.isfinite(y).all())
+    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=39)
+    ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"], points=pts)
     assert_bf16_close(gather(y, pts), ref, s["name"])

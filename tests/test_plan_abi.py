@@ -183,6 +183,27 @@ def test_strided_tap_intervals_match_brute_force_enumeration():
     assert checked > 300
 
 
+@pytest.mark.parametrize("kw", [
+    dict(k=(3, 5, 5), padding=(2, 2)),
+    dict(stride=(1, 2, 2)),
+    dict(padding=(0, 0)),
+    dict(dilation=(1, 2, 2), padding=(2, 2)),
+    dict(k=(3, 1, 3), padding=(0, 1)),
+    dict(k=(3, 3, 3), stride=(2, 2, 2), padding=(1, 1)),
+])
+def test_general_spatial_parameters_take_the_gather_kernel(kw):
+    """bf16 calls outside the halo-staged kernels' envelope (3x3 "same" or
+    1x1, stride and dilation 1) run on the general-spatial kernel, which
+    reads W as it is (its workspace holds a copy of W)."""
+    p = cc3d.causal_conv3d_plan(_desc(c_in=32, c_out=40, h=20, w=36, **kw))
+    assert p.info["kernel_name"] == "bf16_gen_n32_p8x32" and p.info["block_m"] == 256 and p.info["block_n"] == 32
+    k = kw.get("k", (3, 3, 3))
+    assert p.info["workspace_bytes"] >= 40 * k[0] * k[1] * k[2] * 32 * 2
+    for name in ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32", "bf16_s1_n32_p8x32"]:
+        with pytest.raises(cc3d.CC3DError):
+            cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=96, h=20, w=36, **kw), name)
+
+
 def test_strided_calls_never_take_the_head_kernel():
     d = _desc(c_in=96, c_out=3, h=64, w=64, t_x=4, t_cache=2, stride=(2, 1, 1))
     assert cc3d.causal_conv3d_plan(d).info["kernel_name"] == "bf16_s3_n32_p8x32"
@@ -206,9 +227,7 @@ def test_flops_and_bytes():
 @pytest.mark.parametrize("kw,status", [
     (dict(groups=2), cc3d.CC3D_ERR_UNSUPPORTED),
     (dict(k=(9, 3, 3), p_base=8), cc3d.CC3D_ERR_UNSUPPORTED),      # k_t above the maximum
-    (dict(k=(3, 5, 5), padding=(2, 2)), cc3d.CC3D_ERR_UNSUPPORTED),  # bf16 spatial envelope
-    (dict(stride=(1, 2, 2)), cc3d.CC3D_ERR_UNSUPPORTED),
-    (dict(padding=(0, 0)), cc3d.CC3D_ERR_UNSUPPORTED),
+    (dict(k=(5, 3, 3), p_base=4), cc3d.CC3D_ERR_UNSUPPORTED),      # bf16: k_t > 4
     (dict(c_in=24), cc3d.CC3D_ERR_UNSUPPORTED),                    # bf16 needs C_in % 16 == 0
     (dict(n=0), cc3d.CC3D_ERR_INVALID_ARG),
     (dict(t_x=0), cc3d.CC3D_ERR_INVALID_ARG),
