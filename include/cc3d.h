@@ -144,10 +144,12 @@ typedef struct cc3d_counters {
  * Contract (the paper's lowering covers 5-D tensors with unit temporal
  * stride and one group; every call it observed has k_t = 3; temporal stride
  * > 1 is supported here as well):
- *   CC3D_ERR_UNSUPPORTED when groups != 1, k_t > CC3D_MAX_KT, or,
- *   for bf16: k_t > 4, spatial stride or dilation != 1, k_h != k_w, k_h not in {1, 3},
- *   padding other than (k_h-1)/2, C_in not a multiple of 16, or one frame
- *   (H*W*max(C_in, C_out) elements) or the weights reaching 2^31 bytes.
+ *   CC3D_ERR_UNSUPPORTED when groups != 1, k_t > CC3D_MAX_KT, or, for
+ *   bf16: k_t > 4, C_in not a multiple of 16, or one frame (input or
+ *   output) or the weights reaching 2^31 bytes.  Any spatial kernel size,
+ *   stride, dilation and padding runs: 3x3 "same" and 1x1 convs with unit
+ *   spatial stride and dilation on the halo-staged kernels, the others on
+ *   the gather kernel "bf16_gen_n32_p8x32".
  *   CC3D_ERR_INVALID_ARG for a NULL pointer, a size < 1 (t_cache < 0), an
  *   unknown dtype, or an empty output (T_o, H_o or W_o < 1).
  */
@@ -165,6 +167,11 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *                              (default for the RGB head)
  *   "bf16_s1_n192_p8x32"      1x1, C_out % 192 == 0, C_in % 32 == 0
  *   "bf16_s1_n32_p8x32"       1x1, any C_out
+ *   (the variants above need unit spatial stride and dilation and "same"
+ *   padding)
+ *   "bf16_gen_n32_p8x32"      any spatial parameters (default outside that
+ *                              envelope): input pixels gathered per spatial
+ *                              tap, W read as it is from a workspace copy
  *   "f32_direct"              fp32
  * Every variant computes the same operation; bf16 results of different
  * variants may differ in the last bit (fp32 accumulation order).
