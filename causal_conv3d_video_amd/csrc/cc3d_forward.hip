@@ -1319,14 +1319,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // copy of W in the workspace ([C_out][k_t][k_h][k_w][C_in] as it is).  No
 // halo is shared between spatial taps, so the input is read k_h * k_w times
 // from L2: the kernel covers the shapes the halo-staged ones do not.
-// Tile: 8 x 32 output pixels x 32 output channels; wave w owns rows 2w and
-// 2w + 1 (two 32 x 32 accumulators); double-buffered stages.
+// Tile: 8 x 32 output pixels x 64 output channels; wave w owns rows 2w and
+// 2w + 1 (four 32 x 32 accumulators).
 __global__ __launch_bounds__(256) void conv_bf16_gen(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int TH = 8, TW = 32, BN = 32, NT = 256, PPX = 4;  // 16-byte pieces per pixel: 32 channels
-  constexpr int ASL = TH * TW * PPX, BSL = BN * PPX;           // LDS slots per stage
-  __shared__ uint4 al[2 * ASL];
-  __shared__ uint4 bl[2 * BSL];
+  constexpr int TH = 8, TW = 32, BN = 64, CW = BN / 32, NT = 256, PPX = 4;  // pieces per pixel: 32 channels
+  constexpr int ASL = TH * TW * PPX, BSL = BN * PPX;                          // LDS slots per stage
+  constexpr int NB = 3;                                                       // stage buffers (ring)
+  __shared__ uint4 al[NB * ASL];
+  __shared__ uint4 bl[NB * BSL];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
@@ -1399,6 +1400,7 @@ __global__ __launch_bounds__(256) void conv_bf16_gen(ConvArgs a) {
           r_z, (__attribute__((address_space(3))) void*)(al + buf * ASL + it * NT + wave * 64), 16,
           in ? ((iy * a.wd + ix) * a.cin + ch) * 2 : OOB, 0, 0, 0);
     }
+    static_assert(BSL <= NT, "one weight piece per thread");
     if (wave < BSL / 64) {
       const int co = tid >> 2, q = (tid & 3) ^ (co & 3), ch = cc * 32 + q * 8;
       const bool in = n0 + co < a.cout && ch < a.cin;
@@ -1413,37 +1415,51 @@ __global__ __launch_bounds__(256) void conv_bf16_gen(ConvArgs a) {
     asm volatile("" ::: "memory");
   };
 
-  f32x16_t acc[2];
+  // Ring of three stage buffers, one barrier per stage: stage st + 2 is
+  // issued after the barrier of stage st, when every wave has finished
+  // stage st - 1, the last reader of its buffer.
+  f32x16_t acc[CW][2];
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int cb = 0; cb < CW; ++cb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[r][v] = 0.f;
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[cb][r][v] = 0.f;
   if (nst > 0) issue(0, 0);
+  if (nst > 1) issue(1, 1);
   for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
+    const int buf = st % NB;
+    // stage st has landed once only stage st + 1's loads are in flight
     if (st + 1 < nst) {
-      issue(st + 1, buf ^ 1);
-      // stage st has landed once only stage st + 1's loads are in flight
       if (wave < BSL / 64) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ASL / NT + 1) : "memory");
       else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ASL / NT) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     barrier();
+    if (st + 2 < nst) issue(st + 2, (st + 2) % NB);
     const uint4* ab = al + buf * ASL;
     const uint4* bb = bl + buf * BSL;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int q = kk * 2 + g;  // 8-channel piece of this lane's k range
-      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, bb[l32 * 4 + (q ^ (l32 & 3))]);
+      bf16x8_t wf[CW], pf[2];
+#pragma unroll
+      for (int cb = 0; cb < CW; ++cb) {
+        const int co = cb * 32 + l32;
+        wf[cb] = __builtin_bit_cast(bf16x8_t, bb[co * 4 + (q ^ (co & 3))]);
+      }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int px = (wave * 2 + r) * 32 + l32;
-        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, ab[px * 4 + (q ^ (px & 3))]);
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, pf, acc[r], 0, 0, 0);
+        pf[r] = __builtin_bit_cast(bf16x8_t, ab[px * 4 + (q ^ (px & 3))]);
       }
+#pragma unroll
+      for (int cb = 0; cb < CW; ++cb)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          acc[cb][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb], pf[r], acc[cb][r], 0, 0, 0);
     }
-    barrier();  // before stage st + 2 overwrites this buffer
   }
 
   // epilogue: bias once in fp32, round to nearest even, channels-last stores
@@ -1454,10 +1470,12 @@ __global__ __launch_bounds__(256) void conv_bf16_gen(ConvArgs a) {
     if (oy >= a.ho || ox >= a.wo) continue;
     unsigned short* op = os + (((int64_t(nn) * a.to + o) * a.ho + oy) * a.wo + ox) * a.cout;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int co = n0 + (v >> 2) * 8 + g * 4 + (v & 3);
-      if (co < a.cout) op[co] = f32_to_bf16(acc[r][v] + (a.has_bias ? bf16_to_f32(bs[co]) : 0.f));
-    }
+    for (int cb = 0; cb < CW; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int co = n0 + cb * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (co < a.cout) op[co] = f32_to_bf16(acc[cb][r][v] + (a.has_bias ? bf16_to_f32(bs[co]) : 0.f));
+      }
   }
 #endif
 }
@@ -1855,7 +1873,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     case CC3D_K_BF16_S3_N96_G32W8:
       e = launch_g32<96, 16, 8>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
       break;
-    case CC3D_K_BF16_GEN_N32: e = launch_gen(a, in.tiles, pack, runs, s); break;
+    case CC3D_K_BF16_GEN_N64: e = launch_gen(a, in.tiles, pack, runs, s); break;
     case CC3D_K_BF16_S3_FEW:
       switch (d.c_out) {
         case 1: e = launch_few_cin<1>(a, in.tiles, cus, pack, runs, s); break;

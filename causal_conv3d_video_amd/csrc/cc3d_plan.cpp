@@ -49,8 +49,8 @@ bool same_spatial(const cc3d_desc_t& d) {
 
 bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   const std::string n(name);
-  if (n == "bf16_gen_n32_p8x32") {  // any spatial parameters
-    *v = {CC3D_K_BF16_GEN_N32, 8, 32, 32, 32, "bf16_gen_n32_p8x32"};
+  if (n == "bf16_gen_n64_p8x32") {  // any spatial parameters
+    *v = {CC3D_K_BF16_GEN_N64, 8, 32, 64, 32, "bf16_gen_n64_p8x32"};
     return true;
   }
   if (!same_spatial(d)) return false;
@@ -91,7 +91,7 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
 // small ones keep two smaller workgroups per compute unit so that every
 // unit gets tiles.  causal_conv3d_plan_autotune times the alternatives.
 const char* default_variant(const cc3d_desc_t& d) {
-  if (!same_spatial(d)) return "bf16_gen_n32_p8x32";
+  if (!same_spatial(d)) return "bf16_gen_n64_p8x32";
   if (d.k_h == 3) {
     if (d.c_out % 96 == 0) {
       const int64_t big_tiles = int64_t(d.n) * ((d.h + 15) / 16) * ((d.w + 31) / 32) * (d.c_out / 96) *
@@ -223,7 +223,7 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     const int64_t slots = (int64_t(v.block_n) * ks * ks * (v.cin_chunk / 8) + 255) / 256 * 256;
     p->wpk_bytes = int64_t(d.k_t) * (d.c_in / v.cin_chunk) * p->nblk_n * slots * 16;
     if (v.id == CC3D_K_BF16_S3_FEW) p->wpk_bytes = int64_t(d.c_in / 32) * 9 * 64 * 16;  // register fragments
-    if (v.id == CC3D_K_BF16_GEN_N32) p->wpk_bytes = w_bytes;  // a copy of W, read as it is
+    if (v.id == CC3D_K_BF16_GEN_N64) p->wpk_bytes = w_bytes;  // a copy of W, read as it is
     p->sched_off = (p->wpk_bytes + 255) / 256 * 256;
     in.workspace_bytes = p->sched_off + int64_t(kSchedSlots) * kSchedInts * 4;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);

@@ -149,7 +149,7 @@ typedef struct cc3d_counters {
  *   output) or the weights reaching 2^31 bytes.  Any spatial kernel size,
  *   stride, dilation and padding runs: 3x3 "same" and 1x1 convs with unit
  *   spatial stride and dilation on the halo-staged kernels, the others on
- *   the gather kernel "bf16_gen_n32_p8x32".
+ *   the gather kernel "bf16_gen_n64_p8x32".
  *   CC3D_ERR_INVALID_ARG for a NULL pointer, a size < 1 (t_cache < 0), an
  *   unknown dtype, or an empty output (T_o, H_o or W_o < 1).
  */
@@ -169,7 +169,7 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *   "bf16_s1_n32_p8x32"       1x1, any C_out
  *   (the variants above need unit spatial stride and dilation and "same"
  *   padding)
- *   "bf16_gen_n32_p8x32"      any spatial parameters (default outside that
+ *   "bf16_gen_n64_p8x32"      any spatial parameters (default outside that
  *                              envelope): input pixels gathered per spatial
  *                              tap, W read as it is from a workspace copy
  *   "f32_direct"              fp32

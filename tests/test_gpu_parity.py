@@ -582,7 +582,7 @@ def test_general_spatial_parameters_full_compare(cuda_device, case):
                                    has_bias=bias)
     y, co, plan = run(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, st=st, sst=sst, sdil=sdil)
     torch.cuda.synchronize()
-    assert plan.info["kernel_name"] == "bf16_gen_n32_p8x32"
+    assert plan.info["kernel_name"] == "bf16_gen_n64_p8x32"
     ref = _oracle(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, st=st, sst=sst, sdil=sdil)
     assert_bf16_close(y, ref, "general %s" % (case,))
     z = x if c is None else torch.cat([c, x], 1)
@@ -596,7 +596,7 @@ def test_gather_kernel_on_same_convs_full_compare(cuda_device, case):
     cin, cout, h, w_, tx, tc, k, dt, p_base, n, bias = case
     x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV, seed=synth.SEED_BASE + 390 + h,
                                    has_bias=bias)
-    y, _, plan = run(x, c, w, b, k=k, dt=dt, p_base=p_base, variant="bf16_gen_n32_p8x32")
+    y, _, plan = run(x, c, w, b, k=k, dt=dt, p_base=p_base, variant="bf16_gen_n64_p8x32")
     torch.cuda.synchronize()
     assert_bf16_close(y, _oracle(x, c, w, b, k=k, dt=dt, p_base=p_base), "gather kernel")
 
@@ -608,7 +608,7 @@ def test_general_spatial_full_size_sampled(cuda_device, sig):
                                    seed=synth.SEED_BASE + 395)
     y, _, plan = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"])
     torch.cuda.synchronize()
-    assert plan.info["kernel_name"] == "bf16_gen_n32_p8x32"
+    assert plan.info["kernel_name"] == "bf16_gen_n64_p8x32"
     assert bool(torch.isfinite(y).all())
     pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=39)
     ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"], points=pts)

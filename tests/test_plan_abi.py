@@ -196,7 +196,7 @@ def test_general_spatial_parameters_take_the_gather_kernel(kw):
     1x1, stride and dilation 1) run on the general-spatial kernel, which
     reads W as it is (its workspace holds a copy of W)."""
     p = cc3d.causal_conv3d_plan(_desc(c_in=32, c_out=40, h=20, w=36, **kw))
-    assert p.info["kernel_name"] == "bf16_gen_n32_p8x32" and p.info["block_m"] == 256 and p.info["block_n"] == 32
+    assert p.info["kernel_name"] == "bf16_gen_n64_p8x32" and p.info["block_m"] == 256 and p.info["block_n"] == 64
     k = kw.get("k", (3, 3, 3))
     assert p.info["workspace_bytes"] >= 40 * k[0] * k[1] * k[2] * 32 * 2
     for name in ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32", "bf16_s1_n32_p8x32"]:
