@@ -1075,7 +1075,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
 // within each 16-lane row (DPP row_shr) moves slot k to slot k+1 for the next
 // frame.  Weights stay in registers for the whole kernel.
 template <int COUT, int NCH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv_bf16_few(ConvArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_bf16_few(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int TH = 16, TW = 32, HP = TH + 2, WP = TW + 2, PZ = 4;
   constexpr int ZCH = HP * WP * PZ;
@@ -1084,7 +1084,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int RW = 8;                     // output rows per wave (waves: 2 x 2 over the patch)
   constexpr int NCOL = 3 * COUT;            // used accumulator columns
   static_assert(NCOL <= 16 && NCH >= 1 && NCH <= 3, "few-channel kernel shape");
-  __shared__ uint4 zl[2 * ZSLOTS];
+  // A ring of four halo buffers: three stages in flight while one is
+  // multiplied (the kernel is bound by reading the input; one workgroup per
+  // compute unit holds ~117 KB of loads in flight).
+  constexpr int NBUF = 4;
+  static_assert(NBUF * ZSLOTS * 16 <= 160 * 1024, "LDS budget");
+  __shared__ uint4 zl[NBUF * ZSLOTS];
+  constexpr auto zcnt = [](int w) {  // halo load instructions of wave w per stage
+    int n = 0;
+    for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
+    return n;
+  };
+  static_assert((NBUF - 2) * zcnt(0) <= 63, "vmcnt range");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1268,13 +1279,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
   };
 
-  // load cursor: one stage ahead, across patch boundaries
+  // Load cursor: the next stage to issue, NBUF - 1 stages ahead of the one
+  // multiplied, across patch boundaries.  Stage i goes to buffer i % NBUF.
   int ltile = ctile, lst = 0;
   Patch lp = decode(ltile);
   halo_offsets(lp);
-  issue_stage(lp, 0, 0);
+  int issued = 0;
+  auto issue_next = [&]() {
+    issue_stage(lp, lst, issued % NBUF);
+    ++issued;
+    if (++lst == nst) {
+      lst = 0;
+      ltile = next_tile(ltile);
+      if (ltile >= 0) {
+        lp = decode(ltile);
+        halo_offsets(lp);
+      }
+    }
+  };
+  // wait for stage pos: with NBUF - 2 later stages in flight, all but their
+  // loads (loads complete in order; the output stores only add to the count)
+  auto wait_stage = [&](int ahead) {
+    if (ahead < NBUF - 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return;
+    }
+    switch (wave) {
+      case 0: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(0)) : "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(1)) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(2)) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(3)) : "memory"); break;
+    }
+  };
+  for (int i = 0; i < NBUF - 1 && ltile >= 0; ++i) issue_next();
   int pos = 0;
-  Patch cp = lp;
+  Patch cp = decode(ctile);
   emit_offsets(cp);
   for (;;) {
 #pragma unroll
@@ -1284,19 +1323,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int zi = 0; zi < a.tz - z_lo; ++zi) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch, ++pos) {
-        // next stage (possibly the next patch's first) into the other buffer
-        if (++lst == nst) {
-          lst = 0;
-          ltile = next_tile(ltile);
-          if (ltile >= 0) {
-            lp = decode(ltile);
-            halo_offsets(lp);
-          }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        barrier();  // stage pos has landed everywhere; buffer (pos+1)%2 is free
-        if (ltile >= 0) issue_stage(lp, lst, (pos + 1) & 1);
-        compute(zl + (pos & 1) * ZSLOTS, wreg[ch]);
+        wait_stage(issued - pos - 1);
+        barrier();  // stage pos has landed everywhere; buffer (pos - 1) % NBUF is free
+        if (ltile >= 0) issue_next();
+        compute(zl + (pos % NBUF) * ZSLOTS, wreg[ch]);
       }
       emit(cp, z_lo + zi + p_l - 2);
       rotate();
