@@ -880,9 +880,11 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     return (a.has_bias && tid < BN && c.n0 + tid < a.cout) ? bs[c.n0 + tid] : (unsigned short)0;
   };
 
-  // Load cursor: the group after the one being computed.  It enters the next
-  // tile during the current tile's last group, when that tile (tnext) is
-  // already known.  zoff holds the halo offsets of its tile.
+  // Load cursor: the group after the one being computed; it moves on at the
+  // end of each group, after the barrier that publishes a claimed tile.  Its
+  // tile is the current one or the next (tnext); the tile after that is the
+  // one claimed during the current tile's first group (tnn), which a tile of
+  // a single group already needs.  zoff holds the halo offsets of its tile.
   Grp nx{ctile, 0, 0};
   Tile nt{};
   bool nx_ok = ctile >= 0;
@@ -895,7 +897,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
       nx.ti = 0;
       if (++nx.gz == ngrp) {
         nx.gz = 0;
-        nx.t = tnext;
+        nx.t = nx.t == ctile ? tnext : tnn;
         if (nx.t < 0) {
           nx_ok = false;
           return;
@@ -1007,10 +1009,10 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
           }
           claim_lds = t;
         }
-        if (more) nx_advance();
         vm_drain();
         barrier();
         if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
+        if (more) nx_advance();
         hpar ^= 1;
       }
       // (the output stores may stay in flight across this barrier)

@@ -613,3 +613,15 @@ def test_general_spatial_full_size_sampled(cuda_device, sig):
     pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=39)
     ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"], points=pts)
     assert_bf16_close(gather(y, pts), ref, s["name"])
+
+
+def test_group_staged_schedule_with_single_group_tiles(cuda_device):
+    """Tiles of a single group (C_in = 32, one active tap: the first chunk of
+    a stream with no cache) with about three tiles per workgroup: the load
+    cursor steps past a whole tile within one group, to a tile claimed in
+    that same group."""
+    x, _, w, b = synth.conv_inputs(1, 32, 96, 512, 800, 1, 0, device=DEV, seed=synth.SEED_BASE + 96)
+    y, _, plan = run(x, None, w, b, variant="bf16_s3_n96_p16x32_g32")
+    torch.cuda.synchronize()
+    assert plan.info["tiles"] == 800 and plan.info["taps"][2]["active"] and not plan.info["taps"][0]["active"]
+    assert_bf16_close(y, _oracle(x, None, w, b), "single-group tiles")
