@@ -405,3 +405,18 @@ def test_plan_variant_refuses_null_name():
     h = ctypes.c_void_p(1)
     assert lib.causal_conv3d_plan_variant(ctypes.addressof(d), None, ctypes.byref(h)) == cc3d.CC3D_ERR_INVALID_ARG
     assert h.value is None
+
+
+def test_size_limits_of_the_32_bit_buffer_offsets():
+    """The bf16 kernels address one frame and the weights with 32-bit byte
+    offsets: a frame (input or output) or the weights reaching 2^31 bytes is
+    refused as unsupported; just below, the call plans."""
+    ok = cc3d.causal_conv3d_plan(_desc(c_in=112, c_out=112, h=2048, w=4096, t_x=1, t_cache=2))
+    assert 2048 * 4096 * 112 * 2 < 2 ** 31 and ok.info["kernel_name"].startswith("bf16_")
+    for kw in [dict(c_in=128, c_out=16, h=2048, w=4096),                  # input frame = 2^31 bytes
+               dict(c_in=16, c_out=128, h=2048, w=4096),                  # output frame = 2^31 bytes
+               dict(c_in=8192, c_out=4864, h=8, w=8, k=(3, 3, 3))]:      # weights >= 2^31 bytes
+        with pytest.raises(cc3d.CC3DError) as e:
+            cc3d.causal_conv3d_plan(_desc(t_x=1, t_cache=2, **kw))
+        assert e.value.status == cc3d.CC3D_ERR_UNSUPPORTED, kw
+    assert 8192 * 4864 * 27 * 2 >= 2 ** 31
