@@ -625,3 +625,41 @@ def test_group_staged_schedule_with_single_group_tiles(cuda_device):
     torch.cuda.synchronize()
     assert plan.info["tiles"] == 800 and plan.info["taps"][2]["active"] and not plan.info["taps"][0]["active"]
     assert_bf16_close(y, _oracle(x, None, w, b), "single-group tiles")
+
+
+@pytest.mark.parametrize("variant", ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2"])
+def test_graph_replays_match_eager(cuda_device, variant):
+    """The packed-weights forward (with its cache-out copy) captured in a HIP
+    graph: the group-staged kernel's tile counters are cleared by the kernel
+    itself (no memset nodes), and every replay reuses the captured counter
+    slot.  Several replays, each into a NaN-poisoned output with eager work
+    and synchronisations between them, all equal the eager call bitwise."""
+    import causal_conv3d_video_amd as cc3d
+    x, c, w, b = synth.conv_inputs(1, 32, 96, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 97)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant=variant)
+    cc3d.causal_conv3d_pack_weights(plan, w)
+    ref = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=DEV)
+    cc3d.causal_conv3d_forward_packed(plan, x, c, b, ref, None)
+    out = torch.empty_like(ref)
+    co = torch.empty(plan.shapes()["cache_out"], dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, co)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, co)
+    other = torch.empty_like(ref)
+    for i in range(5):
+        out.fill_(float("nan"))
+        co.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d" % i
+        assert torch.equal(co, x[:, -2:]), "replay %d cache" % i
+        cc3d.causal_conv3d_forward_packed(plan, x, c, b, other, None)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref)
