@@ -663,3 +663,23 @@ def test_graph_replays_match_eager(cuda_device, variant):
         cc3d.causal_conv3d_forward_packed(plan, x, c, b, other, None)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(other, ref)
+
+
+def test_packed_forwards_of_one_plan_overlap_on_two_streams(cuda_device):
+    """Launches of one plan on two streams may run at the same time: each
+    takes its own slot of the group-staged kernel's tile counters.  Twelve
+    interleaved launches, no synchronisation between them; every output is
+    the eager one bitwise."""
+    import causal_conv3d_video_amd as cc3d
+    x, c, w, b = synth.conv_inputs(1, 32, 96, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 98)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant="bf16_s3_n96_p16x32_g32")
+    cc3d.causal_conv3d_pack_weights(plan, w)
+    ref = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=DEV)
+    cc3d.causal_conv3d_forward_packed(plan, x, c, b, ref, None)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full_like(ref, float("nan")) for _ in range(12)]
+    for i, o in enumerate(outs):
+        cc3d.causal_conv3d_forward_packed(plan, x, c, b, o, None, stream=streams[i % 2])
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, ref) for o in outs)
