@@ -358,11 +358,25 @@ def main():
         print(json.dumps({"copy_bytes": src.numel() * 2, "launches": args.kernel_launches}))
         return
     if args.only:
-        wk = next(w for w in work if w["sig"]["name"] == args.only)
-        plan = wk["plans"][2]
-        cin_buf = wk["caches"][1][:, :plan.desc.t_cache]
-        cin_buf.copy_(torch.cat(wk["xs"][:2], 1)[:, -plan.desc.t_cache:])  # chunk 2's carried frames
-        cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
+        wk = next((w for w in work if w["sig"]["name"] == args.only), None)
+        if wk is not None:
+            plan = wk["plans"][2]
+            cin_buf = wk["caches"][1][:, :plan.desc.t_cache]
+            cin_buf.copy_(torch.cat(wk["xs"][:2], 1)[:, -plan.desc.t_cache:])  # chunk 2's carried frames
+            cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
+        else:  # a single-call configuration (2 cached frames)
+            import synth
+            s = next(v for v in synth.SINGLE_CALLS + synth.ENCODER_DOWNSAMPLE + synth.GENERAL_SPATIAL
+                     if v["name"] == args.only)
+            x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
+                                           device=device, seed=synth.SEED_BASE + 200)
+            plan = cc3d.causal_conv3d_plan(cc3d.make_desc(
+                1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], k=s["k"], stride=(s["st"],) + s["sst"],
+                dilation=(s["dt"],) + s["sdil"], padding=s["pad"], p_base=s["p_base"]))
+            out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
+            wk = {"xs": [None, None, x], "b": b, "outs": [None, None, out]}
+            cin_buf = c
+            cc3d.causal_conv3d_pack_weights(plan, w, stream)
         # untimed launches for at least --warm-seconds, then the counted ones
         # (a profile of this mode takes its statistics over the last
         # --kernel-launches dispatches of the conv kernel)
