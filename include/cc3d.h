@@ -43,16 +43,18 @@
  *
  * Ownership: every tensor is caller-owned device memory.  A bf16 plan also
  * owns one device workspace (workspace_bytes, allocated by its first forward
- * call on the device current then, freed by causal_conv3d_plan_destroy): the
- * weights repacked into the kernel's stage order, rewritten by every forward
- * call before the convolution on the same stream, and 64 slots of tile
- * counters for the group-staged kernel's dynamic schedule (each launch takes
- * the next slot and leaves it zeroed when it completes, so at most 64
- * convolutions of one plan may be in flight at once).  Nothing else is kept.
- * Threading: a plan's shape data is immutable and any thread may call
- * forward; because the workspace is rewritten per call, forward calls that
- * share one plan must be ordered on one stream (use one plan per stream for
- * concurrent streams).  Counters are atomic.
+ * or pack call on the device current then, freed by
+ * causal_conv3d_plan_destroy): the weights repacked into the kernel's stage
+ * order (for the gather kernel a plain copy of W), rewritten by every
+ * causal_conv3d_forward before the convolution on the same stream, and 64
+ * slots of tile counters for the group-staged kernel's dynamic schedule
+ * (each launch takes the next slot and leaves it zeroed when it completes).
+ * Nothing else is kept.
+ * Threading: a plan's shape data is immutable and any thread may call it.
+ * causal_conv3d_forward rewrites the workspace, so those calls on one plan
+ * must be ordered on one stream (use one plan per stream for concurrent
+ * streams).  causal_conv3d_forward_packed calls of one plan may overlap on
+ * different streams, at most 64 in flight at once.  Counters are atomic.
  * Errors: every check is synchronous and happens before any launch; a launch
  * failure reported by the runtime returns CC3D_ERR_DEVICE; faults during
  * execution surface at the caller's next synchronisation.  The library never
