@@ -190,7 +190,7 @@ def time_single_calls(device, launches, stream, warm_seconds=0.2):
             frac_mfma_peak=info["flops_active"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
             frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
-        if info["kernel_name"] == "bf16_s3_few_p16x32":
+        if info["kernel_name"].startswith("bf16_s3_few_"):
             # the head with 8-bit pixel output fused (one byte per channel)
             o8 = torch.empty(plan.shapes()["out"], dtype=torch.uint8, device=device)
             for _ in range(3):

@@ -71,8 +71,10 @@ struct ConvArgs {
   int ina_lo[kMaxFrameIv + 1], ina_n[kMaxFrameIv + 1], nina_iv;
   int nat;
   int* sched;
-  // Few-output-channel kernel: write 8-bit pixel codes instead of bf16,
+  // Few-output-channel kernel: output rows per patch (1..16), and 8-bit
+  // pixel codes instead of bf16 output,
   // code = trunc(clamp(fma(y, px_scale, px_offset) * 255, 0, 255)) in fp32.
+  int tile_h;
   int out_u8;
   float px_scale, px_offset;
 };
@@ -1060,37 +1062,52 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
 #endif
 }
 
+// Calls f(std::integral_constant<int, i>) for i = I, I+1, .. N-1, unrolled,
+// while f returns true (each call nested in the previous one's branch).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_while(F&& f) {
+  if constexpr (I < N) {
+    if (f(std::integral_constant<int, I>{})) static_for_while<I + 1, N>(f);
+  }
+}
+
 // bf16 kernel for few output channels (C_out <= 5; the decoder's RGB head):
 // 3x3 spatial taps, k_t = 3, unit temporal dilation, C_in = 32 * NCH.
 //
 // With three output channels a GEMM tile over output channels is almost all
-// padding, and the work is bound by reading the input once.  Each workgroup
-// owns a 16 x 32 output patch and walks the source frames z of Z = [C; X] in
-// time order, loading each frame's halo once (32 channels at a time, 64-byte
-// pixel pieces, through LDS).  One v_mfma_f32_16x16x32_bf16 multiplies 16
-// pixels x 32 channels of frame z by a 32 x 16 weight block whose 16 columns
-// are (temporal tap k, output channel co) pairs, so a single pass over frame z
-// produces its contributions to the three output frames o = z + p_l - k.  The
-// accumulator column for tap slot k holds output frame z + p_l - k: after
-// frame z the slot-2 columns hold a finished output frame, which is written
-// (bias added once, rounded to nearest even), and a lane shift by C_out
-// within each 16-lane row (DPP row_shr) moves slot k to slot k+1 for the next
-// frame.  Weights stay in registers for the whole kernel.
+// padding, and the work is bound by reading the input once.  One
+// v_mfma_f32_16x16x32_bf16 multiplies 16 pixels x 32 channels of source frame
+// z by a 32 x 16 weight block whose 16 columns are (temporal tap k, output
+// channel co) pairs, so a single pass over frame z produces its contributions
+// to the three output frames o = z + p_l - k.  The accumulator column for tap
+// slot k holds output frame z + p_l - k: after frame z the slot-2 columns hold
+// a finished output frame, which is written (bias added once, rounded to
+// nearest even), and a lane shift by C_out within each 16-lane row (DPP
+// row_shr) moves slot k to slot k+1 for the next frame.  Weights stay in
+// registers for the whole kernel.
+//
+// Each workgroup owns a patch of a.tile_h (<= 16) output rows by 128 columns
+// (eight waves of 16 columns each) and walks the source frames of Z = [C; X]
+// in time order.  A stage is one halo row of one frame: 130 pixels with all
+// C_in channels, a single contiguous run of the channels-last input, copied
+// to LDS in memory order (so every load instruction reads 1 KB of
+// consecutive bytes, and each cache line is used whole by one stage).  Halo
+// row hr feeds output rows hr - kh for the three row taps kh; the
+// accumulators of every output row of the patch stay in registers while the
+// frame's halo rows stream through.
 template <int COUT, int NCH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_bf16_few(ConvArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv_bf16_few(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int TH = 16, TW = 32, HP = TH + 2, WP = TW + 2, PZ = 4;
-  constexpr int ZCH = HP * WP * PZ;
-  constexpr int ZSLOTS = (ZCH + 63) / 64 * 64;
-  constexpr int NT = 256, ZIT = (ZSLOTS + NT - 1) / NT;
-  constexpr int RW = 8;                     // output rows per wave (waves: 2 x 2 over the patch)
-  constexpr int NCOL = 3 * COUT;            // used accumulator columns
-  static_assert(NCOL <= 16 && NCH >= 1 && NCH <= 3, "few-channel kernel shape");
-  // A ring of four halo buffers: three stages in flight while one is
-  // multiplied (the kernel is bound by reading the input; one workgroup per
-  // compute unit holds ~117 KB of loads in flight).
-  constexpr int NBUF = 4;
-  static_assert(NBUF * ZSLOTS * 16 <= 160 * 1024, "LDS budget");
+  constexpr int TW = 128, WP = TW + 2;       // output columns, halo columns
+  constexpr int PP = 4 * NCH;                // 16-byte pieces per pixel
+  constexpr int THMAX = 16;                  // accumulator rows
+  constexpr int ZSLOTS = (WP * PP + 63) / 64 * 64;
+  constexpr int NT = 512, ZIT = (ZSLOTS + NT - 1) / NT;
+  static_assert(3 * COUT <= 16 && NCH >= 1 && NCH <= 3, "few-channel kernel shape");
+  // A ring of halo-row buffers, as many as LDS holds (up to eight): all but
+  // one in flight while one is multiplied.
+  constexpr int NBUF = std::min(8, int(160 * 1024 / (ZSLOTS * 16)));
+  static_assert(NBUF >= 4 && NBUF * ZSLOTS * 16 <= 160 * 1024, "LDS budget");
   __shared__ uint4 zl[NBUF * ZSLOTS];
   constexpr auto zcnt = [](int w) {  // halo load instructions of wave w per stage
     int n = 0;
@@ -1098,13 +1115,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return n;
   };
   static_assert((NBUF - 2) * zcnt(0) <= 63, "vmcnt range");
+  static_assert(zcnt(1) == zcnt(7), "waves 1-7 issue alike");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
   const int m = lane & 15, q = lane >> 4;   // A operand: pixel m, 8-channel piece q; D: column m
+  const int th = a.tile_h, hrows = th + 2;  // output rows per patch, halo rows per frame
 
-  // persistent schedule over spatial patches, one contiguous range per XCD
+  // persistent schedule over patches, one contiguous range per XCD
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int nblk_here = (int(gridDim.x) >> 3) + (xcd < int(gridDim.x & 7) ? 1 : 0);
   const int tq = a.ntiles >> 3, tr = a.ntiles & 7;
@@ -1115,12 +1133,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto next_tile = [&](int t) { return t + nblk_here < t_end ? t + nblk_here : -1; };
 
   const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
-  const int frame_bytes = int(frame_el * 2);
+  const int row_el = a.wd * a.cin, row_bytes = row_el * 2;
   const unsigned short* __restrict__ xs = static_cast<const unsigned short*>(a.x);
   const unsigned short* __restrict__ cs = static_cast<const unsigned short*>(a.cache);
   const int p_l = -a.delta[0];              // delta_0 = -p_l
   const int z_lo = max(0, -p_l);            // first source frame any output reads
-  const int nst = (a.tz - z_lo) * NCH;      // stages per patch: (frame, 32-channel chunk)
 
   // weights: B fragments [chunk][spatial tap], prepacked by the launcher
   bf16x8_t wreg[NCH][9];
@@ -1149,33 +1166,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     Patch p;
     p.x0 = (t % a.tiles_x) * TW;
     t /= a.tiles_x;
-    p.y0 = (t % a.tiles_y) * TH;
+    p.y0 = (t % a.tiles_y) * th;
     p.nn = t / a.tiles_y;
     return p;
   };
+  // LDS slot of (halo pixel px, piece j) in a halo-row buffer: memory order,
+  // with the 8-channel piece within each 32-channel chunk XOR-swizzled by
+  // pixel so that 16 consecutive pixels at one piece hit 16 distinct 16-byte
+  // bank groups (a pixel is PP slots, a multiple of 4).
   constexpr int OOB = int(0x80000000u);
   int zoff[ZIT];
   auto halo_offsets = [&](const Patch& c) {
 #pragma unroll
     for (int it = 0; it < ZIT; ++it) {
-      const int id = tid + NT * it;
+      const int s = tid + NT * it;
       int off = OOB;
-      if (id < ZCH) {
-        const int pix = id / PZ;
-        const int qq = (id % PZ) ^ swz<PZ>(pix % WP);
-        const int y = c.y0 - 1 + pix / WP, x = c.x0 - 1 + pix % WP;
-        if (y >= 0 && y < a.h && x >= 0 && x < a.wd) off = ((y * a.wd + x) * a.cin + qq * 8) * 2;
+      if (s < WP * PP) {
+        const int px = s / PP, j = s % PP;
+        const int x = c.x0 - 1 + px;
+        if (x >= 0 && x < a.wd) off = (x * a.cin + ((j & ~3) | ((j & 3) ^ swz<4>(px))) * 8) * 2;
       }
       zoff[it] = off;
     }
   };
-  auto issue_stage = [&](const Patch& c, int st, int buf) {
-    const int z = z_lo + st / NCH, ch = st % NCH;
-    const unsigned short* fp = static_cast<const unsigned short*>(
-        uniform((z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
-                          : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el) + ch * 32));
+  auto frame_ptr = [&](const Patch& c, int z) {
+    return static_cast<const unsigned short*>(uniform(z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
+                                                               : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el));
+  };
+  // halo row y of the frame at fp into buffer buf
+  auto issue_stage = [&](const unsigned short* fp, int y, int buf) {
+    const bool yin = y >= 0 && y < a.h;
+    // a halo row outside the map reads as zeros: an empty buffer range
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(fp + (yin ? y : 0) * row_el)), 0,
+                                          __builtin_amdgcn_readfirstlane(yin ? row_bytes : 0), 0x00020000);
 #pragma unroll
     for (int it = 0; it < ZIT; ++it)
       if (ZSLOTS % NT == 0 || it * NT + wave * 64 < ZSLOTS)
@@ -1188,39 +1212,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     asm volatile("" ::: "memory");
   };
 
-  f32x4_t acc[RW];
-  // one stage: the 9 spatial taps of one 32-channel chunk.  Input row r of
-  // the wave's halo window, shifted by column tap c, feeds output rows r - ta
-  // for ta = 0..2; the 3 x (RW+2) operand reads are consumed in order from a
-  // ring of four registers, three reads ahead of their MFMAs.
-  constexpr int NRD = 3 * (RW + 2), AHEAD = 3;
-  // the swizzle depends on the column in the halo row only, so every row of
-  // one column tap is one per-lane slot plus a constant
+  f32x4_t acc[THMAX];
+  // the A operand of column tap c for this lane: halo pixel wave*16 + m + c,
+  // piece q of a chunk (plus 4 * chunk slots)
   int lane_slot[3];
 #pragma unroll
   for (int c = 0; c < 3; ++c) {
-    const int col = wc * 16 + m + c;
-    lane_slot[c] = (wr * RW * WP + col) * PZ + (q ^ swz<PZ>(col));
+    const int px = wave * 16 + m + c;
+    lane_slot[c] = px * PP + (q ^ swz<4>(px));
   }
-  auto read_a = [&](const uint4* zb, int idx) {
-    const int c = idx / (RW + 2), r = idx % (RW + 2);
-    return __builtin_bit_cast(bf16x8_t, (zb + lane_slot[c])[r * WP * PZ]);
-  };
-  auto compute = [&](const uint4* zb, const bf16x8_t* wv) {
-    bf16x8_t ring[AHEAD + 1];
+  // one stage: halo row HR of a frame, every chunk and column tap, into
+  // output rows HR - kh.  Rows at or past the patch height (which only the
+  // last two halo rows reach) collect values that are never written.
+  auto compute = [&](const uint4* zb, auto hr_c) {
+    constexpr int HR = decltype(hr_c)::value;
+    bf16x8_t af[2][3];
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) ring[i] = read_a(zb, i);
+    for (int c = 0; c < 3; ++c) af[0][c] = __builtin_bit_cast(bf16x8_t, zb[lane_slot[c]]);
 #pragma unroll
-    for (int idx = 0; idx < NRD; ++idx) {
-      if (idx + AHEAD < NRD) ring[(idx + AHEAD) % (AHEAD + 1)] = read_a(zb, idx + AHEAD);
-      __builtin_amdgcn_sched_barrier(0);
-      const int c = idx / (RW + 2), r = idx % (RW + 2);
+    for (int ch = 0; ch < NCH; ++ch) {
+      if (ch + 1 < NCH)
 #pragma unroll
-      for (int ta = 0; ta < 3; ++ta)
-        if (r - ta >= 0 && r - ta < RW)
-          acc[r - ta] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[idx % (AHEAD + 1)], wv[ta * 3 + c], acc[r - ta], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < 3; ++c) af[(ch + 1) & 1][c] = __builtin_bit_cast(bf16x8_t, zb[lane_slot[c] + (ch + 1) * 4]);
+#pragma unroll
+      for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+          if (HR - kh >= 0 && HR - kh < THMAX)
+            acc[HR - kh] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ch & 1][c], wreg[ch][kh * 3 + c], acc[HR - kh], 0, 0, 0);
     }
   };
   // Write output frame o from the tap-slot-2 columns (bias added once) with
@@ -1236,7 +1256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto emit_offsets = [&](const Patch& c) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int x = c.x0 + wc * 16 + q * 4 + v;
+      const int x = c.x0 + wave * 16 + q * 4 + v;
       eoff[v] = (emits && x < a.wo) ? (x * COUT + emit_co) * esz : OOB;
     }
   };
@@ -1244,34 +1264,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto emit = [&](const Patch& c, int o) {
     if (o < 0 || o >= a.to) return;  // uniform
     unsigned char* of = static_cast<unsigned char*>(a.out) + ((int64_t(c.nn) * a.to + o) * a.ho * int64_t(a.wo) * COUT) * esz;
-    const __amdgpu_buffer_rsrc_t r_out =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(of)), 0, frame_out_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t r_out = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(uniform(of)), 0, __builtin_amdgcn_readfirstlane(frame_out_bytes), 0x00020000);
+    const int rows = __builtin_amdgcn_readfirstlane(min(th, a.ho - c.y0));
+    const int y0 = __builtin_amdgcn_readfirstlane(c.y0);
     if (a.out_u8) {  // uniform
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        const int y = c.y0 + wr * RW + r;
-        if (y >= a.ho) break;  // uniform
+      for (int r = 0; r < THMAX; ++r) {
+        if (r < rows) {  // uniform (a loop exit here would index acc at run time)
+          const int y = y0 + r;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = __builtin_fmaf(acc[r][v] + bias, a.px_scale, a.px_offset) * 255.f;
-          const unsigned code = unsigned(fminf(fmaxf(p, 0.f), 255.f));  // truncates
-          __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, r_out, eoff[v], y * a.wo * COUT, 0);
+          for (int v = 0; v < 4; ++v) {
+            const float p = __builtin_fmaf(acc[r][v] + bias, a.px_scale, a.px_offset) * 255.f;
+            const unsigned code = unsigned(fminf(fmaxf(p, 0.f), 255.f));  // truncates
+            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, r_out, eoff[v], y * a.wo * COUT, 0);
+          }
         }
       }
       return;
     }
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const int y = c.y0 + wr * RW + r;
-      if (y >= a.ho) break;  // uniform
+    for (int r = 0; r < THMAX; ++r) {
+      if (r < rows) {  // uniform
+        const int y = y0 + r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[r][v] + bias), r_out, eoff[v], y * a.wo * COUT * 2, 0);
+        for (int v = 0; v < 4; ++v)
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[r][v] + bias), r_out, eoff[v], y * a.wo * COUT * 2, 0);
+      }
     }
   };
   auto rotate = [&]() {  // tap slot k -> k+1 (columns are lanes within 16-lane rows)
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int r = 0; r < THMAX; ++r)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         // (a vector element is copied to a scalar first: bit-casting the
@@ -1283,20 +1307,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // Load cursor: the next stage to issue, NBUF - 1 stages ahead of the one
   // multiplied, across patch boundaries.  Stage i goes to buffer i % NBUF.
-  int ltile = ctile, lst = 0;
+  int ltile = ctile, lz = z_lo, ly = 0;  // ly: halo row, 0 .. hrows - 1
   Patch lp = decode(ltile);
   halo_offsets(lp);
-  int issued = 0;
+  const unsigned short* lfp = frame_ptr(lp, lz);
+  int issued = 0, ibuf = 0;  // stages issued, and the next one's buffer
   auto issue_next = [&]() {
-    issue_stage(lp, lst, issued % NBUF);
+    issue_stage(lfp, lp.y0 - 1 + ly, ibuf);
     ++issued;
-    if (++lst == nst) {
-      lst = 0;
-      ltile = next_tile(ltile);
-      if (ltile >= 0) {
-        lp = decode(ltile);
-        halo_offsets(lp);
+    ibuf = ibuf + 1 == NBUF ? 0 : ibuf + 1;
+    if (++ly == hrows) {
+      ly = 0;
+      if (++lz == a.tz) {
+        lz = z_lo;
+        ltile = next_tile(ltile);
+        if (ltile >= 0) {
+          lp = decode(ltile);
+          halo_offsets(lp);
+        }
       }
+      if (ltile >= 0) lfp = frame_ptr(lp, lz);
     }
   };
   // wait for stage pos: with NBUF - 2 later stages in flight, all but their
@@ -1306,30 +1336,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       return;
     }
-    switch (wave) {
-      case 0: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(0)) : "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(1)) : "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(2)) : "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(3)) : "memory"); break;
-    }
+    if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(0)) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(1)) : "memory");
   };
   for (int i = 0; i < NBUF - 1 && ltile >= 0; ++i) issue_next();
-  int pos = 0;
+  int pos = 0, cbuf = 0;  // stage multiplied next, and its buffer
   Patch cp = decode(ctile);
   emit_offsets(cp);
   for (;;) {
 #pragma unroll
-    for (int r = 0; r < RW; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < THMAX; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // output frames no tap reaches (p_l > 2) are the bias alone
     for (int o = 0; o < min(a.to, p_l - 2); ++o) emit(cp, o);
     for (int zi = 0; zi < a.tz - z_lo; ++zi) {
-#pragma unroll
-      for (int ch = 0; ch < NCH; ++ch, ++pos) {
+      // halo rows 0 .. hrows - 1 (uniform), nested so that each test runs
+      // only where the previous row was taken
+      static_for_while<0, THMAX + 2>([&](auto hr_c) {
+        if (decltype(hr_c)::value >= hrows) return false;
         wait_stage(issued - pos - 1);
         barrier();  // stage pos has landed everywhere; buffer (pos - 1) % NBUF is free
         if (ltile >= 0) issue_next();
-        compute(zl + (pos % NBUF) * ZSLOTS, wreg[ch]);
-      }
+        compute(zl + cbuf * ZSLOTS, hr_c);
+        ++pos;
+        cbuf = cbuf + 1 == NBUF ? 0 : cbuf + 1;
+        return true;
+      });
       emit(cp, z_lo + zi + p_l - 2);
       rotate();
     }
@@ -1684,7 +1715,7 @@ hipError_t launch_few(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, 
     if (e != hipSuccess) return e;
   }
   if (!conv) return hipSuccess;
-  return launch_persistent<&few_kernel<COUT, NCH>>(a, tiles, cus, 256, s);
+  return launch_persistent<&few_kernel<COUT, NCH>>(a, tiles, cus, 512, s);
 }
 template <int COUT>
 hipError_t launch_few_cin(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
@@ -1849,6 +1880,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   a.st = d.s_t;
   a.tiles_x = plan->tiles_x;
   a.tiles_y = plan->tiles_y;
+  a.tile_h = plan->tile_h;
   a.nblk_n = plan->nblk_n;
   a.ntiles = int(in.tiles);
   a.has_bias = d.has_bias;
@@ -1980,8 +2012,16 @@ extern "C" cc3d_status_t causal_conv3d_forward_u8(cc3d_plan_t plan, const void* 
 extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, const void* x, const void* cache_in,
                                                      const void* w, const void* b, void* out, int launches,
                                                      void* stream, cc3d_plan_t* out_plan, float* best_ms) {
-  static const char* const kCandidates[] = {"bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32",
-                                            "bf16_s3_few_p16x32",     "bf16_s1_n192_p8x32",   "bf16_s1_n32_p8x32"};
+  // (nullptr: the default variant, whose geometry may be none of these)
+  static const char* const kCandidates[] = {nullptr,
+                                            "bf16_s3_n96_p16x32_g32",
+                                            "bf16_s3_n96_p8x32_x2",
+                                            "bf16_s3_n32_p8x32",
+                                            "bf16_s3_few_p16x128",
+                                            "bf16_s3_few_p12x128",
+                                            "bf16_s3_few_p8x128",
+                                            "bf16_s1_n192_p8x32",
+                                            "bf16_s1_n32_p8x32"};
   if (!out_plan) return invalid();
   *out_plan = nullptr;
   if (best_ms) *best_ms = 0.f;
@@ -1999,7 +2039,7 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
   cc3d_status_t st = CC3D_ERR_UNSUPPORTED;
   for (const char* name : kCandidates) {
     cc3d_plan_t p = nullptr;
-    const cc3d_status_t ps = causal_conv3d_plan_variant(desc, name, &p);
+    const cc3d_status_t ps = name ? causal_conv3d_plan_variant(desc, name, &p) : causal_conv3d_plan(desc, &p);
     if (ps == CC3D_ERR_UNSUPPORTED) continue;
     if (ps != CC3D_OK) {
       st = ps;

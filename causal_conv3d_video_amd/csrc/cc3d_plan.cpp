@@ -47,6 +47,35 @@ bool same_spatial(const cc3d_desc_t& d) {
          d.p_h == (d.k_h - 1) / 2 && d.p_w == (d.k_w - 1) / 2;
 }
 
+// The few-output-channel kernel streams halo rows through patches of 4 to
+// 16 output rows by 128 columns.
+constexpr int kFewRowsMin = 4, kFewRowsMax = 16;
+const char* const kFewNames[] = {"bf16_s3_few_p4x128",  "bf16_s3_few_p5x128",  "bf16_s3_few_p6x128",
+                                 "bf16_s3_few_p7x128",  "bf16_s3_few_p8x128",  "bf16_s3_few_p9x128",
+                                 "bf16_s3_few_p10x128", "bf16_s3_few_p11x128", "bf16_s3_few_p12x128",
+                                 "bf16_s3_few_p13x128", "bf16_s3_few_p14x128", "bf16_s3_few_p15x128",
+                                 "bf16_s3_few_p16x128"};
+static_assert(sizeof kFewNames / sizeof kFewNames[0] == kFewRowsMax - kFewRowsMin + 1, "few-kernel names");
+
+// Patch height of the few-output-channel kernel: each compute unit (256 on
+// the target) runs ceil(patches / 256) patches of rows + 2 halo rows per
+// frame; take the height with the fewest halo rows per unit, the tallest on
+// ties (less halo re-read in total).
+int few_rows(const cc3d_desc_t& d) {
+  const int64_t strips = int64_t(d.n) * ((d.w + 127) / 128);
+  int best = kFewRowsMax;
+  int64_t best_cost = -1;
+  for (int r = kFewRowsMax; r >= kFewRowsMin; --r) {
+    const int64_t rounds = (strips * ((d.h + r - 1) / r) + 255) / 256;
+    const int64_t cost = rounds * (r + 2);
+    if (best_cost < 0 || cost < best_cost) {
+      best = r;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   const std::string n(name);
   if (n == "bf16_gen_n64_p8x32") {  // any spatial parameters
@@ -64,10 +93,11 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
     *v = {CC3D_K_BF16_S3_N96_X2, 8, 32, 96, 16, "bf16_s3_n96_p8x32_x2"};
     return s3 && d.c_out % 96 == 0;
   }
-  if (n == "bf16_s3_few_p16x32") {
-    *v = {CC3D_K_BF16_S3_FEW, 16, 32, d.c_out, 32, "bf16_s3_few_p16x32"};
-    return s3 && d.k_t == 3 && d.d_t == 1 && d.s_t == 1 && d.c_out <= 5 && d.c_in % 32 == 0 && d.c_in <= 96;
-  }
+  for (int r = kFewRowsMin; r <= kFewRowsMax; ++r)
+    if (n == kFewNames[r - kFewRowsMin]) {
+      *v = {CC3D_K_BF16_S3_FEW, r, 128, d.c_out, 32, kFewNames[r - kFewRowsMin]};
+      return s3 && d.k_t == 3 && d.d_t == 1 && d.s_t == 1 && d.c_out <= 5 && d.c_in % 32 == 0 && d.c_in <= 96;
+    }
   if (n == "bf16_s3_n32_p8x32") {
     *v = {CC3D_K_BF16_S3_N32, 8, 32, 32, 16, "bf16_s3_n32_p8x32"};
     return s3;
@@ -100,7 +130,7 @@ const char* default_variant(const cc3d_desc_t& d) {
       return "bf16_s3_n96_p8x32_x2";
     }
     if (d.c_out <= 5 && d.k_t == 3 && d.d_t == 1 && d.s_t == 1 && d.c_in % 32 == 0 && d.c_in <= 96)
-      return "bf16_s3_few_p16x32";
+      return kFewNames[few_rows(d) - kFewRowsMin];
     return "bf16_s3_n32_p8x32";
   }
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;

@@ -165,8 +165,10 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *                              (default for large maps)
  *   "bf16_s3_n96_p8x32_x2"    3x3, C_out % 96 == 0
  *   "bf16_s3_n32_p8x32"       3x3, any C_out
- *   "bf16_s3_few_p16x32"      3x3, k_t = 3, d_t = 1, C_out <= 5, C_in in {32, 64, 96}
- *                              (default for the RGB head)
+ *   "bf16_s3_few_p<R>x128"    3x3, k_t = 3, d_t = 1, s_t = 1, C_out <= 5,
+ *                              C_in in {32, 64, 96}; patches of R output rows
+ *                              (4 <= R <= 16) by 128 columns (default for the
+ *                              RGB head, with R chosen for the map size)
  *   "bf16_s1_n192_p8x32"      1x1, C_out % 192 == 0, C_in % 32 == 0
  *   "bf16_s1_n32_p8x32"       1x1, any C_out
  *   (the variants above need unit spatial stride and dilation and "same"
@@ -267,7 +269,7 @@ cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const void* x, cons
  * causal_conv3d_forward_packed); otherwise w is packed first (as
  * causal_conv3d_forward).  cache_out is written as by causal_conv3d_forward.
  * out needs no alignment.  Returns CC3D_ERR_UNSUPPORTED unless the plan runs
- * on the few-output-channel kernel ("bf16_s3_few_p16x32"),
+ * on the few-output-channel kernel ("bf16_s3_few_p<R>x128"),
  * CC3D_ERR_INVALID_ARG for a NaN scale or offset and as
  * causal_conv3d_forward otherwise.
  */

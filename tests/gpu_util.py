@@ -1,5 +1,7 @@
 """Test-side helpers for the GPU parity tests: run the library through its
 binding, and compare against the oracle with the stated tolerances."""
+import re
+
 import numpy as np
 import torch
 
@@ -67,6 +69,13 @@ def assert_f32_close(got, ref, what=""):
     assert m["nonfinite_gpu"] == 0, (what, m)
     assert m["max_abs"] <= F32_ABS_TOL, (what, m)
     return m
+
+
+def tile_of(plan):
+    """(rows, columns) of the plan's output tile, from its kernel name
+    ("..._p<rows>x<cols>..."); (8, 32) for kernels without one."""
+    m = re.search(r"_p(\d+)x(\d+)", plan.info["kernel_name"])
+    return (int(m.group(1)), int(m.group(2))) if m else (8, 32)
 
 
 def sample_points(n, to, ho, wo, count, seed, tile_h=8, tile_w=32):

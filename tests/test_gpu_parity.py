@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 from gpu_util import (assert_bf16_close, assert_f32_close, gather, metrics, plan_for, run,
-                      sample_points)
+                      sample_points, tile_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,7 +123,8 @@ def test_bf16_pinned_variants_full_compare(cuda_device, case, variant):
 
 
 # (C_in, C_out, H, W, T_x, T_cache, p_base, N, bias) on the few-output-channel
-# kernel (frames walked in time order, tap slots rotated across lanes).
+# kernel (frames walked in time order, halo rows streamed, tap slots rotated
+# across lanes).
 FEW_CHANNELS = [
     (96, 3, 20, 70, 4, 2, 2, 1, True),     # the RGB head's channels, ragged patches
     (32, 1, 17, 33, 3, 0, 2, 1, True),     # one output channel, no cache (p_l = 2)
@@ -131,17 +132,23 @@ FEW_CHANNELS = [
     (96, 3, 18, 40, 2, 0, 4, 1, True),     # p_base = 4: two bias-only output frames
     (32, 2, 9, 50, 5, 1, 2, 2, False),     # batch 2, no bias, p_l = 1
     (64, 4, 33, 65, 1, 2, 2, 1, True),     # a single new frame behind a 2-frame cache
+    (96, 3, 37, 300, 2, 2, 2, 1, True),    # three 128-column strips, the last ragged
+    (64, 3, 21, 129, 3, 2, 2, 1, True),    # a second strip of one column
 ]
+# patch heights: the tallest, and an odd short one (several patches per
+# column, rows past the patch height computed and dropped)
+FEW_HEIGHTS = ["bf16_s3_few_p16x128", "bf16_s3_few_p5x128"]
 
 
+@pytest.mark.parametrize("variant", FEW_HEIGHTS)
 @pytest.mark.parametrize("case", FEW_CHANNELS, ids=[str(i) for i in range(len(FEW_CHANNELS))])
-def test_bf16_few_channel_kernel_full_compare(cuda_device, case):
+def test_bf16_few_channel_kernel_full_compare(cuda_device, case, variant):
     cin, cout, h, w_, tx, tc, p_base, n, bias = case
     x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, device=DEV,
                                    seed=synth.SEED_BASE + 400 + FEW_CHANNELS.index(case), has_bias=bias)
-    y, co, plan = run(x, c, w, b, p_base=p_base, variant="bf16_s3_few_p16x32")
+    y, co, plan = run(x, c, w, b, p_base=p_base, variant=variant)
     torch.cuda.synchronize()
-    assert plan.info["kernel_name"] == "bf16_s3_few_p16x32"
+    assert plan.info["kernel_name"] == variant
     ref = _oracle(x, c, w, b, p_base=p_base)
     assert tuple(y.shape) == ref.shape
     assert_bf16_close(y, ref, "few")
@@ -171,8 +178,9 @@ def test_full_size_signatures_sampled(cuda_device, sig):
     # properties over the whole output
     assert bool(torch.isfinite(y).all())
     assert torch.equal(co, x[:, 2:4])
+    th, tw = tile_of(plan)
     pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 600,
-                        seed=synth.SINGLE_CALLS.index(s), tile_h=max(plan.info["block_m"] // 32, 1))
+                        seed=synth.SINGLE_CALLS.index(s), tile_h=th, tile_w=tw)
     ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], points=pts)
     assert_bf16_close(gather(y, pts), ref, s["name"])
 
@@ -248,7 +256,7 @@ def test_autotune_returns_the_fastest_runnable_variant(cuda_device, name):
     desc = cc3d.make_desc(1, s["cin"], s["cout"], 40, 72, s["tx"], s["tc"], k=s["k"], padding=s["pad"],
                           p_base=s["p_base"])
     runnable = []
-    for v in ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32", "bf16_s3_few_p16x32",
+    for v in ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32", "bf16_s3_few_p16x128",
               "bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32"]:
         try:
             cc3d.causal_conv3d_plan_variant(desc, v).close()
@@ -361,7 +369,7 @@ def test_repeated_runs_are_bitwise_identical(cuda_device):
     (16, 192, None),
     (32, 96, "bf16_s3_n96_p16x32_g32"),
     (16, 32, "bf16_s3_n32_p8x32"),
-    (32, 3, "bf16_s3_few_p16x32"),
+    (32, 3, "bf16_s3_few_p16x128"),
 ])
 def test_epilogue_rounds_to_nearest_even(cuda_device, cin, cout, variant):
     """With a single unit source value the fp32 sum is exactly w + b, so the
@@ -442,7 +450,7 @@ def test_head_u8_codes_match_oracle(cuda_device):
     x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], 40, 72, s["tx"], s["tc"], device=DEV,
                                    seed=synth.SEED_BASE + 340)
     plan = plan_for(x, s["tc"], w, k=(3, 3, 3), pad=(1, 1))
-    assert plan.info["kernel_name"] == "bf16_s3_few_p16x32"
+    assert plan.info["kernel_name"].startswith("bf16_s3_few_")
     out = torch.zeros(plan.shapes()["out"], dtype=torch.uint8, device=DEV)
     co = torch.empty(plan.shapes()["cache_out"], dtype=x.dtype, device=DEV)
     cc3d.causal_conv3d_forward_u8(plan, x, c, w, b, out, co)
@@ -470,13 +478,15 @@ def test_head_u8_full_size_sampled(cuda_device):
     out = torch.zeros(plan.shapes()["out"], dtype=torch.uint8, device=DEV)
     cc3d.causal_conv3d_forward_u8(plan, x, c, None, b, out, None)
     torch.cuda.synchronize()
-    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 600, seed=34, tile_h=16)
+    th, tw = tile_of(plan)
+    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 600, seed=34, tile_h=th,
+                        tile_w=tw)
     ref = _oracle(x, c, w, b, points=pts)
     _u8_compare(gather(out, pts), ref, "head u8 full size")
     # bias-only leading frames
     x2, _, w2, b2 = synth.conv_inputs(1, 64, 3, 18, 40, 2, 0, device=DEV, seed=synth.SEED_BASE + 342)
     p2 = plan_for(x2, 0, w2, k=(3, 3, 3), pad=(1, 1), p_base=4)
-    assert p2.info["kernel_name"] == "bf16_s3_few_p16x32" and p2.info["t_out"] == 4
+    assert p2.info["kernel_name"].startswith("bf16_s3_few_") and p2.info["t_out"] == 4
     o2 = torch.zeros(p2.shapes()["out"], dtype=torch.uint8, device=DEV)
     cc3d.causal_conv3d_forward_u8(p2, x2, None, w2, b2, o2, None)
     torch.cuda.synchronize()

@@ -204,11 +204,26 @@ def test_general_spatial_parameters_take_the_gather_kernel(kw):
             cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=96, h=20, w=36, **kw), name)
 
 
+def test_head_patch_height_rule():
+    """The default few-channel patch height: the one (4 .. 16) with the fewest
+    halo rows per compute unit, ceil(patches / 256) * (rows + 2), tallest on
+    ties; checked against brute force over map sizes and batches."""
+    import math
+    for (n, h, w) in [(1, 720, 1280), (1, 480, 848), (1, 360, 640), (2, 180, 320), (1, 40, 72), (1, 1, 1),
+                      (1, 17, 129), (3, 1080, 1920), (1, 256, 4096)]:
+        strips = n * math.ceil(w / 128)
+        cost = {r: math.ceil(strips * math.ceil(h / r) / 256) * (r + 2) for r in range(4, 17)}
+        want = max(r for r in cost if cost[r] == min(cost.values()))
+        p = cc3d.causal_conv3d_plan(_desc(n=n, c_in=96, c_out=3, h=h, w=w, t_x=2, t_cache=2))
+        assert p.info["kernel_name"] == "bf16_s3_few_p%dx128" % want, (n, h, w)
+        assert p.info["tiles"] == strips * math.ceil(h / want) and p.info["block_m"] == want * 128
+
+
 def test_strided_calls_never_take_the_head_kernel():
     d = _desc(c_in=96, c_out=3, h=64, w=64, t_x=4, t_cache=2, stride=(2, 1, 1))
     assert cc3d.causal_conv3d_plan(d).info["kernel_name"] == "bf16_s3_n32_p8x32"
     with pytest.raises(cc3d.CC3DError) as e:
-        cc3d.causal_conv3d_plan_variant(d, "bf16_s3_few_p16x32")
+        cc3d.causal_conv3d_plan_variant(d, "bf16_s3_few_p16x128")
     assert e.value.status == cc3d.CC3D_ERR_UNSUPPORTED
 
 
@@ -327,9 +342,9 @@ def test_default_kernel_choice():
     odd = cc3d.causal_conv3d_plan(_desc(c_in=48, c_out=96, h=360, w=640, t_x=4, t_cache=2))
     assert odd.info["kernel_name"] == "bf16_s3_n96_p8x32_x2"   # C_in % 32 != 0
     head = cc3d.causal_conv3d_plan(_desc(c_in=96, c_out=3, h=720, w=1280, t_x=4, t_cache=2))
-    assert head.info["kernel_name"] == "bf16_s3_few_p16x32"
+    assert head.info["kernel_name"] == "bf16_s3_few_p15x128"
     # one patch walks all output frames: tiles count patches only
-    assert head.info["tiles"] == 45 * 40 and head.info["block_n"] == 3
+    assert head.info["tiles"] == 48 * 10 and head.info["block_n"] == 3
     wide = cc3d.causal_conv3d_plan(_desc(c_in=128, c_out=3, h=64, w=64, t_x=4, t_cache=2))
     assert wide.info["kernel_name"] == "bf16_s3_n32_p8x32"     # C_in > 96
     dil = cc3d.causal_conv3d_plan(_desc(c_in=96, c_out=3, h=64, w=64, t_x=4, t_cache=4, dilation=(2, 1, 1), p_base=4))
@@ -353,7 +368,7 @@ def test_every_decoder_signature_takes_a_bf16_fast_path():
 
 
 VARIANTS_3X3 = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32"]
-VARIANTS_FEW = ["bf16_s3_few_p16x32", "bf16_s3_n32_p8x32"]
+VARIANTS_FEW = ["bf16_s3_few_p4x128", "bf16_s3_few_p11x128", "bf16_s3_few_p16x128", "bf16_s3_n32_p8x32"]
 VARIANTS_1X1 = ["bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32"]
 
 
@@ -385,11 +400,14 @@ def test_plan_variant_pins_the_kernel():
     ("f32_direct", dict(c_in=32, c_out=32)),                  # fp32 kernel on a bf16 call
     ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, dtype=torch.float32)),
     ("no_such_kernel", dict(c_in=32, c_out=32)),
-    ("bf16_s3_few_p16x32", dict(c_in=32, c_out=6)),           # C_out > 5
-    ("bf16_s3_few_p16x32", dict(c_in=128, c_out=3)),          # C_in > 96
-    ("bf16_s3_few_p16x32", dict(c_in=48, c_out=3)),           # C_in % 32 != 0
-    ("bf16_s3_few_p16x32", dict(c_in=32, c_out=3, k=(2, 3, 3), p_base=1)),        # k_t != 3
-    ("bf16_s3_few_p16x32", dict(c_in=32, c_out=3, dilation=(2, 1, 1), p_base=4)),  # d_t != 1
+    ("bf16_s3_few_p16x128", dict(c_in=32, c_out=6)),          # C_out > 5
+    ("bf16_s3_few_p16x128", dict(c_in=128, c_out=3)),         # C_in > 96
+    ("bf16_s3_few_p16x128", dict(c_in=48, c_out=3)),          # C_in % 32 != 0
+    ("bf16_s3_few_p16x128", dict(c_in=32, c_out=3, k=(2, 3, 3), p_base=1)),        # k_t != 3
+    ("bf16_s3_few_p16x128", dict(c_in=32, c_out=3, dilation=(2, 1, 1), p_base=4)),  # d_t != 1
+    ("bf16_s3_few_p3x128", dict(c_in=32, c_out=3)),           # patch heights are 4 .. 16
+    ("bf16_s3_few_p17x128", dict(c_in=32, c_out=3)),
+    ("bf16_s3_few_p16x32", dict(c_in=32, c_out=3)),           # strips are 128 columns
 ])
 def test_plan_variant_refuses_what_it_cannot_run(name, kw):
     with pytest.raises(cc3d.CC3DError) as e:
