@@ -75,6 +75,10 @@ struct ConvArgs {
   // pixel codes instead of bf16 output,
   // code = trunc(clamp(fma(y, px_scale, px_offset) * 255, 0, 255)) in fp32.
   int tile_h;
+  // Few-output-channel kernel: it also writes the cache-out (source frames
+  // co_lo .. tz - 1 into cache_out[n][0 .. tz - co_lo)); co_lo = tz when not.
+  void* cache_out;
+  int co_lo;
   int out_u8;
   float px_scale, px_offset;
 };
@@ -1095,7 +1099,7 @@ __device__ __forceinline__ void static_for_while(F&& f) {
 // row hr feeds output rows hr - kh for the three row taps kh; the
 // accumulators of every output row of the patch stay in registers while the
 // frame's halo rows stream through.
-template <int COUT, int NCH>
+template <int COUT, int NCH, bool CO>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv_bf16_few(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int TW = 128, WP = TW + 2;       // output columns, halo columns
@@ -1114,7 +1118,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
     return n;
   };
-  static_assert((NBUF - 2) * zcnt(0) <= 63, "vmcnt range");
+  constexpr int NCO = CO ? NCH : 0;  // cache-out stores per wave and stage
+  static_assert((NBUF - 2) * (zcnt(0) + NCO) <= 63, "vmcnt range");
   static_assert(zcnt(1) == zcnt(7), "waves 1-7 issue alike");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1260,6 +1265,50 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       eoff[v] = (emits && x < a.wo) ? (x * COUT + emit_co) * esz : OOB;
     }
   };
+  // Cache-out rows.  The last frames of Z (from a.co_lo on) are also the
+  // carry to the next call.  Each stage of such a frame whose halo row is
+  // one of the patch's own rows writes that row's 128 interior pixels from
+  // LDS to cache_out, in memory order, so the carried frames are not read
+  // from HBM a second time.  In the instantiation that writes the cache-out
+  // (CO) every stage issues NCH 16-byte stores per wave (out of range where
+  // there is nothing to write), which keeps the wait counts fixed; the other
+  // issues none.
+  int cslot[NCH], coff[NCH];
+#pragma unroll
+  for (int it = 0; it < NCH; ++it) {
+    const int s = it * NT + tid, px = s / PP, jm = s % PP;  // piece jm of pixel x0 + px
+    cslot[it] = (px + 1) * PP + ((jm & ~3) | ((jm & 3) ^ swz<4>(px + 1)));
+  }
+  auto co_offsets = [&](const Patch& c) {
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+      const int s = it * NT + tid, px = s / PP, jm = s % PP;
+      const int x = c.x0 + px;
+      coff[it] = x < a.wd ? (x * a.cin + jm * 8) * 2 : OOB;
+    }
+  };
+  const int nco = a.tz - a.co_lo;  // frames carried
+  // cof: the cache-out frame of the frame being multiplied (or null), own:
+  // the patch's rows inside the map; halo row hr is output row hr - 1
+  auto store_cache = [&](const unsigned short* cof, int own, int y0, int hr, const uint4* zb) {
+    if constexpr (!CO) return;
+    // (fresh copies of own and y0 per stage: the comparisons and row
+    // offsets of loop-invariant values for each unrolled row would be
+    // hoisted, and held in scalar registers, which then spill)
+    int own_now, y0_now;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(own_now) : "s"(own));
+    asm volatile("s_mov_b32 %0, %1" : "=s"(y0_now) : "s"(y0));
+    const bool act = cof != nullptr && unsigned(hr - 1) < unsigned(own_now);  // uniform
+    const unsigned short* rp = act ? cof + (y0_now + hr - 1) * int64_t(row_el) : xs;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(uniform(rp)), 0, __builtin_amdgcn_readfirstlane(act ? row_bytes : 0), 0x00020000);
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (act) v = zb[cslot[it]];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, coff[it], 0, 0);
+    }
+  };
   const int frame_out_bytes = a.ho * a.wo * COUT * esz;
   auto emit = [&](const Patch& c, int o) {
     if (o < 0 || o >= a.to) return;  // uniform
@@ -1329,32 +1378,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (ltile >= 0) lfp = frame_ptr(lp, lz);
     }
   };
-  // wait for stage pos: with NBUF - 2 later stages in flight, all but their
-  // loads (loads complete in order; the output stores only add to the count)
+  // Wait for stage pos.  Each stage's loads are issued right after its NCO
+  // cache-out stores, so with NBUF - 2 later stages in flight all but their
+  // loads and stores must be done (memory operations complete in order; the
+  // output stores at frame ends only add to the count).
   auto wait_stage = [&](int ahead) {
     if (ahead < NBUF - 2) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       return;
     }
-    if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(0)) : "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * zcnt(1)) : "memory");
+    if (wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * (zcnt(0) + NCO)) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * (zcnt(1) + NCO)) : "memory");
   };
-  for (int i = 0; i < NBUF - 1 && ltile >= 0; ++i) issue_next();
-  int pos = 0, cbuf = 0;  // stage multiplied next, and its buffer
   Patch cp = decode(ctile);
   emit_offsets(cp);
+  co_offsets(cp);
+  // the stores ahead of the first loads write nothing
+  for (int i = 0; i < NBUF - 1 && ltile >= 0; ++i) {
+    store_cache(nullptr, 0, 0, 0, zl);
+    issue_next();
+  }
+  int pos = 0, cbuf = 0;  // stage multiplied next, and its buffer
   for (;;) {
 #pragma unroll
     for (int r = 0; r < THMAX; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // output frames no tap reaches (p_l > 2) are the bias alone
     for (int o = 0; o < min(a.to, p_l - 2); ++o) emit(cp, o);
+    const int own = __builtin_amdgcn_readfirstlane(min(th, a.h - cp.y0));
     for (int zi = 0; zi < a.tz - z_lo; ++zi) {
+      const int z = z_lo + zi;
+      const unsigned short* cof =
+          z >= a.co_lo ? static_cast<const unsigned short*>(uniform(static_cast<const unsigned short*>(a.cache_out) +
+                                                                    (int64_t(cp.nn) * nco + (z - a.co_lo)) * frame_el))
+                       : nullptr;
       // halo rows 0 .. hrows - 1 (uniform), nested so that each test runs
       // only where the previous row was taken
       static_for_while<0, THMAX + 2>([&](auto hr_c) {
         if (decltype(hr_c)::value >= hrows) return false;
         wait_stage(issued - pos - 1);
         barrier();  // stage pos has landed everywhere; buffer (pos - 1) % NBUF is free
+        store_cache(cof, own, cp.y0, decltype(hr_c)::value, zl + cbuf * ZSLOTS);
         if (ltile >= 0) issue_next();
         compute(zl + cbuf * ZSLOTS, hr_c);
         ++pos;
@@ -1368,6 +1431,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (ctile < 0) break;
     cp = decode(ctile);
     emit_offsets(cp);
+    co_offsets(cp);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #endif
@@ -1697,9 +1761,9 @@ template <int BN, int TH, int WM>
 const void* g32_kernel() {
   return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM>);
 }
-template <int COUT, int NCH>
+template <int COUT, int NCH, bool CO>
 const void* few_kernel() {
-  return reinterpret_cast<const void*>(&conv_bf16_few<COUT, NCH>);
+  return reinterpret_cast<const void*>(&conv_bf16_few<COUT, NCH, CO>);
 }
 
 // The few-output-channel kernel packs its weights as register fragments.
@@ -1715,7 +1779,8 @@ hipError_t launch_few(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, 
     if (e != hipSuccess) return e;
   }
   if (!conv) return hipSuccess;
-  return launch_persistent<&few_kernel<COUT, NCH>>(a, tiles, cus, 512, s);
+  if (a.cache_out) return launch_persistent<&few_kernel<COUT, NCH, true>>(a, tiles, cus, 512, s);
+  return launch_persistent<&few_kernel<COUT, NCH, false>>(a, tiles, cus, 512, s);
 }
 template <int COUT>
 hipError_t launch_few_cin(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
@@ -1881,6 +1946,10 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   a.tiles_x = plan->tiles_x;
   a.tiles_y = plan->tiles_y;
   a.tile_h = plan->tile_h;
+  // the few-output-channel kernel writes the cache-out itself
+  const bool fused_co = in.kernel_id == CC3D_K_BF16_S3_FEW && cache_out && in.t_cache_out > 0;
+  a.cache_out = fused_co ? cache_out : nullptr;
+  a.co_lo = fused_co ? a.tz - in.t_cache_out : a.tz;
   a.nblk_n = plan->nblk_n;
   a.ntiles = int(in.tiles);
   a.has_bias = d.has_bias;
@@ -1959,7 +2028,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     default:
       return invalid();
   }
-  if (e == hipSuccess && runs && cache_out && in.t_cache_out > 0) {
+  if (e == hipSuccess && runs && cache_out && in.t_cache_out > 0 && !fused_co) {
     const int64_t frame_bytes = int64_t(d.h) * d.w * d.c_in * plan->elem;
     int vec16 = (frame_bytes % 16 == 0) && aligned(x, 16) && aligned(cache_in, 16) && aligned(cache_out, 16);
     const int64_t units = vec16 ? frame_bytes / 16 : frame_bytes;
