@@ -252,7 +252,10 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     const int64_t ks = d.k_h;
     const int64_t slots = (int64_t(v.block_n) * ks * ks * (v.cin_chunk / 8) + 255) / 256 * 256;
     p->wpk_bytes = int64_t(d.k_t) * (d.c_in / v.cin_chunk) * p->nblk_n * slots * 16;
-    if (v.id == CC3D_K_BF16_S3_FEW) p->wpk_bytes = int64_t(d.c_in / 32) * 9 * 64 * 16;  // register fragments
+    if (v.id == CC3D_K_BF16_S3_FEW) {
+      p->wpk_bytes = int64_t(d.c_in / 32) * 9 * 64 * 16;  // register fragments
+      in.bytes_cache_out /= 2;                            // written from the staged rows, not re-read
+    }
     if (v.id == CC3D_K_BF16_GEN_N64) p->wpk_bytes = w_bytes;  // a copy of W, read as it is
     p->sched_off = (p->wpk_bytes + 255) / 256 * 256;
     in.workspace_bytes = p->sched_off + int64_t(kSchedSlots) * kSchedInts * 4;

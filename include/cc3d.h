@@ -121,7 +121,10 @@ typedef struct cc3d_plan_info {
   double flops_active;    /* the same counted over active (o, k) pairs only */
   double bytes_conv;      /* algorithmic HBM bytes of the conv kernel: each
                              read source frame once, W, b, the output */
-  double bytes_cache_out; /* bytes read + written by the cache-out writer */
+  double bytes_cache_out; /* HBM bytes the cache-out adds: read + written by
+                             the copy kernel; written only on the
+                             few-output-channel kernel, which stores it from
+                             the rows it stages */
   int32_t kernel_id;      /* which kernel variant forward launches */
   int32_t block_m, block_n; /* output pixels x output channels per tile */
   int64_t tiles;          /* output tiles of the conv kernel (bf16: processed by

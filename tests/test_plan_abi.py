@@ -235,6 +235,9 @@ def test_flops_and_bytes():
     frame = 360 * 640 * 192 * 2
     assert p["bytes_conv"] == 6 * frame + 192 * 27 * 192 * 2 + 192 * 2 + 4 * frame
     assert p["bytes_cache_out"] == 2 * 2 * frame
+    # the head kernel writes the cache-out from its staged rows: written only
+    h = cc3d.causal_conv3d_plan(_desc(c_in=96, c_out=3, h=72, w=128, t_x=4, t_cache=2)).info
+    assert h["kernel_name"].startswith("bf16_s3_few_") and h["bytes_cache_out"] == 2 * 72 * 128 * 96 * 2
     q = cc3d.causal_conv3d_plan(_desc(c_in=16, c_out=16, t_x=1, t_cache=0)).info
     assert q["flops_active"] == q["flops_nominal"] / 3
 
