@@ -637,15 +637,17 @@ def test_group_staged_schedule_with_single_group_tiles(cuda_device):
     assert_bf16_close(y, _oracle(x, None, w, b), "single-group tiles")
 
 
-@pytest.mark.parametrize("variant", ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2"])
-def test_graph_replays_match_eager(cuda_device, variant):
-    """The packed-weights forward (with its cache-out copy) captured in a HIP
+@pytest.mark.parametrize("cin,cout,variant", [(32, 96, "bf16_s3_n96_p16x32_g32"), (32, 96, "bf16_s3_n96_p8x32_x2"),
+                                               (96, 3, "bf16_s3_few_p16x128")])
+def test_graph_replays_match_eager(cuda_device, cin, cout, variant):
+    """The packed-weights forward (with its cache-out) captured in a HIP
     graph: the group-staged kernel's tile counters are cleared by the kernel
     itself (no memset nodes), and every replay reuses the captured counter
-    slot.  Several replays, each into a NaN-poisoned output with eager work
-    and synchronisations between them, all equal the eager call bitwise."""
+    slot; the head kernel writes the cache-out itself.  Several replays, each
+    into a NaN-poisoned output with eager work and synchronisations between
+    them, all equal the eager call bitwise."""
     import causal_conv3d_video_amd as cc3d
-    x, c, w, b = synth.conv_inputs(1, 32, 96, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 97)
+    x, c, w, b = synth.conv_inputs(1, cin, cout, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 97)
     plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant=variant)
     cc3d.causal_conv3d_pack_weights(plan, w)
     ref = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=DEV)
