@@ -310,11 +310,12 @@ def cpu_baseline(work, target_seconds):
                       + ", ".join(desc) + "; %.1f s, %.1f GFLOP" % (total_s, total_flops / 1e9)}
 
 
-def traffic_for(kernel_name):
+def traffic_for(kernel_name, signature=None):
     """HBM bytes per launch of ``kernel_name`` from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by the
     counter's reading on a plain copy of known size), or None when there is
-    none for this kernel or the kernel source changed since it was taken."""
+    none for this kernel, it was taken on another workload than
+    ``signature``, or the kernel source changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % kernel_name)
     try:
         rec = {}
@@ -326,6 +327,8 @@ def traffic_for(kernel_name):
     except OSError:
         return None
     if rec.get("kernel_source_sha256") != _source_hash():
+        return None
+    if signature is not None and not rec.get("workload", "").startswith(signature + " "):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -442,7 +445,7 @@ def main():
     flops = kern[sig]["flops"]                                         # algorithmic flops per launch
     nbytes = kern[sig]["bytes"]                                        # algorithmic bytes per launch
     mfma_bound = flops / nbytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    traffic = traffic_for(dom)
+    traffic = traffic_for(dom, sig)
     if mfma_bound:
         achieved = flops / (us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -1958,7 +1958,9 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     a.px_scale = px->scale;
     a.px_offset = px->offset;
   }
-  if (in.kernel_id == CC3D_K_BF16_S3_N96_G32W8 && !frame_intervals(plan, a)) return invalid();
+  if ((in.kernel_id == CC3D_K_BF16_S3_N96_G32W8 || in.kernel_id == CC3D_K_BF16_S3_N64_G32W8) &&
+      !frame_intervals(plan, a))
+    return invalid();
 
   int cus = 256;
   if (bf16) {
@@ -2005,6 +2007,9 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     case CC3D_K_BF16_S3_N32: e = launch_bf16<32, 8, 4, 1, 3, 16, 3, 2>(a, in.tiles, cus, pack, runs, s); break;
     case CC3D_K_BF16_S3_N96_G32W8:
       e = launch_g32<96, 16, 8>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
+      break;
+    case CC3D_K_BF16_S3_N64_G32W8:
+      e = launch_g32<64, 24, 8>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
       break;
     case CC3D_K_BF16_GEN_N64: e = launch_gen(a, in.tiles, pack, runs, s); break;
     case CC3D_K_BF16_S3_FEW:
@@ -2084,6 +2089,7 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
   // (nullptr: the default variant, whose geometry may be none of these)
   static const char* const kCandidates[] = {nullptr,
                                             "bf16_s3_n96_p16x32_g32",
+                                            "bf16_s3_n64_p24x32_g32",
                                             "bf16_s3_n96_p8x32_x2",
                                             "bf16_s3_n32_p8x32",
                                             "bf16_s3_few_p16x128",

@@ -17,9 +17,11 @@ enum cc3d_kernel_id : int32_t {
   CC3D_K_BF16_S3_N96_G32W8 = 10, // 3x3 spatial, 512 px (16x32) x 96 channels, halo staged by 32
                                  // channels, 8 waves (two per SIMD, 2 rows each)
   CC3D_K_BF16_S3_FEW = 11,   // 3x3 spatial, k_t = 3, d_t = 1, C_out <= 5, C_in in {32, 64, 96}:
-                             // 512 px (16x32) patches walked through time
+                             // R x 128 px patches walked through time, halo rows streamed
   CC3D_K_BF16_GEN_N64 = 12,  // any spatial kernel size, stride, dilation and padding:
                              // 256 px (8x32) x 64 channels, input pixels gathered per spatial tap
+  CC3D_K_BF16_S3_N64_G32W8 = 13, // as CC3D_K_BF16_S3_N96_G32W8 with 768 px (24x32) x 64 channels
+                                 // (3 rows per wave)
 };
 
 // Scheduler counters of the group-staged kernel, kept after the packed

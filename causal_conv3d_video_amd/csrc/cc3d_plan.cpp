@@ -85,6 +85,10 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   if (!same_spatial(d)) return false;
   const bool s3 = d.k_h == 3;
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
+  if (n == "bf16_s3_n64_p24x32_g32") {
+    *v = {CC3D_K_BF16_S3_N64_G32W8, 24, 32, 64, 16, "bf16_s3_n64_p24x32_g32"};
+    return s3 && d.c_out % 64 == 0 && d.c_in % 32 == 0;
+  }
   if (n == "bf16_s3_n96_p16x32_g32") {
     *v = {CC3D_K_BF16_S3_N96_G32W8, 16, 32, 96, 16, "bf16_s3_n96_p16x32_g32"};
     return s3 && d.c_out % 96 == 0 && d.c_in % 32 == 0;
@@ -115,14 +119,22 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   return false;
 }
 
-// Default choice.  Large 3x3 maps take 16x32 patches with the halo staged by
-// 32 channels and one workgroup per compute unit (from three rounds of 256
-// tiles: 384->384 at 180x320 with 2 frames, 960 tiles, runs 8% faster so);
-// small ones keep two smaller workgroups per compute unit so that every
-// unit gets tiles.  causal_conv3d_plan_autotune times the alternatives.
+// Default choice.  Large 3x3 maps take the group-staged kernel: the halo
+// staged by 32 channels, one workgroup per compute unit (from three rounds of
+// 256 tiles: 384->384 at 180x320 with 2 frames, 960 tiles, runs 8% faster
+// than the two-workgroup kernel).  Where C_out is a multiple of 64 its
+// 24x32-pixel x 64-channel tile (three rows per wave) reads 15% fewer LDS
+// bytes per MFMA than the 16x32 x 96 one and runs 1-3% faster.  Small maps
+// keep two smaller workgroups per compute unit so that every unit gets
+// tiles.  causal_conv3d_plan_autotune times the alternatives.
 const char* default_variant(const cc3d_desc_t& d) {
   if (!same_spatial(d)) return "bf16_gen_n64_p8x32";
   if (d.k_h == 3) {
+    if (d.c_out % 64 == 0 && d.c_in % 32 == 0) {
+      const int64_t tiles64 =
+          int64_t(d.n) * ((d.h + 23) / 24) * ((d.w + 31) / 32) * (d.c_out / 64) * std::max(1, d.t_x);
+      if (tiles64 >= 768) return "bf16_s3_n64_p24x32_g32";
+    }
     if (d.c_out % 96 == 0) {
       const int64_t big_tiles = int64_t(d.n) * ((d.h + 15) / 16) * ((d.w + 31) / 32) * (d.c_out / 96) *
                                 std::max(1, d.t_x);

@@ -164,8 +164,10 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  * As causal_conv3d_plan, but run the call with the named kernel variant
  * instead of the default choice (for tests that pin a variant and for
  * tuning; the name is the one plan_info reports).  Variants:
- *   "bf16_s3_n96_p16x32_g32"  3x3, C_out % 96 == 0, C_in % 32 == 0
+ *   "bf16_s3_n64_p24x32_g32"  3x3, C_out % 64 == 0, C_in % 32 == 0
  *                              (default for large maps)
+ *   "bf16_s3_n96_p16x32_g32"  3x3, C_out % 96 == 0, C_in % 32 == 0
+ *                              (default for large maps where C_out % 64 != 0)
  *   "bf16_s3_n96_p8x32_x2"    3x3, C_out % 96 == 0
  *   "bf16_s3_n32_p8x32"       3x3, any C_out
  *   "bf16_s3_few_p<R>x128"    3x3, k_t = 3, d_t = 1, s_t = 1, C_out <= 5,

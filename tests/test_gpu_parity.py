@@ -106,6 +106,39 @@ GROUP_STAGED = [
 ]
 
 
+# The same checks on the group-staged 24x32-pixel x 64-channel tile (three
+# rows per wave; C_out a multiple of 64).
+GROUP_STAGED_N64 = [
+    (32, 64, 30, 70, 2, 2, (3, 3, 3), 1, 2, 1, True),    # ragged rows (2nd patch row: 6 of 24) and columns
+    (64, 128, 25, 45, 3, 2, (3, 3, 3), 1, 2, 1, True),   # 2 channel groups, 2 channel blocks, 1-row tail
+    (96, 192, 48, 64, 4, 2, (3, 3, 3), 1, 2, 1, True),   # 3 channel groups, 3 blocks, exact rows and columns
+    (32, 64, 24, 32, 1, 0, (3, 3, 3), 1, 2, 2, True),    # batch 2, one active tap (p_l = 2)
+    (32, 64, 26, 40, 4, 2, (3, 3, 3), 2, 4, 1, True),    # temporal dilation 2
+    (32, 64, 24, 40, 3, 1, (2, 3, 3), 1, 1, 1, True),    # k_t = 2
+    (64, 64, 24, 33, 2, 0, (3, 3, 3), 1, 4, 1, True),    # p_base > (k_t-1)*d_t: bias-only frames
+    (32, 384, 20, 50, 2, 3, (3, 3, 3), 1, 2, 1, False),  # no bias, |C| > p_base, 6 blocks, one patch row
+]
+
+
+def _pinned_case(case, seed, variant):
+    cin, cout, h, w_, tx, tc, k, dt, p_base, n, bias = case
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV, seed=seed, has_bias=bias)
+    y, co, plan = run(x, c, w, b, k=k, dt=dt, p_base=p_base, variant=variant)
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == variant
+    ref = _oracle(x, c, w, b, k=k, dt=dt, p_base=p_base)
+    assert tuple(y.shape) == ref.shape
+    assert_bf16_close(y, ref, variant)
+    z = x if c is None else torch.cat([c, x], 1)
+    keep = min(p_base, z.shape[1])
+    assert torch.equal(co, z[:, z.shape[1] - keep:])
+
+
+@pytest.mark.parametrize("case", GROUP_STAGED_N64, ids=[str(i) for i in range(len(GROUP_STAGED_N64))])
+def test_bf16_group_staged_n64_full_compare(cuda_device, case):
+    _pinned_case(case, synth.SEED_BASE + 360 + GROUP_STAGED_N64.index(case), "bf16_s3_n64_p24x32_g32")
+
+
 @pytest.mark.parametrize("variant", ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2"])
 @pytest.mark.parametrize("case", GROUP_STAGED, ids=[str(i) for i in range(len(GROUP_STAGED))])
 def test_bf16_pinned_variants_full_compare(cuda_device, case, variant):
@@ -326,17 +359,20 @@ def test_unread_frames_and_guard_bands_are_never_touched(cuda_device):
     assert_bf16_close(results[0], ref, "poisoned")
 
 
-def test_group_staged_schedule_writes_every_tile_across_launches(cuda_device):
-    """640 tiles on at most 256 workgroups: two fixed tiles each, the rest
-    claimed from per-XCD counters (and stolen across XCDs).  Every launch
-    takes the next of the plan's 64 counter slots, and the kernel leaves its
-    slot zeroed, so 130 launches reuse every slot twice.  The output is
-    poisoned with NaN before each launch: every tile must be written every
-    time, bitwise equal to the first launch and within tolerance of the oracle."""
+@pytest.mark.parametrize("cout,variant,tiles", [(96, "bf16_s3_n96_p16x32_g32", 640),
+                                                (128, "bf16_s3_n64_p24x32_g32", 880)])
+def test_group_staged_schedule_writes_every_tile_across_launches(cuda_device, cout, variant, tiles):
+    """640 (880) tiles on at most 256 workgroups: two fixed tiles each, the
+    rest claimed from per-XCD counters (and stolen across XCDs).  Every
+    launch takes the next of the plan's 64 counter slots, and the kernel
+    leaves its slot zeroed, so 130 launches reuse every slot twice.  The
+    output is poisoned with NaN before each launch: every tile must be
+    written every time, bitwise equal to the first launch and within
+    tolerance of the oracle."""
     import causal_conv3d_video_amd as cc3d
-    x, c, w, b = synth.conv_inputs(1, 32, 96, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 90)
-    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant="bf16_s3_n96_p16x32_g32")
-    assert plan.info["tiles"] == 640
+    x, c, w, b = synth.conv_inputs(1, 32, cout, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 90)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant=variant)
+    assert plan.info["tiles"] == tiles
     cc3d.causal_conv3d_pack_weights(plan, w)
     first = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=DEV)
     first.fill_(float("nan"))
@@ -351,7 +387,9 @@ def test_group_staged_schedule_writes_every_tile_across_launches(cuda_device):
     torch.cuda.synchronize()
     assert not bad, "launches with unwritten or different tiles: %s" % bad[:10]
     assert bool(torch.isfinite(first).all())
-    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=90, tile_h=16)
+    th, tw = tile_of(plan)
+    pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=90, tile_h=th,
+                        tile_w=tw)
     ref = _oracle(x, c, w, b, points=pts)
     assert_bf16_close(gather(first, pts), ref, "dynamic schedule")
 
@@ -368,6 +406,7 @@ def test_repeated_runs_are_bitwise_identical(cuda_device):
 @pytest.mark.parametrize("cin,cout,variant", [
     (16, 192, None),
     (32, 96, "bf16_s3_n96_p16x32_g32"),
+    (32, 64, "bf16_s3_n64_p24x32_g32"),
     (16, 32, "bf16_s3_n32_p8x32"),
     (32, 3, "bf16_s3_few_p16x128"),
 ])
@@ -507,6 +546,7 @@ def test_u8_output_refused_off_the_head_kernel(cuda_device):
 # T_x, T_cache, k, s_t, variant) on every kernel that runs it.
 STRIDED = [
     (32, 96, 20, 70, 4, 2, (3, 3, 3), 2, "bf16_s3_n96_p16x32_g32"),
+    (32, 128, 30, 70, 4, 2, (3, 3, 3), 2, "bf16_s3_n64_p24x32_g32"),
     (64, 192, 17, 45, 6, 2, (3, 3, 3), 2, "bf16_s3_n96_p8x32_x2"),
     (32, 40, 13, 41, 5, 0, (3, 3, 3), 2, "bf16_s3_n32_p8x32"),       # chunk 0: odd length, no cache
     (64, 192, 16, 40, 4, 2, (3, 1, 1), 2, "bf16_s1_n192_p8x32"),
@@ -625,20 +665,21 @@ def test_general_spatial_full_size_sampled(cuda_device, sig):
     assert_bf16_close(gather(y, pts), ref, s["name"])
 
 
-def test_group_staged_schedule_with_single_group_tiles(cuda_device):
+@pytest.mark.parametrize("cout,h,variant", [(96, 512, "bf16_s3_n96_p16x32_g32"), (64, 768, "bf16_s3_n64_p24x32_g32")])
+def test_group_staged_schedule_with_single_group_tiles(cuda_device, cout, h, variant):
     """Tiles of a single group (C_in = 32, one active tap: the first chunk of
     a stream with no cache) with about three tiles per workgroup: the load
     cursor steps past a whole tile within one group, to a tile claimed in
     that same group."""
-    x, _, w, b = synth.conv_inputs(1, 32, 96, 512, 800, 1, 0, device=DEV, seed=synth.SEED_BASE + 96)
-    y, _, plan = run(x, None, w, b, variant="bf16_s3_n96_p16x32_g32")
+    x, _, w, b = synth.conv_inputs(1, 32, cout, h, 800, 1, 0, device=DEV, seed=synth.SEED_BASE + 96)
+    y, _, plan = run(x, None, w, b, variant=variant)
     torch.cuda.synchronize()
     assert plan.info["tiles"] == 800 and plan.info["taps"][2]["active"] and not plan.info["taps"][0]["active"]
     assert_bf16_close(y, _oracle(x, None, w, b), "single-group tiles")
 
 
 @pytest.mark.parametrize("cin,cout,variant", [(32, 96, "bf16_s3_n96_p16x32_g32"), (32, 96, "bf16_s3_n96_p8x32_x2"),
-                                               (96, 3, "bf16_s3_few_p16x128")])
+                                               (32, 64, "bf16_s3_n64_p24x32_g32"), (96, 3, "bf16_s3_few_p16x128")])
 def test_graph_replays_match_eager(cuda_device, cin, cout, variant):
     """The packed-weights forward (with its cache-out) captured in a HIP
     graph: the group-staged kernel's tile counters are cleared by the kernel

@@ -199,9 +199,10 @@ def test_general_spatial_parameters_take_the_gather_kernel(kw):
     assert p.info["kernel_name"] == "bf16_gen_n64_p8x32" and p.info["block_m"] == 256 and p.info["block_n"] == 64
     k = kw.get("k", (3, 3, 3))
     assert p.info["workspace_bytes"] >= 40 * k[0] * k[1] * k[2] * 32 * 2
-    for name in ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32", "bf16_s1_n32_p8x32"]:
+    for name in ["bf16_s3_n96_p16x32_g32", "bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32",
+                 "bf16_s1_n32_p8x32"]:
         with pytest.raises(cc3d.CC3DError):
-            cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=96, h=20, w=36, **kw), name)
+            cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=192, h=20, w=36, **kw), name)
 
 
 def test_head_patch_height_rule():
@@ -334,12 +335,19 @@ def test_packed_entry_points_refuse_fp32_plans_and_null_pointers():
 
 
 def test_default_kernel_choice():
-    # large 3x3 maps with C_in % 32 == 0 and C_out % 96 == 0: the group-staged
-    # 16x32 kernel; small maps: the two-workgroup 8x32 kernel
+    # large 3x3 maps with C_in % 32 == 0: the group-staged kernel, 24x32 x 64
+    # channels where C_out % 64 == 0, else 16x32 x 96 where C_out % 96 == 0;
+    # small maps: the two-workgroup 8x32 kernel
     big = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2))
-    assert big.info["kernel_name"] == "bf16_s3_n96_p16x32_g32"
-    assert big.info["block_m"] == 512 and big.info["block_n"] == 96
-    assert big.info["tiles"] == 23 * 20 * 2 * 4
+    assert big.info["kernel_name"] == "bf16_s3_n64_p24x32_g32"
+    assert big.info["block_m"] == 768 and big.info["block_n"] == 64
+    assert big.info["tiles"] == 15 * 20 * 3 * 4
+    big96 = cc3d.causal_conv3d_plan(_desc(c_in=96, c_out=96, h=720, w=1280, t_x=4, t_cache=2))
+    assert big96.info["kernel_name"] == "bf16_s3_n96_p16x32_g32"
+    assert big96.info["block_m"] == 512 and big96.info["block_n"] == 96
+    assert big96.info["tiles"] == 45 * 40 * 1 * 4
+    mid = cc3d.causal_conv3d_plan(_desc(c_in=64, c_out=128, h=360, w=640, t_x=4, t_cache=2))
+    assert mid.info["kernel_name"] == "bf16_s3_n64_p24x32_g32"   # C_out % 96 != 0
     lat = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2))
     assert lat.info["kernel_name"] == "bf16_s3_n96_p8x32_x2"
     odd = cc3d.causal_conv3d_plan(_desc(c_in=48, c_out=96, h=360, w=640, t_x=4, t_cache=2))
@@ -370,7 +378,7 @@ def test_every_decoder_signature_takes_a_bf16_fast_path():
     assert calls == 5 * len(synth.DECODER_SIGNATURES)
 
 
-VARIANTS_3X3 = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32"]
+VARIANTS_3X3 = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32"]
 VARIANTS_FEW = ["bf16_s3_few_p4x128", "bf16_s3_few_p11x128", "bf16_s3_few_p16x128", "bf16_s3_n32_p8x32"]
 VARIANTS_1X1 = ["bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32"]
 
@@ -396,6 +404,9 @@ def test_plan_variant_pins_the_kernel():
 @pytest.mark.parametrize("name,kw", [
     ("bf16_s3_n96_p16x32_g32", dict(c_in=48, c_out=96)),      # C_in % 32 != 0
     ("bf16_s3_n96_p16x32_g32", dict(c_in=32, c_out=64)),      # C_out % 96 != 0
+    ("bf16_s3_n64_p24x32_g32", dict(c_in=32, c_out=96)),      # C_out % 64 != 0
+    ("bf16_s3_n64_p24x32_g32", dict(c_in=48, c_out=64)),      # C_in % 32 != 0
+    ("bf16_s3_n64_p24x32_g32", dict(c_in=32, c_out=64, k=(3, 1, 1), padding=(0, 0))),  # not 3x3
     ("bf16_s3_n96_p8x32_x2", dict(c_in=32, c_out=40)),
     ("bf16_s1_n32_p8x32", dict(c_in=32, c_out=32)),           # 1x1 variant on a 3x3 call
     ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, k=(3, 1, 1), padding=(0, 0))),
