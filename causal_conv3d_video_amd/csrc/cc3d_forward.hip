@@ -1446,13 +1446,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // copy of W in the workspace ([C_out][k_t][k_h][k_w][C_in] as it is).  No
 // halo is shared between spatial taps, so the input is read k_h * k_w times
 // from L2: the kernel covers the shapes the halo-staged ones do not.
-// Tile: 8 x 32 output pixels x 64 output channels; wave w owns rows 2w and
-// 2w + 1 (four 32 x 32 accumulators).
+// Tile: 8 x 32 output pixels x BN (64 or 96) output channels; wave w owns
+// rows 2w and 2w + 1 (2 x BN/32 accumulators of 32 x 32).  The gathered
+// pixels dominate the staged bytes, so the wider tile stages fewer bytes per
+// MFMA (470 against 640).
+template <int BN>
 __global__ __launch_bounds__(256) void conv_bf16_gen(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int TH = 8, TW = 32, BN = 64, CW = BN / 32, NT = 256, PPX = 4;  // pieces per pixel: 32 channels
-  constexpr int ASL = TH * TW * PPX, BSL = BN * PPX;                          // LDS slots per stage
-  constexpr int NB = 3;                                                       // stage buffers (ring)
+  constexpr int TH = 8, TW = 32, CW = BN / 32, NT = 256, PPX = 4;  // pieces per pixel: 32 channels
+  constexpr int ASL = TH * TW * PPX, BSL = BN * PPX;               // LDS slots per stage
+  constexpr int BIT = (BSL + NT - 1) / NT;                         // weight load rounds
+  constexpr int NB = 3;                                            // stage buffers (ring)
+  static_assert(BN % 32 == 0 && BSL % 64 == 0, "tile width");
+  constexpr auto bcnt = [](int w) {  // weight load instructions of wave w per stage
+    int n = 0;
+    for (int it = 0; it < BIT; ++it) n += it * NT + w * 64 < BSL;
+    return n;
+  };
   __shared__ uint4 al[NB * ASL];
   __shared__ uint4 bl[NB * BSL];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1527,13 +1537,16 @@ __global__ __launch_bounds__(256) void conv_bf16_gen(ConvArgs a) {
           r_z, (__attribute__((address_space(3))) void*)(al + buf * ASL + it * NT + wave * 64), 16,
           in ? ((iy * a.wd + ix) * a.cin + ch) * 2 : OOB, 0, 0, 0);
     }
-    static_assert(BSL <= NT, "one weight piece per thread");
-    if (wave < BSL / 64) {
-      const int co = tid >> 2, q = (tid & 3) ^ (co & 3), ch = cc * 32 + q * 8;
-      const bool in = n0 + co < a.cout && ch < a.cin;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r_w, (__attribute__((address_space(3))) void*)(bl + buf * BSL + wave * 64), 16,
-          in ? ((((n0 + co) * a.kt + k) * nsp + sp) * a.cin + ch) * 2 : OOB, 0, 0, 0);
+#pragma unroll
+    for (int it = 0; it < BIT; ++it) {
+      const int sl = it * NT + tid;
+      if (it * NT + wave * 64 < BSL) {  // wave-uniform
+        const int co = sl >> 2, q = (sl & 3) ^ (co & 3), ch = cc * 32 + q * 8;
+        const bool in = n0 + co < a.cout && ch < a.cin;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r_w, (__attribute__((address_space(3))) void*)(bl + buf * BSL + it * NT + wave * 64), 16,
+            in ? ((((n0 + co) * a.kt + k) * nsp + sp) * a.cin + ch) * 2 : OOB, 0, 0, 0);
+      }
     }
   };
   auto barrier = [&]() {
@@ -1558,8 +1571,9 @@ __global__ __launch_bounds__(256) void conv_bf16_gen(ConvArgs a) {
     const int buf = st % NB;
     // stage st has landed once only stage st + 1's loads are in flight
     if (st + 1 < nst) {
-      if (wave < BSL / 64) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ASL / NT + 1) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ASL / NT) : "memory");
+      static_assert(bcnt(0) == BIT && bcnt(3) >= BIT - 1, "two weight load counts");
+      if (bcnt(wave) == BIT) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ASL / NT + BIT) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ASL / NT + BIT - 1) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -1803,6 +1817,7 @@ hipError_t launch_bf16(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv,
 
 // The general-spatial kernel reads W as it is, from a copy in the workspace
 // (so the packed-weights path works the same way); one workgroup per tile.
+template <int BN>
 hipError_t launch_gen(ConvArgs a, int64_t tiles, bool pack, bool conv, hipStream_t s) {
   if (pack) {
     const size_t w_bytes = size_t(a.cout) * a.kt * a.kh * a.kw * a.cin * 2;
@@ -1810,7 +1825,7 @@ hipError_t launch_gen(ConvArgs a, int64_t tiles, bool pack, bool conv, hipStream
     if (e != hipSuccess) return e;
   }
   if (!conv) return hipSuccess;
-  return launch_conv(reinterpret_cast<const void*>(&conv_bf16_gen), a, tiles, s, 256);
+  return launch_conv(reinterpret_cast<const void*>(&conv_bf16_gen<BN>), a, tiles, s, 256);
 }
 
 // The group-staged 3x3 kernel (16-channel weight sub-stages, same packing).
@@ -2011,7 +2026,8 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     case CC3D_K_BF16_S3_N64_G32W8:
       e = launch_g32<64, 24, 8>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
       break;
-    case CC3D_K_BF16_GEN_N64: e = launch_gen(a, in.tiles, pack, runs, s); break;
+    case CC3D_K_BF16_GEN_N64: e = launch_gen<64>(a, in.tiles, pack, runs, s); break;
+    case CC3D_K_BF16_GEN_N96: e = launch_gen<96>(a, in.tiles, pack, runs, s); break;
     case CC3D_K_BF16_S3_FEW:
       switch (d.c_out) {
         case 1: e = launch_few_cin<1>(a, in.tiles, cus, pack, runs, s); break;

@@ -22,6 +22,7 @@ enum cc3d_kernel_id : int32_t {
                              // 256 px (8x32) x 64 channels, input pixels gathered per spatial tap
   CC3D_K_BF16_S3_N64_G32W8 = 13, // as CC3D_K_BF16_S3_N96_G32W8 with 768 px (24x32) x 64 channels
                                  // (3 rows per wave)
+  CC3D_K_BF16_GEN_N96 = 14,  // as CC3D_K_BF16_GEN_N64 with 96 output channels per tile
 };
 
 // Scheduler counters of the group-staged kernel, kept after the packed

@@ -82,6 +82,10 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
     *v = {CC3D_K_BF16_GEN_N64, 8, 32, 64, 32, "bf16_gen_n64_p8x32"};
     return true;
   }
+  if (n == "bf16_gen_n96_p8x32") {  // any spatial parameters, C_out % 96 == 0
+    *v = {CC3D_K_BF16_GEN_N96, 8, 32, 96, 32, "bf16_gen_n96_p8x32"};
+    return d.c_out % 96 == 0;
+  }
   if (!same_spatial(d)) return false;
   const bool s3 = d.k_h == 3;
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
@@ -128,7 +132,7 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
 // keep two smaller workgroups per compute unit so that every unit gets
 // tiles.  causal_conv3d_plan_autotune times the alternatives.
 const char* default_variant(const cc3d_desc_t& d) {
-  if (!same_spatial(d)) return "bf16_gen_n64_p8x32";
+  if (!same_spatial(d)) return d.c_out % 96 == 0 ? "bf16_gen_n96_p8x32" : "bf16_gen_n64_p8x32";
   if (d.k_h == 3) {
     if (d.c_out % 64 == 0 && d.c_in % 32 == 0) {
       const int64_t tiles64 =
@@ -268,7 +272,7 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
       p->wpk_bytes = int64_t(d.c_in / 32) * 9 * 64 * 16;  // register fragments
       in.bytes_cache_out /= 2;                            // written from the staged rows, not re-read
     }
-    if (v.id == CC3D_K_BF16_GEN_N64) p->wpk_bytes = w_bytes;  // a copy of W, read as it is
+    if (v.id == CC3D_K_BF16_GEN_N64 || v.id == CC3D_K_BF16_GEN_N96) p->wpk_bytes = w_bytes;  // a copy of W, read as it is
     p->sched_off = (p->wpk_bytes + 255) / 256 * 256;
     in.workspace_bytes = p->sched_off + int64_t(kSchedSlots) * kSchedInts * 4;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);

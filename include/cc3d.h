@@ -154,7 +154,8 @@ typedef struct cc3d_counters {
  *   output) or the weights reaching 2^31 bytes.  Any spatial kernel size,
  *   stride, dilation and padding runs: 3x3 "same" and 1x1 convs with unit
  *   spatial stride and dilation on the halo-staged kernels, the others on
- *   the gather kernel "bf16_gen_n64_p8x32".
+ *   the gather kernel ("bf16_gen_n96_p8x32" where C_out % 96 == 0, else
+ *   "bf16_gen_n64_p8x32").
  *   CC3D_ERR_INVALID_ARG for a NULL pointer, a size < 1 (t_cache < 0), an
  *   unknown dtype, or an empty output (T_o, H_o or W_o < 1).
  */
@@ -181,6 +182,8 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *   "bf16_gen_n64_p8x32"      any spatial parameters (default outside that
  *                              envelope): input pixels gathered per spatial
  *                              tap, W read as it is from a workspace copy
+ *   "bf16_gen_n96_p8x32"      the same, 96 output channels per tile,
+ *                              C_out % 96 == 0 (the default there)
  *   "f32_direct"              fp32
  * Every variant computes the same operation; bf16 results of different
  * variants may differ in the last bit (fp32 accumulation order).

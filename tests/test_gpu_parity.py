@@ -622,7 +622,13 @@ GENERAL = [
     (32, 40, 12, 20, 2, 2, (3, 3, 3), (1, 1), (2, 1), (1, 1), 1, 1, 2, 2, True),   # batch 2, stride (2, 1)
     (16, 32, 14, 30, 4, 4, (3, 3, 3), (2, 1), (1, 1), (2, 1), 1, 2, 4, 1, False),  # d_t 2, d_h 2, no bias
     (48, 33, 9, 70, 1, 0, (3, 3, 3), (1, 1), (1, 2), (1, 1), 1, 1, 2, 1, True),    # one frame, no cache
+    (32, 192, 17, 35, 2, 2, (3, 3, 3), (1, 1), (2, 2), (1, 1), 1, 1, 2, 1, True),  # stride 2, two 96-wide blocks
+    (64, 192, 13, 40, 3, 1, (3, 3, 3), (2, 2), (1, 1), (2, 2), 1, 1, 2, 1, False), # dilation 2, no bias
 ]
+
+
+def _gen_name(cout):
+    return "bf16_gen_n96_p8x32" if cout % 96 == 0 else "bf16_gen_n64_p8x32"
 
 
 @pytest.mark.parametrize("case", GENERAL)
@@ -632,21 +638,22 @@ def test_general_spatial_parameters_full_compare(cuda_device, case):
                                    has_bias=bias)
     y, co, plan = run(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, st=st, sst=sst, sdil=sdil)
     torch.cuda.synchronize()
-    assert plan.info["kernel_name"] == "bf16_gen_n64_p8x32"
+    assert plan.info["kernel_name"] == _gen_name(cout)
     ref = _oracle(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, st=st, sst=sst, sdil=sdil)
     assert_bf16_close(y, ref, "general %s" % (case,))
     z = x if c is None else torch.cat([c, x], 1)
     assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
 
 
+@pytest.mark.parametrize("variant", ["bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32"])
 @pytest.mark.parametrize("case", GROUP_STAGED[:4])
-def test_gather_kernel_on_same_convs_full_compare(cuda_device, case):
-    """The gather kernel pinned on the 3x3 "same" shapes the halo-staged
-    kernels run, against the oracle."""
+def test_gather_kernel_on_same_convs_full_compare(cuda_device, case, variant):
+    """The gather kernel (both tile widths) pinned on the 3x3 "same" shapes
+    the halo-staged kernels run, against the oracle."""
     cin, cout, h, w_, tx, tc, k, dt, p_base, n, bias = case
     x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV, seed=synth.SEED_BASE + 390 + h,
                                    has_bias=bias)
-    y, _, plan = run(x, c, w, b, k=k, dt=dt, p_base=p_base, variant="bf16_gen_n64_p8x32")
+    y, _, plan = run(x, c, w, b, k=k, dt=dt, p_base=p_base, variant=variant)
     torch.cuda.synchronize()
     assert_bf16_close(y, _oracle(x, c, w, b, k=k, dt=dt, p_base=p_base), "gather kernel")
 
@@ -658,7 +665,7 @@ def test_general_spatial_full_size_sampled(cuda_device, sig):
                                    seed=synth.SEED_BASE + 395)
     y, _, plan = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"])
     torch.cuda.synchronize()
-    assert plan.info["kernel_name"] == "bf16_gen_n64_p8x32"
+    assert plan.info["kernel_name"] == _gen_name(s["cout"])
     assert bool(torch.isfinite(y).all())
     pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=39)
     ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"], points=pts)

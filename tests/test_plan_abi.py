@@ -203,6 +203,11 @@ def test_general_spatial_parameters_take_the_gather_kernel(kw):
                  "bf16_s1_n32_p8x32"]:
         with pytest.raises(cc3d.CC3DError):
             cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=192, h=20, w=36, **kw), name)
+    # C_out a multiple of 96: the 96-wide gather tile; it refuses other C_out
+    q = cc3d.causal_conv3d_plan(_desc(c_in=32, c_out=192, h=20, w=36, **kw))
+    assert q.info["kernel_name"] == "bf16_gen_n96_p8x32" and q.info["block_n"] == 96 and q.info["tiles"] % 2 == 0
+    with pytest.raises(cc3d.CC3DError):
+        cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=40, h=20, w=36, **kw), "bf16_gen_n96_p8x32")
 
 
 def test_head_patch_height_rule():
