@@ -110,7 +110,8 @@ def time_kernels(work, launches, stream, warm_seconds=0.2):
     """Average conv-kernel launch time per signature at the steady-state chunk
     (cache present): weights packed once, then causal_conv3d_forward_packed
     launches only the conv kernel; HIP events on the launch stream.  Each
-    signature is first run untimed for warm_seconds (steady-state clocks)."""
+    signature is first run untimed for warm_seconds (steady-state clocks).
+    Also the median of the same number of launches timed one by one."""
     import torch
 
     import causal_conv3d_video_amd as cc3d
@@ -136,6 +137,15 @@ def time_kernels(work, launches, stream, warm_seconds=0.2):
         e1.record(stream)
         e1.synchronize()
         ms = e0.elapsed_time(e1) / launches
+        # the same launches with an event pair around each (median)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for a_, b_ in ev:
+            a_.record(stream)
+            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c], None, stream)
+            b_.record(stream)
+        ev[-1][1].synchronize()
+        per = sorted(a_.elapsed_time(b_) for a_, b_ in ev)
+        med_us = (per[(launches - 1) // 2] + per[launches // 2]) / 2 * 1e3
         info = plan.info
         res[wk["sig"]["name"]] = dict(
             kernel=info["kernel_name"], us_per_launch=ms * 1e3,
@@ -143,7 +153,7 @@ def time_kernels(work, launches, stream, warm_seconds=0.2):
             frac_mfma_peak=info["flops_active"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
             frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            flops=info["flops_active"], bytes=info["bytes_conv"], tiles=info["tiles"])
+            flops=info["flops_active"], bytes=info["bytes_conv"], tiles=info["tiles"], us_per_launch_median=med_us)
         # A working set that fits the 256 MB MALL stays there between
         # launches of one buffer set; also time launches that rotate over
         # enough copies of x, cache and out (>= 4, >= 512 MB) to start cold.
