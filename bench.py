@@ -334,9 +334,25 @@ def cpu_baseline(work, target_seconds):
         total_s += time.perf_counter() - t
         total_flops += npx * per_px
         desc.append("%s:%dpx" % (s["name"], npx))
+    # the tiny fp32 workload's two calls (A: no cache; B: A's last two frames
+    # as cache) on one thread, whole outputs, repeated for about half a second
+    import synth
+    g = torch.Generator().manual_seed(synth.SEED_BASE)
+    wt = synth.draw((8, 3, 3, 3, 8), "uniform", g, "cpu", torch.float32, 1.0)
+    bt = synth.draw((8,), "uniform", g, "cpu", torch.float32, 0.1)
+    xa = synth.draw((1, 4, 16, 16, 8), "uniform", g, "cpu", torch.float32, 1.0)
+    xb = synth.draw((1, 4, 16, 16, 8), "uniform", g, "cpu", torch.float32, 1.0)
+    tiny_flops = 2.0 * 16 * 16 * 8 * 8 * 9 * (3 + 3 + 2 + 1 + 4 * 3)  # active taps of calls A and B
+    reps, t = 0, time.perf_counter()
+    while time.perf_counter() - t < 0.5:
+        oracle.conv3d(xa, None, wt, bt, nthreads=1)
+        oracle.conv3d(xb, xa[:, 2:4], wt, bt, nthreads=1)
+        reps += 1
+    tiny_rate = reps * tiny_flops / (time.perf_counter() - t)
     return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "fp64 oracle, random output pixels (all channels) of chunk 2 of each signature: "
-                      + ", ".join(desc) + "; %.1f s, %.1f GFLOP" % (total_s, total_flops / 1e9)}
+                      + ", ".join(desc) + "; %.1f s, %.1f GFLOP" % (total_s, total_flops / 1e9),
+            "tiny_fp32_one_thread_gflops": tiny_rate / 1e9}
 
 
 def traffic_for(kernel_name, signature=None):
