@@ -384,7 +384,7 @@ def traffic_for(kernel_name, signature=None):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
