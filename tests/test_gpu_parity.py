@@ -725,20 +725,21 @@ def test_graph_replays_match_eager(cuda_device, cin, cout, variant):
         assert torch.equal(other, ref)
 
 
-def test_packed_forwards_of_one_plan_overlap_on_two_streams(cuda_device):
+@pytest.mark.parametrize("cout,variant", [(96, "bf16_s3_n96_p16x32_g32"), (128, "bf16_s3_n64_p24x32_g32")])
+def test_packed_forwards_of_one_plan_overlap_on_two_streams(cuda_device, cout, variant):
     """Launches of one plan on two streams may run at the same time: each
     takes its own slot of the group-staged kernel's tile counters.  Twelve
     interleaved launches, no synchronisation between them; every output is
     the eager one bitwise."""
     import causal_conv3d_video_amd as cc3d
-    x, c, w, b = synth.conv_inputs(1, 32, 96, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 98)
-    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant="bf16_s3_n96_p16x32_g32")
+    x, c, w, b = synth.conv_inputs(1, 32, cout, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 98)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant=variant)
     cc3d.causal_conv3d_pack_weights(plan, w)
     ref = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=DEV)
     cc3d.causal_conv3d_forward_packed(plan, x, c, b, ref, None)
-    torch.cuda.synchronize()
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = [torch.full_like(ref, float("nan")) for _ in range(12)]
+    torch.cuda.synchronize()  # the NaN fills (current stream) before the side-stream launches
     for i, o in enumerate(outs):
         cc3d.causal_conv3d_forward_packed(plan, x, c, b, o, None, stream=streams[i % 2])
     torch.cuda.synchronize()
