@@ -12,20 +12,27 @@
 //   GEMM view per output frame:  D[co][pixel] = sum_K  W[co][K] * Z[K][pixel]
 //   K = (active tap k, spatial tap (a, c), input channel ci)
 //
-// bf16 kernel (one workgroup = 4 waves = one output frame, one patch of
-// TH x 32 output pixels, BN output channels):
-//   * a pipeline stage is (active tap, chunk of CB input channels); its
-//     operands are the (TH+2) x 34 pixel halo of the source frame (zero
-//     outside the image) and the BN x 9 x CB weight slice, both staged through
-//     LDS, double-buffered, with the next stage's global loads in flight while
-//     the current stage's MFMAs run;
-//   * LDS rows are padded by 16 bytes so that the 16-byte operand reads of
-//     any 8 consecutive lanes fall in distinct banks;
-//   * v_mfma_f32_32x32x16_bf16: A = 32 output channels x 16 input channels of
-//     W, B = 16 input channels x 32 pixels (one patch row, shifted by the
-//     spatial tap) of the halo; fp32 accumulation in registers;
-//   * epilogue: fp32 bias added once, round to nearest even to bf16,
-//     channels-last stores of 4 channels per lane.
+// The kernels (all channels-last, fp32 accumulation, bias added once in
+// fp32 and rounded to nearest even at the end; the launcher picks one per
+// plan, see cc3d_plan.cpp):
+//   * conv_bf16_g32: large 3x3 maps.  One workgroup of 8 waves per compute
+//     unit, persistent, with per-XCD tile counters; a tile is one output
+//     frame x a 16x32 (or 24x32) patch x 96 (or 64) output channels.  The
+//     halo of one (active tap, 32-channel group) is staged once into LDS and
+//     serves 9 spatial taps x 2 sub-stages of 16 channels;
+//     v_mfma_f32_32x32x16_bf16 with the weights as A and the halo pixels as B.
+//   * conv_bf16_mfma: smaller 3x3 maps (two workgroups per compute unit),
+//     other C_out, and the 1x1 / (k_t,1,1) convs.
+//   * conv_bf16_few: C_out <= 5 (the RGB head).  Walks time per patch,
+//     streaming whole halo rows; the (temporal tap, output channel) pairs are
+//     the MFMA columns, rotated across lanes after each frame.
+//   * conv_bf16_gen: any other spatial kernel size, stride, dilation or
+//     padding, gathering each spatial tap's input pixels.
+//   * conv_f32_direct: the fp32 path, one output per thread.
+//   * copy_tail_frames: the cache-out (the head kernel writes its own).
+// Operands reach LDS through direct-to-LDS buffer loads; the buffer range
+// check writes the zero padding.  LDS layouts are XOR-swizzled so that the
+// 16-byte operand reads of a fragment hit distinct banks.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
