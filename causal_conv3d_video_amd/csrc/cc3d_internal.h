@@ -23,6 +23,8 @@ enum cc3d_kernel_id : int32_t {
   CC3D_K_BF16_S3_N64_G32W8 = 13, // as CC3D_K_BF16_S3_N96_G32W8 with 768 px (24x32) x 64 channels
                                  // (3 rows per wave)
   CC3D_K_BF16_GEN_N96 = 14,  // as CC3D_K_BF16_GEN_N64 with 96 output channels per tile
+  CC3D_K_BF16_S3D2_N64_G32W8 = 15, // the group-staged kernel on 3x3 taps at spatial dilation 2,
+                                   // padding 2: 512 px (16x32) x 64 channels
 };
 
 // Scheduler counters of the group-staged kernel, kept after the packed

@@ -76,6 +76,13 @@ int few_rows(const cc3d_desc_t& d) {
   return best;
 }
 
+// 3x3 taps at spatial dilation 2 with the padding that keeps the map size
+// (2), unit spatial stride: the dilated group-staged kernel's envelope.
+bool dilated_same(const cc3d_desc_t& d) {
+  return d.k_h == 3 && d.k_w == 3 && d.s_h == 1 && d.s_w == 1 && d.d_h == 2 && d.d_w == 2 && d.p_h == 2 &&
+         d.p_w == 2;
+}
+
 bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   const std::string n(name);
   if (n == "bf16_gen_n64_p8x32") {  // any spatial parameters
@@ -85,6 +92,10 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   if (n == "bf16_gen_n96_p8x32") {  // any spatial parameters, C_out % 96 == 0
     *v = {CC3D_K_BF16_GEN_N96, 8, 32, 96, 32, "bf16_gen_n96_p8x32"};
     return d.c_out % 96 == 0;
+  }
+  if (n == "bf16_s3d2_n64_p16x32_g32") {  // 3x3 "same" at spatial dilation 2
+    *v = {CC3D_K_BF16_S3D2_N64_G32W8, 16, 32, 64, 16, "bf16_s3d2_n64_p16x32_g32"};
+    return dilated_same(d) && d.c_out % 64 == 0 && d.c_in % 32 == 0;
   }
   if (!same_spatial(d)) return false;
   const bool s3 = d.k_h == 3;
@@ -132,7 +143,10 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
 // keep two smaller workgroups per compute unit so that every unit gets
 // tiles.  causal_conv3d_plan_autotune times the alternatives.
 const char* default_variant(const cc3d_desc_t& d) {
-  if (!same_spatial(d)) return d.c_out % 96 == 0 ? "bf16_gen_n96_p8x32" : "bf16_gen_n64_p8x32";
+  if (!same_spatial(d)) {
+    if (dilated_same(d) && d.c_out % 64 == 0 && d.c_in % 32 == 0) return "bf16_s3d2_n64_p16x32_g32";
+    return d.c_out % 96 == 0 ? "bf16_gen_n96_p8x32" : "bf16_gen_n64_p8x32";
+  }
   if (d.k_h == 3) {
     if (d.c_out % 64 == 0 && d.c_in % 32 == 0) {
       const int64_t tiles64 =

@@ -155,7 +155,8 @@ typedef struct cc3d_counters {
  *   stride, dilation and padding runs: 3x3 "same" and 1x1 convs with unit
  *   spatial stride and dilation on the halo-staged kernels, the others on
  *   the gather kernel ("bf16_gen_n96_p8x32" where C_out % 96 == 0, else
- *   "bf16_gen_n64_p8x32").
+ *   "bf16_gen_n64_p8x32"), but for 3x3 "same" convs at spatial dilation 2,
+ *   which have a halo-staged kernel of their own.
  *   CC3D_ERR_INVALID_ARG for a NULL pointer, a size < 1 (t_cache < 0), an
  *   unknown dtype, or an empty output (T_o, H_o or W_o < 1).
  */
@@ -184,6 +185,9 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *                              tap, W read as it is from a workspace copy
  *   "bf16_gen_n96_p8x32"      the same, 96 output channels per tile,
  *                              C_out % 96 == 0 (the default there)
+ *   "bf16_s3d2_n64_p16x32_g32" 3x3 at spatial dilation 2, padding 2, unit
+ *                              spatial stride, C_out % 64 == 0, C_in % 32 == 0
+ *                              (the default there): the halo-staged kernel
  *   "f32_direct"              fp32
  * Every variant computes the same operation; bf16 results of different
  * variants may differ in the last bit (fp32 accumulation order).

@@ -627,7 +627,11 @@ GENERAL = [
 ]
 
 
-def _gen_name(cout):
+def _gen_name(cout, cin=32, k=(3, 3, 3), pad=(1, 1), sst=(1, 1), sdil=(1, 1)):
+    """The default kernel of a call outside the 3x3 / 1x1 "same" envelope."""
+    if (k[1:] == (3, 3) and sst == (1, 1) and sdil == (2, 2) and tuple(pad) == (2, 2) and cout % 64 == 0
+            and cin % 32 == 0):
+        return "bf16_s3d2_n64_p16x32_g32"
     return "bf16_gen_n96_p8x32" if cout % 96 == 0 else "bf16_gen_n64_p8x32"
 
 
@@ -638,9 +642,38 @@ def test_general_spatial_parameters_full_compare(cuda_device, case):
                                    has_bias=bias)
     y, co, plan = run(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, st=st, sst=sst, sdil=sdil)
     torch.cuda.synchronize()
-    assert plan.info["kernel_name"] == _gen_name(cout)
+    assert plan.info["kernel_name"] == _gen_name(cout, cin, k, pad, sst, sdil)
     ref = _oracle(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, st=st, sst=sst, sdil=sdil)
     assert_bf16_close(y, ref, "general %s" % (case,))
+    z = x if c is None else torch.cat([c, x], 1)
+    assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
+
+
+# The group-staged kernel at spatial dilation 2 ("same": padding 2): (C_in,
+# C_out, H, W, T_x, T_cache, k, d_t, p_base, N, bias), full compare.
+DILATED = [
+    (32, 64, 20, 70, 2, 2, (3, 3, 3), 1, 2, 1, True),    # ragged rows and columns, halo reaching 2 past
+    (64, 128, 17, 45, 3, 2, (3, 3, 3), 1, 2, 1, True),   # 2 channel groups, 2 channel blocks, 1-row tail
+    (96, 192, 33, 64, 4, 2, (3, 3, 3), 1, 2, 1, False),  # 3 groups, 3 blocks, no bias
+    (32, 64, 16, 32, 1, 0, (3, 3, 3), 1, 2, 2, True),    # batch 2, one active tap
+    (32, 64, 18, 40, 4, 2, (3, 3, 3), 2, 4, 1, True),    # temporal dilation 2 as well
+    (32, 64, 16, 40, 3, 1, (2, 3, 3), 1, 1, 1, True),    # k_t = 2
+    (64, 64, 16, 33, 2, 0, (3, 3, 3), 1, 4, 1, True),    # bias-only output frames
+    (32, 64, 3, 5, 2, 2, (3, 3, 3), 1, 2, 1, True),      # map smaller than the dilated window
+]
+
+
+@pytest.mark.parametrize("case", DILATED, ids=[str(i) for i in range(len(DILATED))])
+def test_dilated_group_staged_full_compare(cuda_device, case):
+    cin, cout, h, w_, tx, tc, k, dt, p_base, n, bias = case
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
+                                   seed=synth.SEED_BASE + 420 + DILATED.index(case), has_bias=bias)
+    y, co, plan = run(x, c, w, b, k=k, pad=(2, 2), dt=dt, p_base=p_base, sdil=(2, 2))
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == "bf16_s3d2_n64_p16x32_g32"
+    ref = _oracle(x, c, w, b, k=k, pad=(2, 2), dt=dt, p_base=p_base, sdil=(2, 2))
+    assert tuple(y.shape) == ref.shape
+    assert_bf16_close(y, ref, "dilated %s" % (case,))
     z = x if c is None else torch.cat([c, x], 1)
     assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
 
@@ -665,7 +698,7 @@ def test_general_spatial_full_size_sampled(cuda_device, sig):
                                    seed=synth.SEED_BASE + 395)
     y, _, plan = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"])
     torch.cuda.synchronize()
-    assert plan.info["kernel_name"] == _gen_name(s["cout"])
+    assert plan.info["kernel_name"] == _gen_name(s["cout"], s["cin"], s["k"], s["pad"], s["sst"], s["sdil"])
     assert bool(torch.isfinite(y).all())
     pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=39)
     ref = _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], sst=s["sst"], sdil=s["sdil"], points=pts)

@@ -21,7 +21,7 @@ DEV = "cuda:0"
 
 VARIANTS = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32",
             "bf16_s3_few_p16x128", "bf16_s3_few_p7x128", "bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32",
-            "bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32"]
+            "bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32", "bf16_s3d2_n64_p16x32_g32"]
 
 
 def _cases(count, seed):
@@ -49,7 +49,7 @@ def _cases(count, seed):
                 ks = int(rng.choice([1, 3, 5]))
                 k = (kt, ks, int(rng.choice([1, 3])))
                 sst = (int(rng.choice([1, 2])), int(rng.choice([1, 2])))
-                sdil = (int(rng.choice([1, 2])), 1)
+                sdil = (int(rng.choice([1, 2])), 1) if ks != 3 or rng.integers(0, 2) else (2, 2)
                 # at most the kernel's reach: an output row or column that
                 # sees only padding holds exactly the bias
                 pad = (int(rng.integers(0, sdil[0] * (k[1] - 1) + 1)), int(rng.integers(0, sdil[1] * (k[2] - 1) + 1)))

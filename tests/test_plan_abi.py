@@ -204,10 +204,16 @@ def test_general_spatial_parameters_take_the_gather_kernel(kw):
         with pytest.raises(cc3d.CC3DError):
             cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=192, h=20, w=36, **kw), name)
     # C_out a multiple of 96: the 96-wide gather tile; it refuses other C_out
-    q = cc3d.causal_conv3d_plan(_desc(c_in=32, c_out=192, h=20, w=36, **kw))
+    # (and 3x3 "same" at dilation 2 has a halo-staged kernel of its own)
+    cin = 32
+    if kw.get("dilation") == (1, 2, 2) and kw.get("padding") == (2, 2):
+        d2 = cc3d.causal_conv3d_plan(_desc(c_in=32, c_out=192, h=20, w=36, **kw))
+        assert d2.info["kernel_name"] == "bf16_s3d2_n64_p16x32_g32" and d2.info["block_n"] == 64
+        cin = 48  # C_in % 32 != 0: not the dilated kernel
+    q = cc3d.causal_conv3d_plan(_desc(c_in=cin, c_out=192, h=20, w=36, **kw))
     assert q.info["kernel_name"] == "bf16_gen_n96_p8x32" and q.info["block_n"] == 96 and q.info["tiles"] % 2 == 0
     with pytest.raises(cc3d.CC3DError):
-        cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=40, h=20, w=36, **kw), "bf16_gen_n96_p8x32")
+        cc3d.causal_conv3d_plan_variant(_desc(c_in=cin, c_out=40, h=20, w=36, **kw), "bf16_gen_n96_p8x32")
 
 
 def test_head_patch_height_rule():
@@ -412,6 +418,11 @@ def test_plan_variant_pins_the_kernel():
     ("bf16_s3_n64_p24x32_g32", dict(c_in=32, c_out=96)),      # C_out % 64 != 0
     ("bf16_s3_n64_p24x32_g32", dict(c_in=48, c_out=64)),      # C_in % 32 != 0
     ("bf16_s3_n64_p24x32_g32", dict(c_in=32, c_out=64, k=(3, 1, 1), padding=(0, 0))),  # not 3x3
+    ("bf16_s3d2_n64_p16x32_g32", dict(c_in=32, c_out=64)),   # dilation 1
+    ("bf16_s3d2_n64_p16x32_g32", dict(c_in=32, c_out=96, dilation=(1, 2, 2), padding=(2, 2))),  # C_out % 64
+    ("bf16_s3d2_n64_p16x32_g32", dict(c_in=48, c_out=64, dilation=(1, 2, 2), padding=(2, 2))),  # C_in % 32
+    ("bf16_s3d2_n64_p16x32_g32", dict(c_in=32, c_out=64, dilation=(1, 2, 2), padding=(1, 1))),  # not "same"
+    ("bf16_s3d2_n64_p16x32_g32", dict(c_in=32, c_out=64, dilation=(1, 2, 2), padding=(2, 2), stride=(1, 2, 2))),
     ("bf16_s3_n96_p8x32_x2", dict(c_in=32, c_out=40)),
     ("bf16_s1_n32_p8x32", dict(c_in=32, c_out=32)),           # 1x1 variant on a 3x3 call
     ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, k=(3, 1, 1), padding=(0, 0))),
