@@ -608,11 +608,22 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
 // DD is the spatial dilation of the 3x3 taps (1, or 2 for the dilated
 // "same" conv, padding 2): the halo grows by DD on every side, and column
 // tap c, row tap ta read halo column l + c*DD, halo row r + ta*DD.
-template <int BN, int TH, int WM, int DD = 1>
+//
+// SS is the spatial stride (1, or 2 with padding 1 and no dilation, the
+// encoder's downsampling conv).  At stride 2 output pixel (r, l) of the tile
+// reads input row 2r + ta and input column 2l + c of the halo, which spans
+// 2*TH + 1 rows by 2*32 + 1 columns.  Each halo row is stored with its even
+// input columns first (33 of them), then its odd ones (32): column tap c then
+// reads the 32 consecutive stored pixels from l + c/2 (c even) or 33 + l
+// (c = 1), the same conflict-free fragment pattern as at stride 1.
+template <int BN, int TH, int WM, int DD = 1, int SS = 1>
 __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4, WM / 4))) void conv_bf16_g32(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using WT = WTile<BN, 3, 16>;
-  constexpr int TW = 32, HP = TH + 2 * DD, WP = TW + 2 * DD, S = 9;
+  static_assert(SS == 1 || (SS == 2 && DD == 1), "stride 2 runs undilated");
+  constexpr int TW = 32, S = 9;
+  constexpr int HP = SS * (TH - 1) + 2 * DD + 1;             // halo rows
+  constexpr int WP = SS == 1 ? TW + 2 * DD : 2 * TW + 1;     // halo columns
   constexpr int PZ = 4;                          // 16-byte pieces per halo pixel
   constexpr int ZCH = HP * WP * PZ;
   constexpr int ZSLOTS = (ZCH + 63) / 64 * 64;
@@ -620,7 +631,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   constexpr int WSLOTS = WT::WSLOTS;
   constexpr int ZIT = (ZSLOTS + NT - 1) / NT, WIT = (WSLOTS + NT - 1) / NT;
   constexpr int RW = TH / WM, CW = BN / 32;
-  constexpr int ZR = RW + 2 * DD;                // halo rows a wave reads per column tap
+  constexpr int ZR = SS * (RW - 1) + 2 * DD + 1; // halo rows a wave reads per column tap
   constexpr int EROW = CW * 32 * 2 + 16;         // epilogue LDS bytes per pixel (padded)
   static_assert((WM == 4 || WM == 8) && TH % WM == 0 && BN % 32 == 0, "wave tiling");
   // epilogue staging: waves 0-3 use the idle weight buffer, waves 4-7 the idle halo buffer
@@ -743,7 +754,10 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
       if (id < ZCH) {
         const int pix = id / PZ;
         const int q = (id % PZ) ^ swz<PZ>(pix);
-        const int y = c.y0 - DD + pix / WP, x = c.x0 - DD + pix % WP;
+        const int col = pix % WP;
+        // input column of the stored pixel: at stride 2 the even ones, then the odd
+        const int u = SS == 1 ? col : col <= TW ? 2 * col : 2 * (col - TW - 1) + 1;
+        const int y = SS * c.y0 - DD + pix / WP, x = SS * c.x0 - DD + u;
         if (y >= 0 && y < a.h && x >= 0 && x < a.wd) off = ((y * a.wd + x) * a.cin + q * 8) * 2;
       }
       zoff[it] = off;
@@ -793,15 +807,16 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   };
 
   // One sub-stage = 9 steps, one per spatial tap (ta, tcol), grouped by
-  // column tap: the RW+2 halo rows read for a column tap serve its 3 row
-  // taps.  Fragments of step i+1 are read before step i's MFMAs issue.
+  // column tap: the halo rows read for a column tap serve its 3 row taps.
+  // Fragments of step i+1 are read before step i's MFMAs issue.
   // Sub-stage J multiplies the 16 channels [16J, 16J+16) of the group.
   constexpr int NSTEP = 9;
   auto read_z = [&](const uint4* zb, int tcol, int J, bf16x8_t* zf) {
     const int q = 2 * J + g;
+    const int col = SS == 1 ? tcol * DD : (tcol & 1) ? TW + 1 : tcol >> 1;
 #pragma unroll
     for (int r = 0; r < ZR; ++r) {
-      const int pix = (wave * RW + r) * WP + l32 + tcol * DD;
+      const int pix = (wave * RW * SS + r) * WP + l32 + col;
       zf[r] = __builtin_bit_cast(bf16x8_t, zb[pix * PZ + (q ^ swz<PZ>(pix))]);
     }
   };
@@ -835,7 +850,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
       for (int c = 0; c < CW; ++c)
 #pragma unroll
         for (int r = 0; r < RW; ++r)
-          acc[c][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i & 1][c], zf[zsel][r + ta * DD], acc[c][r], 0, 0, 0);
+          acc[c][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i & 1][c], zf[zsel][SS * r + ta * DD], acc[c][r], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < NL; ++k)
@@ -1782,9 +1797,9 @@ template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
 const void* mfma_kernel() {
   return reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF, OCC>);
 }
-template <int BN, int TH, int WM, int DD>
+template <int BN, int TH, int WM, int DD, int SS>
 const void* g32_kernel() {
-  return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM, DD>);
+  return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM, DD, SS>);
 }
 template <int COUT, int NCH, bool CO>
 const void* few_kernel() {
@@ -1840,14 +1855,14 @@ hipError_t launch_gen(ConvArgs a, int64_t tiles, bool pack, bool conv, hipStream
 }
 
 // The group-staged 3x3 kernel (16-channel weight sub-stages, same packing).
-template <int BN, int TH, int WM, int DD = 1>
+template <int BN, int TH, int WM, int DD = 1, int SS = 1>
 hipError_t launch_g32(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
   if (pack) {
     const hipError_t e = pack_bf16<BN, 3, 16>(a, s);
     if (e != hipSuccess) return e;
   }
   if (!conv) return hipSuccess;
-  return launch_persistent<&g32_kernel<BN, TH, WM, DD>>(a, tiles, cus, WM * 64, s);
+  return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS>>(a, tiles, cus, WM * 64, s);
 }
 
 }  // namespace
@@ -1985,7 +2000,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     a.px_offset = px->offset;
   }
   if ((in.kernel_id == CC3D_K_BF16_S3_N96_G32W8 || in.kernel_id == CC3D_K_BF16_S3_N64_G32W8 ||
-       in.kernel_id == CC3D_K_BF16_S3D2_N64_G32W8) &&
+       in.kernel_id == CC3D_K_BF16_S3D2_N64_G32W8 || in.kernel_id == CC3D_K_BF16_S3S2_N96_G32W4) &&
       !frame_intervals(plan, a))
     return invalid();
 
@@ -2040,6 +2055,9 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
       break;
     case CC3D_K_BF16_S3D2_N64_G32W8:
       e = launch_g32<64, 16, 8, 2>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
+      break;
+    case CC3D_K_BF16_S3S2_N96_G32W4:
+      e = launch_g32<96, 4, 4, 1, 2>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
       break;
     case CC3D_K_BF16_GEN_N64: e = launch_gen<64>(a, in.tiles, pack, runs, s); break;
     case CC3D_K_BF16_GEN_N96: e = launch_gen<96>(a, in.tiles, pack, runs, s); break;
@@ -2129,6 +2147,7 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
                                             "bf16_s1_n192_p8x32",
                                             "bf16_s1_n32_p8x32",
                                             "bf16_s3d2_n64_p16x32_g32",
+                                            "bf16_s3s2_n96_p4x32_g32",
                                             "bf16_gen_n96_p8x32",
                                             "bf16_gen_n64_p8x32"};
   if (!out_plan) return invalid();

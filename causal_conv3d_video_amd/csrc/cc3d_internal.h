@@ -25,6 +25,8 @@ enum cc3d_kernel_id : int32_t {
   CC3D_K_BF16_GEN_N96 = 14,  // as CC3D_K_BF16_GEN_N64 with 96 output channels per tile
   CC3D_K_BF16_S3D2_N64_G32W8 = 15, // the group-staged kernel on 3x3 taps at spatial dilation 2,
                                    // padding 2: 512 px (16x32) x 64 channels
+  CC3D_K_BF16_S3S2_N96_G32W4 = 16, // the group-staged kernel on 3x3 taps at spatial stride 2,
+                                   // padding 1: 128 output px (4x32) x 96 channels, 4 waves
 };
 
 // Scheduler counters of the group-staged kernel, kept after the packed

@@ -83,6 +83,13 @@ bool dilated_same(const cc3d_desc_t& d) {
          d.p_w == 2;
 }
 
+// 3x3 taps at spatial stride 2 with padding 1, no spatial dilation (the
+// encoder's downsampling conv): the strided group-staged kernel's envelope.
+bool strided_3x3(const cc3d_desc_t& d) {
+  return d.k_h == 3 && d.k_w == 3 && d.s_h == 2 && d.s_w == 2 && d.d_h == 1 && d.d_w == 1 && d.p_h == 1 &&
+         d.p_w == 1;
+}
+
 bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   const std::string n(name);
   if (n == "bf16_gen_n64_p8x32") {  // any spatial parameters
@@ -96,6 +103,10 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   if (n == "bf16_s3d2_n64_p16x32_g32") {  // 3x3 "same" at spatial dilation 2
     *v = {CC3D_K_BF16_S3D2_N64_G32W8, 16, 32, 64, 16, "bf16_s3d2_n64_p16x32_g32"};
     return dilated_same(d) && d.c_out % 64 == 0 && d.c_in % 32 == 0;
+  }
+  if (n == "bf16_s3s2_n96_p4x32_g32") {  // 3x3 at spatial stride 2, padding 1
+    *v = {CC3D_K_BF16_S3S2_N96_G32W4, 4, 32, 96, 16, "bf16_s3s2_n96_p4x32_g32"};
+    return strided_3x3(d) && d.c_out % 96 == 0 && d.c_in % 32 == 0;
   }
   if (!same_spatial(d)) return false;
   const bool s3 = d.k_h == 3;
@@ -145,6 +156,7 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
 const char* default_variant(const cc3d_desc_t& d) {
   if (!same_spatial(d)) {
     if (dilated_same(d) && d.c_out % 64 == 0 && d.c_in % 32 == 0) return "bf16_s3d2_n64_p16x32_g32";
+    if (strided_3x3(d) && d.c_out % 96 == 0 && d.c_in % 32 == 0) return "bf16_s3s2_n96_p4x32_g32";
     return d.c_out % 96 == 0 ? "bf16_gen_n96_p8x32" : "bf16_gen_n64_p8x32";
   }
   if (d.k_h == 3) {

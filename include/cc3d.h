@@ -188,6 +188,10 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *   "bf16_s3d2_n64_p16x32_g32" 3x3 at spatial dilation 2, padding 2, unit
  *                              spatial stride, C_out % 64 == 0, C_in % 32 == 0
  *                              (the default there): the halo-staged kernel
+ *   "bf16_s3s2_n96_p4x32_g32" 3x3 at spatial stride 2, padding 1, spatial
+ *                              dilation 1, C_out % 96 == 0, C_in % 32 == 0
+ *                              (the default there): the halo-staged kernel
+ *                              on 4x32-output-pixel tiles
  *   "f32_direct"              fp32
  * Every variant computes the same operation; bf16 results of different
  * variants may differ in the last bit (fp32 accumulation order).

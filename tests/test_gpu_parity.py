@@ -632,6 +632,9 @@ def _gen_name(cout, cin=32, k=(3, 3, 3), pad=(1, 1), sst=(1, 1), sdil=(1, 1)):
     if (k[1:] == (3, 3) and sst == (1, 1) and sdil == (2, 2) and tuple(pad) == (2, 2) and cout % 64 == 0
             and cin % 32 == 0):
         return "bf16_s3d2_n64_p16x32_g32"
+    if (k[1:] == (3, 3) and sst == (2, 2) and sdil == (1, 1) and tuple(pad) == (1, 1) and cout % 96 == 0
+            and cin % 32 == 0):
+        return "bf16_s3s2_n96_p4x32_g32"
     return "bf16_gen_n96_p8x32" if cout % 96 == 0 else "bf16_gen_n64_p8x32"
 
 
@@ -676,6 +679,52 @@ def test_dilated_group_staged_full_compare(cuda_device, case):
     assert_bf16_close(y, ref, "dilated %s" % (case,))
     z = x if c is None else torch.cat([c, x], 1)
     assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
+
+
+# The group-staged kernel at spatial stride 2 (3x3, padding 1): (C_in, C_out,
+# H, W, T_x, T_cache, k, d_t, s_t, p_base, N, bias), full compare.  Output
+# tiles are 4 rows x 32 columns of the half-size map.
+STRIDED_3X3 = [
+    (32, 96, 21, 37, 2, 2, (3, 3, 3), 1, 1, 2, 1, True),    # odd sizes: ragged rows and columns
+    (64, 192, 17, 70, 3, 2, (3, 3, 3), 1, 1, 2, 1, True),   # 2 channel groups, 2 channel blocks
+    (96, 96, 33, 130, 2, 2, (3, 3, 3), 1, 1, 2, 1, False),  # 3 groups, 1-row and 1-column tails, no bias
+    (32, 96, 16, 64, 1, 0, (3, 3, 3), 1, 1, 2, 2, True),    # exact tiles, batch 2, one active tap
+    (32, 192, 18, 40, 4, 2, (3, 3, 3), 2, 1, 4, 1, True),   # temporal dilation 2
+    (32, 96, 14, 44, 4, 2, (3, 3, 3), 1, 2, 2, 1, True),    # temporal stride 2
+    (32, 96, 16, 40, 3, 1, (2, 3, 3), 1, 1, 1, 1, True),    # k_t = 2
+    (64, 96, 16, 33, 2, 0, (3, 3, 3), 1, 1, 4, 1, True),    # bias-only output frames
+    (32, 96, 3, 5, 2, 2, (3, 3, 3), 1, 1, 2, 1, True),      # map smaller than one tile
+    (32, 96, 1, 1, 2, 2, (3, 3, 3), 1, 1, 2, 1, True),      # a single pixel
+]
+
+
+@pytest.mark.parametrize("case", STRIDED_3X3, ids=[str(i) for i in range(len(STRIDED_3X3))])
+def test_strided_group_staged_full_compare(cuda_device, case):
+    cin, cout, h, w_, tx, tc, k, dt, st, p_base, n, bias = case
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
+                                   seed=synth.SEED_BASE + 440 + STRIDED_3X3.index(case), has_bias=bias)
+    y, co, plan = run(x, c, w, b, k=k, dt=dt, st=st, p_base=p_base, sst=(2, 2))
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == "bf16_s3s2_n96_p4x32_g32"
+    ref = _oracle(x, c, w, b, k=k, dt=dt, st=st, p_base=p_base, sst=(2, 2))
+    assert tuple(y.shape) == ref.shape
+    assert_bf16_close(y, ref, "strided %s" % (case,))
+    z = x if c is None else torch.cat([c, x], 1)
+    assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
+
+
+@pytest.mark.parametrize("variant", ["bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32"])
+@pytest.mark.parametrize("case", STRIDED_3X3[:3], ids=[str(i) for i in range(3)])
+def test_gather_kernel_on_strided_convs_full_compare(cuda_device, case, variant):
+    """The gather kernel pinned on stride-2 shapes (the strided halo-staged
+    kernel is their default), against the oracle."""
+    cin, cout, h, w_, tx, tc, k, dt, st, p_base, n, bias = case
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
+                                   seed=synth.SEED_BASE + 440 + STRIDED_3X3.index(case), has_bias=bias)
+    y, _, plan = run(x, c, w, b, k=k, dt=dt, st=st, p_base=p_base, sst=(2, 2), variant=variant)
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == variant
+    assert_bf16_close(y, _oracle(x, c, w, b, k=k, dt=dt, st=st, p_base=p_base, sst=(2, 2)), "gather strided")
 
 
 @pytest.mark.parametrize("variant", ["bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32"])

@@ -204,12 +204,18 @@ def test_general_spatial_parameters_take_the_gather_kernel(kw):
         with pytest.raises(cc3d.CC3DError):
             cc3d.causal_conv3d_plan_variant(_desc(c_in=32, c_out=192, h=20, w=36, **kw), name)
     # C_out a multiple of 96: the 96-wide gather tile; it refuses other C_out
-    # (and 3x3 "same" at dilation 2 has a halo-staged kernel of its own)
+    # (3x3 "same" at dilation 2, and 3x3 at stride 2 with padding 1, have
+    # halo-staged kernels of their own)
     cin = 32
     if kw.get("dilation") == (1, 2, 2) and kw.get("padding") == (2, 2):
         d2 = cc3d.causal_conv3d_plan(_desc(c_in=32, c_out=192, h=20, w=36, **kw))
         assert d2.info["kernel_name"] == "bf16_s3d2_n64_p16x32_g32" and d2.info["block_n"] == 64
         cin = 48  # C_in % 32 != 0: not the dilated kernel
+    if kw.get("stride", (1, 1, 1))[1:] == (2, 2) and kw.get("padding", (1, 1)) == (1, 1):
+        s2 = cc3d.causal_conv3d_plan(_desc(c_in=32, c_out=192, h=20, w=36, **kw))
+        assert s2.info["kernel_name"] == "bf16_s3s2_n96_p4x32_g32" and s2.info["block_n"] == 96
+        assert s2.info["block_m"] == 128 and s2.info["h_out"] == 10 and s2.info["w_out"] == 18
+        cin = 48  # C_in % 32 != 0: not the strided kernel
     q = cc3d.causal_conv3d_plan(_desc(c_in=cin, c_out=192, h=20, w=36, **kw))
     assert q.info["kernel_name"] == "bf16_gen_n96_p8x32" and q.info["block_n"] == 96 and q.info["tiles"] % 2 == 0
     with pytest.raises(cc3d.CC3DError):
@@ -423,6 +429,13 @@ def test_plan_variant_pins_the_kernel():
     ("bf16_s3d2_n64_p16x32_g32", dict(c_in=48, c_out=64, dilation=(1, 2, 2), padding=(2, 2))),  # C_in % 32
     ("bf16_s3d2_n64_p16x32_g32", dict(c_in=32, c_out=64, dilation=(1, 2, 2), padding=(1, 1))),  # not "same"
     ("bf16_s3d2_n64_p16x32_g32", dict(c_in=32, c_out=64, dilation=(1, 2, 2), padding=(2, 2), stride=(1, 2, 2))),
+    ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=96)),     # stride 1
+    ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=64, stride=(1, 2, 2))),   # C_out % 96
+    ("bf16_s3s2_n96_p4x32_g32", dict(c_in=48, c_out=96, stride=(1, 2, 2))),   # C_in % 32
+    ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=96, stride=(1, 2, 2), padding=(0, 0))),   # padding 0
+    ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=96, stride=(1, 2, 1))),   # stride 2 in one axis
+    ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=96, stride=(1, 2, 2), dilation=(1, 2, 2), padding=(2, 2))),
+    ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=96, k=(3, 5, 5), stride=(1, 2, 2), padding=(2, 2))),
     ("bf16_s3_n96_p8x32_x2", dict(c_in=32, c_out=40)),
     ("bf16_s1_n32_p8x32", dict(c_in=32, c_out=32)),           # 1x1 variant on a 3x3 call
     ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, k=(3, 1, 1), padding=(0, 0))),
