@@ -2000,7 +2000,8 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     a.px_offset = px->offset;
   }
   if ((in.kernel_id == CC3D_K_BF16_S3_N96_G32W8 || in.kernel_id == CC3D_K_BF16_S3_N64_G32W8 ||
-       in.kernel_id == CC3D_K_BF16_S3D2_N64_G32W8 || in.kernel_id == CC3D_K_BF16_S3S2_N96_G32W4) &&
+       in.kernel_id == CC3D_K_BF16_S3D2_N64_G32W8 || in.kernel_id == CC3D_K_BF16_S3S2_N96_G32W4 ||
+       in.kernel_id == CC3D_K_BF16_S3S2_N64_G32W4) &&
       !frame_intervals(plan, a))
     return invalid();
 
@@ -2058,6 +2059,9 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
       break;
     case CC3D_K_BF16_S3S2_N96_G32W4:
       e = launch_g32<96, 4, 4, 1, 2>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
+      break;
+    case CC3D_K_BF16_S3S2_N64_G32W4:
+      e = launch_g32<64, 4, 4, 1, 2>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
       break;
     case CC3D_K_BF16_GEN_N64: e = launch_gen<64>(a, in.tiles, pack, runs, s); break;
     case CC3D_K_BF16_GEN_N96: e = launch_gen<96>(a, in.tiles, pack, runs, s); break;
@@ -2148,6 +2152,7 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
                                             "bf16_s1_n32_p8x32",
                                             "bf16_s3d2_n64_p16x32_g32",
                                             "bf16_s3s2_n96_p4x32_g32",
+                                            "bf16_s3s2_n64_p4x32_g32",
                                             "bf16_gen_n96_p8x32",
                                             "bf16_gen_n64_p8x32"};
   if (!out_plan) return invalid();

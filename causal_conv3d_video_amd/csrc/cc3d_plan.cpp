@@ -108,6 +108,10 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
     *v = {CC3D_K_BF16_S3S2_N96_G32W4, 4, 32, 96, 16, "bf16_s3s2_n96_p4x32_g32"};
     return strided_3x3(d) && d.c_out % 96 == 0 && d.c_in % 32 == 0;
   }
+  if (n == "bf16_s3s2_n64_p4x32_g32") {  // the same with 64 output channels per tile
+    *v = {CC3D_K_BF16_S3S2_N64_G32W4, 4, 32, 64, 16, "bf16_s3s2_n64_p4x32_g32"};
+    return strided_3x3(d) && d.c_out % 64 == 0 && d.c_in % 32 == 0;
+  }
   if (!same_spatial(d)) return false;
   const bool s3 = d.k_h == 3;
   const int cb = d.c_in % 64 == 0 ? 64 : d.c_in % 32 == 0 ? 32 : 16;
@@ -156,7 +160,9 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
 const char* default_variant(const cc3d_desc_t& d) {
   if (!same_spatial(d)) {
     if (dilated_same(d) && d.c_out % 64 == 0 && d.c_in % 32 == 0) return "bf16_s3d2_n64_p16x32_g32";
+    // (the 96-wide tile has 3 MFMAs per spatial tap and wave, the 64-wide one 2)
     if (strided_3x3(d) && d.c_out % 96 == 0 && d.c_in % 32 == 0) return "bf16_s3s2_n96_p4x32_g32";
+    if (strided_3x3(d) && d.c_out % 64 == 0 && d.c_in % 32 == 0) return "bf16_s3s2_n64_p4x32_g32";
     return d.c_out % 96 == 0 ? "bf16_gen_n96_p8x32" : "bf16_gen_n64_p8x32";
   }
   if (d.k_h == 3) {

@@ -192,6 +192,8 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *                              dilation 1, C_out % 96 == 0, C_in % 32 == 0
  *                              (the default there): the halo-staged kernel
  *                              on 4x32-output-pixel tiles
+ *   "bf16_s3s2_n64_p4x32_g32" the same with C_out % 64 == 0 (the default
+ *                              there where C_out % 96 != 0)
  *   "f32_direct"              fp32
  * Every variant computes the same operation; bf16 results of different
  * variants may differ in the last bit (fp32 accumulation order).

@@ -635,6 +635,9 @@ def _gen_name(cout, cin=32, k=(3, 3, 3), pad=(1, 1), sst=(1, 1), sdil=(1, 1)):
     if (k[1:] == (3, 3) and sst == (2, 2) and sdil == (1, 1) and tuple(pad) == (1, 1) and cout % 96 == 0
             and cin % 32 == 0):
         return "bf16_s3s2_n96_p4x32_g32"
+    if (k[1:] == (3, 3) and sst == (2, 2) and sdil == (1, 1) and tuple(pad) == (1, 1) and cout % 64 == 0
+            and cin % 32 == 0):
+        return "bf16_s3s2_n64_p4x32_g32"
     return "bf16_gen_n96_p8x32" if cout % 96 == 0 else "bf16_gen_n64_p8x32"
 
 
@@ -695,6 +698,8 @@ STRIDED_3X3 = [
     (64, 96, 16, 33, 2, 0, (3, 3, 3), 1, 1, 4, 1, True),    # bias-only output frames
     (32, 96, 3, 5, 2, 2, (3, 3, 3), 1, 1, 2, 1, True),      # map smaller than one tile
     (32, 96, 1, 1, 2, 2, (3, 3, 3), 1, 1, 2, 1, True),      # a single pixel
+    (64, 128, 19, 70, 2, 2, (3, 3, 3), 1, 1, 2, 1, True),   # 64-wide tile: 2 blocks, ragged
+    (32, 64, 16, 64, 3, 1, (3, 3, 3), 2, 1, 3, 2, False),   # 64-wide tile: batch 2, d_t 2, no bias
 ]
 
 
@@ -705,7 +710,7 @@ def test_strided_group_staged_full_compare(cuda_device, case):
                                    seed=synth.SEED_BASE + 440 + STRIDED_3X3.index(case), has_bias=bias)
     y, co, plan = run(x, c, w, b, k=k, dt=dt, st=st, p_base=p_base, sst=(2, 2))
     torch.cuda.synchronize()
-    assert plan.info["kernel_name"] == "bf16_s3s2_n96_p4x32_g32"
+    assert plan.info["kernel_name"] == ("bf16_s3s2_n96_p4x32_g32" if cout % 96 == 0 else "bf16_s3s2_n64_p4x32_g32")
     ref = _oracle(x, c, w, b, k=k, dt=dt, st=st, p_base=p_base, sst=(2, 2))
     assert tuple(y.shape) == ref.shape
     assert_bf16_close(y, ref, "strided %s" % (case,))
@@ -713,11 +718,13 @@ def test_strided_group_staged_full_compare(cuda_device, case):
     assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
 
 
-@pytest.mark.parametrize("variant", ["bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32"])
-@pytest.mark.parametrize("case", STRIDED_3X3[:3], ids=[str(i) for i in range(3)])
+@pytest.mark.parametrize("case,variant", [(STRIDED_3X3[i], v) for i in range(3)
+                                          for v in ["bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32"]] +
+                         [(STRIDED_3X3[1], "bf16_s3s2_n64_p4x32_g32")],
+                         ids=["%d-%s" % (i, v) for i in range(3) for v in ["gen64", "gen96"]] + ["1-s3s2_n64"])
 def test_gather_kernel_on_strided_convs_full_compare(cuda_device, case, variant):
-    """The gather kernel pinned on stride-2 shapes (the strided halo-staged
-    kernel is their default), against the oracle."""
+    """The gather kernel, and the 64-wide strided tile, pinned on stride-2
+    shapes whose default is the 96-wide strided tile, against the oracle."""
     cin, cout, h, w_, tx, tc, k, dt, st, p_base, n, bias = case
     x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
                                    seed=synth.SEED_BASE + 440 + STRIDED_3X3.index(case), has_bias=bias)

@@ -21,7 +21,8 @@ DEV = "cuda:0"
 
 VARIANTS = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32",
             "bf16_s3_few_p16x128", "bf16_s3_few_p7x128", "bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32",
-            "bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32", "bf16_s3d2_n64_p16x32_g32", "bf16_s3s2_n96_p4x32_g32"]
+            "bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32", "bf16_s3d2_n64_p16x32_g32", "bf16_s3s2_n96_p4x32_g32",
+            "bf16_s3s2_n64_p4x32_g32"]
 
 
 def _cases(count, seed):

@@ -436,6 +436,9 @@ def test_plan_variant_pins_the_kernel():
     ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=96, stride=(1, 2, 1))),   # stride 2 in one axis
     ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=96, stride=(1, 2, 2), dilation=(1, 2, 2), padding=(2, 2))),
     ("bf16_s3s2_n96_p4x32_g32", dict(c_in=32, c_out=96, k=(3, 5, 5), stride=(1, 2, 2), padding=(2, 2))),
+    ("bf16_s3s2_n64_p4x32_g32", dict(c_in=32, c_out=96, stride=(1, 2, 2))),   # C_out % 64
+    ("bf16_s3s2_n64_p4x32_g32", dict(c_in=48, c_out=64, stride=(1, 2, 2))),   # C_in % 32
+    ("bf16_s3s2_n64_p4x32_g32", dict(c_in=32, c_out=64)),     # stride 1
     ("bf16_s3_n96_p8x32_x2", dict(c_in=32, c_out=40)),
     ("bf16_s1_n32_p8x32", dict(c_in=32, c_out=32)),           # 1x1 variant on a 3x3 call
     ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, k=(3, 1, 1), padding=(0, 0))),
