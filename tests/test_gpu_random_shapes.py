@@ -69,7 +69,35 @@ def _cases(count, seed):
     return out
 
 
-CASES = _cases(48, 20261203 + 777)
+def _halo_staged_spatial_cases(count, seed):
+    """3x3 convs at spatial stride 2 (padding 1) or spatial dilation 2
+    (padding 2): the envelopes of the strided and dilated group-staged
+    kernels (which the draws above rarely reach), with channel counts they
+    accept and ones they refuse."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        strided = bool(rng.integers(0, 2))
+        cin = int(rng.choice([32, 64, 96, 48]))
+        cout = int(rng.choice([64, 96, 128, 192, 40]))
+        n = int(rng.choice([1, 1, 2]))
+        h, w = int(rng.integers(1, 41)), int(rng.integers(1, 101))
+        tx, tc = int(rng.integers(1, 5)), int(rng.integers(0, 4))
+        kt = int(rng.choice([2, 3, 3]))
+        dt, st = int(rng.choice([1, 1, 2])), int(rng.choice([1, 1, 2]))
+        k = (kt, 3, 3)
+        sst, sdil, pad = ((2, 2), (1, 1), (1, 1)) if strided else ((1, 1), (2, 2), (2, 2))
+        p_base = dt * (kt - 1)
+        z = tx + tc
+        t_out = (z + p_base - tc - dt * (kt - 1) - 1) // st + 1
+        if t_out < 1:
+            continue
+        bias = bool(rng.integers(0, 4) > 0)
+        out.append((cin, cout, h, w, tx, tc, k, pad, sst, sdil, st, dt, p_base, n, bias))
+    return out
+
+
+CASES = _cases(48, 20261203 + 777) + _halo_staged_spatial_cases(12, 20261203 + 778)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
