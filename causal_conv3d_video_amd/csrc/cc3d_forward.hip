@@ -15,12 +15,14 @@
 // The kernels (all channels-last, fp32 accumulation, bias added once in
 // fp32 and rounded to nearest even at the end; the launcher picks one per
 // plan, see cc3d_plan.cpp):
-//   * conv_bf16_g32: large 3x3 maps.  One workgroup of 8 waves per compute
-//     unit, persistent, with per-XCD tile counters; a tile is one output
-//     frame x a 16x32 (or 24x32) patch x 96 (or 64) output channels.  The
-//     halo of one (active tap, 32-channel group) is staged once into LDS and
-//     serves 9 spatial taps x 2 sub-stages of 16 channels;
-//     v_mfma_f32_32x32x16_bf16 with the weights as A and the halo pixels as B.
+//   * conv_bf16_g32: large 3x3 maps, also at spatial dilation 2 ("same")
+//     and at spatial stride 2.  One persistent workgroup per compute unit (8
+//     waves; 4 at stride 2) with per-XCD tile counters; a tile is one output
+//     frame x a 16x32 or 24x32 output patch (4x32 at stride 2) x 96 or 64
+//     output channels.  The halo of one (active tap, 32-channel group) is
+//     staged once into LDS and serves 9 spatial taps x 2 sub-stages of 16
+//     channels; v_mfma_f32_32x32x16_bf16 with the weights as A and the halo
+//     pixels as B.
 //   * conv_bf16_mfma: smaller 3x3 maps (two workgroups per compute unit),
 //     other C_out, and the 1x1 / (k_t,1,1) convs.
 //   * conv_bf16_few: C_out <= 5 (the RGB head).  Walks time per patch,
