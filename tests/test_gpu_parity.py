@@ -359,19 +359,21 @@ def test_unread_frames_and_guard_bands_are_never_touched(cuda_device):
     assert_bf16_close(results[0], ref, "poisoned")
 
 
-@pytest.mark.parametrize("cout,variant,tiles", [(96, "bf16_s3_n96_p16x32_g32", 640),
-                                                (128, "bf16_s3_n64_p24x32_g32", 880)])
-def test_group_staged_schedule_writes_every_tile_across_launches(cuda_device, cout, variant, tiles):
+@pytest.mark.parametrize("cout,variant,tiles,sst", [(96, "bf16_s3_n96_p16x32_g32", 640, (1, 1)),
+                                                    (128, "bf16_s3_n64_p24x32_g32", 880, (1, 1)),
+                                                    (96, "bf16_s3s2_n96_p4x32_g32", 640, (2, 2))])
+def test_group_staged_schedule_writes_every_tile_across_launches(cuda_device, cout, variant, tiles, sst):
     """640 (880) tiles on at most 256 workgroups: two fixed tiles each, the
     rest claimed from per-XCD counters (and stolen across XCDs).  Every
     launch takes the next of the plan's 64 counter slots, and the kernel
     leaves its slot zeroed, so 130 launches reuse every slot twice.  The
     output is poisoned with NaN before each launch: every tile must be
     written every time, bitwise equal to the first launch and within
-    tolerance of the oracle."""
+    tolerance of the oracle.  (The strided kernel's 4x32 tiles of the
+    half-size map come to 640 as well.)"""
     import causal_conv3d_video_amd as cc3d
     x, c, w, b = synth.conv_inputs(1, 32, cout, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 90)
-    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant=variant)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant=variant, sst=sst)
     assert plan.info["tiles"] == tiles
     cc3d.causal_conv3d_pack_weights(plan, w)
     first = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=DEV)
@@ -390,7 +392,7 @@ def test_group_staged_schedule_writes_every_tile_across_launches(cuda_device, co
     th, tw = tile_of(plan)
     pts = sample_points(1, plan.info["t_out"], plan.info["h_out"], plan.info["w_out"], 400, seed=90, tile_h=th,
                         tile_w=tw)
-    ref = _oracle(x, c, w, b, points=pts)
+    ref = _oracle(x, c, w, b, points=pts, sst=sst)
     assert_bf16_close(gather(first, pts), ref, "dynamic schedule")
 
 
