@@ -777,7 +777,8 @@ def test_group_staged_schedule_with_single_group_tiles(cuda_device, cout, h, var
 
 
 @pytest.mark.parametrize("cin,cout,variant", [(32, 96, "bf16_s3_n96_p16x32_g32"), (32, 96, "bf16_s3_n96_p8x32_x2"),
-                                               (32, 64, "bf16_s3_n64_p24x32_g32"), (96, 3, "bf16_s3_few_p16x128")])
+                                               (32, 64, "bf16_s3_n64_p24x32_g32"), (96, 3, "bf16_s3_few_p16x128"),
+                                               (32, 96, "bf16_s3s2_n96_p4x32_g32")])
 def test_graph_replays_match_eager(cuda_device, cin, cout, variant):
     """The packed-weights forward (with its cache-out) captured in a HIP
     graph: the group-staged kernel's tile counters are cleared by the kernel
@@ -787,7 +788,8 @@ def test_graph_replays_match_eager(cuda_device, cin, cout, variant):
     them, all equal the eager call bitwise."""
     import causal_conv3d_video_amd as cc3d
     x, c, w, b = synth.conv_inputs(1, cin, cout, 256, 320, 4, 2, device=DEV, seed=synth.SEED_BASE + 97)
-    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant=variant)
+    sst = (2, 2) if "s3s2" in variant else (1, 1)
+    plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1), variant=variant, sst=sst)
     cc3d.causal_conv3d_pack_weights(plan, w)
     ref = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=DEV)
     cc3d.causal_conv3d_forward_packed(plan, x, c, b, ref, None)
