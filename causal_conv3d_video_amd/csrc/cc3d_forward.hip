@@ -17,7 +17,7 @@
 // plan, see cc3d_plan.cpp):
 //   * conv_bf16_g32: large 3x3 maps, also at spatial dilation 2 ("same")
 //     and at spatial stride 2.  One persistent workgroup per compute unit (8
-//     waves; 4 at stride 2) with per-XCD tile counters; a tile is one output
+//     waves; 4 or 8 at stride 2) with per-XCD tile counters; a tile is one output
 //     frame x a 16x32 or 24x32 output patch (4x32 at stride 2) x 96 or 64
 //     output channels.  The halo of one (active tap, 32-channel group) is
 //     staged once into LDS and serves 9 spatial taps x 2 sub-stages of 16
@@ -618,7 +618,14 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
 // input columns first (33 of them), then its odd ones (32): column tap c then
 // reads the 32 consecutive stored pixels from l + c/2 (c even) or 33 + l
 // (c = 1), the same conflict-free fragment pattern as at stride 1.
-template <int BN, int TH, int WM, int DD = 1, int SS = 1>
+//
+// KSP = 2 splits each group's two 16-channel halves between two waves of
+// the same rows (waves w and w + WM/2), so a tile of TH rows runs WM waves
+// with one barrier per group instead of two; the group's two weight halves
+// are staged together (double-buffered: the next group's load during this
+// one), and the waves of the second half add their sums into those of the
+// first through LDS before the epilogue.
+template <int BN, int TH, int WM, int DD = 1, int SS = 1, int KSP = 1>
 __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4, WM / 4))) void conv_bf16_g32(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using WT = WTile<BN, 3, 16>;
@@ -632,13 +639,16 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   constexpr int NW = WM, NT = NW * 64;
   constexpr int WSLOTS = WT::WSLOTS;
   constexpr int ZIT = (ZSLOTS + NT - 1) / NT, WIT = (WSLOTS + NT - 1) / NT;
-  constexpr int RW = TH / WM, CW = BN / 32;
+  constexpr int RW = TH / (WM / KSP), CW = BN / 32;
   constexpr int ZR = SS * (RW - 1) + 2 * DD + 1; // halo rows a wave reads per column tap
   constexpr int EROW = CW * 32 * 2 + 16;         // epilogue LDS bytes per pixel (padded)
-  static_assert((WM == 4 || WM == 8) && TH % WM == 0 && BN % 32 == 0, "wave tiling");
+  static_assert((WM == 4 || WM == 8) && TH % (WM / KSP) == 0 && BN % 32 == 0, "wave tiling");
+  static_assert(KSP == 1 || (KSP == 2 && WM == 8), "channel-half split");
   // epilogue staging: waves 0-3 use the idle weight buffer, waves 4-7 the idle halo buffer
   static_assert(4 * 32 * EROW <= WSLOTS * 16 && (NW - 4) * 32 * EROW <= ZSLOTS * 16, "epilogue staging");
-  static_assert((2 * (ZSLOTS + WSLOTS)) * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
+  static_assert((2 * ZSLOTS + 2 * KSP * WSLOTS) * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
+  // channel-half split: the second half's sums pass through an idle halo buffer
+  static_assert(KSP == 1 || (WM / 2) * CW * RW * 16 * 64 * 4 <= ZSLOTS * 16, "partial sums");
   constexpr auto zcnt = [](int w) {  // halo load instructions of wave w per group
     int n = 0;
     for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
@@ -647,13 +657,17 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   static_assert(zcnt(0) + WIT <= 63, "vmcnt range");
 
   __shared__ uint4 zl[2 * ZSLOTS];
-  __shared__ uint4 wl[2 * WSLOTS];
+  __shared__ uint4 wl[2 * KSP * WSLOTS];
   __shared__ float bias_lds[2][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
+  // row group and channel half of this wave (the row group is the wave
+  // itself unless the halves are split between waves)
+  const int wr = KSP == 1 ? wave : wave & (WM / 2 - 1);
+  const int wj = KSP == 1 ? 0 : wave / (WM / 2);
 
   // Persistent schedule over the tiles of the output frames with an active
   // tap.  Each XCD owns one contiguous range of them (neighbouring tiles
@@ -818,7 +832,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     const int col = SS == 1 ? tcol * DD : (tcol & 1) ? TW + 1 : tcol >> 1;
 #pragma unroll
     for (int r = 0; r < ZR; ++r) {
-      const int pix = (wave * RW * SS + r) * WP + l32 + col;
+      const int pix = (wr * RW * SS + r) * WP + l32 + col;
       zf[r] = __builtin_bit_cast(bf16x8_t, zb[pix * PZ + (q ^ swz<PZ>(pix))]);
     }
   };
@@ -863,14 +877,14 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
 
   // Epilogue: bias added once in fp32 (all of this lane's bias values are
   // read before the first staging write), round to nearest even, staged per
-  // wave through the idle weight buffer W[1] (waves 0-3) or the idle halo
+  // wave through an idle weight buffer (waves 0-3) or the idle halo
   // buffer (waves 4-7) so global stores are whole 16-byte runs of channels.
   // C_out is a multiple of BN here: every channel of the tile exists, and
   // only the pixel column is range-checked.
   constexpr int EPIX = CW * 4;
   constexpr int EIT = (32 * EPIX + 63) / 64;
-  auto epilogue = [&](const Tile& c, int par, int hidle) {
-    unsigned char* eb = wave < 4 ? reinterpret_cast<unsigned char*>(wl + WSLOTS) + wave * 32 * EROW
+  auto epilogue = [&](const Tile& c, int par, int hidle, int widle) {
+    unsigned char* eb = wave < 4 ? reinterpret_cast<unsigned char*>(wl + widle * WSLOTS) + wave * 32 * EROW
                                  : reinterpret_cast<unsigned char*>(zl + hidle * ZSLOTS) + (wave - 4) * 32 * EROW;
     float4 bias[CW][4];
 #pragma unroll
@@ -880,7 +894,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
         bias[q][v4] = *reinterpret_cast<const float4*>(&bias_lds[par][q * 32 + v4 * 8 + g * 4]);
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      const int y = c.y0 + wave * RW + r;
+      const int y = c.y0 + wr * RW + r;
       if (y >= a.ho) continue;
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
@@ -974,90 +988,189 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     asm volatile("" ::: "memory");
   };
 
-  // prologue: the first group's halo and first weight sub-stage
-  int hpar = 0;
-  if (nx_ok) {
-    const unsigned short* fp = halo_src(nt, nx.ti, nx.gz);
-    const unsigned char* wp = wsrc(nt, nx.ti, nx.gz * 2);
+  if constexpr (KSP == 2) {
+    // prologue: the first group's halo and both weight halves (group buffer 0)
+    int wcur = 0;  // weight group buffer of the current group: halves 2*wcur, 2*wcur+1
+    if (nx_ok) {
+      const unsigned short* fp = halo_src(nt, nx.ti, nx.gz);
+      const unsigned char* w0p = wsrc(nt, nx.ti, nx.gz * 2);
+      const unsigned char* w1p = wsrc(nt, nx.ti, nx.gz * 2 + 1);
 #pragma unroll
-    for (int it = 0; it < ZIT; ++it) issue_z(fp, 0, it);
+      for (int it = 0; it < ZIT; ++it) issue_z(fp, 0, it);
 #pragma unroll
-    for (int it = 0; it < WIT; ++it) issue_w(wp, 0, it);
-    nx_advance();
-    vm_drain();
-    barrier();
-  }
-
-  int par = 0;
-  if (ctile >= 0) {
-    Tile ct = decode(ctile);
-    for (;;) {
-      zero_acc();
-      const bool claims = tnext >= 0;  // claim the tile after tnext while this one runs
-      const int ngt = ct.nact * ngrp;  // >= 1: only frames with an active tap have tiles
-      const bool rows_in = ct.y0 + wave * RW < a.ho;  // wave-uniform
-      for (int gi = 0; gi < ngt; ++gi) {
-        // group-major order: the active taps of one 32-channel group run back
-        // to back, so a source frame's group is reused by the output frames of
-        // the neighbouring tiles within a few groups, while it is still in L2
-        const int gz = gi / ct.nact, ti = gi - gz * ct.nact;
-        const uint4* zb = zl + hpar * ZSLOTS;
-        unsigned short bval = 0;
-        if (gi == 0) bval = bias_value(ct);
-        const bool more = nx_ok;
-        // sub-stage 0: load W[1] <- (this group, second half), H[next] <- next group
-        {
-          const unsigned char* wp1 = wsrc(ct, ti, gz * 2 + 1);
-          const unsigned short* fpn = more ? halo_src(nt, nx.ti, nx.gz) : xs;
-          const int hn = __builtin_amdgcn_readfirstlane(hpar ^ 1);
-          compute(zb, wl, rows_in, std::integral_constant<int, 0>{}, std::integral_constant<int, WIT + ZIT>{},
-                  std::integral_constant<int, NSTEP>{}, [&](int k) {
-                    if (k < WIT) issue_w(wp1, 1, k);
-                    else if (more) issue_z(fpn, hn, k - WIT);
-                  });
-        }
-        if (more) wait_halo_in_flight();
-        else vm_drain();
-        if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
-        barrier();
-        // sub-stage 1: load W[0] <- next group, first half.  In the first
-        // group, thread 0 also claims a tile (the atomic's latency hides
-        // behind the sub-stage; the claim is published at its barrier).
-        const int cx = (xcd + steal) & 7;
-        int v = 0;
-        if (gi == 0 && claims && tid == 0) v = claim(cx);
-        {
-          const unsigned char* wpn = more ? wsrc(nt, nx.ti, nx.gz * 2) : wpk;
-          compute(zb, wl + WSLOTS, rows_in, std::integral_constant<int, 1>{}, std::integral_constant<int, WIT>{},
-                  std::integral_constant<int, (NSTEP + 1) / 2>{}, [&](int k) {
-                    if (more) issue_w(wpn, 0, k);
-                  });
-        }
-        asm volatile("" ::: "memory");  // the claim is read only after the sub-stage
-        if (gi == 0 && claims && tid == 0) {
-          int t = claimed(cx, v);
-          while (t < 0 && steal < 7) {
-            ++steal;
-            const int x = (xcd + steal) & 7;
-            t = claimed(x, claim(x));
-          }
-          claim_lds = t;
-        }
-        vm_drain();
-        barrier();
-        if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
-        if (more) nx_advance();
-        hpar ^= 1;
-      }
-      // (the output stores may stay in flight across this barrier)
-      epilogue(ct, par, hpar ^ 1);
+      for (int it = 0; it < WIT; ++it) issue_w(w0p, 0, it);
+#pragma unroll
+      for (int it = 0; it < WIT; ++it) issue_w(w1p, 1, it);
+      nx_advance();
+      vm_drain();
       barrier();
-      par ^= 1;
-      ctile = tnext;
-      tnext = tnn;
-      tnn = -1;
-      if (ctile < 0) break;
-      ct = decode(ctile);
+    }
+    int hpar = 0, par = 0;
+    if (ctile >= 0) {
+      Tile ct = decode(ctile);
+      for (;;) {
+        zero_acc();
+        const bool claims = tnext >= 0;
+        const int ngt = ct.nact * ngrp;
+        const bool rows_in = ct.y0 + wr * RW < a.ho;  // wave-uniform
+        for (int gi = 0; gi < ngt; ++gi) {
+          const uint4* zb = zl + hpar * ZSLOTS;
+          unsigned short bval = 0;
+          if (gi == 0) bval = bias_value(ct);
+          const bool more = nx_ok;
+          // in the first group thread 0 claims a tile (published at the barrier)
+          const int cx = (xcd + steal) & 7;
+          int v = 0;
+          if (gi == 0 && claims && tid == 0) v = claim(cx);
+          {
+            // load the next group's weight halves and halo into the free buffers
+            const unsigned char* wn0 = more ? wsrc(nt, nx.ti, nx.gz * 2) : wpk;
+            const unsigned char* wn1 = more ? wsrc(nt, nx.ti, nx.gz * 2 + 1) : wpk;
+            const unsigned short* fpn = more ? halo_src(nt, nx.ti, nx.gz) : xs;
+            const int hn = __builtin_amdgcn_readfirstlane(hpar ^ 1);
+            const int wn = __builtin_amdgcn_readfirstlane((wcur ^ 1) * 2);
+            compute(zb, wl + (wcur * 2 + wj) * WSLOTS, rows_in, wj, std::integral_constant<int, 2 * WIT + ZIT>{},
+                    std::integral_constant<int, NSTEP>{}, [&](int k) {
+                      if (!more) return;
+                      if (k < WIT) issue_w(wn0, wn, k);
+                      else if (k < 2 * WIT) issue_w(wn1, wn + 1, k - WIT);
+                      else issue_z(fpn, hn, k - 2 * WIT);
+                    });
+          }
+          asm volatile("" ::: "memory");  // the claim is read only after the group
+          if (gi == 0 && claims && tid == 0) {
+            int t = claimed(cx, v);
+            while (t < 0 && steal < 7) {
+              ++steal;
+              const int x = (xcd + steal) & 7;
+              t = claimed(x, claim(x));
+            }
+            claim_lds = t;
+          }
+          if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+          vm_drain();
+          barrier();
+          if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
+          if (more) nx_advance();
+          hpar ^= 1;
+          wcur ^= 1;
+        }
+        // the second half's sums join the first's through the idle halo buffer
+        float* red = reinterpret_cast<float*>(zl + (hpar ^ 1) * ZSLOTS);
+        if (wj == 1) {
+#pragma unroll
+          for (int c = 0; c < CW; ++c)
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) red[(((wr * CW + c) * RW + r) * 16 + e) * 64 + lane] = acc[c][r][e];
+        }
+        barrier();
+        if (wj == 0) {
+#pragma unroll
+          for (int c = 0; c < CW; ++c)
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[c][r][e] += red[(((wr * CW + c) * RW + r) * 16 + e) * 64 + lane];
+          // (the output stores may stay in flight across the barrier below)
+          epilogue(ct, par, hpar ^ 1, (wcur ^ 1) * 2);
+        }
+        barrier();
+        par ^= 1;
+        ctile = tnext;
+        tnext = tnn;
+        tnn = -1;
+        if (ctile < 0) break;
+        ct = decode(ctile);
+      }
+    }
+  } else {
+    // prologue: the first group's halo and first weight sub-stage
+    int hpar = 0;
+    if (nx_ok) {
+      const unsigned short* fp = halo_src(nt, nx.ti, nx.gz);
+      const unsigned char* wp = wsrc(nt, nx.ti, nx.gz * 2);
+#pragma unroll
+      for (int it = 0; it < ZIT; ++it) issue_z(fp, 0, it);
+#pragma unroll
+      for (int it = 0; it < WIT; ++it) issue_w(wp, 0, it);
+      nx_advance();
+      vm_drain();
+      barrier();
+    }
+
+    int par = 0;
+    if (ctile >= 0) {
+      Tile ct = decode(ctile);
+      for (;;) {
+        zero_acc();
+        const bool claims = tnext >= 0;  // claim the tile after tnext while this one runs
+        const int ngt = ct.nact * ngrp;  // >= 1: only frames with an active tap have tiles
+        const bool rows_in = ct.y0 + wr * RW < a.ho;  // wave-uniform
+        for (int gi = 0; gi < ngt; ++gi) {
+          // group-major order: the active taps of one 32-channel group run back
+          // to back, so a source frame's group is reused by the output frames of
+          // the neighbouring tiles within a few groups, while it is still in L2
+          const int gz = gi / ct.nact, ti = gi - gz * ct.nact;
+          const uint4* zb = zl + hpar * ZSLOTS;
+          unsigned short bval = 0;
+          if (gi == 0) bval = bias_value(ct);
+          const bool more = nx_ok;
+          // sub-stage 0: load W[1] <- (this group, second half), H[next] <- next group
+          {
+            const unsigned char* wp1 = wsrc(ct, ti, gz * 2 + 1);
+            const unsigned short* fpn = more ? halo_src(nt, nx.ti, nx.gz) : xs;
+            const int hn = __builtin_amdgcn_readfirstlane(hpar ^ 1);
+            compute(zb, wl, rows_in, std::integral_constant<int, 0>{}, std::integral_constant<int, WIT + ZIT>{},
+                    std::integral_constant<int, NSTEP>{}, [&](int k) {
+                      if (k < WIT) issue_w(wp1, 1, k);
+                      else if (more) issue_z(fpn, hn, k - WIT);
+                    });
+          }
+          if (more) wait_halo_in_flight();
+          else vm_drain();
+          if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+          barrier();
+          // sub-stage 1: load W[0] <- next group, first half.  In the first
+          // group, thread 0 also claims a tile (the atomic's latency hides
+          // behind the sub-stage; the claim is published at its barrier).
+          const int cx = (xcd + steal) & 7;
+          int v = 0;
+          if (gi == 0 && claims && tid == 0) v = claim(cx);
+          {
+            const unsigned char* wpn = more ? wsrc(nt, nx.ti, nx.gz * 2) : wpk;
+            compute(zb, wl + WSLOTS, rows_in, std::integral_constant<int, 1>{}, std::integral_constant<int, WIT>{},
+                    std::integral_constant<int, (NSTEP + 1) / 2>{}, [&](int k) {
+                      if (more) issue_w(wpn, 0, k);
+                    });
+          }
+          asm volatile("" ::: "memory");  // the claim is read only after the sub-stage
+          if (gi == 0 && claims && tid == 0) {
+            int t = claimed(cx, v);
+            while (t < 0 && steal < 7) {
+              ++steal;
+              const int x = (xcd + steal) & 7;
+              t = claimed(x, claim(x));
+            }
+            claim_lds = t;
+          }
+          vm_drain();
+          barrier();
+          if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
+          if (more) nx_advance();
+          hpar ^= 1;
+        }
+        // (the output stores may stay in flight across this barrier)
+        epilogue(ct, par, hpar ^ 1, 1);
+        barrier();
+        par ^= 1;
+        ctile = tnext;
+        tnext = tnn;
+        tnn = -1;
+        if (ctile < 0) break;
+        ct = decode(ctile);
+      }
     }
   }
 
@@ -1799,9 +1912,9 @@ template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
 const void* mfma_kernel() {
   return reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF, OCC>);
 }
-template <int BN, int TH, int WM, int DD, int SS>
+template <int BN, int TH, int WM, int DD, int SS, int KSP>
 const void* g32_kernel() {
-  return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM, DD, SS>);
+  return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM, DD, SS, KSP>);
 }
 template <int COUT, int NCH, bool CO>
 const void* few_kernel() {
@@ -1857,14 +1970,14 @@ hipError_t launch_gen(ConvArgs a, int64_t tiles, bool pack, bool conv, hipStream
 }
 
 // The group-staged 3x3 kernel (16-channel weight sub-stages, same packing).
-template <int BN, int TH, int WM, int DD = 1, int SS = 1>
+template <int BN, int TH, int WM, int DD = 1, int SS = 1, int KSP = 1>
 hipError_t launch_g32(ConvArgs a, int64_t tiles, int cus, bool pack, bool conv, hipStream_t s) {
   if (pack) {
     const hipError_t e = pack_bf16<BN, 3, 16>(a, s);
     if (e != hipSuccess) return e;
   }
   if (!conv) return hipSuccess;
-  return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS>>(a, tiles, cus, WM * 64, s);
+  return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS, KSP>>(a, tiles, cus, WM * 64, s);
 }
 
 }  // namespace
@@ -2003,7 +2116,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   }
   if ((in.kernel_id == CC3D_K_BF16_S3_N96_G32W8 || in.kernel_id == CC3D_K_BF16_S3_N64_G32W8 ||
        in.kernel_id == CC3D_K_BF16_S3D2_N64_G32W8 || in.kernel_id == CC3D_K_BF16_S3S2_N96_G32W4 ||
-       in.kernel_id == CC3D_K_BF16_S3S2_N64_G32W4) &&
+       in.kernel_id == CC3D_K_BF16_S3S2_N64_G32W8) &&
       !frame_intervals(plan, a))
     return invalid();
 
@@ -2062,8 +2175,8 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     case CC3D_K_BF16_S3S2_N96_G32W4:
       e = launch_g32<96, 4, 4, 1, 2>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
       break;
-    case CC3D_K_BF16_S3S2_N64_G32W4:
-      e = launch_g32<64, 4, 4, 1, 2>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
+    case CC3D_K_BF16_S3S2_N64_G32W8:
+      e = launch_g32<64, 4, 8, 1, 2, 2>(a, std::max<int64_t>(a.nat, 1), cus, pack, runs, s);
       break;
     case CC3D_K_BF16_GEN_N64: e = launch_gen<64>(a, in.tiles, pack, runs, s); break;
     case CC3D_K_BF16_GEN_N96: e = launch_gen<96>(a, in.tiles, pack, runs, s); break;

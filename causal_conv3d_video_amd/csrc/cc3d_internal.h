@@ -27,7 +27,8 @@ enum cc3d_kernel_id : int32_t {
                                    // padding 2: 512 px (16x32) x 64 channels
   CC3D_K_BF16_S3S2_N96_G32W4 = 16, // the group-staged kernel on 3x3 taps at spatial stride 2,
                                    // padding 1: 128 output px (4x32) x 96 channels, 4 waves
-  CC3D_K_BF16_S3S2_N64_G32W4 = 17, // as CC3D_K_BF16_S3S2_N96_G32W4 with 64 channels
+  CC3D_K_BF16_S3S2_N64_G32W8 = 17, // as CC3D_K_BF16_S3S2_N96_G32W4 with 64 channels, 8 waves (each
+                                   // group's two 16-channel halves on two waves of the same rows)
 };
 
 // Scheduler counters of the group-staged kernel, kept after the packed

@@ -109,7 +109,7 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
     return strided_3x3(d) && d.c_out % 96 == 0 && d.c_in % 32 == 0;
   }
   if (n == "bf16_s3s2_n64_p4x32_g32") {  // the same with 64 output channels per tile
-    *v = {CC3D_K_BF16_S3S2_N64_G32W4, 4, 32, 64, 16, "bf16_s3s2_n64_p4x32_g32"};
+    *v = {CC3D_K_BF16_S3S2_N64_G32W8, 4, 32, 64, 16, "bf16_s3s2_n64_p4x32_g32"};
     return strided_3x3(d) && d.c_out % 64 == 0 && d.c_in % 32 == 0;
   }
   if (!same_spatial(d)) return false;
