@@ -26,11 +26,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+# MI355X's published dense bf16 MFMA peak (2.5 PFLOP/s); the unit count
+# gives 256 CU x 4096 flop/clk x 2.4 GHz = 2516.6 TFLOP/s before rounding.
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MALL_BYTES = 256 * 2 ** 20      # MI355X Infinity Cache
 METRIC = "causal Conv3D BF16 TFLOP/s and % MFMA peak; 17-frame conv-replay ms"
-KERNEL_SRC = os.path.join(ROOT, "causal_conv3d_video_amd", "csrc", "cc3d_forward.hip")
+CSRC = os.path.join(ROOT, "causal_conv3d_video_amd", "csrc")
 
 
 def _parse():
@@ -53,14 +55,50 @@ def _parse():
     return p.parse_args()
 
 
-def _source_hash():
+def _kernel_sources(kernel_name=None):
+    """The source files a kernel variant is built from (all kernel sources
+    when no name is given)."""
+    common = ["cc3d_device.h", "cc3d_internal.h"]
+    if kernel_name is None:
+        return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".inc", ".h", ".cpp")))
+    if kernel_name.endswith("_g32"):
+        return common + ["cc3d_k_g32.hip"]
+    if kernel_name.startswith("bf16_s3_few_"):
+        return common + ["cc3d_few.inc"]
+    if kernel_name.startswith("bf16_gen_") or kernel_name == "f32_direct":
+        return common + ["cc3d_k_misc.hip"]
+    return common + ["cc3d_k_mfma.hip"]
+
+
+def _source_hash(kernel_name=None):
     h = hashlib.sha256()
-    with open(KERNEL_SRC, "rb") as f:
-        h.update(f.read())
+    for name in _kernel_sources(kernel_name):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def build_workload(device):
+def _desc(cc3d, s, tx, tc, n=1):
+    return cc3d.make_desc(n, s["cin"], s["cout"], s["h"], s["w"], tx, tc, k=s["k"], stride=(s["st"],) + s["sst"],
+                          dilation=(s["dt"],) + s["sdil"], padding=s["pad"], p_base=s["p_base"])
+
+
+def _packed_images(cc3d, plans, w, stream):
+    """One packed weight image per distinct weight layout of ``plans`` (the
+    chunk plans of one signature share one)."""
+    images = {}
+    for p in plans:
+        key = (p.info["weight_layout"], p.info["packed_weight_bytes"])
+        if key not in images:
+            images[key] = cc3d.causal_conv3d_pack_weights(p, w, stream=stream)
+    return images
+
+
+def _image(wk, plan):
+    return wk["wpk"][(plan.info["weight_layout"], plan.info["packed_weight_bytes"])]
+
+
+def build_workload(device, stream):
     import torch
 
     import causal_conv3d_video_amd as cc3d
@@ -75,21 +113,24 @@ def build_workload(device):
         plans, outs = [], []
         tc = 0
         for c in range(synth.REPLAY_CHUNKS):
-            desc = cc3d.make_desc(1, s["cin"], s["cout"], s["h"], s["w"], frames[c], tc, k=s["k"],
-                                  dilation=(s["dt"], 1, 1), padding=s["pad"], p_base=s["p_base"])
-            plan = cc3d.causal_conv3d_plan(desc)
+            plan = cc3d.causal_conv3d_plan(_desc(cc3d, s, frames[c], tc))
             plans.append(plan)
             outs.append(torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device))
             tc = plan.info["t_cache_out"]
         cache_shape = plans[-1].shapes()["cache_out"]
         caches = [torch.empty(cache_shape, dtype=torch.bfloat16, device=device) for _ in range(2)]
-        work.append(dict(sig=s, w=w, b=b, xs=xs, plans=plans, outs=outs, caches=caches))
+        ws_bytes = max(p.info["workspace_bytes"] for p in plans)
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes else None
+        work.append(dict(sig=s, w=w, b=b, xs=xs, plans=plans, outs=outs, caches=caches,
+                         wpk=_packed_images(cc3d, plans, w, stream), ws=ws))
     return work
 
 
-def run_step(work, stream, packed=False):
+def run_step(work, stream, packed=True):
     """One pass of the replay: every chunk through every signature, carrying
-    each signature's cache through two ping-pong buffers."""
+    each signature's cache through two ping-pong buffers.  packed: the
+    weights come from each signature's packed image (fixed decoder weights,
+    packed once); otherwise every call reads W in place."""
     import causal_conv3d_video_amd as cc3d
 
     chunks = len(work[0]["xs"])
@@ -99,19 +140,62 @@ def run_step(work, stream, packed=False):
             cin_buf = None if c == 0 else wk["caches"][(c - 1) % 2][:, :plan.desc.t_cache]
             cout_buf = wk["caches"][c % 2][:, :plan.info["t_cache_out"]]
             if packed:
-                cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c],
-                                                  cout_buf, stream)
+                cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, _image(wk, plan), wk["b"], wk["outs"][c],
+                                                  cout_buf, wk["ws"], stream)
             else:
                 cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c],
                                            cout_buf, stream)
 
 
+def time_launches(launch, launches, stream, warm_seconds=0.2, per_launch=False):
+    """Average time of ``launches`` calls of ``launch()`` between one pair of
+    HIP events on ``stream``, after ``warm_seconds`` of untimed calls
+    (steady-state clocks); with per_launch also the median of as many calls
+    timed one by one.  Returns (avg_us, median_us or None)."""
+    import torch
+
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(3):
+            launch()
+        stream.synchronize()
+        if time.perf_counter() - t0 >= warm_seconds:
+            break
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        launch()
+    e1.record(stream)
+    e1.synchronize()
+    avg_us = e0.elapsed_time(e1) / launches * 1e3
+    med_us = None
+    if per_launch:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for a_, b_ in ev:
+            a_.record(stream)
+            launch()
+            b_.record(stream)
+        ev[-1][1].synchronize()
+        per = sorted(a_.elapsed_time(b_) for a_, b_ in ev)
+        med_us = (per[(launches - 1) // 2] + per[launches // 2]) / 2 * 1e3
+    return avg_us, med_us
+
+
+def _rates(info, us):
+    return dict(us_per_launch=us, tflops=info["flops_active"] / (us * 1e-6) / 1e12,
+                frac_mfma_peak=info["flops_active"] / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                gbs=info["bytes_conv"] / (us * 1e-6) / 1e9,
+                frac_hbm_peak=info["bytes_conv"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
+
+
 def time_kernels(work, launches, stream, warm_seconds=0.2):
-    """Average conv-kernel launch time per signature at the steady-state chunk
-    (cache present): weights packed once, then causal_conv3d_forward_packed
-    launches only the conv kernel; HIP events on the launch stream.  Each
-    signature is first run untimed for warm_seconds (steady-state clocks).
-    Also the median of the same number of launches timed one by one."""
+    """Conv-kernel launch time per replay signature at its steady-state chunk
+    (cache present): causal_conv3d_forward_packed from the signature's packed
+    image, no cache-out, HIP events on the launch stream: the mean over the
+    launches between one event pair (used for the roofline) and the median of
+    as many launches timed one by one.  Also the same launches reading W in
+    place (causal_conv3d_forward)."""
     import torch
 
     import causal_conv3d_video_amd as cc3d
@@ -121,67 +205,47 @@ def time_kernels(work, launches, stream, warm_seconds=0.2):
         c = 2
         plan = wk["plans"][c]
         cin_buf = wk["caches"][(c - 1) % 2][:, :plan.desc.t_cache]
-        cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
-        t0 = time.perf_counter()
-        while True:
-            for _ in range(3):
-                cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c], None, stream)
-            stream.synchronize()
-            if time.perf_counter() - t0 >= warm_seconds:
-                break
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(launches):
-            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c], None, stream)
-        e1.record(stream)
-        e1.synchronize()
-        ms = e0.elapsed_time(e1) / launches
-        # the same launches with an event pair around each (median)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
-        for a_, b_ in ev:
-            a_.record(stream)
-            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, wk["b"], wk["outs"][c], None, stream)
-            b_.record(stream)
-        ev[-1][1].synchronize()
-        per = sorted(a_.elapsed_time(b_) for a_, b_ in ev)
-        med_us = (per[(launches - 1) // 2] + per[launches // 2]) / 2 * 1e3
+        img = _image(wk, plan)
+
+        def packed(plan=plan, wk=wk, cin_buf=cin_buf, img=img, c=c):
+            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][c], cin_buf, img, wk["b"], wk["outs"][c], None, wk["ws"],
+                                              stream)
+
+        def in_place(plan=plan, wk=wk, cin_buf=cin_buf, c=c):
+            cc3d.causal_conv3d_forward(plan, wk["xs"][c], cin_buf, wk["w"], wk["b"], wk["outs"][c], None, stream)
+
+        us, med = time_launches(packed, launches, stream, warm_seconds, per_launch=True)
+        us_w, _ = time_launches(in_place, launches, stream, warm_seconds)
         info = plan.info
-        res[wk["sig"]["name"]] = dict(
-            kernel=info["kernel_name"], us_per_launch=ms * 1e3,
-            tflops=info["flops_active"] / (ms * 1e-3) / 1e12,
-            frac_mfma_peak=info["flops_active"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
-            frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            flops=info["flops_active"], bytes=info["bytes_conv"], tiles=info["tiles"], us_per_launch_median=med_us)
+        res[wk["sig"]["name"]] = dict(kernel=info["kernel_name"], **_rates(info, us), flops=info["flops_active"],
+                                      bytes=info["bytes_conv"], tiles=info["tiles"], us_per_launch_median=med,
+                                      us_per_launch_w_in_place=us_w)
         # A working set that fits the 256 MB MALL stays there between
         # launches of one buffer set; also time launches that rotate over
         # enough copies of x, cache and out (>= 4, >= 512 MB) to start cold.
         if info["bytes_conv"] < MALL_BYTES:
             copies = max(4, -(-2 * MALL_BYTES // int(info["bytes_conv"])))
             sets = [(wk["xs"][c].clone(), cin_buf.clone(), torch.empty_like(wk["outs"][c])) for _ in range(copies)]
-            for xs_, cs_, os_ in sets:
-                cc3d.causal_conv3d_forward_packed(plan, xs_, cs_, wk["b"], os_, None, stream)
-            stream.synchronize()
-            e0.record(stream)
-            for i in range(launches):
-                xs_, cs_, os_ = sets[i % copies]
-                cc3d.causal_conv3d_forward_packed(plan, xs_, cs_, wk["b"], os_, None, stream)
-            e1.record(stream)
-            e1.synchronize()
-            res[wk["sig"]["name"]].update(
-                us_per_launch_cold=e0.elapsed_time(e1) / launches * 1e3, cold_buffer_sets=copies)
+            it = [0]
+
+            def cold(plan=plan, wk=wk, img=img, sets=sets, it=it):
+                xs_, cs_, os_ = sets[it[0] % len(sets)]
+                it[0] += 1
+                cc3d.causal_conv3d_forward_packed(plan, xs_, cs_, img, wk["b"], os_, None, wk["ws"], stream)
+
+            us_cold, _ = time_launches(cold, launches, stream, 0.0)
+            res[wk["sig"]["name"]].update(us_per_launch_cold=us_cold, cold_buffer_sets=copies)
             del sets
     return res
 
 
 def time_single_calls(device, launches, stream, warm_seconds=0.2):
-    """Average conv-kernel launch time of each single-call configuration (the
-    latent, mid-resolution 192->192 and 384->192, full-resolution 96->96 and
-    96->3 calls, each with 2 cached frames, the encoder's stride-2 temporal
+    """Conv-kernel launch time of each single-call configuration (the latent,
+    mid-resolution 192->192 and 384->192, full-resolution 96->96 and 96->3
+    calls, each with 2 cached frames, the encoder's stride-2 temporal
     downsampling convs, and two convs with spatial stride or dilation 2),
-    weights packed once; HIP events on the launch stream after warm_seconds
-    of untimed launches."""
+    from the packed weight image; HIP events on the launch stream after
+    warm_seconds of untimed launches."""
     import torch
 
     import causal_conv3d_video_amd as cc3d
@@ -191,59 +255,34 @@ def time_single_calls(device, launches, stream, warm_seconds=0.2):
     for i, s in enumerate(synth.SINGLE_CALLS + synth.ENCODER_DOWNSAMPLE + synth.GENERAL_SPATIAL):
         x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
                                        device=device, seed=synth.SEED_BASE + 200 + i)
-        desc = cc3d.make_desc(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], k=s["k"],
-                              stride=(s["st"],) + s["sst"], dilation=(s["dt"],) + s["sdil"], padding=s["pad"],
-                              p_base=s["p_base"])
-        plan = cc3d.causal_conv3d_plan(desc)
+        plan = cc3d.causal_conv3d_plan(_desc(cc3d, s, s["tx"], s["tc"]))
         out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
-        cc3d.causal_conv3d_pack_weights(plan, w, stream)
-        t0 = time.perf_counter()
-        while True:
-            for _ in range(3):
-                cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, None, stream)
-            stream.synchronize()
-            if time.perf_counter() - t0 >= warm_seconds:
-                break
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(launches):
-            cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, None, stream)
-        e1.record(stream)
-        e1.synchronize()
-        ms = e0.elapsed_time(e1) / launches
+        img = cc3d.causal_conv3d_pack_weights(plan, w, stream=stream)
+        ws = torch.zeros(plan.info["workspace_bytes"], dtype=torch.uint8, device=device) \
+            if plan.info["workspace_bytes"] else None
+        us, _ = time_launches(lambda: cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, out, None, ws, stream),
+                              launches, stream, warm_seconds)
         info = plan.info
-        res[s["name"]] = dict(
-            kernel=info["kernel_name"], us_per_launch=ms * 1e3,
-            tflops=info["flops_active"] / (ms * 1e-3) / 1e12,
-            frac_mfma_peak=info["flops_active"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            gbs=info["bytes_conv"] / (ms * 1e-3) / 1e9,
-            frac_hbm_peak=info["bytes_conv"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        res[s["name"]] = dict(kernel=info["kernel_name"], **_rates(info, us))
         if info["kernel_name"].startswith("bf16_s3_few_"):
             # the head with 8-bit pixel output fused (one byte per channel)
             o8 = torch.empty(plan.shapes()["out"], dtype=torch.uint8, device=device)
-            for _ in range(3):
-                cc3d.causal_conv3d_forward_u8(plan, x, c, None, b, o8, None, stream=stream)
-            e0.record(stream)
-            for _ in range(launches):
-                cc3d.causal_conv3d_forward_u8(plan, x, c, None, b, o8, None, stream=stream)
-            e1.record(stream)
-            e1.synchronize()
-            ms8 = e0.elapsed_time(e1) / launches
+            us8, _ = time_launches(lambda: cc3d.causal_conv3d_forward_u8(plan, x, c, w, b, o8, None, stream=stream),
+                                   launches, stream, warm_seconds)
             nbytes = info["bytes_conv"] - o8.numel()   # half the bf16 output bytes
-            res[s["name"] + "_u8"] = dict(kernel=info["kernel_name"] + "+u8", us_per_launch=ms8 * 1e3,
-                                          gbs=nbytes / (ms8 * 1e-3) / 1e9,
-                                          frac_hbm_peak=nbytes / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            res[s["name"] + "_u8"] = dict(kernel=info["kernel_name"] + "+u8", us_per_launch=us8,
+                                          gbs=nbytes / (us8 * 1e-6) / 1e9,
+                                          frac_hbm_peak=nbytes / (us8 * 1e-6) / 1e9 / HBM_PEAK_GBS)
             del o8
-        del x, c, w, b, out, plan
+        del x, c, w, b, out, plan, img, ws
         torch.cuda.empty_cache()
     return res
 
 
-def time_decoder_signatures(device, launches, stream, warm_seconds=0.2):
-    """Every causal Conv3D signature of the 17-frame decoder at full size
+def time_decoder_signatures(device, launches, stream, table, warm_seconds=0.2):
+    """Every causal Conv3D signature of a decoder table at full size
     (steady-state chunk: its frames plus a 2-frame cache): the default
-    kernel's average launch time (weights packed once, HIP events), and the
+    kernel's average launch time from the packed image (HIP events), and the
     variant causal_conv3d_plan_autotune picks with its own timing."""
     import torch
 
@@ -251,29 +290,17 @@ def time_decoder_signatures(device, launches, stream, warm_seconds=0.2):
     import synth
 
     res = {}
-    for i, s in enumerate(synth.DECODER_SIGNATURES):
+    for i, s in enumerate(table):
         x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
                                        device=device, seed=synth.SEED_BASE + 400 + i)
-        desc = cc3d.make_desc(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], k=s["k"],
-                              dilation=(s["dt"], 1, 1), padding=s["pad"], p_base=s["p_base"])
+        desc = _desc(cc3d, s, s["tx"], s["tc"])
         plan = cc3d.causal_conv3d_plan(desc)
         out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
-        cc3d.causal_conv3d_pack_weights(plan, w, stream)
-        t0 = time.perf_counter()
-        while True:
-            for _ in range(3):
-                cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, None, stream)
-            stream.synchronize()
-            if time.perf_counter() - t0 >= warm_seconds:
-                break
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(launches):
-            cc3d.causal_conv3d_forward_packed(plan, x, c, b, out, None, stream)
-        e1.record(stream)
-        e1.synchronize()
-        us = e0.elapsed_time(e1) / launches * 1e3
+        img = cc3d.causal_conv3d_pack_weights(plan, w, stream=stream)
+        ws = torch.zeros(plan.info["workspace_bytes"], dtype=torch.uint8, device=device) \
+            if plan.info["workspace_bytes"] else None
+        us, _ = time_launches(lambda: cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, out, None, ws, stream),
+                              launches, stream, warm_seconds)
         tuned, tuned_ms = cc3d.causal_conv3d_plan_autotune(desc, x, c, w, b, out, launches=5, stream=stream)
         flops = plan.info["flops_active"]
         res[s["name"]] = dict(kernel=plan.info["kernel_name"], us_per_launch=us,
@@ -282,19 +309,46 @@ def time_decoder_signatures(device, launches, stream, warm_seconds=0.2):
                               flops=flops)
         tuned.close()
         plan.close()
-        del x, c, w, b, out
+        del x, c, w, b, out, img, ws
         torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(work, target_seconds):
-    """The fp64 CPU oracle on a bounded sample of the same workload: random
-    output pixels (all output channels) of the steady-state chunk of every
-    signature, over that chunk's own [cache; x]."""
+def _cpu_model():
+    """The host CPU's model name (lscpu), or the /proc/cpuinfo entry."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(work, target_seconds, device):
+    """The fp64 CPU oracle as it stands, on the host cores:
+      * a bounded sample of the replay workload: random output pixels (all
+        output channels) of the steady-state chunk of every signature, over
+        that chunk's own [cache; x], sized to about target_seconds;
+      * one whole call of the latent-resolution configuration (384->384 at
+        90x160, 2 cached frames + 1), median of 3;
+      * the tiny fp32 configuration's two calls on one thread."""
+    import statistics
+
     import numpy as np
     import torch
 
     import oracle
+    import synth
 
     threads = oracle.default_threads()
     rng = np.random.default_rng(11)
@@ -334,9 +388,20 @@ def cpu_baseline(work, target_seconds):
         total_s += time.perf_counter() - t
         total_flops += npx * per_px
         desc.append("%s:%dpx" % (s["name"], npx))
+    # one whole call of the latent-resolution configuration, median of 3
+    s = synth.LATENT
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
+                                   device=device, seed=synth.SEED_BASE + 1)
+    x, c, w, b = x.cpu(), c.cpu(), w.cpu(), b.cpu()
+    latent_flops = 2.0 * s["h"] * s["w"] * s["cout"] * s["cin"] * 27
+    times = []
+    for _ in range(3):
+        t = time.perf_counter()
+        oracle.conv3d(x, c, w, b, nthreads=threads)
+        times.append(time.perf_counter() - t)
+    latent_s = statistics.median(times)
     # the tiny fp32 workload's two calls (A: no cache; B: A's last two frames
     # as cache) on one thread, whole outputs, repeated for about half a second
-    import synth
     g = torch.Generator().manual_seed(synth.SEED_BASE)
     wt = synth.draw((8, 3, 3, 3, 8), "uniform", g, "cpu", torch.float32, 1.0)
     bt = synth.draw((8,), "uniform", g, "cpu", torch.float32, 0.1)
@@ -350,8 +415,11 @@ def cpu_baseline(work, target_seconds):
         reps += 1
     tiny_rate = reps * tiny_flops / (time.perf_counter() - t)
     return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": "fp64 oracle, random output pixels (all channels) of chunk 2 of each signature: "
                       + ", ".join(desc) + "; %.1f s, %.1f GFLOP" % (total_s, total_flops / 1e9),
+            "latent_384_whole_call_s": latent_s,
+            "latent_384_whole_call_tflops": latent_flops / latent_s / 1e12,
             "tiny_fp32_one_thread_gflops": tiny_rate / 1e9}
 
 
@@ -360,7 +428,7 @@ def traffic_for(kernel_name, signature=None):
     counter summary (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by the
     counter's reading on a plain copy of known size), or None when there is
     none for this kernel, it was taken on another workload than
-    ``signature``, or the kernel source changed since it was taken."""
+    ``signature``, or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.txt" % kernel_name)
     try:
         rec = {}
@@ -371,7 +439,7 @@ def traffic_for(kernel_name, signature=None):
                     rec[key.strip()] = val.strip()
     except OSError:
         return None
-    if rec.get("kernel_source_sha256") != _source_hash():
+    if rec.get("kernel_source_sha256") != _source_hash(kernel_name):
         return None
     if signature is not None and not rec.get("workload", "").startswith(signature + " "):
         return None
@@ -379,6 +447,45 @@ def traffic_for(kernel_name, signature=None):
         return float(rec["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def _only(args, work, device, stream):
+    """Profiling aid: one signature's conv kernel alone, from its packed
+    image: --warm-seconds of untimed launches, then --kernel-launches
+    counted ones (a profile of this mode takes its statistics over the last
+    --kernel-launches dispatches of the conv kernel)."""
+    import torch
+
+    import causal_conv3d_video_amd as cc3d
+    import synth
+
+    wk = next((w for w in work if w["sig"]["name"] == args.only), None)
+    if wk is not None:
+        plan = wk["plans"][2]
+        cin_buf = wk["caches"][1][:, :plan.desc.t_cache]
+        cin_buf.copy_(torch.cat(wk["xs"][:2], 1)[:, -plan.desc.t_cache:])  # chunk 2's carried frames
+        x, b, out, img, ws = wk["xs"][2], wk["b"], wk["outs"][2], _image(wk, plan), wk["ws"]
+    else:  # a single-call configuration (2 cached frames) or a decoder signature
+        s = next(v for v in synth.SINGLE_CALLS + synth.ENCODER_DOWNSAMPLE + synth.GENERAL_SPATIAL
+                 + synth.DECODER_SIGNATURES + synth.DECODER_SIGNATURES_480 if v["name"] == args.only)
+        x, cin_buf, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
+                                             device=device, seed=synth.SEED_BASE + 200)
+        plan = cc3d.causal_conv3d_plan(_desc(cc3d, s, s["tx"], s["tc"]))
+        out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
+        img = cc3d.causal_conv3d_pack_weights(plan, w, stream=stream)
+        ws = torch.zeros(plan.info["workspace_bytes"], dtype=torch.uint8, device=device) \
+            if plan.info["workspace_bytes"] else None
+    warm, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.warm_seconds:
+        for _ in range(3):
+            cc3d.causal_conv3d_forward_packed(plan, x, cin_buf, img, b, out, None, ws, stream)
+        stream.synchronize()
+        warm += 3
+    for _ in range(args.kernel_launches):
+        cc3d.causal_conv3d_forward_packed(plan, x, cin_buf, img, b, out, None, ws, stream)
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "kernel": plan.info["kernel_name"], "warm_launches": warm,
+                      "launches": args.kernel_launches}))
 
 
 def main():
@@ -390,12 +497,11 @@ def main():
     import torch
 
     import causal_conv3d_video_amd as cc3d  # noqa: F401  (fails loudly if the library is missing)
+    import synth
 
     device = "cuda:0"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    work = build_workload(device)
-    torch.cuda.synchronize()
 
     if args.copy_mib:
         src = torch.ones(args.copy_mib << 19, dtype=torch.bfloat16, device=device)
@@ -405,43 +511,16 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel() * 2, "launches": args.kernel_launches}))
         return
+    work = build_workload(device, stream)
+    torch.cuda.synchronize()
     if args.only:
-        wk = next((w for w in work if w["sig"]["name"] == args.only), None)
-        if wk is not None:
-            plan = wk["plans"][2]
-            cin_buf = wk["caches"][1][:, :plan.desc.t_cache]
-            cin_buf.copy_(torch.cat(wk["xs"][:2], 1)[:, -plan.desc.t_cache:])  # chunk 2's carried frames
-            cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
-        else:  # a single-call configuration (2 cached frames)
-            import synth
-            s = next(v for v in synth.SINGLE_CALLS + synth.ENCODER_DOWNSAMPLE + synth.GENERAL_SPATIAL
-                     if v["name"] == args.only)
-            x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
-                                           device=device, seed=synth.SEED_BASE + 200)
-            plan = cc3d.causal_conv3d_plan(cc3d.make_desc(
-                1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], k=s["k"], stride=(s["st"],) + s["sst"],
-                dilation=(s["dt"],) + s["sdil"], padding=s["pad"], p_base=s["p_base"]))
-            out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
-            wk = {"xs": [None, None, x], "b": b, "outs": [None, None, out]}
-            cin_buf = c
-            cc3d.causal_conv3d_pack_weights(plan, w, stream)
-        # untimed launches for at least --warm-seconds, then the counted ones
-        # (a profile of this mode takes its statistics over the last
-        # --kernel-launches dispatches of the conv kernel)
-        warm, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < args.warm_seconds:
-            for _ in range(3):
-                cc3d.causal_conv3d_forward_packed(plan, wk["xs"][2], cin_buf, wk["b"], wk["outs"][2], None, stream)
-            stream.synchronize()
-            warm += 3
-        for _ in range(args.kernel_launches):
-            cc3d.causal_conv3d_forward_packed(plan, wk["xs"][2], cin_buf, wk["b"], wk["outs"][2], None, stream)
-        torch.cuda.synchronize()
-        print(json.dumps({"only": args.only, "kernel": plan.info["kernel_name"], "warm_launches": warm,
-                          "launches": args.kernel_launches}))
+        _only(args, work, device, stream)
         return
 
-    # warm-up: at least args.warmup steps and at least args.warm_seconds
+    # The step: every call from its signature's packed weight image (fixed
+    # decoder weights, packed once before timing; the images are shared by
+    # the five chunk plans of a signature).  Warm-up: at least args.warmup
+    # steps and at least args.warm_seconds.
     t0 = time.perf_counter()
     done = 0
     while done < args.warmup or time.perf_counter() - t0 < args.warm_seconds:
@@ -462,19 +541,15 @@ def main():
     flops_nominal = sum(p.info["flops_nominal"] for wk in work for p in wk["plans"])
     tflops = flops_step / (ms * 1e-3) / 1e12
 
-    # the same step with weights packed once beforehand (fixed decoder
-    # weights): conv kernels and cache-out writers only
-    for wk in work:
-        for plan in wk["plans"]:
-            cc3d.causal_conv3d_pack_weights(plan, wk["w"], stream)
-    run_step(work, stream, packed=True)
+    # the same step with every call reading W in place (causal_conv3d_forward)
+    run_step(work, stream, packed=False)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        run_step(work, stream, packed=True)
+        run_step(work, stream, packed=False)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_packed = e0.elapsed_time(e1) / args.steps
+    ms_w = e0.elapsed_time(e1) / args.steps
 
     kern = time_kernels(work, args.kernel_launches, stream)
     # dominant kernel: the variant with the largest share of a step (each
@@ -503,11 +578,12 @@ def main():
                  "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
 
     single = time_single_calls(device, args.kernel_launches, stream)
-    decoder = time_decoder_signatures(device, args.kernel_launches, stream)
+    decoder = time_decoder_signatures(device, args.kernel_launches, stream, synth.DECODER_SIGNATURES)
+    decoder_480 = time_decoder_signatures(device, args.kernel_launches, stream, synth.DECODER_SIGNATURES_480)
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(work, args.cpu_seconds)
+        cpu = cpu_baseline(work, args.cpu_seconds, device)
 
     line = {
         "metric": METRIC,
@@ -527,18 +603,20 @@ def main():
             "workload": "streaming 17-frame decoder conv replay: 5 chunks x [384->384 (3,3,3) 90x160 1f; "
                         "384->768 (3,1,1) 90x160 1f; 192->192 (3,3,3) 360x640 4f; 96->96 (3,3,3) 720x1280 4f; "
                         "96->3 (3,3,3) 720x1280 4f] + 192->192 (3,3,3) d_t=2 360x640 4f; chunk 0 zero-padded, "
-                        "cache carry thereafter; 30 calls per step incl. cache-out writers",
+                        "cache carry thereafter; 30 calls per step incl. cache-out writers; weights packed once "
+                        "per signature",
             "batch": 1, "calls_per_step": sum(len(wk["plans"]) for wk in work),
         },
         "mfma_peak_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-        "ms_per_step_weights_prepacked": ms_packed,
-        "tflops_weights_prepacked": flops_step / (ms_packed * 1e-3) / 1e12,
+        "ms_per_step_w_in_place": ms_w,
+        "tflops_w_in_place": flops_step / (ms_w * 1e-3) / 1e12,
         "flops_active_per_step": flops_step,
         "flops_nominal_per_step": flops_nominal,
         "wall_s_timed": wall,
         "signatures": kern,
         "single_calls": single,
         "decoder_signatures": decoder,
+        "decoder_signatures_480x832": decoder_480,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),

@@ -27,7 +27,7 @@ __all__ = [
     "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
     "causal_conv3d_forward_u8", "causal_conv3d_status_string", "causal_conv3d_counters", "library_path",
-    "EXPORTED_SYMBOLS",
+    "EXPORTED_SYMBOLS", "VARIANTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +39,12 @@ EXPORTED_SYMBOLS = (
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
     "causal_conv3d_forward_u8", "causal_conv3d_status_string", "causal_conv3d_counters",
 )
+
+# Every kernel variant name causal_conv3d_plan_variant accepts (include/cc3d.h).
+VARIANTS = (("bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32")
+            + tuple("bf16_s3_few_p%dx128" % r for r in range(4, 17))
+            + ("bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32", "bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32",
+               "bf16_s3d2_n64_p16x32_g32", "bf16_s3s2_n96_p4x32_g32", "bf16_s3s2_n64_p4x32_g32", "f32_direct"))
 
 CC3D_OK, CC3D_ERR_INVALID_ARG, CC3D_ERR_UNSUPPORTED, CC3D_ERR_DEVICE, CC3D_ERR_NO_MEMORY = range(5)
 CC3D_F32, CC3D_BF16 = 0, 1
@@ -65,7 +71,8 @@ class PlanInfo(ctypes.Structure):
         ("flops_nominal", ctypes.c_double), ("flops_active", ctypes.c_double),
         ("bytes_conv", ctypes.c_double), ("bytes_cache_out", ctypes.c_double),
         ("kernel_id", _i32), ("block_m", _i32), ("block_n", _i32), ("tiles", ctypes.c_int64),
-        ("workspace_bytes", ctypes.c_int64),
+        ("packed_weight_bytes", ctypes.c_int64), ("weight_layout", ctypes.c_uint64),
+        ("workspace_bytes", ctypes.c_int64), ("splits", _i32),
         ("kernel_name", ctypes.c_char * 64),
     ]
 
@@ -93,9 +100,9 @@ def _load():
     lib.causal_conv3d_plan_destroy.restype = None
     lib.causal_conv3d_forward.argtypes = [vp] * 8
     lib.causal_conv3d_forward.restype = ctypes.c_int
-    lib.causal_conv3d_pack_weights.argtypes = [vp] * 3
+    lib.causal_conv3d_pack_weights.argtypes = [vp] * 4
     lib.causal_conv3d_pack_weights.restype = ctypes.c_int
-    lib.causal_conv3d_forward_packed.argtypes = [vp] * 7
+    lib.causal_conv3d_forward_packed.argtypes = [vp] * 8 + [ctypes.c_int64, vp]
     lib.causal_conv3d_forward_packed.restype = ctypes.c_int
     lib.causal_conv3d_forward_u8.argtypes = [vp] * 7 + [ctypes.c_float, ctypes.c_float, vp]
     lib.causal_conv3d_forward_u8.restype = ctypes.c_int
@@ -135,7 +142,7 @@ def make_desc(n, c_in, c_out, h, w, t_x, t_cache, k=(3, 3, 3), stride=(1, 1, 1),
 
 
 class Plan:
-    """Owns a plan handle (host metadata only)."""
+    """Owns a plan handle (host metadata only: a plan holds no device memory)."""
 
     def __init__(self, handle, desc):
         self.handle = handle
@@ -190,9 +197,9 @@ def causal_conv3d_plan_variant(desc, kernel_name):
 
 
 def causal_conv3d_plan_autotune(desc, x, cache_in, w, b, out, launches=5, stream=None):
-    """Time every bf16 variant that can run ``desc`` on these buffers and
-    return (plan of the fastest, with its weights packed; its ms per call).
-    Blocking; overwrites ``out``."""
+    """Time every bf16 variant that can run ``desc`` on these buffers (each
+    from its packed weight image) and return (plan of the fastest, its ms per
+    call).  Blocking; overwrites ``out``."""
     probe = causal_conv3d_plan(desc)  # validates desc and gives the buffer shapes
     try:
         p = _marshal(probe, {"x": x, "cache_in": cache_in if desc.t_cache > 0 else None, "w": w,
@@ -272,21 +279,50 @@ def causal_conv3d_forward(plan, x, cache_in, w, b, out, cache_out=None, stream=N
         raise CC3DError(st, "causal_conv3d_forward")
 
 
-def causal_conv3d_pack_weights(plan, w, stream=None):
-    """Repack ``w`` into the plan's workspace (bf16 plans), for
-    causal_conv3d_forward_packed."""
+def _device_bytes(t, nbytes, name, like):
+    """Pointer of a caller-owned device buffer of at least ``nbytes`` bytes."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous CUDA (HIP) tensor" % name)
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes, the plan needs %d" % (name, t.numel() * t.element_size(), nbytes))
+    if like is not None and t.device != like.device:
+        raise ValueError("%s is on %s, the other buffers on %s" % (name, t.device, like.device))
+    return t.data_ptr()
+
+
+def causal_conv3d_pack_weights(plan, w, w_packed=None, stream=None):
+    """Write the plan's packed weight image of ``w`` (bf16 plans) into
+    ``w_packed`` (a caller-owned CUDA tensor of at least
+    plan.info["packed_weight_bytes"] bytes; allocated here as a uint8 tensor
+    when None) and return it.  Plans with the same info["weight_layout"]
+    read the same image."""
     p = _marshal(plan, {"w": w})
-    st = _lib.causal_conv3d_pack_weights(plan.handle, p["w"], _stream_handle(stream, w))
+    nbytes = plan.info["packed_weight_bytes"]
+    if w_packed is None:
+        w_packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+    dst = _device_bytes(w_packed, nbytes, "w_packed", w)
+    st = _lib.causal_conv3d_pack_weights(plan.handle, p["w"], dst, _stream_handle(stream, w))
     if st != CC3D_OK:
         raise CC3DError(st, "causal_conv3d_pack_weights")
+    return w_packed
 
 
-def causal_conv3d_forward_packed(plan, x, cache_in, b, out, cache_out=None, stream=None):
-    """The convolution with the weights last packed into ``plan``."""
+def causal_conv3d_forward_packed(plan, x, cache_in, w_packed, b, out, cache_out=None, workspace=None, stream=None):
+    """The convolution from a packed weight image (causal_conv3d_pack_weights).
+    ``workspace``: a CUDA tensor of at least plan.info["workspace_bytes"]
+    bytes, zero-filled before its first use (None when that is 0)."""
     p = _marshal(plan, {"x": x, "cache_in": cache_in if plan.desc.t_cache > 0 else None,
                         "b": b if plan.desc.has_bias else None, "out": out, "cache_out": cache_out})
-    st = _lib.causal_conv3d_forward_packed(plan.handle, p["x"], p["cache_in"], p["b"], p["out"],
-                                           p["cache_out"], _stream_handle(stream, x))
+    wp = _device_bytes(w_packed, plan.info["packed_weight_bytes"], "w_packed", x)
+    ws_bytes = plan.info["workspace_bytes"]
+    ws = None
+    if workspace is not None:
+        ws = _device_bytes(workspace, ws_bytes, "workspace", x)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    elif ws_bytes > 0:
+        raise ValueError("this plan needs a workspace of %d bytes" % ws_bytes)
+    st = _lib.causal_conv3d_forward_packed(plan.handle, p["x"], p["cache_in"], wp, p["b"], p["out"],
+                                           p["cache_out"], ws, int(ws_bytes if ws else 0), _stream_handle(stream, x))
     if st != CC3D_OK:
         raise CC3DError(st, "causal_conv3d_forward_packed")
 
@@ -294,7 +330,7 @@ def causal_conv3d_forward_packed(plan, x, cache_in, b, out, cache_out=None, stre
 def causal_conv3d_forward_u8(plan, x, cache_in, w, b, out, cache_out=None, scale=0.5, offset=0.5, stream=None):
     """The RGB head with 8-bit pixel output: ``out`` is a uint8 CUDA tensor of
     the plan's output shape, code = trunc(clamp(fma(y, scale, offset) * 255,
-    0, 255)) in fp32.  ``w`` None runs with the weights last packed."""
+    0, 255)) in fp32."""
     if not isinstance(out, torch.Tensor) or not out.is_cuda or out.dtype != torch.uint8:
         raise TypeError("out must be a uint8 CUDA (HIP) tensor")
     _physical(out, plan.shapes()["out"], "out")

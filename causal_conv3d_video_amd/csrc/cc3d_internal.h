@@ -4,7 +4,6 @@
 
 #include <atomic>
 #include <cstdint>
-#include <mutex>
 
 // Kernel variants the planner can pick.  The bf16 ones are implicit-GEMM
 // MFMA kernels (block tile = block_m output pixels x block_n output channels).
@@ -31,13 +30,7 @@ enum cc3d_kernel_id : int32_t {
                                    // group's two 16-channel halves on two waves of the same rows)
 };
 
-// Scheduler counters of the group-staged kernel, kept after the packed
-// weights in the plan's workspace: kSchedSlots slots of kSchedInts ints (a
-// tile counter per XCD and a finished-workgroup count).  Each launch takes
-// the next slot; the kernel leaves its slot zeroed when it finishes.
-constexpr int kSchedInts = 16;
-constexpr int kSchedSlots = 64;
-
+// A plan is host metadata only, immutable once built.
 struct cc3d_plan {
   cc3d_desc_t d{};
   cc3d_plan_info_t info{};
@@ -45,17 +38,9 @@ struct cc3d_plan {
   int32_t tile_w = 0;      // output columns per workgroup patch
   int32_t tiles_y = 0, tiles_x = 0, nblk_n = 0;
   int32_t cin_chunk = 0;   // input channels per pipeline stage
+  int32_t pack_kind = 0;   // packed weight image: 0 none (fp32), 1 stage-ordered tiles, 2 a copy of W
   int64_t x_bytes = 0, cache_bytes = 0, w_bytes = 0, b_bytes = 0, out_bytes = 0, cache_out_bytes = 0;
   int32_t elem = 0;        // bytes per element
-  // Device workspace of the bf16 kernels: the weights repacked in stage
-  // order, rewritten by every forward call.  Allocated on first use on the
-  // device current at that time.
-  int64_t wpk_bytes = 0;
-  int64_t sched_off = 0;   // byte offset of the scheduler counters in the workspace
-  void* wpk = nullptr;
-  int wpk_device = -1;
-  std::atomic<uint32_t> sched_seq{0};
-  std::mutex mu;
 };
 
 namespace cc3d {

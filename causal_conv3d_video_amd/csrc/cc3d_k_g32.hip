@@ -1,0 +1,683 @@
+// conv_bf16_g32: the group-staged kernel of the large 3x3 maps (also at
+// spatial dilation 2 and at spatial stride 2).
+#include "cc3d_device.h"
+
+namespace {
+
+// The scheduler counters of every launch of this kernel on the device:
+// cc3d::kSchedSlots slots of kSchedInts ints (a tile counter per XCD, then
+// the count of finished workgroups).  Zero when the code object is loaded;
+// each launch leaves its slot zero when it completes.
+constexpr int kSchedInts = 16;
+__device__ __attribute__((unused)) int g32_sched[cc3d::kSchedSlots * kSchedInts];
+// bf16 kernel for 3x3 spatial taps with the halo staged by 32-channel groups.
+//
+// The stage loads of the kernel above fetch 32 bytes (16 channels) of every
+// halo pixel per stage; the vector memory pipeline pays per 128-byte line
+// touched by a wave instruction, so three quarters of each halo line fetch are
+// wasted there and the halo stream alone keeps that pipeline about as busy as
+// the MFMAs keep the matrix cores.  This kernel stages the halo of a
+// (temporal tap, 32-channel group) once -- 64 bytes per pixel -- and runs the
+// group's two 16-channel weight sub-stages against it, and its tiles are
+// 16 x 32 output pixels, so each weight byte fetched feeds twice the MFMA work.
+// One workgroup per compute unit: WM = 4 waves (one per SIMD, each a 4-row x
+// 32-pixel x BN-channel register tile) or WM = 8 (two per SIMD, 2 rows each).
+//
+// LDS: two halo buffers (group g and g+1) and two weight buffers (sub-stages 0
+// and 1 of a group).  Schedule of group g (buffers H[g%2], W[0], W[1]):
+//   sub-stage 0: MFMAs on H[g%2] x W[0]; meanwhile load W[1] <- weights of
+//                (g, second 16 channels), then H[(g+1)%2] <- halo of g+1;
+//                wait for W[1] only; barrier.
+//   sub-stage 1: MFMAs on H[g%2] x W[1]; meanwhile load W[0] <- weights of
+//                (g+1, first 16 channels); wait for everything; barrier.
+// The group sequence runs across tile boundaries, so the next tile's first
+// loads overlap the current tile's last MFMAs and its epilogue.
+//
+// DD is the spatial dilation of the 3x3 taps (1, or 2 for the dilated
+// "same" conv, padding 2): the halo grows by DD on every side, and column
+// tap c, row tap ta read halo column l + c*DD, halo row r + ta*DD.
+//
+// SS is the spatial stride (1, or 2 with padding 1 and no dilation, the
+// encoder's downsampling conv).  At stride 2 output pixel (r, l) of the tile
+// reads input row 2r + ta and input column 2l + c of the halo, which spans
+// 2*TH + 1 rows by 2*32 + 1 columns.  Each halo row is stored with its even
+// input columns first (33 of them), then its odd ones (32): column tap c then
+// reads the 32 consecutive stored pixels from l + c/2 (c even) or 33 + l
+// (c = 1), the same conflict-free fragment pattern as at stride 1.
+//
+// KSP = 2 splits each group's two 16-channel halves between two waves of
+// the same rows (waves w and w + WM/2), so a tile of TH rows runs WM waves
+// with one barrier per group instead of two; the group's two weight halves
+// are staged together (double-buffered: the next group's load during this
+// one), and the waves of the second half add their sums into those of the
+// first through LDS before the epilogue.
+//
+// WPK: the weight sub-stages come from the packed image (a.wpk), one
+// contiguous run each; otherwise each slot's 16-byte piece is gathered from W
+// as the caller stores it, into the same LDS layout.
+template <int BN, int TH, int WM, int DD, int SS, int KSP, bool WPK>
+__global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4, WM / 4))) void conv_bf16_g32(ConvArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using WT = WTile<BN, 3, 16>;
+  static_assert(SS == 1 || (SS == 2 && DD == 1), "stride 2 runs undilated");
+  constexpr int TW = 32, S = 9;
+  constexpr int HP = SS * (TH - 1) + 2 * DD + 1;             // halo rows
+  constexpr int WP = SS == 1 ? TW + 2 * DD : 2 * TW + 1;     // halo columns
+  constexpr int PZ = 4;                          // 16-byte pieces per halo pixel
+  constexpr int ZCH = HP * WP * PZ;
+  constexpr int ZSLOTS = (ZCH + 63) / 64 * 64;
+  constexpr int NW = WM, NT = NW * 64;
+  constexpr int WSLOTS = WT::WSLOTS;
+  constexpr int ZIT = (ZSLOTS + NT - 1) / NT, WIT = (WSLOTS + NT - 1) / NT;
+  constexpr int RW = TH / (WM / KSP), CW = BN / 32;
+  constexpr int ZR = SS * (RW - 1) + 2 * DD + 1; // halo rows a wave reads per column tap
+  constexpr int EROW = CW * 32 * 2 + 16;         // epilogue LDS bytes per pixel (padded)
+  static_assert((WM == 4 || WM == 8) && TH % (WM / KSP) == 0 && BN % 32 == 0, "wave tiling");
+  static_assert(KSP == 1 || (KSP == 2 && WM == 8), "channel-half split");
+  // epilogue staging: waves 0-3 use the idle weight buffer, waves 4-7 the idle halo buffer
+  static_assert(4 * 32 * EROW <= WSLOTS * 16 && (NW - 4) * 32 * EROW <= ZSLOTS * 16, "epilogue staging");
+  static_assert((2 * ZSLOTS + 2 * KSP * WSLOTS) * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
+  // channel-half split: the second half's sums pass through an idle halo buffer
+  static_assert(KSP == 1 || (WM / 2) * CW * RW * 16 * 64 * 4 <= ZSLOTS * 16, "partial sums");
+  constexpr auto zcnt = [](int w) {  // halo load instructions of wave w per group
+    int n = 0;
+    for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
+    return n;
+  };
+  static_assert(zcnt(0) + WIT <= 63, "vmcnt range");
+
+  __shared__ uint4 zl[2 * ZSLOTS];
+  __shared__ uint4 wl[2 * KSP * WSLOTS];
+  __shared__ float bias_lds[2][BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  // row group and channel half of this wave (the row group is the wave
+  // itself unless the halves are split between waves)
+  const int wr = KSP == 1 ? wave : wave & (WM / 2 - 1);
+  const int wj = KSP == 1 ? 0 : wave / (WM / 2);
+
+  // Persistent schedule over the tiles of the output frames with an active
+  // tap.  Each XCD owns one contiguous range of them (neighbouring tiles
+  // share source frames in its L2).  A workgroup's first two tiles are
+  // fixed; it claims each later one while the tile before it runs, from its
+  // XCD's counter and, once that range is used up, from the other XCDs'
+  // counters, so XCDs that run at different clocks still finish together.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  auto xcd_wgs = [&](int x) { return (int(gridDim.x) >> 3) + (x < int(gridDim.x & 7) ? 1 : 0); };
+  auto xcd_begin = [&](int x) { return x * (a.nat >> 3) + min(x, a.nat & 7); };
+  auto xcd_len = [&](int x) { return (a.nat >> 3) + (x < (a.nat & 7) ? 1 : 0); };
+  auto fixed_tile = [&](int k) {  // k-th fixed tile (k = 0, 1) of this workgroup, or -1
+    const int r = slot + k * xcd_wgs(xcd);
+    return r < xcd_len(xcd) ? xcd_begin(xcd) + r : -1;
+  };
+  int* const sched = g32_sched + a.sched_slot * kSchedInts;
+  auto claim = [&](int x) {  // next claim number on XCD x's counter
+    return __hip_atomic_fetch_add(sched + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto claimed = [&](int x, int v) {  // the tile of claim v on XCD x, or -1 once its range is used up
+    const int r = 2 * xcd_wgs(x) + v;
+    return r < xcd_len(x) ? xcd_begin(x) + r : -1;
+  };
+  int ctile = fixed_tile(0), tnext = fixed_tile(1), tnn = -1;  // this tile, the next two
+  int steal = 0;  // (thread 0) offset of the XCD whose counter it claims from
+  __shared__ int claim_lds;
+
+  const int ngrp = a.cin / 32;                   // 32-channel groups per tap
+  const int nch = a.cin / 16;                    // 16-channel weight sub-stages per tap
+  const int64_t frame_el = int64_t(a.h) * a.wd * a.cin;
+  const int frame_bytes = int(frame_el * 2);
+  const unsigned short* __restrict__ xs = static_cast<const unsigned short*>(a.x);
+  const unsigned short* __restrict__ cs = static_cast<const unsigned short*>(a.cache);
+  const unsigned char* __restrict__ wpk = static_cast<const unsigned char*>(WPK ? a.wpk : a.w);
+  const int64_t w_bytes = int64_t(a.cout) * a.kt * 9 * a.cin * 2;
+  const unsigned short* __restrict__ bs = static_cast<const unsigned short*>(a.b);
+  unsigned short* __restrict__ os = static_cast<unsigned short*>(a.out);
+
+  struct Tile {
+    int o, nb, nn, x0, y0, n0, nact;
+    int k0, k1, k2, k3;
+    int z0, z1, z2, z3;
+  };
+  auto act_frame = [&](int j) {  // the j-th output frame with an active tap
+    int o = a.act_lo[0] + j;
+#pragma unroll
+    for (int i = 0; i + 1 < kMaxFrameIv; ++i)
+      if (i + 1 < a.nact_iv && j >= a.act_n[i]) {
+        j -= a.act_n[i];
+        o = a.act_lo[i + 1] + j;
+      }
+    return o;
+  };
+  auto decode = [&](int t) {
+    Tile c;
+    c.o = act_frame(t % a.ta_n);
+    t /= a.ta_n;
+    c.nb = t % a.nblk_n;
+    t /= a.nblk_n;
+    const int tile_x = t % a.tiles_x;
+    t /= a.tiles_x;
+    const int tile_y = t % a.tiles_y;
+    c.nn = t / a.tiles_y;
+    c.x0 = tile_x * TW;
+    c.y0 = tile_y * TH;
+    c.n0 = c.nb * BN;
+    c.nact = 0;
+    c.k0 = c.k1 = c.k2 = c.k3 = 0;
+    c.z0 = c.z1 = c.z2 = c.z3 = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxTapsBf16; ++k) {
+      const int z = c.o * a.st + a.delta[k];
+      if (k < a.kt && z >= 0 && z < a.tz) {
+        if (c.nact == 0) { c.k0 = k; c.z0 = z; }
+        else if (c.nact == 1) { c.k1 = k; c.z1 = z; }
+        else if (c.nact == 2) { c.k2 = k; c.z2 = z; }
+        else { c.k3 = k; c.z3 = z; }
+        ++c.nact;
+      }
+    }
+    return c;
+  };
+  auto pick = [](int i, int v0, int v1, int v2, int v3) { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; };
+  auto uniform = [](const void* p) { return uniform_ptr(p); };
+  // gather offsets of this thread's weight slots (in-place weights)
+  int woff[WIT];
+#pragma unroll
+  for (int it = 0; it < WIT; ++it) woff[it] = WPK ? (it * NT + tid) * 16 : w_gather_offset<BN, 3, 16>(it * NT + tid, a.kt, a.cin);
+
+  // Byte offsets within a frame of the halo slots this thread fills (slot id
+  // = it*NT + tid; 4 slots of 16 bytes per pixel, XOR-swizzled); slots in the
+  // spatial zero padding get an offset past the buffer's record count, and
+  // the buffer load's range check writes zeros for them.
+  constexpr int OOB = int(0x80000000u);
+  int zoff[ZIT];
+  auto halo_offsets = [&](const Tile& c) {
+#pragma unroll
+    for (int it = 0; it < ZIT; ++it) {
+      const int id = tid + NT * it;
+      int off = OOB;
+      if (id < ZCH) {
+        const int pix = id / PZ;
+        const int q = (id % PZ) ^ swz<PZ>(pix);
+        const int col = pix % WP;
+        // input column of the stored pixel: at stride 2 the even ones, then the odd
+        const int u = SS == 1 ? col : col <= TW ? 2 * col : 2 * (col - TW - 1) + 1;
+        const int y = SS * c.y0 - DD + pix / WP, x = SS * c.x0 - DD + u;
+        if (y >= 0 && y < a.h && x >= 0 && x < a.wd) off = ((y * a.wd + x) * a.cin + q * 8) * 2;
+      }
+      zoff[it] = off;
+    }
+  };
+
+  // A group position: tile, active-tap index, 32-channel group.
+  struct Grp {
+    int t, ti, gz;
+  };
+  auto halo_src = [&](const Tile& c, int ti, int gz) {
+    const int z = pick(ti, c.z0, c.z1, c.z2, c.z3);
+    return static_cast<const unsigned short*>(uniform((z < a.tc ? cs + (int64_t(c.nn) * a.tc + z) * frame_el
+                                                                : xs + (int64_t(c.nn) * a.tx + (z - a.tc)) * frame_el) +
+                                                     gz * 32));
+  };
+  // the weights of sub-stage cc (16 channels) of active tap ti: the packed
+  // tile, or the stage's first piece in W and the bytes of W from there on
+  struct WSrc {
+    const unsigned char* p;
+    int rec;
+  };
+  auto wsrc = [&](const Tile& c, int ti, int cc) {
+    const int k = pick(ti, c.k0, c.k1, c.k2, c.k3);
+    WSrc r;
+    if constexpr (WPK) {
+      r.p = static_cast<const unsigned char*>(uniform(wpk + ((int64_t(c.nb) * nch + cc) * a.kt + k) * (WSLOTS * 16)));
+      r.rec = WSLOTS * 16;
+    } else {
+      const int64_t off = ((int64_t(c.nb) * BN * a.kt + k) * 9 * a.cin + cc * 16) * 2;
+      r.p = static_cast<const unsigned char*>(uniform(wpk + off));
+      r.rec = __builtin_amdgcn_readfirstlane(int(w_bytes - off));
+    }
+    return r;
+  };
+  const WSrc wnone{wpk, 0};
+  auto issue_z = [&](const unsigned short* fp, int zb, int it) {
+    if (ZSLOTS % NT == 0 || it * NT + wave * 64 < ZSLOTS) {
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(zl + zb * ZSLOTS + it * NT + wave * 64), 16, zoff[it], 0, 0, 0);
+    }
+  };
+  auto issue_w = [&](const WSrc& wp, int wb, int it) {
+    if (WSLOTS % NT == 0 || it * NT + wave * 64 < WSLOTS) {
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(wp.p), 0, wp.rec, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(wl + wb * WSLOTS + it * NT + wave * 64), 16, woff[it],
+          0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[CW][RW];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int q = 0; q < CW; ++q)
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[q][r][v] = 0.f;
+  };
+
+  // One sub-stage = 9 steps, one per spatial tap (ta, tcol), grouped by
+  // column tap: the halo rows read for a column tap serve its 3 row taps.
+  // Fragments of step i+1 are read before step i's MFMAs issue.
+  // Sub-stage J multiplies the 16 channels [16J, 16J+16) of the group.
+  constexpr int NSTEP = 9;
+  auto read_z = [&](const uint4* zb, int tcol, int J, bf16x8_t* zf) {
+    const int q = 2 * J + g;
+    const int col = SS == 1 ? tcol * DD : (tcol & 1) ? TW + 1 : tcol >> 1;
+#pragma unroll
+    for (int r = 0; r < ZR; ++r) {
+      const int pix = (wr * RW * SS + r) * WP + l32 + col;
+      zf[r] = __builtin_bit_cast(bf16x8_t, zb[pix * PZ + (q ^ swz<PZ>(pix))]);
+    }
+  };
+  auto read_w = [&](const uint4* wb, int step, bf16x8_t* wf) {
+    const int s = (step % 3) * 3 + step / 3;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) wf[c] = __builtin_bit_cast(bf16x8_t, wb[g * WT::PLANE + (c * 32 + l32) * S + s]);
+  };
+  // issue(k) is called once for k = 0..NL-1, spread over the first ISS steps
+  // A wave whose rows all lie below the image (the last patch row of a map
+  // whose height is not a multiple of TH) only issues its share of the loads.
+  auto compute = [&](const uint4* zb, const uint4* wb, bool rows_in, auto J, auto NLc, auto ISSc, auto&& issue) {
+    constexpr int NL = decltype(NLc)::value, ISS = decltype(ISSc)::value;
+    if (!rows_in) {
+#pragma unroll
+      for (int k = 0; k < NL; ++k) issue(k);
+      return;
+    }
+    bf16x8_t zf[2][ZR], wf[2][CW];
+    read_z(zb, 0, J, zf[0]);
+    read_w(wb, 0, wf[0]);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 1 < NSTEP) {
+        read_w(wb, i + 1, wf[(i + 1) & 1]);
+        if ((i + 1) % 3 == 0) read_z(zb, (i + 1) / 3, J, zf[((i + 1) / 3) & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int ta = i % 3, zsel = (i / 3) & 1;
+#pragma unroll
+      for (int c = 0; c < CW; ++c)
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+          acc[c][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i & 1][c], zf[zsel][SS * r + ta * DD], acc[c][r], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < NL; ++k)
+        if (k * ISS / NL == i) issue(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Epilogue: bias added once in fp32 (all of this lane's bias values are
+  // read before the first staging write), round to nearest even, staged per
+  // wave through an idle weight buffer (waves 0-3) or the idle halo
+  // buffer (waves 4-7) so global stores are whole 16-byte runs of channels.
+  // C_out is a multiple of BN here: every channel of the tile exists, and
+  // only the pixel column is range-checked.
+  constexpr int EPIX = CW * 4;
+  constexpr int EIT = (32 * EPIX + 63) / 64;
+  auto epilogue = [&](const Tile& c, int par, int hidle, int widle) {
+    unsigned char* eb = wave < 4 ? reinterpret_cast<unsigned char*>(wl + widle * WSLOTS) + wave * 32 * EROW
+                                 : reinterpret_cast<unsigned char*>(zl + hidle * ZSLOTS) + (wave - 4) * 32 * EROW;
+    float4 bias[CW][4];
+#pragma unroll
+    for (int q = 0; q < CW; ++q)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4)
+        bias[q][v4] = *reinterpret_cast<const float4*>(&bias_lds[par][q * 32 + v4 * 8 + g * 4]);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int y = c.y0 + wr * RW + r;
+      if (y >= a.ho) continue;
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const float4 bv = bias[q][v4];
+          const f32x16_t& v = acc[q][r];
+          uint2 pk;
+          pk.x = pack_bf16x2(v[v4 * 4 + 0] + bv.x, v[v4 * 4 + 1] + bv.y);
+          pk.y = pack_bf16x2(v[v4 * 4 + 2] + bv.z, v[v4 * 4 + 3] + bv.w);
+          *reinterpret_cast<uint2*>(eb + l32 * EROW + (q * 32 + v4 * 8 + g * 4) * 2) = pk;
+        }
+      }
+      unsigned short* orow = os + ((int64_t(c.nn) * a.to + c.o) * a.ho + y) * int64_t(a.wo) * a.cout + c.n0;
+#pragma unroll
+      for (int it = 0; it < EIT; ++it) {
+        const int piece = it * 64 + lane;
+        if (piece < 32 * EPIX) {
+          const int px = piece / EPIX, ch = (piece % EPIX) * 8;
+          const int xo = c.x0 + px;
+          const uint4 v = *reinterpret_cast<const uint4*>(eb + px * EROW + ch * 2);
+          // streaming store: the output is not read again by this kernel
+          if (xo < a.wo)
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v),
+                                        reinterpret_cast<u32x4_t*>(orow + int64_t(xo) * a.cout + ch));
+        }
+      }
+    }
+  };
+  auto bias_value = [&](const Tile& c) {
+    return (a.has_bias && tid < BN && c.n0 + tid < a.cout) ? bs[c.n0 + tid] : (unsigned short)0;
+  };
+
+  // Load cursor: the group after the one being computed; it moves on at the
+  // end of each group, after the barrier that publishes a claimed tile.  Its
+  // tile is the current one or the next (tnext); the tile after that is the
+  // one claimed during the current tile's first group (tnn), which a tile of
+  // a single group already needs.  zoff holds the halo offsets of its tile.
+  Grp nx{ctile, 0, 0};
+  Tile nt{};
+  bool nx_ok = ctile >= 0;
+  if (nx_ok) {
+    nt = decode(ctile);
+    halo_offsets(nt);
+  }
+  auto nx_advance = [&]() {
+    if (++nx.ti == nt.nact) {
+      nx.ti = 0;
+      if (++nx.gz == ngrp) {
+        nx.gz = 0;
+        nx.t = nx.t == ctile ? tnext : tnn;
+        if (nx.t < 0) {
+          nx_ok = false;
+          return;
+        }
+        nt = decode(nx.t);
+        halo_offsets(nt);
+      }
+    }
+  };
+
+  auto wait_halo_in_flight = [&]() {  // all but this wave's halo loads of the last group
+    switch (wave) {
+      case 0: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(0)) : "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(1)) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(2)) : "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(3)) : "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(4 % NW)) : "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(5 % NW)) : "memory"); break;
+      case 6: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(6 % NW)) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(7 % NW)) : "memory"); break;
+    }
+  };
+
+  // Wait for every vector memory operation.  The inline-asm waits are
+  // invisible to the compiler's own wait-count tracking; the builtin after
+  // it tells the compiler they have completed, so it does not drain loads
+  // again where it reuses the register of an earlier load or atomic.
+  auto vm_drain = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0), other counters unconstrained
+  };
+
+  // Workgroup barrier with explicit waits only: the caller has waited for
+  // the loads that must have landed; this waits for the wave's own LDS
+  // accesses.  (__syncthreads() would also drain every load in flight,
+  // including the next group's halo.)
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if constexpr (KSP == 2) {
+    // prologue: the first group's halo and both weight halves (group buffer 0)
+    int wcur = 0;  // weight group buffer of the current group: halves 2*wcur, 2*wcur+1
+    if (nx_ok) {
+      const unsigned short* fp = halo_src(nt, nx.ti, nx.gz);
+      const WSrc w0p = wsrc(nt, nx.ti, nx.gz * 2);
+      const WSrc w1p = wsrc(nt, nx.ti, nx.gz * 2 + 1);
+#pragma unroll
+      for (int it = 0; it < ZIT; ++it) issue_z(fp, 0, it);
+#pragma unroll
+      for (int it = 0; it < WIT; ++it) issue_w(w0p, 0, it);
+#pragma unroll
+      for (int it = 0; it < WIT; ++it) issue_w(w1p, 1, it);
+      nx_advance();
+      vm_drain();
+      barrier();
+    }
+    int hpar = 0, par = 0;
+    if (ctile >= 0) {
+      Tile ct = decode(ctile);
+      for (;;) {
+        zero_acc();
+        const bool claims = tnext >= 0;
+        const int ngt = ct.nact * ngrp;
+        const bool rows_in = ct.y0 + wr * RW < a.ho;  // wave-uniform
+        for (int gi = 0; gi < ngt; ++gi) {
+          const uint4* zb = zl + hpar * ZSLOTS;
+          unsigned short bval = 0;
+          if (gi == 0) bval = bias_value(ct);
+          const bool more = nx_ok;
+          // in the first group thread 0 claims a tile (published at the barrier)
+          const int cx = (xcd + steal) & 7;
+          int v = 0;
+          if (gi == 0 && claims && tid == 0) v = claim(cx);
+          {
+            // load the next group's weight halves and halo into the free buffers
+            const WSrc wn0 = more ? wsrc(nt, nx.ti, nx.gz * 2) : wnone;
+            const WSrc wn1 = more ? wsrc(nt, nx.ti, nx.gz * 2 + 1) : wnone;
+            const unsigned short* fpn = more ? halo_src(nt, nx.ti, nx.gz) : xs;
+            const int hn = __builtin_amdgcn_readfirstlane(hpar ^ 1);
+            const int wn = __builtin_amdgcn_readfirstlane((wcur ^ 1) * 2);
+            compute(zb, wl + (wcur * 2 + wj) * WSLOTS, rows_in, wj, std::integral_constant<int, 2 * WIT + ZIT>{},
+                    std::integral_constant<int, NSTEP>{}, [&](int k) {
+                      if (!more) return;
+                      if (k < WIT) issue_w(wn0, wn, k);
+                      else if (k < 2 * WIT) issue_w(wn1, wn + 1, k - WIT);
+                      else issue_z(fpn, hn, k - 2 * WIT);
+                    });
+          }
+          asm volatile("" ::: "memory");  // the claim is read only after the group
+          if (gi == 0 && claims && tid == 0) {
+            int t = claimed(cx, v);
+            while (t < 0 && steal < 7) {
+              ++steal;
+              const int x = (xcd + steal) & 7;
+              t = claimed(x, claim(x));
+            }
+            claim_lds = t;
+          }
+          if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+          vm_drain();
+          barrier();
+          if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
+          if (more) nx_advance();
+          hpar ^= 1;
+          wcur ^= 1;
+        }
+        // the second half's sums join the first's through the idle halo buffer
+        float* red = reinterpret_cast<float*>(zl + (hpar ^ 1) * ZSLOTS);
+        if (wj == 1) {
+#pragma unroll
+          for (int c = 0; c < CW; ++c)
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) red[(((wr * CW + c) * RW + r) * 16 + e) * 64 + lane] = acc[c][r][e];
+        }
+        barrier();
+        if (wj == 0) {
+#pragma unroll
+          for (int c = 0; c < CW; ++c)
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[c][r][e] += red[(((wr * CW + c) * RW + r) * 16 + e) * 64 + lane];
+          // (the output stores may stay in flight across the barrier below)
+          epilogue(ct, par, hpar ^ 1, (wcur ^ 1) * 2);
+        }
+        barrier();
+        par ^= 1;
+        ctile = tnext;
+        tnext = tnn;
+        tnn = -1;
+        if (ctile < 0) break;
+        ct = decode(ctile);
+      }
+    }
+  } else {
+    // prologue: the first group's halo and first weight sub-stage
+    int hpar = 0;
+    if (nx_ok) {
+      const unsigned short* fp = halo_src(nt, nx.ti, nx.gz);
+      const WSrc wp = wsrc(nt, nx.ti, nx.gz * 2);
+#pragma unroll
+      for (int it = 0; it < ZIT; ++it) issue_z(fp, 0, it);
+#pragma unroll
+      for (int it = 0; it < WIT; ++it) issue_w(wp, 0, it);
+      nx_advance();
+      vm_drain();
+      barrier();
+    }
+
+    int par = 0;
+    if (ctile >= 0) {
+      Tile ct = decode(ctile);
+      for (;;) {
+        zero_acc();
+        const bool claims = tnext >= 0;  // claim the tile after tnext while this one runs
+        const int ngt = ct.nact * ngrp;  // >= 1: only frames with an active tap have tiles
+        const bool rows_in = ct.y0 + wr * RW < a.ho;  // wave-uniform
+        for (int gi = 0; gi < ngt; ++gi) {
+          // group-major order: the active taps of one 32-channel group run back
+          // to back, so a source frame's group is reused by the output frames of
+          // the neighbouring tiles within a few groups, while it is still in L2
+          const int gz = gi / ct.nact, ti = gi - gz * ct.nact;
+          const uint4* zb = zl + hpar * ZSLOTS;
+          unsigned short bval = 0;
+          if (gi == 0) bval = bias_value(ct);
+          const bool more = nx_ok;
+          // sub-stage 0: load W[1] <- (this group, second half), H[next] <- next group
+          {
+            const WSrc wp1 = wsrc(ct, ti, gz * 2 + 1);
+            const unsigned short* fpn = more ? halo_src(nt, nx.ti, nx.gz) : xs;
+            const int hn = __builtin_amdgcn_readfirstlane(hpar ^ 1);
+            compute(zb, wl, rows_in, std::integral_constant<int, 0>{}, std::integral_constant<int, WIT + ZIT>{},
+                    std::integral_constant<int, NSTEP>{}, [&](int k) {
+                      if (k < WIT) issue_w(wp1, 1, k);
+                      else if (more) issue_z(fpn, hn, k - WIT);
+                    });
+          }
+          if (more) wait_halo_in_flight();
+          else vm_drain();
+          if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+          barrier();
+          // sub-stage 1: load W[0] <- next group, first half.  In the first
+          // group, thread 0 also claims a tile (the atomic's latency hides
+          // behind the sub-stage; the claim is published at its barrier).
+          const int cx = (xcd + steal) & 7;
+          int v = 0;
+          if (gi == 0 && claims && tid == 0) v = claim(cx);
+          {
+            const WSrc wpn = more ? wsrc(nt, nx.ti, nx.gz * 2) : wnone;
+            compute(zb, wl + WSLOTS, rows_in, std::integral_constant<int, 1>{}, std::integral_constant<int, WIT>{},
+                    std::integral_constant<int, (NSTEP + 1) / 2>{}, [&](int k) {
+                      if (more) issue_w(wpn, 0, k);
+                    });
+          }
+          asm volatile("" ::: "memory");  // the claim is read only after the sub-stage
+          if (gi == 0 && claims && tid == 0) {
+            int t = claimed(cx, v);
+            while (t < 0 && steal < 7) {
+              ++steal;
+              const int x = (xcd + steal) & 7;
+              t = claimed(x, claim(x));
+            }
+            claim_lds = t;
+          }
+          vm_drain();
+          barrier();
+          if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
+          if (more) nx_advance();
+          hpar ^= 1;
+        }
+        // (the output stores may stay in flight across this barrier)
+        epilogue(ct, par, hpar ^ 1, 1);
+        barrier();
+        par ^= 1;
+        ctile = tnext;
+        tnext = tnn;
+        tnn = -1;
+        if (ctile < 0) break;
+        ct = decode(ctile);
+      }
+    }
+  }
+
+  // Output frames without an active tap hold the bias: every workgroup
+  // writes a strided share of them (C_out % 8 == 0: 16-byte runs).
+  {
+    const int64_t fpx = int64_t(a.ho) * a.wo;
+    const int cpp = a.cout >> 3;
+#pragma unroll 1
+    for (int i = 0; i < a.nina_iv; ++i) {
+      const int64_t per_n = int64_t(a.ina_n[i]) * fpx * cpp;
+      for (int64_t e = int64_t(blockIdx.x) * NT + tid; e < per_n * a.n; e += int64_t(gridDim.x) * NT) {
+        const int nn = int(e / per_n);
+        const int64_t r = e - nn * per_n;
+        const int cc = int(r % cpp);
+        unsigned short v8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v8[q] = a.has_bias ? bs[cc * 8 + q] : (unsigned short)0;
+        uint4 val;
+        __builtin_memcpy(&val, v8, 16);
+        *reinterpret_cast<uint4*>(os + ((int64_t(nn) * a.to + a.ina_lo[i]) * fpx + r / cpp) * a.cout + cc * 8) = val;
+      }
+    }
+  }
+
+  // The last workgroup to finish clears the counters for the next launch
+  // that uses them (its claims and every other workgroup's are done: each
+  // workgroup counts itself after its last claim).
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(sched + 8, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == int(gridDim.x) - 1)
+      for (int x = 0; x < 9; ++x) __hip_atomic_store(sched + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#endif
+}
+
+template <int BN, int TH, int WM, int DD, int SS, int KSP, bool WPK>
+const void* g32_kernel() {
+  return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM, DD, SS, KSP, WPK>);
+}
+
+template <int BN, int TH, int WM, int DD = 1, int SS = 1, int KSP = 1>
+hipError_t launch_g32(const ConvArgs& a, int64_t tiles, int cus, hipStream_t s) {
+  if (a.wpk) return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS, KSP, true>>(a, tiles, cus, WM * 64, s);
+  return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS, KSP, false>>(a, tiles, cus, WM * 64, s);
+}
+
+}  // namespace
+
+namespace cc3d {
+
+hipError_t launch_g32_family(int kernel_id, const ConvArgs& a, int64_t tiles, int cus, hipStream_t s) {
+  switch (kernel_id) {
+    case CC3D_K_BF16_S3_N96_G32W8: return launch_g32<96, 16, 8>(a, tiles, cus, s);
+    case CC3D_K_BF16_S3_N64_G32W8: return launch_g32<64, 24, 8>(a, tiles, cus, s);
+    case CC3D_K_BF16_S3D2_N64_G32W8: return launch_g32<64, 16, 8, 2>(a, tiles, cus, s);
+    case CC3D_K_BF16_S3S2_N96_G32W4: return launch_g32<96, 4, 4, 1, 2>(a, tiles, cus, s);
+    case CC3D_K_BF16_S3S2_N64_G32W8: return launch_g32<64, 4, 8, 1, 2, 2>(a, tiles, cus, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cc3d

@@ -90,6 +90,20 @@ bool strided_3x3(const cc3d_desc_t& d) {
          d.p_w == 1;
 }
 
+// Fingerprint of a packed weight image: plans whose fingerprints (and
+// packed_weight_bytes) are equal read the same image, whatever their frame
+// counts, cache depth and map size.  FNV-1a over the fields that shape it.
+uint64_t layout_fingerprint(int32_t kind, int32_t block_n, int32_t ks, int32_t cin_chunk, const cc3d_desc_t& d) {
+  const int32_t f[] = {kind, block_n, ks, cin_chunk, d.c_out, d.c_in, d.k_t, d.k_h, d.k_w};
+  uint64_t h = 1469598103934665603ull;
+  for (int32_t v : f)
+    for (int i = 0; i < 4; ++i) {
+      h ^= uint64_t((uint32_t(v) >> (8 * i)) & 0xFF);
+      h *= 1099511628211ull;
+    }
+  return h;
+}
+
 bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
   const std::string n(name);
   if (n == "bf16_gen_n64_p8x32") {  // any spatial parameters
@@ -296,17 +310,21 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     in.block_n = v.block_n;
     // the few-channel kernel's patches run through every output frame
     in.tiles = int64_t(d.n) * (v.id == CC3D_K_BF16_S3_FEW ? 1 : t_out) * p->tiles_y * p->tiles_x * p->nblk_n;
-    // packed weights: one stage tile of 16-byte slots per (tap, channel chunk, channel block)
+    // Packed weight image: for the halo-staged kernels one stage tile of
+    // 16-byte slots per (channel block, channel chunk, tap), in that order;
+    // the few-channel and gather kernels read W's own layout, so theirs is a
+    // copy of W.
     const int64_t ks = d.k_h;
-    const int64_t slots = (int64_t(v.block_n) * ks * ks * (v.cin_chunk / 8) + 255) / 256 * 256;
-    p->wpk_bytes = int64_t(d.k_t) * (d.c_in / v.cin_chunk) * p->nblk_n * slots * 16;
-    if (v.id == CC3D_K_BF16_S3_FEW) {
-      p->wpk_bytes = int64_t(d.c_in / 32) * 9 * 64 * 16;  // register fragments
-      in.bytes_cache_out /= 2;                            // written from the staged rows, not re-read
+    const int64_t slots = (int64_t(v.block_n) * ks * ks * (v.cin_chunk / 8) + 63) / 64 * 64;
+    p->pack_kind = 1;
+    in.packed_weight_bytes = int64_t(d.k_t) * (d.c_in / v.cin_chunk) * p->nblk_n * slots * 16;
+    if (v.id == CC3D_K_BF16_S3_FEW || v.id == CC3D_K_BF16_GEN_N64 || v.id == CC3D_K_BF16_GEN_N96) {
+      p->pack_kind = 2;
+      in.packed_weight_bytes = w_bytes;
     }
-    if (v.id == CC3D_K_BF16_GEN_N64 || v.id == CC3D_K_BF16_GEN_N96) p->wpk_bytes = w_bytes;  // a copy of W, read as it is
-    p->sched_off = (p->wpk_bytes + 255) / 256 * 256;
-    in.workspace_bytes = p->sched_off + int64_t(kSchedSlots) * kSchedInts * 4;
+    if (v.id == CC3D_K_BF16_S3_FEW) in.bytes_cache_out /= 2;  // written from the staged rows, not re-read
+    in.weight_layout = layout_fingerprint(p->pack_kind, v.block_n, int32_t(ks), v.cin_chunk, d);
+    in.splits = 1;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);
   } else {
     if (kernel && std::strcmp(kernel, "f32_direct") != 0) {
@@ -353,13 +371,7 @@ extern "C" cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_inf
   return CC3D_OK;
 }
 
-void cc3d_release_workspace(cc3d_plan_t plan);  // defined with the kernels
-
-extern "C" void causal_conv3d_plan_destroy(cc3d_plan_t plan) {
-  if (!plan) return;
-  cc3d_release_workspace(plan);
-  delete plan;
-}
+extern "C" void causal_conv3d_plan_destroy(cc3d_plan_t plan) { delete plan; }
 
 extern "C" const char* causal_conv3d_status_string(cc3d_status_t s) {
   switch (s) {

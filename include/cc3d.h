@@ -41,20 +41,19 @@
  *   out        [N][T_o][H_o][W_o][C_out]
  *   cache_out  [N][min(p_base, T_cache + T_x)][H][W][C_in]
  *
- * Ownership: every tensor is caller-owned device memory.  A bf16 plan also
- * owns one device workspace (workspace_bytes, allocated by its first forward
- * or pack call on the device current then, freed by
- * causal_conv3d_plan_destroy): the weights repacked into the kernel's stage
- * order (for the gather kernel a plain copy of W), rewritten by every
- * causal_conv3d_forward before the convolution on the same stream, and 64
- * slots of tile counters for the group-staged kernel's dynamic schedule
- * (each launch takes the next slot and leaves it zeroed when it completes).
- * Nothing else is kept.
- * Threading: a plan's shape data is immutable and any thread may call it.
- * causal_conv3d_forward rewrites the workspace, so those calls on one plan
- * must be ordered on one stream (use one plan per stream for concurrent
- * streams).  causal_conv3d_forward_packed calls of one plan may overlap on
- * different streams, at most 64 in flight at once.  Counters are atomic.
+ * Ownership: every tensor is caller-owned device memory, and so is the packed
+ * weight image of causal_conv3d_pack_weights.  A plan is host metadata only
+ * (no device memory, no device call when it is built); it keeps no weight
+ * copy.  The library's only device state is a static table of tile counters
+ * for the group-staged kernel's dynamic schedule (each launch takes a slot
+ * and leaves it zero when it completes).
+ * Threading: plans are immutable; any thread may use a plan, and calls of
+ * one plan may run at the same time on different streams (at most 1024
+ * launches of the group-staged kernel in flight per process).  A launch
+ * recorded during stream capture keeps its counter slot for every replay of
+ * the graph: two graph launches that share a slot (one in 1024 captured
+ * launches) must not run at the same time; they never share one with an
+ * eager call.  Counters are atomic.
  * Errors: every check is synchronous and happens before any launch; a launch
  * failure reported by the runtime returns CC3D_ERR_DEVICE; faults during
  * execution surface at the caller's next synchronisation.  The library never
@@ -129,7 +128,14 @@ typedef struct cc3d_plan_info {
   int32_t block_m, block_n; /* output pixels x output channels per tile */
   int64_t tiles;          /* output tiles of the conv kernel (bf16: processed by
                              min(tiles, compute units) persistent workgroups) */
-  int64_t workspace_bytes; /* device workspace the plan allocates on first use */
+  int64_t packed_weight_bytes; /* size of the packed weight image (bf16) */
+  uint64_t weight_layout;      /* fingerprint of that image: plans with equal
+                                  weight_layout and packed_weight_bytes read
+                                  the same image (e.g. the chunk plans of one
+                                  streaming signature) */
+  int64_t workspace_bytes;     /* device scratch causal_conv3d_forward_packed
+                                  needs (split reductions); 0: none */
+  int32_t splits;              /* K-splits per tile of forward_packed (1: none) */
   char kernel_name[64];
 } cc3d_plan_info_t;
 
@@ -182,7 +188,7 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *   padding)
  *   "bf16_gen_n64_p8x32"      any spatial parameters (default outside that
  *                              envelope): input pixels gathered per spatial
- *                              tap, W read as it is from a workspace copy
+ *                              tap, W read as it is
  *   "bf16_gen_n96_p8x32"      the same, 96 output channels per tile,
  *                              C_out % 96 == 0 (the default there)
  *   "bf16_s3d2_n64_p16x32_g32" 3x3 at spatial dilation 2, padding 2, unit
@@ -207,14 +213,16 @@ cc3d_status_t causal_conv3d_plan_variant(const cc3d_desc_t* desc, const char* ke
  * Per-signature tuning (the pages time every runtime signature of a decoder;
  * the variant that suits one shape need not suit another).  Plans desc on
  * every bf16 variant that can run it, runs each once on the caller's
- * buffers (which packs its weights), times `launches` further convolutions
- * of it with HIP events on `stream`, and returns in *out the plan of the
- * fastest, its weights packed, with its average time in *best_ms (may be
- * NULL).  fp32 descriptors get causal_conv3d_plan's plan without timing.
+ * buffers with its weights packed into a temporary device buffer (which it
+ * allocates and frees), times `launches` further convolutions of it with HIP
+ * events on `stream`, and returns in *out the plan of the fastest with its
+ * average time in *best_ms (may be NULL).  fp32 descriptors get
+ * causal_conv3d_plan's plan without timing.
  *   x, cache_in, w, b, out  as for causal_conv3d_forward (out is
  *                           overwritten; cache_out is not written)
  *   launches                timed convolutions per variant, >= 1
- * Blocking: it waits for its own launches.  Every launch counts in the
+ * Blocking: it waits for its own launches (a tuning-time call, not for the
+ * decode loop).  Every launch counts in the
  * fast-path counter.  Returns what causal_conv3d_plan returns for a refused
  * descriptor, CC3D_ERR_INVALID_ARG for a NULL out or launches < 1 or a
  * buffer the forward call rejects, and CC3D_ERR_DEVICE when a launch or an
@@ -227,8 +235,8 @@ cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, const void* x
 /* Intervals, sizes, work and launch geometry of a plan (host only). */
 cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_info_t* info);
 
-/* Release a plan and its device workspace; NULL is ignored.  The caller must
- * make sure no forward call of this plan is still executing on the GPU. */
+/* Release a plan (host memory only); NULL is ignored.  Launches already
+ * issued do not depend on the plan. */
 void causal_conv3d_plan_destroy(cc3d_plan_t plan);
 
 /*
@@ -236,41 +244,50 @@ void causal_conv3d_plan_destroy(cc3d_plan_t plan);
  *   x          device pointer, [N][T_x][H][W][C_in]; required.
  *   cache_in   device pointer, [N][T_cache][H][W][C_in]; required when
  *              T_cache > 0, ignored when T_cache = 0.
- *   w          device pointer, [C_out][k_t][k_h][k_w][C_in]; required.
+ *   w          device pointer, [C_out][k_t][k_h][k_w][C_in]; required.  Read
+ *              in place (the kernels gather each stage's weights from it).
  *   b          device pointer, [C_out]; required iff has_bias.
  *   out        device pointer, [N][T_o][H_o][W_o][C_out]; required.
  *   cache_out  device pointer, [N][t_cache_out][H][W][C_in], or NULL when no
  *              carry is wanted.
  *   stream     a hipStream_t (NULL: the null stream).
  * Frames of Z outside every tap's source interval are never read (e.g. the
- * leading |C| - p_base cache frames when |C| > p_base).
+ * leading |C| - p_base cache frames when |C| > p_base).  Allocates nothing,
+ * never synchronises; the call may be recorded in a graph.
  * Returns CC3D_ERR_INVALID_ARG (nothing launched) for a NULL required
  * pointer, a bf16 buffer not 16-byte aligned (fp32: 4-byte), `out`
- * overlapping any other buffer, `cache_out` overlapping x, cache_in, w or
- * b (in a streaming loop ping-pong two cache buffers), or a bf16 plan used
- * on another device than its first forward call.  Returns CC3D_ERR_DEVICE if
- * the runtime rejects a launch or the workspace allocation.
+ * overlapping any other buffer, or `cache_out` overlapping x, cache_in, w or
+ * b (in a streaming loop ping-pong two cache buffers).  Returns
+ * CC3D_ERR_DEVICE if the runtime rejects a launch.
  */
 cc3d_status_t causal_conv3d_forward(cc3d_plan_t plan, const void* x, const void* cache_in,
                                     const void* w, const void* b, void* out, void* cache_out,
                                     void* stream);
 
 /*
- * Weights that do not change between calls (a decoder at inference) need not
- * be repacked by every call.  causal_conv3d_pack_weights repacks w into the
- * plan's workspace on `stream` (bf16 plans; allocates the workspace on first
- * use); causal_conv3d_forward_packed then runs the convolution with the
- * weights last packed into this plan -- by either causal_conv3d_pack_weights
- * or causal_conv3d_forward -- and takes no weight pointer.  Both return
- * CC3D_ERR_INVALID_ARG for an fp32 plan, a NULL required pointer, and
- * (forward_packed) a plan whose weights were never packed; pointer and
- * overlap rules are those of causal_conv3d_forward.  The packed weights are
- * read by the convolution asynchronously: do not repack a plan while an
- * earlier forward_packed of it may still run on another stream.
+ * Weights that do not change between calls (a decoder at inference) can be
+ * packed once into the kernels' stage order, so that every stage's weights
+ * stream into LDS as whole cache lines (the paper keeps the weights
+ * unchanged and slices them per tap; here the one image serves every tap).
+ * causal_conv3d_pack_weights writes plan_info.packed_weight_bytes bytes of
+ * that image from w into the caller-owned device buffer w_packed (16-byte
+ * aligned) on `stream`.  Every plan with the same weight_layout reads the
+ * same image, so the chunk plans of one streaming signature share one.
+ * causal_conv3d_forward_packed then runs the convolution from it; its other
+ * arguments are those of causal_conv3d_forward, plus a caller-owned
+ * workspace of at least plan_info.workspace_bytes (NULL and 0 when that is
+ * 0; zero-filled before its first use; calls that share a workspace must
+ * not overlap).  Both are asynchronous on `stream`, allocate nothing and may
+ * be recorded in a graph.  They return CC3D_ERR_INVALID_ARG for an fp32
+ * plan, a NULL required pointer, a misaligned buffer, w_packed overlapping w
+ * (pack) or out / cache_out (forward), or a workspace smaller than
+ * workspace_bytes; the other rules are causal_conv3d_forward's.  The image
+ * is read asynchronously: do not rewrite it while a call may still read it.
  */
-cc3d_status_t causal_conv3d_pack_weights(cc3d_plan_t plan, const void* w, void* stream);
+cc3d_status_t causal_conv3d_pack_weights(cc3d_plan_t plan, const void* w, void* w_packed, void* stream);
 cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const void* x, const void* cache_in,
-                                           const void* b, void* out, void* cache_out, void* stream);
+                                           const void* w_packed, const void* b, void* out, void* cache_out,
+                                           void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * The RGB head with its pixel quantisation fused in (FastVideo pull request
@@ -283,9 +300,8 @@ cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const void* x, cons
  * decided in fp32 from the unrounded fp32 sum y (bias included).  scale =
  * offset = 0.5 maps a head output in [-1, 1] to [0, 1] first (that mapping is
  * not on the pages; it is the usual video-decoder convention).  A NaN sum
- * gives code 0.  w NULL runs with the weights last packed into the plan (as
- * causal_conv3d_forward_packed); otherwise w is packed first (as
- * causal_conv3d_forward).  cache_out is written as by causal_conv3d_forward.
+ * gives code 0.  w is read in place, as by causal_conv3d_forward; cache_out
+ * is written as by causal_conv3d_forward.
  * out needs no alignment.  Returns CC3D_ERR_UNSUPPORTED unless the plan runs
  * on the few-output-channel kernel ("bf16_s3_few_p<R>x128"),
  * CC3D_ERR_INVALID_ARG for a NaN scale or offset and as

@@ -141,6 +141,39 @@ DECODER_SIGNATURES = [
     _sig("full_96", 96, 96, 720, 1280, 4, 2),
     _sig("head_96_3", 96, 3, 720, 1280, 4, 2),
 ]
+# Causal Conv3D signatures of the two 480x832 decodes the pages run (setup
+# section): the image-to-video decoder whose latents are [1, 48, T, 30, 52]
+# (48 latent channels, 16x spatial compression) and the world-model decoder
+# fed [1, 16, T, 60, 104] latents (16 channels, 8x).  Their layer tables are
+# not on the pages; each is derived as the 720x1280 table above is: the same
+# channel widths per stage (384 at the latent-side stages, 192, then 96 at
+# full resolution), one 2x spatial upsampling between stages, the latent
+# input conv from the latent channels, a temporal (3,1,1) 384->768 conv at
+# each of the two stages that double the frame rate, and 1, 2, then 4 frames
+# per steady-state chunk (the 1 + 4*4 schedule).  The 16x decoder has one
+# 384-channel stage more than the 8x one (30x52 -> 60x104 -> 120x208).  Calls
+# the two decoders share (from 240x416 on) are listed once.
+DECODER_SIGNATURES_480 = [
+    # 48-channel latents at 30x52
+    _sig("conv_in_48_384_30x52", 48, 384, 30, 52, 1, 2),
+    _sig("latent_384_30x52", 384, 384, 30, 52, 1, 2),
+    _sig("temporal_384_768_30x52", 384, 768, 30, 52, 1, 2, k=(3, 1, 1)),
+    _sig("stage_384_60x104_2f", 384, 384, 60, 104, 2, 2),
+    _sig("temporal_384_768_60x104_2f", 384, 768, 60, 104, 2, 2, k=(3, 1, 1)),
+    _sig("stage_384_120x208_4f", 384, 384, 120, 208, 4, 2),
+    # 16-channel latents at 60x104
+    _sig("conv_in_16_384_60x104", 16, 384, 60, 104, 1, 2),
+    _sig("latent_384_60x104", 384, 384, 60, 104, 1, 2),
+    _sig("temporal_384_768_60x104", 384, 768, 60, 104, 1, 2, k=(3, 1, 1)),
+    _sig("stage_384_120x208_2f", 384, 384, 120, 208, 2, 2),
+    _sig("temporal_384_768_120x208_2f", 384, 768, 120, 208, 2, 2, k=(3, 1, 1)),
+    # both decoders from 240x416 on
+    _sig("mid_384_192_240x416", 384, 192, 240, 416, 4, 2),
+    _sig("mid_192_240x416", 192, 192, 240, 416, 4, 2),
+    _sig("full_192_96_480x832", 192, 96, 480, 832, 4, 2),
+    _sig("full_96_480x832", 96, 96, 480, 832, 4, 2),
+    _sig("head_96_3_480x832", 96, 3, 480, 832, 4, 2),
+]
 # The encoder's stride-2 temporal downsampling convs (the pages' only
 # fallbacks: outside the unit-stride contract), as temporal-only (3,1,1)
 # convs at the two coarsest stages of a 720x1280 encoder, four new frames

@@ -1,5 +1,9 @@
 """Test-side helpers for the GPU parity tests: run the library through its
-binding, and compare against the oracle with the stated tolerances."""
+binding, and compare against the oracle with the stated tolerances.
+
+Outputs and carried caches are filled with NaN before every launch, so a
+tile a kernel never writes shows up as NaN (or as a mismatch) instead of
+passing on memory that an earlier launch left correct."""
 import re
 
 import numpy as np
@@ -22,29 +26,51 @@ def plan_for(x, tc, w, *, k, pad, dt=1, p_base=2, has_bias=True, dtype=torch.bfl
     return cc3d.causal_conv3d_plan(desc)
 
 
+def nan_like(shape, dtype, device):
+    return torch.full(shape, float("nan"), dtype=dtype, device=device)
+
+
+def workspace_for(plan, device):
+    nb = plan.info["workspace_bytes"]
+    return torch.zeros(nb, dtype=torch.uint8, device=device) if nb else None
+
+
 def run(x, cache, w, b, *, k=(3, 3, 3), pad=(1, 1), dt=1, p_base=2, want_cache=True, out=None, variant=None, st=1,
-        sst=(1, 1), sdil=(1, 1)):
+        sst=(1, 1), sdil=(1, 1), packed=False, image=None):
     """GPU forward through the C ABI; returns (out, cache_out, plan).  variant
-    pins a kernel variant by name (default: the library's choice)."""
+    pins a kernel variant by name (default: the library's choice).  packed:
+    run causal_conv3d_forward_packed from a packed image (``image``, or one
+    packed here); otherwise causal_conv3d_forward, which reads W in place.
+    out and cache_out are NaN-filled before the launch."""
     tc = 0 if cache is None else cache.shape[1]
     plan = plan_for(x, tc, w, k=k, pad=pad, dt=dt, p_base=p_base, has_bias=b is not None, dtype=x.dtype,
                     variant=variant, st=st, sst=sst, sdil=sdil)
     sh = plan.shapes()
     if out is None:
-        out = torch.empty(sh["out"], dtype=x.dtype, device=x.device)
-    co = torch.empty(sh["cache_out"], dtype=x.dtype, device=x.device) if want_cache else None
-    cc3d.causal_conv3d_forward(plan, x, cache, w, b, out, co)
+        out = nan_like(sh["out"], x.dtype, x.device)
+    co = nan_like(sh["cache_out"], x.dtype, x.device) if want_cache else None
+    if packed and x.dtype == torch.bfloat16:
+        if image is None:
+            image = cc3d.causal_conv3d_pack_weights(plan, w)
+        cc3d.causal_conv3d_forward_packed(plan, x, cache, image, b, out, co, workspace_for(plan, x.device))
+    else:
+        cc3d.causal_conv3d_forward(plan, x, cache, w, b, out, co)
     return out, co, plan
 
 
-def metrics(got, ref):
+def metrics(got, ref, exclude=None):
     """The comparison metrics of the paper's evaluation: max and mean absolute
-    difference, RMSE, cosine similarity (fp64 accumulation), NaN/Inf counts."""
+    difference, RMSE, cosine similarity (fp64 accumulation), NaN/Inf counts.
+    exclude: optional boolean mask (broadcast over channels) of positions left
+    out (the bias-only ones, which are checked bit for bit instead)."""
     g = got.detach().float().cpu().numpy().astype(np.float64) if isinstance(got, torch.Tensor) else got
     r = np.asarray(ref, dtype=np.float64)
     g = g.reshape(r.shape)
+    if exclude is not None:
+        keep = ~np.broadcast_to(exclude, r.shape)
+        g, r = g[keep], r[keep]
     d = g - r
-    rms = float(np.sqrt(np.mean(r * r)))
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     denom = float(np.linalg.norm(g) * np.linalg.norm(r))
     return {
         "max_abs": float(np.max(np.abs(d))) if d.size else 0.0,
@@ -54,11 +80,12 @@ def metrics(got, ref):
         "cos": float(np.sum(g * r) / denom) if denom > 0 else 1.0,
         "nonfinite_gpu": int(np.sum(~np.isfinite(g))),
         "nonfinite_ref": int(np.sum(~np.isfinite(r))),
+        "count": int(r.size),
     }
 
 
-def assert_bf16_close(got, ref, what=""):
-    m = metrics(got, ref)
+def assert_bf16_close(got, ref, what="", exclude=None):
+    m = metrics(got, ref, exclude)
     assert m["nonfinite_gpu"] == 0 and m["nonfinite_ref"] == 0, (what, m)
     assert m["max_abs"] <= BF16_REL_TOL * m["rms_ref"], (what, m)
     return m
@@ -71,6 +98,48 @@ def assert_f32_close(got, ref, what=""):
     return m
 
 
+def bias_only_mask(n, t_out, h_out, w_out, *, tz, p_l, kt=3, kh=3, kw=3, st=1, sh=1, sw=1, dt=1, dh=1, dw=1, ph=1,
+                   pw=1, h, w):
+    """[N][T_o][H_o][W_o][1] mask of the outputs that no term of the sum
+    reaches: output frames with no active temporal tap (every source time
+    o*s_t + k*d_t - p_l outside [0, |Z|)), and rows or columns whose every
+    spatial tap falls in the zero padding.  Their value is the bias alone
+    (zero without a bias), exactly."""
+    def none_in(idx, stride, dil, pad, k, size):
+        pos = idx[:, None] * stride - pad + np.arange(k)[None, :] * dil
+        return ~((pos >= 0) & (pos < size)).any(1)
+    fo = none_in(np.arange(t_out), st, dt, p_l, kt, tz)
+    fr = none_in(np.arange(h_out), sh, dh, ph, kh, h)
+    fc = none_in(np.arange(w_out), sw, dw, pw, kw, w)
+    m = fo[:, None, None] | fr[None, :, None] | fc[None, None, :]
+    return np.broadcast_to(m[None, :, :, :, None], (n, t_out, h_out, w_out, 1)).copy()
+
+
+def assert_bias_only_exact(y, b, mask, what=""):
+    """Every masked output equals the bias exactly (+0 without a bias): the
+    fp32 sum of nothing but the bias, rounded to bf16, is the bf16 bias."""
+    m = torch.from_numpy(np.ascontiguousarray(mask[..., 0])).to(y.device)
+    if not bool(m.any()):
+        return 0
+    got = y[m].view(torch.int16)                             # [P][C_out]
+    if b is None:
+        want = torch.zeros_like(got[0])
+    else:
+        want = b.to(y.dtype).view(torch.int16)
+    bad = int((got != want[None, :]).sum())
+    assert bad == 0, (what, "bias-only outputs that differ from the bias", bad)
+    return int(m.sum())
+
+
+def mask_for(plan, x_shape, *, k=(3, 3, 3), pad=(1, 1), st=1, sst=(1, 1), dt=1, sdil=(1, 1)):
+    """bias_only_mask of a plan's output."""
+    i = plan.info
+    n, _, h, w, _ = x_shape
+    return bias_only_mask(n, i["t_out"], i["h_out"], i["w_out"], tz=i["t_z"], p_l=i["p_l"], kt=k[0], kh=k[1],
+                          kw=k[2], st=st, sh=sst[0], sw=sst[1], dt=dt, dh=sdil[0], dw=sdil[1], ph=pad[0], pw=pad[1],
+                          h=h, w=w)
+
+
 def tile_of(plan):
     """(rows, columns) of the plan's output tile, from its kernel name
     ("..._p<rows>x<cols>..."); (8, 32) for kernels without one."""
@@ -79,9 +148,9 @@ def tile_of(plan):
 
 
 def sample_points(n, to, ho, wo, count, seed, tile_h=8, tile_w=32):
-    """Output positions to check at full size: all corners and edge midpoints,
-    positions on both sides of every few workgroup-tile boundaries, and
-    uniform random positions, for every batch item and output frame."""
+    """Output positions to check: all corners and edge midpoints, positions
+    on both sides of every few workgroup-tile boundaries, and uniform random
+    positions, for every batch item and output frame."""
     rng = np.random.default_rng(seed)
     pts = set()
     for nn in range(n):

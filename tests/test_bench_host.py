@@ -36,19 +36,33 @@ def fake_root(tmp_path, monkeypatch):
     return str(tmp_path)
 
 
+K = "bf16_s3_n64_p24x32_g32"
+
+
 def test_traffic_is_read_for_the_current_source_and_workload(fake_root):
-    _write_profile(fake_root, "k", bench._source_hash(), "mid_192 (C 192->192, ...)", 123456789)
-    assert bench.traffic_for("k", "mid_192") == 123456789.0
-    assert bench.traffic_for("k") == 123456789.0
+    _write_profile(fake_root, K, bench._source_hash(K), "mid_192 (C 192->192, ...)", 123456789)
+    assert bench.traffic_for(K, "mid_192") == 123456789.0
+    assert bench.traffic_for(K) == 123456789.0
+
+
+def test_source_hash_follows_the_kernels_own_files():
+    # the group-staged kernel's hash covers its translation unit and the
+    # shared headers, not the other kernel families
+    files = bench._kernel_sources(K)
+    assert "cc3d_k_g32.hip" in files and "cc3d_device.h" in files and "cc3d_k_mfma.hip" not in files
+    assert "cc3d_few.inc" in bench._kernel_sources("bf16_s3_few_p15x128")
+    assert bench._source_hash(K) != bench._source_hash("bf16_s3_few_p15x128")
+    for f in bench._kernel_sources(None):
+        assert os.path.exists(os.path.join(bench.CSRC, f))
 
 
 def test_traffic_is_null_once_the_source_changed(fake_root):
-    _write_profile(fake_root, "k", "0" * 64, "mid_192 (C 192->192, ...)", 123456789)
-    assert bench.traffic_for("k", "mid_192") is None
+    _write_profile(fake_root, K, "0" * 64, "mid_192 (C 192->192, ...)", 123456789)
+    assert bench.traffic_for(K, "mid_192") is None
 
 
 def test_traffic_is_null_for_another_workload_or_kernel(fake_root):
-    _write_profile(fake_root, "k", bench._source_hash(), "mid_192 (C 192->192, ...)", 123456789)
-    assert bench.traffic_for("k", "mid_192_dt2") is None
+    _write_profile(fake_root, K, bench._source_hash(K), "mid_192 (C 192->192, ...)", 123456789)
+    assert bench.traffic_for(K, "mid_192_dt2") is None
     assert bench.traffic_for("other", "mid_192") is None
 

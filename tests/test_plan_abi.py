@@ -194,11 +194,12 @@ def test_strided_tap_intervals_match_brute_force_enumeration():
 def test_general_spatial_parameters_take_the_gather_kernel(kw):
     """bf16 calls outside the halo-staged kernels' envelope (3x3 "same" or
     1x1, stride and dilation 1) run on the general-spatial kernel, which
-    reads W as it is (its workspace holds a copy of W)."""
+    reads W as it is (its packed image is a copy of W)."""
     p = cc3d.causal_conv3d_plan(_desc(c_in=32, c_out=40, h=20, w=36, **kw))
     assert p.info["kernel_name"] == "bf16_gen_n64_p8x32" and p.info["block_m"] == 256 and p.info["block_n"] == 64
     k = kw.get("k", (3, 3, 3))
-    assert p.info["workspace_bytes"] >= 40 * k[0] * k[1] * k[2] * 32 * 2
+    assert p.info["packed_weight_bytes"] == 40 * k[0] * k[1] * k[2] * 32 * 2
+    assert p.info["workspace_bytes"] == 0
     for name in ["bf16_s3_n96_p16x32_g32", "bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32",
                  "bf16_s1_n32_p8x32"]:
         with pytest.raises(cc3d.CC3DError):
@@ -328,27 +329,65 @@ def test_workload_signatures_get_mfma_kernels():
         pad = (1, 1) if k[1] == 3 else (0, 0)
         p = cc3d.causal_conv3d_plan(_desc(c_in=cin, c_out=cout, h=h, w=w, t_x=tx, t_cache=tc, k=k, padding=pad))
         assert p.info["kernel_name"].startswith("bf16_"), p.info["kernel_name"]
-        assert p.info["tiles"] > 0 and p.info["workspace_bytes"] > 0
+        assert p.info["tiles"] > 0 and p.info["packed_weight_bytes"] >= cout * k[0] * k[1] * k[2] * cin * 2
 
 
 def test_packed_entry_points_refuse_fp32_plans_and_null_pointers():
     lib = ctypes.CDLL(LIB)
-    lib.causal_conv3d_pack_weights.argtypes = [ctypes.c_void_p] * 3
+    vp = ctypes.c_void_p
+    lib.causal_conv3d_pack_weights.argtypes = [vp] * 4
     lib.causal_conv3d_pack_weights.restype = ctypes.c_int
-    lib.causal_conv3d_forward_packed.argtypes = [ctypes.c_void_p] * 7
+    lib.causal_conv3d_forward_packed.argtypes = [vp] * 8 + [ctypes.c_int64, vp]
     lib.causal_conv3d_forward_packed.restype = ctypes.c_int
     f32 = cc3d.causal_conv3d_plan(_desc(dtype=torch.float32))
     bf = cc3d.causal_conv3d_plan(_desc(t_cache=2))
     base = 1 << 40  # never dereferenced: every call below is refused before any device call
     mb = 1 << 20
-    assert lib.causal_conv3d_pack_weights(f32.handle, base, None) == cc3d.CC3D_ERR_INVALID_ARG
-    assert lib.causal_conv3d_forward_packed(f32.handle, base, base + mb, base + 2 * mb, base + 3 * mb, None,
+    x, c, wp, b, out = base, base + mb, base + 2 * mb, base + 3 * mb, base + 4 * mb
+    assert lib.causal_conv3d_pack_weights(f32.handle, x, wp, None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_forward_packed(f32.handle, x, c, wp, b, out, None, None, 0,
                                             None) == cc3d.CC3D_ERR_INVALID_ARG
-    assert lib.causal_conv3d_pack_weights(bf.handle, None, None) == cc3d.CC3D_ERR_INVALID_ARG
-    assert lib.causal_conv3d_forward_packed(bf.handle, None, base + mb, base + 2 * mb, base + 3 * mb, None,
+    assert lib.causal_conv3d_pack_weights(bf.handle, None, wp, None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_pack_weights(bf.handle, x, None, None) == cc3d.CC3D_ERR_INVALID_ARG
+    # the image overlapping the weights it is packed from
+    assert lib.causal_conv3d_pack_weights(bf.handle, x, x + 16, None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_pack_weights(bf.handle, x, wp + 8, None) == cc3d.CC3D_ERR_INVALID_ARG  # misaligned
+    assert lib.causal_conv3d_forward_packed(bf.handle, None, c, wp, b, out, None, None, 0,
                                             None) == cc3d.CC3D_ERR_INVALID_ARG
-    assert lib.causal_conv3d_forward_packed(None, base, base + mb, base + 2 * mb, base + 3 * mb, None,
+    assert lib.causal_conv3d_forward_packed(bf.handle, x, c, None, b, out, None, None, 0,
                                             None) == cc3d.CC3D_ERR_INVALID_ARG
+    # the output overlapping the packed image
+    assert lib.causal_conv3d_forward_packed(bf.handle, x, c, wp, b, wp, None, None, 0,
+                                            None) == cc3d.CC3D_ERR_INVALID_ARG
+    # a negative workspace size, or a size without a buffer
+    assert lib.causal_conv3d_forward_packed(bf.handle, x, c, wp, b, out, None, None, -1,
+                                            None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_forward_packed(bf.handle, x, c, wp, b, out, None, None, 64,
+                                            None) == cc3d.CC3D_ERR_INVALID_ARG
+    assert lib.causal_conv3d_forward_packed(None, x, c, wp, b, out, None, None, 0,
+                                            None) == cc3d.CC3D_ERR_INVALID_ARG
+
+
+def test_plans_hold_no_device_memory_and_chunk_plans_share_one_weight_image():
+    """A plan is host metadata: no device workspace.  The five chunk plans of
+    a streaming signature (chunk 0 without a cache, the others with the
+    2-frame carry) read one packed weight image: equal weight_layout and
+    packed_weight_bytes; the layout changes with the kernel's tile or the
+    weight shape, not with the frame counts."""
+    for cin, cout, h, w, tx, k in [(192, 192, 360, 640, 4, (3, 3, 3)), (96, 96, 720, 1280, 4, (3, 3, 3)),
+                                   (384, 384, 90, 160, 1, (3, 3, 3)), (384, 768, 90, 160, 1, (3, 1, 1)),
+                                   (96, 3, 720, 1280, 4, (3, 3, 3))]:
+        pad = (1, 1) if k[1] == 3 else (0, 0)
+        plans = [cc3d.causal_conv3d_plan(_desc(c_in=cin, c_out=cout, h=h, w=w, t_x=tx, t_cache=tc, k=k, padding=pad))
+                 for tc in (0, 2, 2, 2, 2)]
+        assert len({(p.info["weight_layout"], p.info["packed_weight_bytes"]) for p in plans}) == 1
+        assert all(p.info["workspace_bytes"] == 0 for p in plans)
+    a = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2))
+    b = cc3d.causal_conv3d_plan_variant(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2),
+                                        "bf16_s3_n96_p16x32_g32")
+    c = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=96, h=360, w=640, t_x=4, t_cache=2))
+    assert a.info["weight_layout"] != b.info["weight_layout"]
+    assert a.info["weight_layout"] != c.info["weight_layout"]
 
 
 def test_default_kernel_choice():
