@@ -53,6 +53,16 @@ struct ConvArgs {
   int co_lo;
   int out_u8;
   float px_scale, px_offset;
+  // Split reduction (conv_bf16_mfma): each tile's stages are divided among
+  // `splits` work units (tile-major, split-minor; ntiles counts the units).
+  // With splits > 1 every unit writes its fp32 partial sums to the
+  // workspace at ws + ws_part, counts itself in the tile's arrival counter
+  // at ws (an int per tile, zero at launch), and the last unit to arrive sums
+  // the partials in split order -- the same order whichever unit arrives
+  // last -- adds the bias and stores the tile; it leaves the counter zero.
+  int splits;
+  void* ws;
+  int64_t ws_part;
 };
 
 // Scheduler counter table of the group-staged kernel (a static device array

@@ -105,16 +105,24 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
   const unsigned short* __restrict__ bs = static_cast<const unsigned short*>(a.b);
   unsigned short* __restrict__ os = static_cast<unsigned short*>(a.out);
 
-  // A tile: one output frame o of batch item nn, a TH x 32 patch at (y0, x0),
-  // output channels [n0, n0 + BN); its active taps k[0..nact) read source
-  // frames z[i] = o + delta_k[i] of Z = [cache; x].
+  // A work unit: split `sp` of tile `t` -- one output frame o of batch item
+  // nn, a TH x 32 patch at (y0, x0), output channels [n0, n0 + BN); its
+  // active taps k[0..nact) read source frames z[i] = o + delta_k[i] of
+  // Z = [cache; x].  The tile's stages (active tap major, channel chunk
+  // minor: nact * nch of them) are divided evenly among the splits; this
+  // unit runs stages [s0, s1).
   struct Tile {
     int o, nb, nn, x0, y0, n0, nact;
     int k0, k1, k2, k3;  // active taps, in order
     int z0, z1, z2, z3;  // their source frames
+    int t, sp, s0, s1;
   };
-  auto decode = [&](int t) {
+  const int splits = a.splits;
+  auto decode = [&](int u) {
     Tile c;
+    c.t = u / splits;
+    c.sp = u - c.t * splits;
+    int t = c.t;
     c.o = t % a.to;
     t /= a.to;
     c.nb = t % a.nblk_n;
@@ -140,6 +148,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
         ++c.nact;
       }
     }
+    const int nst = c.nact * (a.cin / CB);
+    c.s0 = c.sp * nst / splits;
+    c.s1 = (c.sp + 1) * nst / splits;
     return c;
   };
   auto pick = [](int i, int v0, int v1, int v2, int v3) { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; };
@@ -354,28 +365,39 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
   };
 
   // Load cursor: runs NBUF-1 stages ahead of the compute cursor over the
-  // flattened (tile, stage) sequence, crossing tile boundaries, so a tile's
-  // first stages load while the previous tile finishes and writes its
-  // outputs.  Stage position p uses LDS buffer p % NBUF.
-  int ltile = ctile, lcc = 0, lti = 0;
+  // flattened (unit, stage) sequence, crossing unit boundaries, so a unit's
+  // first stages load while the previous unit finishes and writes its
+  // outputs.  Stage position p uses LDS buffer p % NBUF.  lst is the stage
+  // of the unit's tile (tap lti = lst / nch, chunk lcc = lst % nch).
+  int ltile = ctile, lcc = 0, lti = 0, lst = 0;
   Tile lt = decode(ltile);
+  auto lt_set = [&]() {
+    lst = lt.s0;
+    lti = lst / nch;
+    lcc = lst - lti * nch;
+  };
   auto lt_advance_tile = [&]() {
-    lcc = 0;
-    lti = 0;
     for (;;) {
       ltile = next_tile(ltile);
       if (ltile < 0) return;
       lt = decode(ltile);
-      if (lt.nact > 0) break;
+      if (lt.s1 > lt.s0) break;
     }
+    lt_set();
     halo_offsets(lt);
   };
-  if (lt.nact > 0) halo_offsets(lt);
-  else lt_advance_tile();
+  if (lt.s1 > lt.s0) {
+    lt_set();
+    halo_offsets(lt);
+  } else {
+    lt_advance_tile();
+  }
   auto advance_load = [&]() {
-    if (++lcc == nch) {
+    if (++lst == lt.s1) {
+      lt_advance_tile();
+    } else if (++lcc == nch) {
       lcc = 0;
-      if (++lti == lt.nact) lt_advance_tile();
+      ++lti;
     }
   };
   auto issue = [&](int buf) {  // whole stage at once (pipeline prologue)
@@ -412,26 +434,79 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  // Split reduction: this thread's share of a unit's fp32 partial sums
+  // (NACC floats, stored as float4 runs interleaved across the workgroup's
+  // threads so that each store instruction writes one contiguous block).
+  constexpr int NACC = CW * RW * 16;
+  int* const arrivals = static_cast<int*>(a.ws);
+  float4* const parts = reinterpret_cast<float4*>(static_cast<unsigned char*>(a.ws) + a.ws_part);
+  __shared__ int last_lds;
+  // Store this unit's partials, count its arrival; returns (uniformly)
+  // whether it arrived last, in which case acc then holds the tile's sum
+  // over all splits, in split order.
+  auto reduce_splits = [&](const Tile& c) {
+    float4* mine = parts + (int64_t(c.t) * splits + c.sp) * (NACC / 4) * NT;
+#pragma unroll
+    for (int q = 0; q < CW; ++q)
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int e4 = (q * RW + r) * 4 + v4;
+          mine[e4 * NT + tid] = make_float4(acc[q][r][v4 * 4], acc[q][r][v4 * 4 + 1], acc[q][r][v4 * 4 + 2],
+                                            acc[q][r][v4 * 4 + 3]);
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) {
+      const int before = __hip_atomic_fetch_add(arrivals + c.t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = before == splits - 1;
+      if (last) __hip_atomic_store(arrivals + c.t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_lds = last;
+    }
+    __syncthreads();
+    const bool last = __builtin_amdgcn_readfirstlane(last_lds) != 0;
+    if (last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      zero_acc();
+      const float4* tp = parts + int64_t(c.t) * splits * (NACC / 4) * NT;
+      for (int sp = 0; sp < splits; ++sp) {
+#pragma unroll
+        for (int q = 0; q < CW; ++q)
+#pragma unroll
+          for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+              const float4 p = tp[(int64_t(sp) * (NACC / 4) + (q * RW + r) * 4 + v4) * NT + tid];
+              acc[q][r][v4 * 4] += p.x;
+              acc[q][r][v4 * 4 + 1] += p.y;
+              acc[q][r][v4 * 4 + 2] += p.z;
+              acc[q][r][v4 * 4 + 3] += p.w;
+            }
+      }
+    }
+    return last;
+  };
+
   int pos = 0, par = 0;
   Tile ct = decode(ctile);
   for (;;) {
     zero_acc();
-    const int nst = ct.nact * nch;
-    if (nst == 0) {
-      // no active tap: the output is the bias alone
+    if (ct.s1 == ct.s0) {
+      // no stage (no active tap, or fewer stages than splits)
       if (tid < BN) bias_lds[par][tid] = bf16_to_f32(bias_value(ct));
       __syncthreads();
-      epilogue(ct, par, pos % NBUF);
+      if (splits == 1 || reduce_splits(ct)) epilogue(ct, par, pos % NBUF);
       __syncthreads();
     } else {
-      for (int st = 0; st < nst; ++st, ++pos) {
+      for (int st = ct.s0; st < ct.s1; ++st, ++pos) {
         unsigned short bval = 0;
-        if (st == 0) bval = bias_value(ct);  // issued before this stage's loads
+        if (st == ct.s0) bval = bias_value(ct);  // issued before this stage's loads
         const bool more = ltile >= 0;
         const StageLoad nl = prep_stage(lt, lcc, lti, (pos + NBUF - 1) % NBUF);
         compute(pos % NBUF, more, nl);
         if (more) advance_load();  // after the pieces: they read this tile's halo offsets
-        if (st == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+        if (st == ct.s0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
         // wait until stage pos+1 has landed (the NBUF-2 newer stages may stay
         // in flight); the barrier then publishes everyone's loads and the
         // bias, and retires this stage's LDS reads
@@ -442,7 +517,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
       // the buffer of the last stage is idle until the next stage's loads are
       // issued: stage the outputs through it, then make sure every wave is
       // done with it before those loads go out
-      epilogue(ct, par, (pos - 1) % NBUF);
+      if (splits == 1 || reduce_splits(ct)) epilogue(ct, par, (pos - 1) % NBUF);
       __syncthreads();
     }
     par ^= 1;

@@ -171,6 +171,7 @@ void plan_args(const cc3d_plan* plan, ConvArgs& a) {
   a.ntiles = int(in.tiles);
   a.has_bias = d.has_bias;
   a.co_lo = in.t_z;
+  a.splits = 1;
 }
 
 // Pixel output of the head: 8-bit codes instead of bf16 (see ConvArgs).
@@ -179,9 +180,11 @@ struct PixelOut {
 };
 
 // One convolution of `plan`.  Exactly one of w (weights as stored) and wpk
-// (the packed image) is given.
+// (the packed image) is given; ws (ws_bytes >= plan_info.workspace_bytes)
+// enables the plan's split reduction.
 cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, const void* w, const void* wpk,
-                       const void* b, void* out, void* cache_out, void* stream, const PixelOut* px = nullptr) {
+                       const void* b, void* out, void* cache_out, void* stream, const PixelOut* px = nullptr,
+                       void* ws = nullptr, int64_t ws_bytes = 0) {
   if (!plan) return invalid();
   const cc3d_desc_t& d = plan->d;
   const cc3d_plan_info_t& in = plan->info;
@@ -208,6 +211,12 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
       overlaps(cache_out, plan->cache_out_bytes, wsrc, wsrc_bytes) ||
       overlaps(cache_out, plan->cache_out_bytes, b, plan->b_bytes))
     return invalid();
+  const bool split = ws && in.splits > 1;
+  if (split && (ws_bytes < in.workspace_bytes || !aligned(ws, 256) || overlaps(ws, ws_bytes, out, out_bytes) ||
+                overlaps(ws, ws_bytes, cache_out, plan->cache_out_bytes) || overlaps(ws, ws_bytes, x, plan->x_bytes) ||
+                overlaps(ws, ws_bytes, cache_in, plan->cache_bytes) || overlaps(ws, ws_bytes, wsrc, wsrc_bytes) ||
+                overlaps(ws, ws_bytes, b, plan->b_bytes)))
+    return invalid();
 
   ConvArgs a{};
   plan_args(plan, a);
@@ -228,6 +237,12 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   const bool fused_co = in.kernel_id == CC3D_K_BF16_S3_FEW && cache_out && in.t_cache_out > 0;
   a.cache_out = fused_co ? cache_out : nullptr;
   a.co_lo = fused_co ? a.tz - in.t_cache_out : a.tz;
+  a.splits = split ? in.splits : 1;
+  a.ntiles = int(in.tiles * a.splits);
+  if (split) {
+    a.ws = ws;
+    a.ws_part = (in.tiles * 4 + 255) / 256 * 256;
+  }
   if (px) {
     a.out_u8 = 1;
     a.px_scale = px->scale;
@@ -251,7 +266,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   hipError_t e = hipSuccess;
   if (in.kernel_id == CC3D_K_F32_DIRECT) e = cc3d::launch_f32_direct(a, in.tiles, s);
   else if (is_g32(in.kernel_id)) e = cc3d::launch_g32_family(in.kernel_id, a, std::max<int64_t>(a.nat, 1), cus, s);
-  else if (is_mfma(in.kernel_id)) e = cc3d::launch_mfma_family(in.kernel_id, plan->cin_chunk, a, in.tiles, cus, s);
+  else if (is_mfma(in.kernel_id)) e = cc3d::launch_mfma_family(in.kernel_id, plan->cin_chunk, a, a.ntiles, cus, s);
   else if (in.kernel_id == CC3D_K_BF16_S3_FEW) {
     switch (d.c_out) {
       case 1: e = cc3d::launch_few_cout<1>(a, in.tiles, cus, s); break;
@@ -307,7 +322,9 @@ extern "C" cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const vo
                                                       void* stream) {
   if (!plan || !w_packed || plan->d.dtype != CC3D_BF16) return invalid();
   if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return invalid();
-  return run_plan(plan, x, cache_in, nullptr, w_packed, b, out, cache_out, stream);
+  if (plan->info.workspace_bytes > 0 && (!workspace || workspace_bytes < plan->info.workspace_bytes)) return invalid();
+  return run_plan(plan, x, cache_in, nullptr, w_packed, b, out, cache_out, stream, nullptr, workspace,
+                  workspace_bytes);
 }
 
 extern "C" cc3d_status_t causal_conv3d_forward_u8(cc3d_plan_t plan, const void* x, const void* cache_in,
@@ -352,7 +369,8 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
     return device_error();
   }
   void* wpk = nullptr;
-  int64_t wpk_bytes = 0;
+  void* ws = nullptr;
+  int64_t wpk_bytes = 0, ws_bytes = 0;
   cc3d_plan_t best = nullptr;
   float best_t = 0.f;
   cc3d_status_t st = CC3D_ERR_UNSUPPORTED;
@@ -365,6 +383,7 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
       break;
     }
     cc3d_status_t rs = CC3D_OK;
+    // temporary packed image and split workspace (zero-filled), grown as needed
     if (p->info.packed_weight_bytes > wpk_bytes) {
       if (wpk) (void)hipFree(wpk);
       wpk = nullptr;
@@ -376,12 +395,23 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
         wpk_bytes = p->info.packed_weight_bytes;
       }
     }
+    if (rs == CC3D_OK && p->info.workspace_bytes > ws_bytes) {
+      if (ws) (void)hipFree(ws);
+      ws = nullptr;
+      ws_bytes = 0;
+      if (hipStreamSynchronize(s) != hipSuccess || hipMalloc(&ws, size_t(p->info.workspace_bytes)) != hipSuccess ||
+          hipMemsetAsync(ws, 0, size_t(p->info.workspace_bytes), s) != hipSuccess) {
+        rs = device_error();
+      } else {
+        ws_bytes = p->info.workspace_bytes;
+      }
+    }
     // pack, one untimed run, then time the convolution alone
     if (rs == CC3D_OK) rs = causal_conv3d_pack_weights(p, w, wpk, stream);
-    if (rs == CC3D_OK) rs = causal_conv3d_forward_packed(p, x, cache_in, wpk, b, out, nullptr, nullptr, 0, stream);
+    if (rs == CC3D_OK) rs = causal_conv3d_forward_packed(p, x, cache_in, wpk, b, out, nullptr, ws, ws_bytes, stream);
     if (rs == CC3D_OK && hipEventRecord(e0, s) != hipSuccess) rs = device_error();
     for (int i = 0; i < launches && rs == CC3D_OK; ++i)
-      rs = causal_conv3d_forward_packed(p, x, cache_in, wpk, b, out, nullptr, nullptr, 0, stream);
+      rs = causal_conv3d_forward_packed(p, x, cache_in, wpk, b, out, nullptr, ws, ws_bytes, stream);
     float ms = 0.f;
     if (rs == CC3D_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
                           hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
@@ -404,6 +434,7 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
   }
   (void)hipStreamSynchronize(s);
   if (wpk) (void)hipFree(wpk);
+  if (ws) (void)hipFree(ws);
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (st != CC3D_OK || !best) {

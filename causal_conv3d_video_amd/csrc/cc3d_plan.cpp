@@ -5,6 +5,7 @@
 // Decoders", lowering section), and the kernel tile choice.  No device calls.
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -46,6 +47,10 @@ bool same_spatial(const cc3d_desc_t& d) {
   return d.k_h == d.k_w && (d.k_h == 1 || d.k_h == 3) && d.s_h == 1 && d.s_w == 1 && d.d_h == 1 && d.d_w == 1 &&
          d.p_h == (d.k_h - 1) / 2 && d.p_w == (d.k_w - 1) / 2;
 }
+
+// Compute units of the target (MI355X); the split heuristic sizes work for
+// them (the kernels themselves run on any count).
+constexpr int kComputeUnits = 256;
 
 // The few-output-channel kernel streams halo rows through patches of 4 to
 // 16 output rows by 128 columns.
@@ -324,7 +329,26 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     }
     if (v.id == CC3D_K_BF16_S3_FEW) in.bytes_cache_out /= 2;  // written from the staged rows, not re-read
     in.weight_layout = layout_fingerprint(p->pack_kind, v.block_n, int32_t(ks), v.cin_chunk, d);
+    // Split reduction (conv_bf16_mfma only; causal_conv3d_forward_packed):
+    // when a call has fewer tiles than the chip has workgroup slots, each
+    // tile's K stages are divided among up to 16 units (at least 4 stages
+    // each) so that the slots fill.  Each unit writes a tile of fp32
+    // partials (block_m * block_n floats) to the workspace, after an int per
+    // tile of arrival counters.
     in.splits = 1;
+    if (v.id == CC3D_K_BF16_S3_N96_X2 || v.id == CC3D_K_BF16_S3_N32 || v.id == CC3D_K_BF16_S1_N192 ||
+        v.id == CC3D_K_BF16_S1_N32) {
+      const int wg_per_cu = (v.id == CC3D_K_BF16_S1_N192 || v.cin_chunk == 64) ? 1 : 2;
+      const int64_t slots = int64_t(kComputeUnits) * wg_per_cu;
+      const int64_t stages = int64_t(in.n_active_taps) * (d.c_in / v.cin_chunk);
+      if (in.tiles < slots) {
+        const int64_t s = std::min<int64_t>({slots / std::max<int64_t>(in.tiles, 1), stages / 4, 16});
+        in.splits = int32_t(std::max<int64_t>(s, 1));
+      }
+      if (in.splits > 1)
+        in.workspace_bytes = (in.tiles * 4 + 255) / 256 * 256 +
+                             in.tiles * in.splits * int64_t(in.block_m) * in.block_n * 4;
+    }
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", v.name);
   } else {
     if (kernel && std::strcmp(kernel, "f32_direct") != 0) {
@@ -339,6 +363,7 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     in.kernel_id = CC3D_K_F32_DIRECT;
     in.block_m = 256;
     in.block_n = 1;
+    in.splits = 1;
     const int64_t total = int64_t(d.n) * t_out * h_out * w_out * d.c_out;
     in.tiles = (total + 255) / 256;
     std::snprintf(in.kernel_name, sizeof in.kernel_name, "%s", "f32_direct");
@@ -354,15 +379,60 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
 
 }  // namespace
 
+namespace {
+
+// With CC3D_LOG=1 in the environment every plan built is printed to stderr:
+// the descriptor, the tap intervals, the kernel and its work.
+bool log_plans() {
+  static const bool on = [] {
+    const char* v = std::getenv("CC3D_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+void dump_plan(const cc3d_plan* p) {
+  const cc3d_desc_t& d = p->d;
+  const cc3d_plan_info_t& i = p->info;
+  std::fprintf(stderr,
+               "cc3d plan: N=%d C_in=%d C_out=%d H=%d W=%d T_x=%d T_cache=%d k=(%d,%d,%d) s=(%d,%d,%d) "
+               "d=(%d,%d,%d) p=(%d,%d) p_base=%d bias=%d %s\n"
+               "  |Z|=%d p_l=%d T_o=%d H_o=%d W_o=%d cache_out=%d active taps=%d\n",
+               d.n, d.c_in, d.c_out, d.h, d.w, d.t_x, d.t_cache, d.k_t, d.k_h, d.k_w, d.s_t, d.s_h, d.s_w, d.d_t,
+               d.d_h, d.d_w, d.p_h, d.p_w, d.p_base, d.has_bias, d.dtype == CC3D_BF16 ? "bf16" : "fp32", i.t_z,
+               i.p_l, i.t_out, i.h_out, i.w_out, i.t_cache_out, i.n_active_taps);
+  for (int k = 0; k < d.k_t; ++k)
+    std::fprintf(stderr, "  tap %d: delta=%d out=[%d,%d) src=[%d,%d)%s\n", k, i.taps[k].delta, i.taps[k].o_lo,
+                 i.taps[k].o_hi, i.taps[k].src_lo, i.taps[k].src_hi, i.taps[k].active ? "" : " inactive");
+  std::fprintf(stderr,
+               "  kernel %s: tile %d px x %d ch, %lld tiles, splits %d, packed weights %lld B, workspace %lld B, "
+               "%.3f GFLOP active (%.3f nominal)\n",
+               i.kernel_name, i.block_m, i.block_n, static_cast<long long>(i.tiles), i.splits,
+               static_cast<long long>(i.packed_weight_bytes), static_cast<long long>(i.workspace_bytes),
+               i.flops_active * 1e-9, i.flops_nominal * 1e-9);
+}
+
+cc3d_status_t plan_logged(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t* out) {
+  const cc3d_status_t s = plan_impl(desc, kernel, out);
+  if (log_plans()) {
+    if (s == CC3D_OK) dump_plan(*out);
+    else std::fprintf(stderr, "cc3d plan refused%s%s: %s\n", kernel ? " for " : "", kernel ? kernel : "",
+                      causal_conv3d_status_string(s));
+  }
+  return s;
+}
+
+}  // namespace
+
 extern "C" cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out) {
-  return plan_impl(desc, nullptr, out);
+  return plan_logged(desc, nullptr, out);
 }
 
 extern "C" cc3d_status_t causal_conv3d_plan_variant(const cc3d_desc_t* desc, const char* kernel_name,
                                                     cc3d_plan_t* out) {
   if (out) *out = nullptr;
   if (!kernel_name) return refuse(CC3D_ERR_INVALID_ARG);
-  return plan_impl(desc, kernel_name, out);
+  return plan_logged(desc, kernel_name, out);
 }
 
 extern "C" cc3d_status_t causal_conv3d_plan_info(cc3d_plan_t plan, cc3d_plan_info_t* info) {

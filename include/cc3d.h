@@ -213,17 +213,17 @@ cc3d_status_t causal_conv3d_plan_variant(const cc3d_desc_t* desc, const char* ke
  * Per-signature tuning (the pages time every runtime signature of a decoder;
  * the variant that suits one shape need not suit another).  Plans desc on
  * every bf16 variant that can run it, runs each once on the caller's
- * buffers with its weights packed into a temporary device buffer (which it
- * allocates and frees), times `launches` further convolutions of it with HIP
- * events on `stream`, and returns in *out the plan of the fastest with its
- * average time in *best_ms (may be NULL).  fp32 descriptors get
+ * buffers through causal_conv3d_forward_packed, with its weights packed
+ * into a temporary device buffer and a temporary split workspace (which it
+ * allocates and frees), times `launches` further convolutions of it with
+ * HIP events on `stream`, and returns in *out the plan of the fastest with
+ * its average time in *best_ms (may be NULL).  fp32 descriptors get
  * causal_conv3d_plan's plan without timing.
  *   x, cache_in, w, b, out  as for causal_conv3d_forward (out is
  *                           overwritten; cache_out is not written)
  *   launches                timed convolutions per variant, >= 1
  * Blocking: it waits for its own launches (a tuning-time call, not for the
- * decode loop).  Every launch counts in the
- * fast-path counter.  Returns what causal_conv3d_plan returns for a refused
+ * decode loop).  Every launch counts in the fast-path counter.  Returns what causal_conv3d_plan returns for a refused
  * descriptor, CC3D_ERR_INVALID_ARG for a NULL out or launches < 1 or a
  * buffer the forward call rejects, and CC3D_ERR_DEVICE when a launch or an
  * event fails; *out is NULL on error.

@@ -462,10 +462,12 @@ def test_packed_weights_path_matches_forward_bitwise(cuda_device):
     layout feeds the same MFMA sequence.  The image packed from one plan
     serves another plan of the same weight layout (a different frame count
     and cache depth), and an image of the wrong size is refused."""
-    x, c, w, b = synth.conv_inputs(1, 48, 96, 20, 70, 2, 2, device=DEV, seed=synth.SEED_BASE + 80)
+    # (enough tiles that the packed call does not split its K stages)
+    x, c, w, b = synth.conv_inputs(1, 48, 96, 136, 512, 2, 2, device=DEV, seed=synth.SEED_BASE + 80)
     plan = plan_for(x, 2, w, k=(3, 3, 3), pad=(1, 1))
+    assert plan.info["splits"] == 1
     y1, _, _ = run(x, c, w, b)
-    x0 = synth.conv_inputs(1, 48, 96, 20, 70, 4, 0, device=DEV, seed=synth.SEED_BASE + 81)[0]
+    x0 = synth.conv_inputs(1, 48, 96, 136, 512, 4, 0, device=DEV, seed=synth.SEED_BASE + 81)[0]
     other = plan_for(x0, 0, w, k=(3, 3, 3), pad=(1, 1))
     assert other.info["weight_layout"] == plan.info["weight_layout"]
     img = cc3d.causal_conv3d_pack_weights(other, w)
@@ -839,17 +841,17 @@ def test_first_forward_of_a_fresh_plan_captured_in_a_graph(cuda_device, cin, cou
     pad = (0, 0) if "s1_" in variant else (1, 1)
     x, c, w, b = synth.conv_inputs(1, cin, cout, 96, 160, 4, 2, k, device=DEV, seed=synth.SEED_BASE + 99)
     eager_plan = plan_for(x, 2, w, k=k, pad=pad, variant=variant)
-    ref, ref_co, _ = run(x, c, w, b, k=k, pad=pad, variant=variant)
+    img = cc3d.causal_conv3d_pack_weights(eager_plan, w) if packed else None
+    ws = workspace_for(eager_plan, DEV) if packed else None  # (a split call, where the plan splits)
+    ref, ref_co, _ = run(x, c, w, b, k=k, pad=pad, variant=variant, packed=packed, image=img)
     torch.cuda.synchronize()
     plan = plan_for(x, 2, w, k=k, pad=pad, variant=variant)  # fresh: never run
-    img = cc3d.causal_conv3d_pack_weights(eager_plan, w) if packed else None
-    torch.cuda.synchronize()
     out = torch.empty_like(ref)
     co = torch.empty_like(ref_co)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         if packed:
-            cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, out, co)
+            cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, out, co, ws)
         else:
             cc3d.causal_conv3d_forward(plan, x, c, w, b, out, co)
     for i in range(4):
@@ -880,3 +882,67 @@ def test_packed_forwards_of_one_plan_overlap_on_two_streams(cuda_device, cout, v
         cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, o, None, stream=streams[i % 2])
     torch.cuda.synchronize()
     assert all(torch.equal(o, ref) for o in outs)
+
+
+# Calls with fewer tiles than workgroup slots: causal_conv3d_forward_packed
+# divides each tile's K stages among several units and sums their fp32
+# partials in split order (plan_info splits > 1, a workspace).
+SPLIT_SIGNATURES = ["latent_384", "conv_in_48_384", "latent_384_30x52", "temporal_384_768_30x52",
+                    "latent_384_60x104", "temporal_384_768_60x104", "stage_384_60x104_2f", "conv_in_48_384_30x52"]
+
+
+@pytest.mark.parametrize("name", SPLIT_SIGNATURES)
+def test_split_reduction_every_output_and_repeatable(cuda_device, name):
+    """Every output against the oracle; five launches into NaN-filled
+    outputs give the same bits (the partials are summed in split order,
+    whichever unit arrives last); the arrival counters are left zero."""
+    s = next(v for v in synth.DECODER_SIGNATURES + synth.DECODER_SIGNATURES_480 if v["name"] == name)
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"], device=DEV,
+                                   seed=synth.SEED_BASE + 600 + SPLIT_SIGNATURES.index(name))
+    plan = plan_for(x, s["tc"], w, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    i = plan.info
+    assert i["splits"] > 1 and i["workspace_bytes"] > 0
+    img = cc3d.causal_conv3d_pack_weights(plan, w)
+    ws = workspace_for(plan, DEV)
+    outs = []
+    for _ in range(5):
+        y = nan_like(plan.shapes()["out"], torch.bfloat16, DEV)
+        co = nan_like(plan.shapes()["cache_out"], torch.bfloat16, DEV)
+        cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, y, co, ws)
+        outs.append(y)
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, outs[0]) for o in outs[1:])
+    assert torch.equal(co, torch.cat([c, x], 1)[:, -2:])
+    counters = ws[: i["tiles"] * 4].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+    assert_bf16_close(outs[0], _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"]), name)
+    # without a workspace the call is refused; forward (W in place) runs unsplit
+    with pytest.raises(ValueError):
+        cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, outs[1], None)
+    y1, _, _ = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], want_cache=False)
+    torch.cuda.synchronize()
+    assert_bf16_close(y1, _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"]), name + " unsplit")
+
+
+def test_split_reduction_replays_in_a_graph(cuda_device):
+    """A split call captured in a graph: the arrival counters are reset by
+    the last unit of each tile, so every replay starts from zero."""
+    s = next(v for v in synth.DECODER_SIGNATURES_480 if v["name"] == "latent_384_30x52")
+    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"], device=DEV,
+                                   seed=synth.SEED_BASE + 610)
+    plan = plan_for(x, s["tc"], w, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    img = cc3d.causal_conv3d_pack_weights(plan, w)
+    ws = workspace_for(plan, DEV)
+    ref = nan_like(plan.shapes()["out"], torch.bfloat16, DEV)
+    cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, ref, None, ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, out, None, ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d" % i

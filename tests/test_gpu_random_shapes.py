@@ -1,7 +1,8 @@
 """Seeded random small shapes, each on the default kernel choice and on every
 bf16 variant that accepts it, against the fp64 oracle (every output) and the
 cache-out against its source frames (byte-exact); each variant also from its
-packed weight image, which must give the same bits as reading W in place.
+packed weight image, which must give the same bits as reading W in place
+(unless the packed call splits its K stages, whose sums round differently).
 
 Outputs that no term of the sum reaches (frames with no active temporal tap,
 rows or columns whose spatial taps all fall in the padding) must equal the
@@ -134,6 +135,11 @@ def test_random_shape_on_every_accepting_variant(cuda_device, case):
         assert_bias_only_exact(y, b, mask, name)
         if not mask.all():
             assert_bf16_close(y, ref, name, exclude=mask)
-        assert torch.equal(y, yp), "packed image and W in place differ: " + name
+        if plan.info["splits"] == 1:
+            assert torch.equal(y, yp), "packed image and W in place differ: " + name
+        else:  # the packed call splits K: other rounding, the same bar
+            assert_bias_only_exact(yp, b, mask, name + " split")
+            if not mask.all():
+                assert_bf16_close(yp, ref, name + " split", exclude=mask)
         keep = min(p_base, z.shape[1])
         assert torch.equal(co, z[:, z.shape[1] - keep:]), plan.info["kernel_name"]

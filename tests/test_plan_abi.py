@@ -381,7 +381,7 @@ def test_plans_hold_no_device_memory_and_chunk_plans_share_one_weight_image():
         plans = [cc3d.causal_conv3d_plan(_desc(c_in=cin, c_out=cout, h=h, w=w, t_x=tx, t_cache=tc, k=k, padding=pad))
                  for tc in (0, 2, 2, 2, 2)]
         assert len({(p.info["weight_layout"], p.info["packed_weight_bytes"]) for p in plans}) == 1
-        assert all(p.info["workspace_bytes"] == 0 for p in plans)
+        assert all((p.info["workspace_bytes"] > 0) == (p.info["splits"] > 1) for p in plans)
     a = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2))
     b = cc3d.causal_conv3d_plan_variant(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2),
                                         "bf16_s3_n96_p16x32_g32")
@@ -523,3 +523,24 @@ def test_size_limits_of_the_32_bit_buffer_offsets():
             cc3d.causal_conv3d_plan(_desc(t_x=1, t_cache=2, **kw))
         assert e.value.status == cc3d.CC3D_ERR_UNSUPPORTED, kw
     assert 8192 * 4864 * 27 * 2 >= 2 ** 31
+
+
+def test_split_reduction_only_where_tiles_leave_slots_idle():
+    """causal_conv3d_forward_packed splits each tile's K stages among units
+    when the call has fewer tiles than workgroup slots (two per compute unit
+    for the two-workgroup kernels, of 256 units): up to 16 units, at least 4
+    stages each.  Its workspace holds an int per tile (rounded to 256 bytes)
+    and one fp32 tile of partials per unit."""
+    lat = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2))
+    i = lat.info
+    assert i["kernel_name"] == "bf16_s3_n96_p8x32_x2" and i["tiles"] == 240 and i["splits"] == 2
+    assert i["workspace_bytes"] == (240 * 4 + 255) // 256 * 256 + 240 * 2 * 256 * 96 * 4
+    small = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=2))
+    assert small.info["tiles"] == 32 and small.info["splits"] == 16          # 72 stages: 4.5 per unit
+    few_stages = cc3d.causal_conv3d_plan(_desc(c_in=16, c_out=384, h=90, w=160, t_x=1, t_cache=2))
+    assert few_stages.info["splits"] == 1 and few_stages.info["workspace_bytes"] == 0  # 3 stages
+    big = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2))
+    assert big.info["splits"] == 1 and big.info["workspace_bytes"] == 0    # the group-staged kernel
+    full = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=768, h=90, w=160, t_x=1, t_cache=2, k=(3, 1, 1),
+                                         padding=(0, 0)))
+    assert full.info["tiles"] == 240 and full.info["splits"] == 1          # one workgroup per unit: 256 slots
