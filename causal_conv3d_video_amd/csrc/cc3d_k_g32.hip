@@ -76,9 +76,12 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   static_assert(KSP == 1 || (KSP == 2 && WM == 8), "channel-half split");
   // epilogue staging: waves 0-3 use the idle weight buffer, waves 4-7 the idle halo buffer
   static_assert(4 * 32 * EROW <= WSLOTS * 16 && (NW - 4) * 32 * EROW <= ZSLOTS * 16, "epilogue staging");
-  static_assert((2 * ZSLOTS + 2 * KSP * WSLOTS) * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
+  static_assert((2 * ZSLOTS + 2 * KSP * WSLOTS + (KSP == 1 ? 0 : 64)) * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
   // channel-half split: the second half's sums pass through an idle halo buffer
   static_assert(KSP == 1 || (WM / 2) * CW * RW * 16 * 64 * 4 <= ZSLOTS * 16, "partial sums");
+  // s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9
+  // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+  constexpr auto vm_imm = [](int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); };
   constexpr auto zcnt = [](int w) {  // halo load instructions of wave w per group
     int n = 0;
     for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
@@ -87,7 +90,14 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   static_assert(zcnt(0) + WIT <= 63, "vmcnt range");
 
   __shared__ uint4 zl[2 * ZSLOTS];
-  __shared__ uint4 wl[2 * KSP * WSLOTS];
+  // Weight buffers.  With KSP = 1 the two sub-stage buffers are separate
+  // arrays, selected at compile time: the compiler's wait-count tracking
+  // then knows that reading one does not depend on a direct-to-LDS load into
+  // the other still in flight (with one array it drains every load before
+  // each sub-stage's first weight read).
+  __shared__ uint4 wl[KSP == 1 ? WSLOTS : 2 * KSP * WSLOTS];
+  __shared__ uint4 wl_b1[KSP == 1 ? WSLOTS : 64];
+  auto wbuf = [&](int b) -> uint4* { return KSP == 1 ? (b ? wl_b1 : wl) : wl + b * WSLOTS; };
   __shared__ float bias_lds[2][BN];
 
   const int tid = threadIdx.x;
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(wp.p), 0, wp.rec, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(wl + wb * WSLOTS + it * NT + wave * 64), 16, woff[it],
+          r, (__attribute__((address_space(3))) void*)(wbuf(wb) + it * NT + wave * 64), 16, woff[it],
           0, 0, 0);
     }
   };
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   constexpr int EPIX = CW * 4;
   constexpr int EIT = (32 * EPIX + 63) / 64;
   auto epilogue = [&](const Tile& c, int par, int hidle, int widle) {
-    unsigned char* eb = wave < 4 ? reinterpret_cast<unsigned char*>(wl + widle * WSLOTS) + wave * 32 * EROW
+    unsigned char* eb = wave < 4 ? reinterpret_cast<unsigned char*>(wbuf(widle)) + wave * 32 * EROW
                                  : reinterpret_cast<unsigned char*>(zl + hidle * ZSLOTS) + (wave - 4) * 32 * EROW;
     float4 bias[CW][4];
 #pragma unroll
@@ -403,17 +413,27 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     }
   };
 
+  // (each inline-asm wait is followed by the same wait as a builtin, which
+  // the compiler's wait-count tracking sees: it then knows that the older
+  // loads -- the weight sub-stage -- have landed, and does not drain the
+  // halo loads still in flight before it reads that sub-stage)
   auto wait_halo_in_flight = [&]() {  // all but this wave's halo loads of the last group
     switch (wave) {
-      case 0: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(0)) : "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(1)) : "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(2)) : "memory"); break;
-      case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(3)) : "memory"); break;
-      case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(4 % NW)) : "memory"); break;
-      case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(5 % NW)) : "memory"); break;
-      case 6: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(6 % NW)) : "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(7 % NW)) : "memory"); break;
+#define CC3D_WAIT_HALO(w)                                             \
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(w)) : "memory"); \
+  __builtin_amdgcn_s_waitcnt(vm_imm(zcnt(w)));                     \
+  break;
+      case 0: CC3D_WAIT_HALO(0)
+      case 1: CC3D_WAIT_HALO(1)
+      case 2: CC3D_WAIT_HALO(2)
+      case 3: CC3D_WAIT_HALO(3)
+      case 4: CC3D_WAIT_HALO(4 % NW)
+      case 5: CC3D_WAIT_HALO(5 % NW)
+      case 6: CC3D_WAIT_HALO(6 % NW)
+      default: CC3D_WAIT_HALO(7 % NW)
+#undef CC3D_WAIT_HALO
     }
+    asm volatile("" ::: "memory");
   };
 
   // Wait for every vector memory operation.  The inline-asm waits are
@@ -494,7 +514,11 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
             }
             claim_lds = t;
           }
-          if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+          if (gi == 0 && tid < BN) {
+            unsigned bv = bval;  // (used here, not right after the load, as below)
+            asm volatile("" : "+v"(bv));
+            bias_lds[par][tid] = bf16_to_f32(static_cast<unsigned short>(bv));
+          }
           vm_drain();
           barrier();
           if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
@@ -569,7 +593,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
             const WSrc wp1 = wsrc(ct, ti, gz * 2 + 1);
             const unsigned short* fpn = more ? halo_src(nt, nx.ti, nx.gz) : xs;
             const int hn = __builtin_amdgcn_readfirstlane(hpar ^ 1);
-            compute(zb, wl, rows_in, std::integral_constant<int, 0>{}, std::integral_constant<int, WIT + ZIT>{},
+            compute(zb, wbuf(0), rows_in, std::integral_constant<int, 0>{}, std::integral_constant<int, WIT + ZIT>{},
                     std::integral_constant<int, NSTEP>{}, [&](int k) {
                       if (k < WIT) issue_w(wp1, 1, k);
                       else if (more) issue_z(fpn, hn, k - WIT);
@@ -577,7 +601,14 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
           }
           if (more) wait_halo_in_flight();
           else vm_drain();
-          if (gi == 0 && tid < BN) bias_lds[par][tid] = bf16_to_f32(bval);
+          if (gi == 0 && tid < BN) {
+            // (the empty asm keeps the use of the bias load -- and so the
+            // compiler's wait for it -- here, after the sub-stage, where the
+            // load has long landed, instead of right after it is issued)
+            unsigned bv = bval;
+            asm volatile("" : "+v"(bv));
+            bias_lds[par][tid] = bf16_to_f32(static_cast<unsigned short>(bv));
+          }
           barrier();
           // sub-stage 1: load W[0] <- next group, first half.  In the first
           // group, thread 0 also claims a tile (the atomic's latency hides
@@ -587,7 +618,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
           if (gi == 0 && claims && tid == 0) v = claim(cx);
           {
             const WSrc wpn = more ? wsrc(nt, nx.ti, nx.gz * 2) : wnone;
-            compute(zb, wl + WSLOTS, rows_in, std::integral_constant<int, 1>{}, std::integral_constant<int, WIT>{},
+            compute(zb, wbuf(1), rows_in, std::integral_constant<int, 1>{}, std::integral_constant<int, WIT>{},
                     std::integral_constant<int, (NSTEP + 1) / 2>{}, [&](int k) {
                       if (more) issue_w(wpn, 0, k);
                     });

@@ -36,8 +36,9 @@ __global__ __launch_bounds__(256) void pack_weights(const unsigned short* __rest
 
 // WPK: the stage weights come from the packed image (a.wpk), one contiguous
 // run per stage; otherwise each slot's 16-byte piece is gathered from W as
-// the caller stores it, into the same LDS layout.
-template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC, bool WPK>
+// the caller stores it, into the same LDS layout.  SPLIT: the instantiation
+// that runs split units (a.splits > 1; the others carry no reduction code).
+template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC, bool WPK, bool SPLIT>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void conv_bf16_mfma(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using WT = WTile<BN, KS, CB>;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
     int z0, z1, z2, z3;  // their source frames
     int t, sp, s0, s1;
   };
-  const int splits = a.splits;
+  const int splits = SPLIT ? a.splits : 1;
   auto decode = [&](int u) {
     Tile c;
     c.t = u / splits;
@@ -426,6 +427,20 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
     }
   };
 
+  // Workgroup barrier with explicit waits only: the caller has waited for
+  // the loads that must have landed; this waits for the wave's own LDS
+  // accesses.  (__syncthreads() would also drain every load in flight,
+  // including the NBUF - 2 stages meant to stay in flight across it.)
+  auto barrier = [&]() {
+    if constexpr (NBUF == 2) {
+      __syncthreads();  // (nothing may stay in flight: the same waits, measured slightly faster)
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+  };
+
   int issued = 0;
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i)
@@ -437,15 +452,25 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
   // Split reduction: this thread's share of a unit's fp32 partial sums
   // (NACC floats, stored as float4 runs interleaved across the workgroup's
   // threads so that each store instruction writes one contiguous block).
+  // The units of a tile may run on different XCDs, whose L2 caches are not
+  // coherent with each other: the partials are written and read with
+  // device-scope (sc1) accesses, which go to the device's coherence point,
+  // and the arrival count is a device-scope atomic, so no cache-wide
+  // write-back or invalidation is needed.
   constexpr int NACC = CW * RW * 16;
+  constexpr int kSC1 = 16;  // cache-policy bits of a buffer access: device scope
   int* const arrivals = static_cast<int*>(a.ws);
-  float4* const parts = reinterpret_cast<float4*>(static_cast<unsigned char*>(a.ws) + a.ws_part);
   __shared__ int last_lds;
   // Store this unit's partials, count its arrival; returns (uniformly)
   // whether it arrived last, in which case acc then holds the tile's sum
   // over all splits, in split order.
   auto reduce_splits = [&](const Tile& c) {
-    float4* mine = parts + (int64_t(c.t) * splits + c.sp) * (NACC / 4) * NT;
+    const int part_bytes = (NACC / 4) * NT * 16;  // one unit's partials
+    const unsigned char* tile_parts =
+        static_cast<const unsigned char*>(a.ws) + a.ws_part + int64_t(c.t) * splits * part_bytes;
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(uniform(tile_parts)), 0, __builtin_amdgcn_readfirstlane(splits * part_bytes), 0x00020000);
+    const int mine = __builtin_amdgcn_readfirstlane(c.sp * part_bytes);
 #pragma unroll
     for (int q = 0; q < CW; ++q)
 #pragma unroll
@@ -453,35 +478,42 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
           const int e4 = (q * RW + r) * 4 + v4;
-          mine[e4 * NT + tid] = make_float4(acc[q][r][v4 * 4], acc[q][r][v4 * 4 + 1], acc[q][r][v4 * 4 + 2],
-                                            acc[q][r][v4 * 4 + 3]);
+          const u32x4_t v = {__float_as_uint(acc[q][r][v4 * 4]), __float_as_uint(acc[q][r][v4 * 4 + 1]),
+                             __float_as_uint(acc[q][r][v4 * 4 + 2]), __float_as_uint(acc[q][r][v4 * 4 + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, pr, tid * 16, mine + e4 * NT * 16, kSC1);
         }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the partials are at the coherence point
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    barrier();
     if (tid == 0) {
-      const int before = __hip_atomic_fetch_add(arrivals + c.t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const int before = __hip_atomic_fetch_add(arrivals + c.t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const bool last = before == splits - 1;
       if (last) __hip_atomic_store(arrivals + c.t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_lds = last;
     }
-    __syncthreads();
+    barrier();
     const bool last = __builtin_amdgcn_readfirstlane(last_lds) != 0;
     if (last) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       zero_acc();
-      const float4* tp = parts + int64_t(c.t) * splits * (NACC / 4) * NT;
+      // (half an accumulator -- two float4 -- at a time: its loads are
+      // issued together, then added; the sum runs in split order)
       for (int sp = 0; sp < splits; ++sp) {
+        const int so = __builtin_amdgcn_readfirstlane(sp * part_bytes);
 #pragma unroll
         for (int q = 0; q < CW; ++q)
 #pragma unroll
           for (int r = 0; r < RW; ++r)
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-              const float4 p = tp[(int64_t(sp) * (NACC / 4) + (q * RW + r) * 4 + v4) * NT + tid];
-              acc[q][r][v4 * 4] += p.x;
-              acc[q][r][v4 * 4 + 1] += p.y;
-              acc[q][r][v4 * 4 + 2] += p.z;
-              acc[q][r][v4 * 4 + 3] += p.w;
+            for (int h2 = 0; h2 < 2; ++h2) {
+              u32x4_t p[2];
+#pragma unroll
+              for (int v = 0; v < 2; ++v)
+                p[v] = __builtin_amdgcn_raw_buffer_load_b128(pr, tid * 16,
+                                                             so + ((q * RW + r) * 4 + h2 * 2 + v) * NT * 16, kSC1);
+#pragma unroll
+              for (int v = 0; v < 2; ++v)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[q][r][(h2 * 2 + v) * 4 + e] += __uint_as_float(p[v][e]);
             }
       }
     }
@@ -496,7 +528,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
       // no stage (no active tap, or fewer stages than splits)
       if (tid < BN) bias_lds[par][tid] = bf16_to_f32(bias_value(ct));
       __syncthreads();
-      if (splits == 1 || reduce_splits(ct)) epilogue(ct, par, pos % NBUF);
+      if (!SPLIT || reduce_splits(ct)) epilogue(ct, par, pos % NBUF);
       __syncthreads();
     } else {
       for (int st = ct.s0; st < ct.s1; ++st, ++pos) {
@@ -512,13 +544,13 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
         // bias, and retires this stage's LDS reads
         if (NBUF > 2 && more) wait_newer_stages();
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        barrier();
       }
       // the buffer of the last stage is idle until the next stage's loads are
       // issued: stage the outputs through it, then make sure every wave is
       // done with it before those loads go out
-      if (splits == 1 || reduce_splits(ct)) epilogue(ct, par, (pos - 1) % NBUF);
-      __syncthreads();
+      if (!SPLIT || reduce_splits(ct)) epilogue(ct, par, (pos - 1) % NBUF);
+      barrier();  // (the output stores may stay in flight)
     }
     par ^= 1;
     ctile = next_tile(ctile);
@@ -528,16 +560,21 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
 #endif
 }
 
-template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC, bool WPK>
+template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC, bool WPK, bool SPLIT>
 const void* mfma_kernel() {
-  return reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF, OCC, WPK>);
+  return reinterpret_cast<const void*>(&conv_bf16_mfma<BN, TH, WM, WN, KS, CB, NBUF, OCC, WPK, SPLIT>);
 }
 
 // Persistent launch with min(tiles, workgroups that fit) workgroups.
 template <int BN, int TH, int WM, int WN, int KS, int CB, int NBUF, int OCC>
 hipError_t launch_mfma(const ConvArgs& a, int64_t tiles, int cus, hipStream_t s) {
-  if (a.wpk) return launch_persistent<&mfma_kernel<BN, TH, WM, WN, KS, CB, NBUF, OCC, true>>(a, tiles, cus, WM * WN * 64, s);
-  return launch_persistent<&mfma_kernel<BN, TH, WM, WN, KS, CB, NBUF, OCC, false>>(a, tiles, cus, WM * WN * 64, s);
+  constexpr int NT = WM * WN * 64;
+  if (a.splits > 1) {  // (split calls run from the packed image only)
+    if (!a.wpk) return hipErrorInvalidValue;
+    return launch_persistent<&mfma_kernel<BN, TH, WM, WN, KS, CB, NBUF, OCC, true, true>>(a, tiles, cus, NT, s);
+  }
+  if (a.wpk) return launch_persistent<&mfma_kernel<BN, TH, WM, WN, KS, CB, NBUF, OCC, true, false>>(a, tiles, cus, NT, s);
+  return launch_persistent<&mfma_kernel<BN, TH, WM, WN, KS, CB, NBUF, OCC, false, false>>(a, tiles, cus, NT, s);
 }
 
 template <int BN, int KS, int CB>

@@ -330,20 +330,25 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     if (v.id == CC3D_K_BF16_S3_FEW) in.bytes_cache_out /= 2;  // written from the staged rows, not re-read
     in.weight_layout = layout_fingerprint(p->pack_kind, v.block_n, int32_t(ks), v.cin_chunk, d);
     // Split reduction (conv_bf16_mfma only; causal_conv3d_forward_packed):
-    // when a call has fewer tiles than the chip has workgroup slots, each
-    // tile's K stages are divided among up to 16 units (at least 4 stages
-    // each) so that the slots fill.  Each unit writes a tile of fp32
-    // partials (block_m * block_n floats) to the workspace, after an int per
-    // tile of arrival counters.
+    // when a call's tiles would leave three quarters or more of the chip's
+    // workgroup slots idle, each tile's K stages are divided among up to 16
+    // units (at least 4 stages each) so that the slots fill.  Each unit
+    // writes a tile of fp32 partials (block_m * block_n floats) to the
+    // workspace, after an int per tile of arrival counters.  Fewer than 4
+    // splits are not taken: the partial-sum traffic and the last arriver's
+    // reduction then cost more than the idle slots.  (Measured on the
+    // two-workgroup kernel: 384->384 at 30x52, 32 tiles, 16 splits, 109 ->
+    // 89 us; at 90x160, 240 tiles, 2 splits gained nothing, and 48->384 at
+    // 30x52, 32 tiles of 9 stages, 2 splits lost time.)
     in.splits = 1;
     if (v.id == CC3D_K_BF16_S3_N96_X2 || v.id == CC3D_K_BF16_S3_N32 || v.id == CC3D_K_BF16_S1_N192 ||
         v.id == CC3D_K_BF16_S1_N32) {
       const int wg_per_cu = (v.id == CC3D_K_BF16_S1_N192 || v.cin_chunk == 64) ? 1 : 2;
       const int64_t slots = int64_t(kComputeUnits) * wg_per_cu;
       const int64_t stages = int64_t(in.n_active_taps) * (d.c_in / v.cin_chunk);
-      if (in.tiles < slots) {
+      if (in.tiles * 4 <= slots) {
         const int64_t s = std::min<int64_t>({slots / std::max<int64_t>(in.tiles, 1), stages / 4, 16});
-        in.splits = int32_t(std::max<int64_t>(s, 1));
+        in.splits = s >= 4 ? int32_t(s) : 1;
       }
       if (in.splits > 1)
         in.workspace_bytes = (in.tiles * 4 + 255) / 256 * 256 +

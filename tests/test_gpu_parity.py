@@ -884,24 +884,39 @@ def test_packed_forwards_of_one_plan_overlap_on_two_streams(cuda_device, cout, v
     assert all(torch.equal(o, ref) for o in outs)
 
 
-# Calls with fewer tiles than workgroup slots: causal_conv3d_forward_packed
-# divides each tile's K stages among several units and sums their fp32
-# partials in split order (plan_info splits > 1, a workspace).
-SPLIT_SIGNATURES = ["latent_384", "conv_in_48_384", "latent_384_30x52", "temporal_384_768_30x52",
-                    "latent_384_60x104", "temporal_384_768_60x104", "stage_384_60x104_2f", "conv_in_48_384_30x52"]
+# Calls whose tiles leave most workgroup slots idle:
+# causal_conv3d_forward_packed divides each tile's K stages among several
+# units and sums their fp32 partials in split order (plan_info splits > 1, a
+# workspace).  (name, n, c_in, c_out, k, h, w, t_x, t_cache, kernel, splits):
+# every kernel that splits, split counts from 4 to 16, stage counts that do
+# not divide evenly, a first chunk (one active temporal tap), two batch items.
+SPLIT_CASES = [
+    ("latent_384_30x52", 1, 384, 384, (3, 3, 3), 30, 52, 1, 2, "bf16_s3_n96_p8x32_x2", 16),
+    ("latent_384_60x104", 1, 384, 384, (3, 3, 3), 60, 104, 1, 2, "bf16_s3_n96_p8x32_x2", 4),
+    ("latent_384_45x80", 1, 384, 384, (3, 3, 3), 45, 80, 1, 2, "bf16_s3_n96_p8x32_x2", 7),
+    ("latent_384_24x40_2f", 1, 384, 384, (3, 3, 3), 24, 40, 2, 2, "bf16_s3_n96_p8x32_x2", 10),
+    ("latent_384_30x52_first", 1, 384, 384, (3, 3, 3), 30, 52, 1, 0, "bf16_s3_n96_p8x32_x2", 6),
+    ("latent_384_12x20_n2", 2, 384, 384, (3, 3, 3), 12, 20, 1, 2, "bf16_s3_n96_p8x32_x2", 16),
+    ("conv_256_96_30x52", 1, 256, 96, (3, 3, 3), 30, 52, 1, 2, "bf16_s3_n96_p8x32_x2", 12),
+    ("conv_96_32_60x104_2f", 1, 96, 32, (3, 3, 3), 60, 104, 2, 2, "bf16_s3_n32_p8x32", 4),
+    ("conv_512_512_24x40", 1, 512, 512, (3, 3, 3), 24, 40, 1, 2, "bf16_s3_n32_p8x32", 5),
+    ("temporal_384_768_30x52", 1, 384, 768, (3, 1, 1), 30, 52, 1, 2, "bf16_s1_n192_p8x32", 4),
+    ("temporal_384_768_16x64_2f", 1, 384, 768, (3, 1, 1), 16, 64, 2, 2, "bf16_s1_n192_p8x32", 4),
+]
 
 
-@pytest.mark.parametrize("name", SPLIT_SIGNATURES)
-def test_split_reduction_every_output_and_repeatable(cuda_device, name):
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_reduction_every_output_and_repeatable(cuda_device, case):
     """Every output against the oracle; five launches into NaN-filled
     outputs give the same bits (the partials are summed in split order,
     whichever unit arrives last); the arrival counters are left zero."""
-    s = next(v for v in synth.DECODER_SIGNATURES + synth.DECODER_SIGNATURES_480 if v["name"] == name)
-    x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"], device=DEV,
-                                   seed=synth.SEED_BASE + 600 + SPLIT_SIGNATURES.index(name))
-    plan = plan_for(x, s["tc"], w, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    name, n, cin, cout, k, h, w_, tx, tc, kernel, splits = case
+    pad = (k[1] // 2, k[2] // 2)
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
+                                   seed=synth.SEED_BASE + 600 + SPLIT_CASES.index(case))
+    plan = plan_for(x, tc, w, k=k, pad=pad, p_base=2)
     i = plan.info
-    assert i["splits"] > 1 and i["workspace_bytes"] > 0
+    assert (i["kernel_name"], i["splits"]) == (kernel, splits) and i["workspace_bytes"] > 0
     img = cc3d.causal_conv3d_pack_weights(plan, w)
     ws = workspace_for(plan, DEV)
     outs = []
@@ -912,16 +927,20 @@ def test_split_reduction_every_output_and_repeatable(cuda_device, name):
         outs.append(y)
     torch.cuda.synchronize()
     assert all(torch.equal(o, outs[0]) for o in outs[1:])
-    assert torch.equal(co, torch.cat([c, x], 1)[:, -2:])
+    z = x if c is None else torch.cat([c, x], 1)
+    assert torch.equal(co, z[:, -min(2, z.shape[1]):])
     counters = ws[: i["tiles"] * 4].view(torch.int32)
     assert int(counters.abs().sum()) == 0
-    assert_bf16_close(outs[0], _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"]), name)
+    ref = _oracle(x, c, w, b, k=k, pad=pad, p_base=2)
+    mask = mask_for(plan, x.shape, k=k, pad=pad)
+    assert_bias_only_exact(outs[0], b, mask, name)
+    assert_bf16_close(outs[0], ref, name, exclude=mask)
     # without a workspace the call is refused; forward (W in place) runs unsplit
     with pytest.raises(ValueError):
         cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, outs[1], None)
-    y1, _, _ = run(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"], want_cache=False)
+    y1, _, _ = run(x, c, w, b, k=k, pad=pad, p_base=2, want_cache=False)
     torch.cuda.synchronize()
-    assert_bf16_close(y1, _oracle(x, c, w, b, k=s["k"], pad=s["pad"], p_base=s["p_base"]), name + " unsplit")
+    assert_bf16_close(y1, ref, name + " unsplit", exclude=mask)
 
 
 def test_split_reduction_replays_in_a_graph(cuda_device):

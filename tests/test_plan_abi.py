@@ -527,16 +527,23 @@ def test_size_limits_of_the_32_bit_buffer_offsets():
 
 def test_split_reduction_only_where_tiles_leave_slots_idle():
     """causal_conv3d_forward_packed splits each tile's K stages among units
-    when the call has fewer tiles than workgroup slots (two per compute unit
-    for the two-workgroup kernels, of 256 units): up to 16 units, at least 4
-    stages each.  Its workspace holds an int per tile (rounded to 256 bytes)
-    and one fp32 tile of partials per unit."""
-    lat = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2))
-    i = lat.info
-    assert i["kernel_name"] == "bf16_s3_n96_p8x32_x2" and i["tiles"] == 240 and i["splits"] == 2
-    assert i["workspace_bytes"] == (240 * 4 + 255) // 256 * 256 + 240 * 2 * 256 * 96 * 4
+    when the call's tiles fill at most a quarter of the workgroup slots (two
+    per compute unit for the two-workgroup kernels, of 256 units): up to 16
+    units, at least 4 stages each, and no split below 4 units.  Its
+    workspace holds an int per tile (rounded to 256 bytes) and one fp32
+    tile of partials per unit."""
     small = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=2))
-    assert small.info["tiles"] == 32 and small.info["splits"] == 16          # 72 stages: 4.5 per unit
+    i = small.info
+    assert i["kernel_name"] == "bf16_s3_n96_p8x32_x2" and i["tiles"] == 32 and i["splits"] == 16  # 72 stages
+    assert i["workspace_bytes"] == 256 + 32 * 16 * 256 * 96 * 4
+    mid = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=60, w=104, t_x=1, t_cache=2))
+    assert mid.info["tiles"] == 128 and mid.info["splits"] == 4               # 512 slots / 128 tiles
+    lat = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2))
+    assert lat.info["tiles"] == 240 and lat.info["splits"] == 1 and lat.info["workspace_bytes"] == 0  # 2 < 4
+    first = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=0))
+    assert first.info["splits"] == 6                                         # one active tap: 24 stages
+    two = cc3d.causal_conv3d_plan(_desc(c_in=48, c_out=384, h=30, w=52, t_x=1, t_cache=2))
+    assert two.info["tiles"] == 32 and two.info["splits"] == 1               # 9 stages: 2 units at most
     few_stages = cc3d.causal_conv3d_plan(_desc(c_in=16, c_out=384, h=90, w=160, t_x=1, t_cache=2))
     assert few_stages.info["splits"] == 1 and few_stages.info["workspace_bytes"] == 0  # 3 stages
     big = cc3d.causal_conv3d_plan(_desc(c_in=192, c_out=192, h=360, w=640, t_x=4, t_cache=2))
