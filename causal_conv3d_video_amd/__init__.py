@@ -26,6 +26,7 @@ __all__ = [
     "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_autotune", "causal_conv3d_plan_info",
     "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
+    "causal_conv3d_forward_packed_noalloc",
     "causal_conv3d_forward_u8", "causal_conv3d_status_string", "causal_conv3d_counters", "library_path",
     "EXPORTED_SYMBOLS", "VARIANTS",
 ]
@@ -37,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "causal_conv3d_plan", "causal_conv3d_plan_variant", "causal_conv3d_plan_autotune", "causal_conv3d_plan_info",
     "causal_conv3d_plan_destroy",
     "causal_conv3d_forward", "causal_conv3d_pack_weights", "causal_conv3d_forward_packed",
+    "causal_conv3d_forward_packed_noalloc",
     "causal_conv3d_forward_u8", "causal_conv3d_status_string", "causal_conv3d_counters",
 )
 
@@ -104,6 +106,8 @@ def _load():
     lib.causal_conv3d_pack_weights.restype = ctypes.c_int
     lib.causal_conv3d_forward_packed.argtypes = [vp] * 8 + [ctypes.c_int64, vp]
     lib.causal_conv3d_forward_packed.restype = ctypes.c_int
+    lib.causal_conv3d_forward_packed_noalloc.argtypes = [vp] * 8
+    lib.causal_conv3d_forward_packed_noalloc.restype = ctypes.c_int
     lib.causal_conv3d_forward_u8.argtypes = [vp] * 7 + [ctypes.c_float, ctypes.c_float, vp]
     lib.causal_conv3d_forward_u8.restype = ctypes.c_int
     lib.causal_conv3d_status_string.argtypes = [ctypes.c_int]
@@ -325,6 +329,22 @@ def causal_conv3d_forward_packed(plan, x, cache_in, w_packed, b, out, cache_out=
                                            p["cache_out"], ws, int(ws_bytes if ws else 0), _stream_handle(stream, x))
     if st != CC3D_OK:
         raise CC3DError(st, "causal_conv3d_forward_packed")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # CC3D_NOALLOC_SCRATCH_BYTES
+
+
+def causal_conv3d_forward_packed_noalloc(plan, x, cache_in, w_packed, b, out, cache_out=None, stream=None):
+    """causal_conv3d_forward_packed with the split workspace in the
+    library's static per-device array: allocates no device memory.  Calls
+    that overlap on one device race."""
+    p = _marshal(plan, {"x": x, "cache_in": cache_in if plan.desc.t_cache > 0 else None,
+                        "b": b if plan.desc.has_bias else None, "out": out, "cache_out": cache_out})
+    wp = _device_bytes(w_packed, plan.info["packed_weight_bytes"], "w_packed", x)
+    st = _lib.causal_conv3d_forward_packed_noalloc(plan.handle, p["x"], p["cache_in"], wp, p["b"], p["out"],
+                                                   p["cache_out"], _stream_handle(stream, x))
+    if st != CC3D_OK:
+        raise CC3DError(st, "causal_conv3d_forward_packed_noalloc")
 
 
 def causal_conv3d_forward_u8(plan, x, cache_in, w, b, out, cache_out=None, scale=0.5, offset=0.5, stream=None):

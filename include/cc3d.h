@@ -290,6 +290,28 @@ cc3d_status_t causal_conv3d_forward_packed(cc3d_plan_t plan, const void* x, cons
                                            void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the convolution of
+ * causal_conv3d_forward_packed with the split workspace in a static device
+ * array of the library (CC3D_NOALLOC_SCRATCH_BYTES, one per device the
+ * library runs on, held until the process ends) instead of a caller
+ * buffer; the array used is the current device's, which must be the
+ * device of `stream` and of the buffers.  It allocates nothing; before a split call it zeroes the array's
+ * arrival counters with a small kernel on `stream`.  Every call on a device
+ * shares that device's array: calls that overlap on one device (other
+ * streams, other threads) race and must not be issued.  Arguments and
+ * errors are those of causal_conv3d_forward_packed, plus
+ * CC3D_ERR_UNSUPPORTED for a plan whose workspace_bytes exceeds
+ * CC3D_NOALLOC_SCRATCH_BYTES and CC3D_ERR_DEVICE when the array's address
+ * cannot be obtained.  Plans without a split need no array and run as
+ * causal_conv3d_forward_packed.
+ */
+#define CC3D_NOALLOC_SCRATCH_BYTES (64u << 20)
+cc3d_status_t causal_conv3d_forward_packed_noalloc(cc3d_plan_t plan, const void* x, const void* cache_in,
+                                                   const void* w_packed, const void* b, void* out, void* cache_out,
+                                                   void* stream);
+
+/*
  * The RGB head with its pixel quantisation fused in (FastVideo pull request
  * "[perf] Quantize frames to uint8 on-device before the post-decode D->H
  * copy": the decoded frames are scaled by 255, clamped to [0, 255] and cast
