@@ -495,27 +495,34 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
     const bool last = __builtin_amdgcn_readfirstlane(last_lds) != 0;
     if (last) {
       zero_acc();
-      // (half an accumulator -- two float4 -- at a time: its loads are
-      // issued together, then added; the sum runs in split order)
-      for (int sp = 0; sp < splits; ++sp) {
-        const int so = __builtin_amdgcn_readfirstlane(sp * part_bytes);
+      // The partials are read at the coherence point, so each load is a
+      // long round trip: per 16-float accumulator run, the loads of four
+      // units (16 float4) are issued together, then added in split order.
 #pragma unroll
-        for (int q = 0; q < CW; ++q)
+      for (int q = 0; q < CW; ++q)
 #pragma unroll
-          for (int r = 0; r < RW; ++r)
+        for (int r = 0; r < RW; ++r) {
+          const int run = (q * RW + r) * 4 * NT * 16;
+          for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+            u32x4_t p[4][4];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              u32x4_t p[2];
+            for (int j = 0; j < 4; ++j)
+              if (sp0 + j < splits) {
+                const int so = __builtin_amdgcn_readfirstlane((sp0 + j) * part_bytes + run);
 #pragma unroll
-              for (int v = 0; v < 2; ++v)
-                p[v] = __builtin_amdgcn_raw_buffer_load_b128(pr, tid * 16,
-                                                             so + ((q * RW + r) * 4 + h2 * 2 + v) * NT * 16, kSC1);
+                for (int v = 0; v < 4; ++v)
+                  p[j][v] = __builtin_amdgcn_raw_buffer_load_b128(pr, tid * 16, so + v * NT * 16, kSC1);
+              }
 #pragma unroll
-              for (int v = 0; v < 2; ++v)
+            for (int j = 0; j < 4; ++j)
+              if (sp0 + j < splits) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[q][r][(h2 * 2 + v) * 4 + e] += __uint_as_float(p[v][e]);
-            }
-      }
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) acc[q][r][v * 4 + e] += __uint_as_float(p[j][v][e]);
+              }
+          }
+        }
     }
     return last;
   };
