@@ -50,6 +50,8 @@ def _parse():
     p.add_argument("--only", default=None,
                    help="profiling aid: run only this signature's conv kernel, --warm-seconds of untimed "
                         "launches and then --kernel-launches counted ones")
+    p.add_argument("--variant", default=None,
+                   help="profiling aid, with --only on a single-call signature: pin this kernel variant")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="profiling aid: run only a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -67,6 +69,8 @@ def _kernel_sources(kernel_name=None):
         return common + ["cc3d_few.inc"]
     if kernel_name.startswith("bf16_gen_") or kernel_name == "f32_direct":
         return common + ["cc3d_k_misc.hip"]
+    if kernel_name.endswith("_rd"):
+        return common + ["cc3d_k_s1.hip"]
     return common + ["cc3d_k_mfma.hip"]
 
 
@@ -255,7 +259,8 @@ def time_single_calls(device, launches, stream, warm_seconds=0.2):
     for i, s in enumerate(synth.SINGLE_CALLS + synth.ENCODER_DOWNSAMPLE + synth.GENERAL_SPATIAL):
         x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
                                        device=device, seed=synth.SEED_BASE + 200 + i)
-        plan = cc3d.causal_conv3d_plan(_desc(cc3d, s, s["tx"], s["tc"]))
+        desc = _desc(cc3d, s, s["tx"], s["tc"])
+        plan = cc3d.causal_conv3d_plan_variant(desc, args.variant) if args.variant else cc3d.causal_conv3d_plan(desc)
         out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
         img = cc3d.causal_conv3d_pack_weights(plan, w, stream=stream)
         ws = torch.zeros(plan.info["workspace_bytes"], dtype=torch.uint8, device=device) \
@@ -470,7 +475,8 @@ def _only(args, work, device, stream):
                  + synth.DECODER_SIGNATURES + synth.DECODER_SIGNATURES_480 if v["name"] == args.only)
         x, cin_buf, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
                                              device=device, seed=synth.SEED_BASE + 200)
-        plan = cc3d.causal_conv3d_plan(_desc(cc3d, s, s["tx"], s["tc"]))
+        desc = _desc(cc3d, s, s["tx"], s["tc"])
+        plan = cc3d.causal_conv3d_plan_variant(desc, args.variant) if args.variant else cc3d.causal_conv3d_plan(desc)
         out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
         img = cc3d.causal_conv3d_pack_weights(plan, w, stream=stream)
         ws = torch.zeros(plan.info["workspace_bytes"], dtype=torch.uint8, device=device) \

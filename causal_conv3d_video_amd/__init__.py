@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = (
 # Every kernel variant name causal_conv3d_plan_variant accepts (include/cc3d.h).
 VARIANTS = (("bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p16x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32")
             + tuple("bf16_s3_few_p%dx128" % r for r in range(4, 17))
-            + ("bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32", "bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32",
+            + ("bf16_s1_n192_p8x32", "bf16_s1_n192_p256_rd", "bf16_s1_n32_p8x32", "bf16_gen_n64_p8x32", "bf16_gen_n96_p8x32",
                "bf16_s3d2_n64_p16x32_g32", "bf16_s3s2_n96_p4x32_g32", "bf16_s3s2_n64_p4x32_g32", "f32_direct"))
 
 CC3D_OK, CC3D_ERR_INVALID_ARG, CC3D_ERR_UNSUPPORTED, CC3D_ERR_DEVICE, CC3D_ERR_NO_MEMORY = range(5)

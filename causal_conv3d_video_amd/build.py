@@ -25,7 +25,8 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 # translation units: (source, compiler)
-HIP_SOURCES = (["cc3d_k_g32.hip", "cc3d_k_mfma.hip", "cc3d_k_misc.hip", "cc3d_launch.hip", "cc3d_noalloc.hip"]
+HIP_SOURCES = (["cc3d_k_g32.hip", "cc3d_k_mfma.hip", "cc3d_k_misc.hip", "cc3d_launch.hip", "cc3d_noalloc.hip",
+                "cc3d_k_s1.hip"]
                + ["cc3d_k_few%d.hip" % c for c in range(1, 6)])
 CXX_SOURCES = ["cc3d_plan.cpp"]
 

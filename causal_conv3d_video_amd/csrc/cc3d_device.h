@@ -83,6 +83,7 @@ hipError_t launch_g32_family(int kernel_id, const ConvArgs& a, int64_t tiles, in
 template <int COUT>
 hipError_t launch_few_cout(const ConvArgs& a, int64_t tiles, int cus, hipStream_t s);  // C_out = COUT (1..5)
 hipError_t launch_gen_family(int kernel_id, const ConvArgs& a, int64_t tiles, hipStream_t s);
+hipError_t launch_s1rd(const ConvArgs& a, int64_t tiles, int cus, hipStream_t s);
 hipError_t launch_f32_direct(const ConvArgs& a, int64_t tiles, hipStream_t s);
 hipError_t launch_copy_tail(const void* x, const void* cache, void* dst, int64_t frame_bytes, int n, int tx, int tc,
                             int frames, bool vec16, hipStream_t s);

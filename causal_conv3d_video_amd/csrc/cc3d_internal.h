@@ -28,6 +28,8 @@ enum cc3d_kernel_id : int32_t {
                                    // padding 1: 128 output px (4x32) x 96 channels, 4 waves
   CC3D_K_BF16_S3S2_N64_G32W8 = 17, // as CC3D_K_BF16_S3S2_N96_G32W4 with 64 channels, 8 waves (each
                                    // group's two 16-channel halves on two waves of the same rows)
+  CC3D_K_BF16_S1_N192_RD = 18, // 1x1 spatial, 256 consecutive px of the flattened frame x 192
+                               // channels, pixels loaded straight into registers
 };
 
 // A plan is host metadata only, immutable once built.

@@ -267,6 +267,7 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
   if (in.kernel_id == CC3D_K_F32_DIRECT) e = cc3d::launch_f32_direct(a, in.tiles, s);
   else if (is_g32(in.kernel_id)) e = cc3d::launch_g32_family(in.kernel_id, a, std::max<int64_t>(a.nat, 1), cus, s);
   else if (is_mfma(in.kernel_id)) e = cc3d::launch_mfma_family(in.kernel_id, plan->cin_chunk, a, a.ntiles, cus, s);
+  else if (in.kernel_id == CC3D_K_BF16_S1_N192_RD) e = cc3d::launch_s1rd(a, in.tiles, cus, s);
   else if (in.kernel_id == CC3D_K_BF16_S3_FEW) {
     switch (d.c_out) {
       case 1: e = cc3d::launch_few_cout<1>(a, in.tiles, cus, s); break;
@@ -351,6 +352,7 @@ extern "C" cc3d_status_t causal_conv3d_plan_autotune(const cc3d_desc_t* desc, co
                                             "bf16_s3_few_p12x128",
                                             "bf16_s3_few_p8x128",
                                             "bf16_s1_n192_p8x32",
+                                            "bf16_s1_n192_p256_rd",
                                             "bf16_s1_n32_p8x32",
                                             "bf16_s3d2_n64_p16x32_g32",
                                             "bf16_s3s2_n96_p4x32_g32",

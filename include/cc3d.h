@@ -183,6 +183,10 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *                              (4 <= R <= 16) by 128 columns (default for the
  *                              RGB head, with R chosen for the map size)
  *   "bf16_s1_n192_p8x32"      1x1, C_out % 192 == 0, C_in % 32 == 0
+ *   "bf16_s1_n192_p256_rd"    1x1, C_out % 192 == 0, C_in % 64 == 0 with
+ *                              C_in / 64 even or a multiple of 3; tiles of 256
+ *                              consecutive pixels, pixels loaded straight into
+ *                              registers
  *   "bf16_s1_n32_p8x32"       1x1, any C_out
  *   (the variants above need unit spatial stride and dilation and "same"
  *   padding)

@@ -51,6 +51,7 @@ def test_source_hash_follows_the_kernels_own_files():
     files = bench._kernel_sources(K)
     assert "cc3d_k_g32.hip" in files and "cc3d_device.h" in files and "cc3d_k_mfma.hip" not in files
     assert "cc3d_few.inc" in bench._kernel_sources("bf16_s3_few_p15x128")
+    assert "cc3d_k_s1.hip" in bench._kernel_sources("bf16_s1_n192_p256_rd")
     assert bench._source_hash(K) != bench._source_hash("bf16_s3_few_p15x128")
     for f in bench._kernel_sources(None):
         assert os.path.exists(os.path.join(bench.CSRC, f))

@@ -563,6 +563,7 @@ STRIDED = [
     (64, 192, 17, 45, 6, 2, (3, 3, 3), 2, "bf16_s3_n96_p8x32_x2"),
     (32, 40, 13, 41, 5, 0, (3, 3, 3), 2, "bf16_s3_n32_p8x32"),       # chunk 0: odd length, no cache
     (64, 192, 16, 40, 4, 2, (3, 1, 1), 2, "bf16_s1_n192_p8x32"),
+    (128, 192, 16, 40, 4, 2, (3, 1, 1), 2, "bf16_s1_n192_p256_rd"),
     (48, 40, 9, 33, 6, 2, (3, 1, 1), 3, "bf16_s1_n32_p8x32"),
     (96, 3, 16, 32, 4, 2, (3, 3, 3), 2, "bf16_s3_n32_p8x32"),         # head shape: not the few kernel
 ]
@@ -830,7 +831,8 @@ def test_graph_replays_match_eager(cuda_device, cin, cout, variant):
 @pytest.mark.parametrize("packed", [False, True], ids=["w_in_place", "packed"])
 @pytest.mark.parametrize("cin,cout,variant", [(32, 96, "bf16_s3_n96_p16x32_g32"), (32, 64, "bf16_s3_n64_p24x32_g32"),
                                                (64, 96, "bf16_s3_n96_p8x32_x2"), (96, 3, "bf16_s3_few_p16x128"),
-                                               (64, 192, "bf16_s1_n192_p8x32")])
+                                               (64, 192, "bf16_s1_n192_p8x32"),
+                                               (128, 192, "bf16_s1_n192_p256_rd")])
 def test_first_forward_of_a_fresh_plan_captured_in_a_graph(cuda_device, cin, cout, variant, packed):
     """A plan is host metadata only and the forward calls allocate, set and
     synchronise nothing, so the very first call of a fresh plan can be
@@ -884,6 +886,47 @@ def test_packed_forwards_of_one_plan_overlap_on_two_streams(cuda_device, cout, v
     assert all(torch.equal(o, ref) for o in outs)
 
 
+# The register-direct 1x1 kernel: (n, C_in, C_out, H, W, T_x, T_cache, k_t,
+# d_t, p_base, bias).  Its stage depth follows C_in / 64 (3 for 3, 6 and 12
+# chunks, 4 for 4 and 8, 2 for 2); frames of any pixel count (the last tile
+# ragged, or a single partial tile); more tiles than workgroups (each runs
+# several, prefetching across tile boundaries); leading output frames with
+# no active tap (bias only); k_t = 1, 2 and temporal dilation 2.
+RD_CASES = [
+    (1, 384, 768, 20, 36, 1, 2, 3, 1, 2, True),     # the decoder's temporal conv, small map
+    (1, 128, 192, 100, 192, 4, 2, 3, 1, 2, True),   # 75 pixel tiles x 4 frames = 300 tiles
+    (2, 128, 192, 17, 23, 3, 0, 3, 1, 2, True),     # two items, first chunk, 391 pixels
+    (1, 256, 384, 9, 13, 2, 2, 3, 2, 4, True),      # depth 4, d_t = 2, one partial tile
+    (1, 192, 192, 31, 33, 5, 1, 2, 1, 1, False),    # k_t = 2, 1-frame cache, no bias
+    (1, 768, 192, 8, 64, 1, 2, 1, 1, 0, True),      # k_t = 1: pointwise, 12 chunks
+    (1, 128, 192, 10, 30, 2, 0, 3, 1, 5, True),     # p_base 5: output frames 0-2 bias only
+]
+
+
+@pytest.mark.parametrize("case", RD_CASES, ids=["%d_%d_%d_%dx%d_%d_%d" % c[:7] for c in RD_CASES])
+def test_register_direct_1x1_every_output(cuda_device, case):
+    """Every output against the oracle (bias-only outputs bit for bit), the
+    cache-out byte for byte, and the packed image giving the same bits as W
+    read in place."""
+    n, cin, cout, h, w_, tx, tc, kt, dt, p_base, bias = case
+    k = (kt, 1, 1)
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV, has_bias=bias,
+                                   seed=synth.SEED_BASE + 640 + RD_CASES.index(case))
+    v = "bf16_s1_n192_p256_rd"
+    y, co, plan = run(x, c, w, b, k=k, pad=(0, 0), dt=dt, p_base=p_base, variant=v)
+    yp, _, _ = run(x, c, w, b, k=k, pad=(0, 0), dt=dt, p_base=p_base, variant=v, packed=True, want_cache=False)
+    torch.cuda.synchronize()
+    assert plan.info["kernel_name"] == v and plan.info["splits"] == 1
+    assert torch.equal(y, yp)
+    ref = _oracle(x, c, w, b, k=k, pad=(0, 0), dt=dt, p_base=p_base)
+    mask = mask_for(plan, x.shape, k=k, pad=(0, 0), dt=dt)
+    assert_bias_only_exact(y, b, mask, str(case))
+    if not mask.all():
+        assert_bf16_close(y, ref, str(case), exclude=mask)
+    z = x if c is None else torch.cat([c, x], 1)
+    assert torch.equal(co, z[:, z.shape[1] - min(p_base, z.shape[1]):])
+
+
 # Calls whose tiles leave most workgroup slots idle:
 # causal_conv3d_forward_packed divides each tile's K stages among several
 # units and sums their fp32 partials in split order (plan_info splits > 1, a
@@ -914,7 +957,7 @@ def test_split_reduction_every_output_and_repeatable(cuda_device, case):
     pad = (k[1] // 2, k[2] // 2)
     x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
                                    seed=synth.SEED_BASE + 600 + SPLIT_CASES.index(case))
-    plan = plan_for(x, tc, w, k=k, pad=pad, p_base=2)
+    plan = plan_for(x, tc, w, k=k, pad=pad, p_base=2, variant=kernel)
     i = plan.info
     assert (i["kernel_name"], i["splits"]) == (kernel, splits) and i["workspace_bytes"] > 0
     img = cc3d.causal_conv3d_pack_weights(plan, w)
@@ -938,7 +981,7 @@ def test_split_reduction_every_output_and_repeatable(cuda_device, case):
     # without a workspace the call is refused; forward (W in place) runs unsplit
     with pytest.raises(ValueError):
         cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, outs[1], None)
-    y1, _, _ = run(x, c, w, b, k=k, pad=pad, p_base=2, want_cache=False)
+    y1, _, _ = run(x, c, w, b, k=k, pad=pad, p_base=2, want_cache=False, variant=kernel)
     torch.cuda.synchronize()
     assert_bf16_close(y1, ref, name + " unsplit", exclude=mask)
 

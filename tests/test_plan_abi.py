@@ -436,7 +436,7 @@ def test_every_decoder_signature_takes_a_bf16_fast_path():
 
 VARIANTS_3X3 = ["bf16_s3_n96_p16x32_g32", "bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p8x32_x2", "bf16_s3_n32_p8x32"]
 VARIANTS_FEW = ["bf16_s3_few_p4x128", "bf16_s3_few_p11x128", "bf16_s3_few_p16x128", "bf16_s3_n32_p8x32"]
-VARIANTS_1X1 = ["bf16_s1_n192_p8x32", "bf16_s1_n32_p8x32"]
+VARIANTS_1X1 = ["bf16_s1_n192_p8x32", "bf16_s1_n192_p256_rd", "bf16_s1_n32_p8x32"]
 
 
 def test_plan_variant_pins_the_kernel():
@@ -450,7 +450,7 @@ def test_plan_variant_pins_the_kernel():
     dfew = _desc(c_in=64, c_out=3, h=20, w=70, t_x=2, t_cache=2)
     for name in VARIANTS_FEW:
         assert cc3d.causal_conv3d_plan_variant(dfew, name).info["kernel_name"] == name
-    d1 = _desc(c_in=64, c_out=192, h=20, w=70, t_x=2, t_cache=2, k=(3, 1, 1), padding=(0, 0))
+    d1 = _desc(c_in=128, c_out=192, h=20, w=70, t_x=2, t_cache=2, k=(3, 1, 1), padding=(0, 0))
     for name in VARIANTS_1X1:
         assert cc3d.causal_conv3d_plan_variant(d1, name).info["kernel_name"] == name
     f32 = _desc(dtype=torch.float32)
@@ -482,6 +482,11 @@ def test_plan_variant_pins_the_kernel():
     ("bf16_s1_n32_p8x32", dict(c_in=32, c_out=32)),           # 1x1 variant on a 3x3 call
     ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, k=(3, 1, 1), padding=(0, 0))),
     ("bf16_s1_n192_p8x32", dict(c_in=16, c_out=192, k=(3, 1, 1), padding=(0, 0))),  # C_in % 32 != 0
+    ("bf16_s1_n192_p256_rd", dict(c_in=64, c_out=192, k=(3, 1, 1), padding=(0, 0))),   # one 64-channel chunk
+    ("bf16_s1_n192_p256_rd", dict(c_in=320, c_out=192, k=(3, 1, 1), padding=(0, 0))),  # 5 chunks
+    ("bf16_s1_n192_p256_rd", dict(c_in=96, c_out=192, k=(3, 1, 1), padding=(0, 0))),   # C_in % 64 != 0
+    ("bf16_s1_n192_p256_rd", dict(c_in=128, c_out=96, k=(3, 1, 1), padding=(0, 0))),   # C_out % 192 != 0
+    ("bf16_s1_n192_p256_rd", dict(c_in=128, c_out=192)),                               # 3x3 call
     ("f32_direct", dict(c_in=32, c_out=32)),                  # fp32 kernel on a bf16 call
     ("bf16_s3_n32_p8x32", dict(c_in=32, c_out=32, dtype=torch.float32)),
     ("no_such_kernel", dict(c_in=32, c_out=32)),
@@ -550,4 +555,5 @@ def test_split_reduction_only_where_tiles_leave_slots_idle():
     assert big.info["splits"] == 1 and big.info["workspace_bytes"] == 0    # the group-staged kernel
     full = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=768, h=90, w=160, t_x=1, t_cache=2, k=(3, 1, 1),
                                          padding=(0, 0)))
-    assert full.info["tiles"] == 240 and full.info["splits"] == 1          # one workgroup per unit: 256 slots
+    assert full.info["kernel_name"] == "bf16_s1_n192_p256_rd"               # 57 pixel tiles x 4 channel blocks
+    assert full.info["tiles"] == 228 and full.info["splits"] == 1          # (this kernel never splits)

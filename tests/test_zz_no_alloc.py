@@ -41,7 +41,7 @@ def _both(s, seed):
 
 
 @pytest.mark.parametrize("first,second", [("latent_384_60x104", "latent_384_30x52"),
-                                          ("temporal_384_768_30x52", "latent_384_12x20")])
+                                          ("latent_384_30x52", "latent_384_12x20")])
 def test_noalloc_matches_the_caller_workspace_call_twice_in_a_row(cuda_device, first, second):
     big, small = _sig(first), _sig(second)
     p1, ref1, rco1, got1, gco1 = _both(big, synth.SEED_BASE + 800)
