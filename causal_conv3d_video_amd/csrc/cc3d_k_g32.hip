@@ -10,6 +10,17 @@ namespace {
 // each launch leaves its slot zero when it completes.
 constexpr int kSchedInts = 16;
 __device__ __attribute__((unused)) int g32_sched[cc3d::kSchedSlots * kSchedInts];
+
+// The kernel's argument block, read through a pointer the compiler cannot
+// see through: fields read this way (by the per-tile bookkeeping, which runs
+// once per tile) are loaded where they are used instead of being held in
+// scalar registers across the MFMA loop.
+typedef const __attribute__((address_space(4))) ConvArgs* KArgs;
+__device__ __forceinline__ KArgs kargs() {
+  KArgs p = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(p));
+  return p;
+}
 // bf16 kernel for 3x3 spatial taps with the halo staged by 32-channel groups.
 //
 // The stage loads of the kernel above fetch 32 bytes (16 channels) of every
@@ -151,26 +162,27 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     int k0, k1, k2, k3;
     int z0, z1, z2, z3;
   };
-  auto act_frame = [&](int j) {  // the j-th output frame with an active tap
-    int o = a.act_lo[0] + j;
+  auto act_frame = [&](KArgs k, int j) {  // the j-th output frame with an active tap
+    int o = k->act_lo[0] + j;
 #pragma unroll
     for (int i = 0; i + 1 < kMaxFrameIv; ++i)
-      if (i + 1 < a.nact_iv && j >= a.act_n[i]) {
-        j -= a.act_n[i];
-        o = a.act_lo[i + 1] + j;
+      if (i + 1 < k->nact_iv && j >= k->act_n[i]) {
+        j -= k->act_n[i];
+        o = k->act_lo[i + 1] + j;
       }
     return o;
   };
   auto decode = [&](int t) {
+    const KArgs k = kargs();
     Tile c;
-    c.o = act_frame(t % a.ta_n);
-    t /= a.ta_n;
-    c.nb = t % a.nblk_n;
-    t /= a.nblk_n;
-    const int tile_x = t % a.tiles_x;
-    t /= a.tiles_x;
-    const int tile_y = t % a.tiles_y;
-    c.nn = t / a.tiles_y;
+    c.o = act_frame(k, t % k->ta_n);
+    t /= k->ta_n;
+    c.nb = t % k->nblk_n;
+    t /= k->nblk_n;
+    const int tile_x = t % k->tiles_x;
+    t /= k->tiles_x;
+    const int tile_y = t % k->tiles_y;
+    c.nn = t / k->tiles_y;
     c.x0 = tile_x * TW;
     c.y0 = tile_y * TH;
     c.n0 = c.nb * BN;
@@ -178,13 +190,13 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     c.k0 = c.k1 = c.k2 = c.k3 = 0;
     c.z0 = c.z1 = c.z2 = c.z3 = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxTapsBf16; ++k) {
-      const int z = c.o * a.st + a.delta[k];
-      if (k < a.kt && z >= 0 && z < a.tz) {
-        if (c.nact == 0) { c.k0 = k; c.z0 = z; }
-        else if (c.nact == 1) { c.k1 = k; c.z1 = z; }
-        else if (c.nact == 2) { c.k2 = k; c.z2 = z; }
-        else { c.k3 = k; c.z3 = z; }
+    for (int q = 0; q < kMaxTapsBf16; ++q) {
+      const int z = c.o * k->st + k->delta[q];
+      if (q < k->kt && z >= 0 && z < k->tz) {
+        if (c.nact == 0) { c.k0 = q; c.z0 = z; }
+        else if (c.nact == 1) { c.k1 = q; c.z1 = z; }
+        else if (c.nact == 2) { c.k2 = q; c.z2 = z; }
+        else { c.k3 = q; c.z3 = z; }
         ++c.nact;
       }
     }
