@@ -260,7 +260,7 @@ def time_single_calls(device, launches, stream, warm_seconds=0.2):
         x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"],
                                        device=device, seed=synth.SEED_BASE + 200 + i)
         desc = _desc(cc3d, s, s["tx"], s["tc"])
-        plan = cc3d.causal_conv3d_plan_variant(desc, args.variant) if args.variant else cc3d.causal_conv3d_plan(desc)
+        plan = cc3d.causal_conv3d_plan(desc)
         out = torch.empty(plan.shapes()["out"], dtype=torch.bfloat16, device=device)
         img = cc3d.causal_conv3d_pack_weights(plan, w, stream=stream)
         ws = torch.zeros(plan.info["workspace_bytes"], dtype=torch.uint8, device=device) \
