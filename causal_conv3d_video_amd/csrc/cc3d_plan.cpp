@@ -200,6 +200,12 @@ const char* default_variant(const cc3d_desc_t& d) {
       const int64_t big_tiles = int64_t(d.n) * ((d.h + 15) / 16) * ((d.w + 31) / 32) * (d.c_out / 96) *
                                 std::max(1, d.t_x);
       if (d.c_in % 32 == 0 && big_tiles >= 768) return "bf16_s3_n96_p16x32_g32";
+      // maps so small that the 96-wide tiles leave three quarters of the
+      // compute units idle take 32-wide tiles (three times as many; 384->384
+      // at 30x52: 32 vs 58 us, 48->384: 15 vs 21 us)
+      const int64_t x2_tiles = int64_t(d.n) * ((d.h + 7) / 8) * ((d.w + 31) / 32) * (d.c_out / 96) *
+                               std::max(1, d.t_x);
+      if (x2_tiles < 64) return "bf16_s3_n32_p8x32";
       return "bf16_s3_n96_p8x32_x2";
     }
     if (d.c_out <= 5 && d.k_t == 3 && d.d_t == 1 && d.s_t == 1 && d.c_in % 32 == 0 && d.c_in <= 96)
@@ -210,9 +216,13 @@ const char* default_variant(const cc3d_desc_t& d) {
   // 1x1: the register-direct kernel where it applies (384->768 (3,1,1):
   // 281 vs 309 us at 180x320, 36 vs 39 us at 90x160; both kernels are bound
   // by the vector-memory address path, not by the matrix cores)
+  // (maps with fewer than 64 of its tiles take the 32-wide tiles, as above:
+  // 384->768 at 30x52, 20 vs 31 us)
   const int nch = d.c_in / 64;
-  if (d.c_out % 192 == 0 && cb == 64 && (nch % 2 == 0 || nch % 3 == 0)) return "bf16_s1_n192_p256_rd";
-  if (d.c_out % 192 == 0 && cb >= 32) return "bf16_s1_n192_p8x32";
+  const int64_t rd_tiles = int64_t(d.n) * std::max(1, d.t_x) * ((int64_t(d.h) * d.w + 255) / 256) * (d.c_out / 192);
+  if (d.c_out % 192 == 0 && cb == 64 && (nch % 2 == 0 || nch % 3 == 0) && rd_tiles >= 64)
+    return "bf16_s1_n192_p256_rd";
+  if (d.c_out % 192 == 0 && cb >= 32 && rd_tiles >= 64) return "bf16_s1_n192_p8x32";
   return "bf16_s1_n32_p8x32";
 }
 

@@ -41,7 +41,7 @@ def main():
         dev = "cuda:0"
         w, b, cache = w.to(dev), b.to(dev), cache.to(dev)
         packed = bool(int(st["packed"]))
-        image = None
+        image, layout = None, None
         for i in range(nchunks):
             x = t16(st["x_%d" % i]).to(dev)
             n, tx, h, wd, cin = x.shape
@@ -50,7 +50,10 @@ def main():
             y = torch.full(plan.shapes()["out"], float("nan"), dtype=torch.bfloat16, device=dev)
             co = torch.full(plan.shapes()["cache_out"], float("nan"), dtype=torch.bfloat16, device=dev)
             if packed:
-                image = cc3d.causal_conv3d_pack_weights(plan, w) if image is None else image
+                # one image per weight layout: the plans of chunks of other lengths may
+                # pick another kernel, whose image differs (plan_info weight_layout)
+                if image is None or layout != plan.info["weight_layout"]:
+                    image, layout = cc3d.causal_conv3d_pack_weights(plan, w), plan.info["weight_layout"]
                 nb = plan.info["workspace_bytes"]
                 ws = torch.zeros(nb, dtype=torch.uint8, device=dev) if nb else None
                 cc3d.causal_conv3d_forward_packed(plan, x, cache, image, b, y, co, ws)

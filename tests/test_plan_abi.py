@@ -537,17 +537,21 @@ def test_split_reduction_only_where_tiles_leave_slots_idle():
     units, at least 4 stages each, and no split below 4 units.  Its
     workspace holds an int per tile (rounded to 256 bytes) and one fp32
     tile of partials per unit."""
-    small = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=2))
+    x2 = "bf16_s3_n96_p8x32_x2"
+    small = cc3d.causal_conv3d_plan_variant(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=2), x2)
     i = small.info
-    assert i["kernel_name"] == "bf16_s3_n96_p8x32_x2" and i["tiles"] == 32 and i["splits"] == 16  # 72 stages
+    assert i["kernel_name"] == x2 and i["tiles"] == 32 and i["splits"] == 16  # 72 stages
     assert i["workspace_bytes"] == 256 + 32 * 16 * 256 * 96 * 4
+    # (by default that map takes the 32-wide tiles: 96 of them, split 5 ways)
+    n32 = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=2)).info
+    assert n32["kernel_name"] == "bf16_s3_n32_p8x32" and n32["tiles"] == 96 and n32["splits"] == 5
     mid = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=60, w=104, t_x=1, t_cache=2))
     assert mid.info["tiles"] == 128 and mid.info["splits"] == 4               # 512 slots / 128 tiles
     lat = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2))
     assert lat.info["tiles"] == 240 and lat.info["splits"] == 1 and lat.info["workspace_bytes"] == 0  # 2 < 4
-    first = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=0))
+    first = cc3d.causal_conv3d_plan_variant(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=0), x2)
     assert first.info["splits"] == 6                                         # one active tap: 24 stages
-    two = cc3d.causal_conv3d_plan(_desc(c_in=48, c_out=384, h=30, w=52, t_x=1, t_cache=2))
+    two = cc3d.causal_conv3d_plan_variant(_desc(c_in=48, c_out=384, h=30, w=52, t_x=1, t_cache=2), x2)
     assert two.info["tiles"] == 32 and two.info["splits"] == 1               # 9 stages: 2 units at most
     few_stages = cc3d.causal_conv3d_plan(_desc(c_in=16, c_out=384, h=90, w=160, t_x=1, t_cache=2))
     assert few_stages.info["splits"] == 1 and few_stages.info["workspace_bytes"] == 0  # 3 stages

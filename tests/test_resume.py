@@ -68,7 +68,7 @@ def test_gpu_stream_resumes_bitwise_from_a_saved_cache(cuda_device, tmp_path, si
     dev = "cuda:0"
     wt, bt, xs = synth.replay_chunks(1, s["cin"], s["cout"], h, w_, frames, s["k"], device=dev,
                                      seed=synth.SEED_BASE + 710)
-    image = None
+    image, layout = None, None
     cache, outs, caches = None, [], []
     for x in xs:
         tc = 0 if cache is None else cache.shape[1]
@@ -77,7 +77,10 @@ def test_gpu_stream_resumes_bitwise_from_a_saved_cache(cuda_device, tmp_path, si
         y = torch.full(plan.shapes()["out"], float("nan"), dtype=torch.bfloat16, device=dev)
         co = torch.full(plan.shapes()["cache_out"], float("nan"), dtype=torch.bfloat16, device=dev)
         if packed:
-            image = cc3d.causal_conv3d_pack_weights(plan, wt) if image is None else image
+            # one image per weight layout: the plans of chunks of other lengths may
+            # pick another kernel, whose image differs (plan_info weight_layout)
+            if image is None or layout != plan.info["weight_layout"]:
+                image, layout = cc3d.causal_conv3d_pack_weights(plan, wt), plan.info["weight_layout"]
             nb = plan.info["workspace_bytes"]
             ws = torch.zeros(nb, dtype=torch.uint8, device=dev) if nb else None
             cc3d.causal_conv3d_forward_packed(plan, x, cache, image, bt, y, co, ws)
