@@ -87,18 +87,15 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   static_assert(KSP == 1 || (KSP == 2 && WM == 8), "channel-half split");
   // epilogue staging: waves 0-3 use the idle weight buffer, waves 4-7 the idle halo buffer
   static_assert(4 * 32 * EROW <= WSLOTS * 16 && (NW - 4) * 32 * EROW <= ZSLOTS * 16, "epilogue staging");
-  static_assert((2 * ZSLOTS + 2 * KSP * WSLOTS + (KSP == 1 ? 0 : 64)) * 16 + 2 * BN * 4 <= 160 * 1024, "LDS budget");
+  // (+ 64 slots: the sink of the loads past the end of a buffer, below)
+  static_assert((2 * ZSLOTS + 2 * KSP * WSLOTS + (KSP == 1 ? 0 : 64) + 64) * 16 + 2 * BN * 4 <= 160 * 1024,
+                "LDS budget");
   // channel-half split: the second half's sums pass through an idle halo buffer
   static_assert(KSP == 1 || (WM / 2) * CW * RW * 16 * 64 * 4 <= ZSLOTS * 16, "partial sums");
   // s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9
   // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
   constexpr auto vm_imm = [](int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); };
-  constexpr auto zcnt = [](int w) {  // halo load instructions of wave w per group
-    int n = 0;
-    for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
-    return n;
-  };
-  static_assert(zcnt(0) + WIT <= 63, "vmcnt range");
+  static_assert(ZIT + WIT <= 63, "vmcnt range");
 
   __shared__ uint4 zl[2 * ZSLOTS];
   // Weight buffers.  With KSP = 1 the two sub-stage buffers are separate
@@ -110,6 +107,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   __shared__ uint4 wl_b1[KSP == 1 ? WSLOTS : 64];
   auto wbuf = [&](int b) -> uint4* { return KSP == 1 ? (b ? wl_b1 : wl) : wl + b * WSLOTS; };
   __shared__ float bias_lds[2][BN];
+  __shared__ uint4 sink[64];  // destination of the load instructions past a buffer's end
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -263,22 +261,26 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     return r;
   };
   const WSrc wnone{wpk, 0};
+  // Every wave issues every load instruction of a stage (ZIT halo, WIT
+  // weight), so each wait below is one count for all waves and the loop has
+  // no per-wave branches: a wave whose 64 slots of the last instruction lie
+  // past the buffer aims it at the sink, with offsets out of range (slot ids
+  // past ZCH / WCH), which the range check turns into zeros.
   auto issue_z = [&](const unsigned short* fp, int zb, int it) {
-    if (ZSLOTS % NT == 0 || it * NT + wave * 64 < ZSLOTS) {
-      const __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(zl + zb * ZSLOTS + it * NT + wave * 64), 16, zoff[it], 0, 0, 0);
-    }
+    const bool in = ZSLOTS % NT == 0 || it * NT + wave * 64 < ZSLOTS;  // wave-uniform
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(fp), 0, frame_bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(in ? zl + zb * ZSLOTS + it * NT + wave * 64 : sink), 16,
+        zoff[it], 0, 0, 0);
   };
   auto issue_w = [&](const WSrc& wp, int wb, int it) {
-    if (WSLOTS % NT == 0 || it * NT + wave * 64 < WSLOTS) {
-      const __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(wp.p), 0, wp.rec, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(wbuf(wb) + it * NT + wave * 64), 16, woff[it],
-          0, 0, 0);
-    }
+    const bool in = WSLOTS % NT == 0 || it * NT + wave * 64 < WSLOTS;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(wp.p), 0, wp.rec, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(in ? wbuf(wb) + it * NT + wave * 64 : sink), 16, woff[it],
+        0, 0, 0);
   };
 
   f32x16_t acc[CW][RW];
@@ -430,21 +432,8 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   // loads -- the weight sub-stage -- have landed, and does not drain the
   // halo loads still in flight before it reads that sub-stage)
   auto wait_halo_in_flight = [&]() {  // all but this wave's halo loads of the last group
-    switch (wave) {
-#define CC3D_WAIT_HALO(w)                                             \
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(zcnt(w)) : "memory"); \
-  __builtin_amdgcn_s_waitcnt(vm_imm(zcnt(w)));                     \
-  break;
-      case 0: CC3D_WAIT_HALO(0)
-      case 1: CC3D_WAIT_HALO(1)
-      case 2: CC3D_WAIT_HALO(2)
-      case 3: CC3D_WAIT_HALO(3)
-      case 4: CC3D_WAIT_HALO(4 % NW)
-      case 5: CC3D_WAIT_HALO(5 % NW)
-      case 6: CC3D_WAIT_HALO(6 % NW)
-      default: CC3D_WAIT_HALO(7 % NW)
-#undef CC3D_WAIT_HALO
-    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(ZIT) : "memory");
+    __builtin_amdgcn_s_waitcnt(vm_imm(ZIT));
     asm volatile("" ::: "memory");
   };
 
