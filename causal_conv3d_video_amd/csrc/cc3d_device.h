@@ -131,6 +131,17 @@ __device__ __forceinline__ __attribute__((unused)) int tap_delta(const ConvArgs&
   return d;
 }
 
+// A kernel's argument block (its first and only argument), read through a pointer the compiler cannot
+// see through: fields read this way (by the per-tile bookkeeping, which runs
+// once per tile) are loaded where they are used instead of being held in
+// scalar registers across the MFMA loop.
+typedef const __attribute__((address_space(4))) ConvArgs* KArgs;
+__device__ __forceinline__ KArgs kargs() {
+  KArgs p = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
 // Wave-uniform copy of a pointer (kept in scalar registers).
 __device__ __forceinline__ __attribute__((unused)) const void* uniform_ptr(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);

@@ -10,17 +10,6 @@ namespace {
 // each launch leaves its slot zero when it completes.
 constexpr int kSchedInts = 16;
 __device__ __attribute__((unused)) int g32_sched[cc3d::kSchedSlots * kSchedInts];
-
-// The kernel's argument block, read through a pointer the compiler cannot
-// see through: fields read this way (by the per-tile bookkeeping, which runs
-// once per tile) are loaded where they are used instead of being held in
-// scalar registers across the MFMA loop.
-typedef const __attribute__((address_space(4))) ConvArgs* KArgs;
-__device__ __forceinline__ KArgs kargs() {
-  KArgs p = (KArgs)(__builtin_amdgcn_kernarg_segment_ptr());
-  asm volatile("" : "+s"(p));
-  return p;
-}
 // bf16 kernel for 3x3 spatial taps with the halo staged by 32-channel groups.
 //
 // The stage loads of the kernel above fetch 32 bytes (16 channels) of every

@@ -58,23 +58,16 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
   constexpr int EROW = CW * 32 * 2 + 16;       // epilogue LDS bytes per pixel (padded)
   constexpr int STAGE = (ZSLOTS + WSLOTS) > (NW * 32 * EROW + 15) / 16 ? (ZSLOTS + WSLOTS)
                                                                         : (NW * 32 * EROW + 15) / 16;
-  // load instructions one wave issues per stage (waves past a tile's last
-  // 64-slot block issue fewer)
-  constexpr auto lps_of = [](int w) {
-    int n = 0;
-    for (int it = 0; it < ZIT; ++it) n += it * NT + w * 64 < ZSLOTS;
-    for (int it = 0; it < WIT; ++it) n += it * NT + w * 64 < WSLOTS;
-    return n;
-  };
-  constexpr int LPS = ZIT + WIT;               // upper bound over the waves
+  constexpr int LPS = ZIT + WIT;               // load instructions of every wave per stage
   static_assert((NW == 4 || NW == 8) && TH % WM == 0 && BN % (32 * WN) == 0, "wave tiling");
   static_assert(PZ == 2 || PZ == 4 || PZ == 8, "stage channels");
   constexpr int WG_PER_CU = OCC * 4 / NW > 0 ? OCC * 4 / NW : 1;  // OCC is waves per SIMD
-  static_assert(NBUF >= 2 && (NBUF * STAGE * 16 + 2 * BN * 4) * WG_PER_CU <= 160 * 1024, "LDS budget");
+  static_assert(NBUF >= 2 && (NBUF * STAGE * 16 + 2 * BN * 4 + 1024) * WG_PER_CU <= 160 * 1024, "LDS budget");
   static_assert(LPS * (NBUF - 2) <= 63, "vmcnt range");
 
   __shared__ uint4 lds[NBUF * STAGE];
   __shared__ float bias_lds[2][BN];
+  __shared__ uint4 sink[64];  // destination of the load instructions past a buffer's end
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,18 +113,23 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
   };
   const int splits = SPLIT ? a.splits : 1;
   auto decode = [&](int u) {
+    // (through the opaque argument pointer: see kargs(); the split
+    // instantiations read `a` -- with the pointer their register allocation
+    // reserves a private-memory slot, which makes the runtime set up scratch)
+    const ConvArgs* k = &a;
+    if constexpr (!SPLIT) k = reinterpret_cast<const ConvArgs*>(kargs());
     Tile c;
     c.t = u / splits;
     c.sp = u - c.t * splits;
     int t = c.t;
-    c.o = t % a.to;
-    t /= a.to;
-    c.nb = t % a.nblk_n;
-    t /= a.nblk_n;
-    const int tile_x = t % a.tiles_x;
-    t /= a.tiles_x;
-    const int tile_y = t % a.tiles_y;
-    c.nn = t / a.tiles_y;
+    c.o = t % k->to;
+    t /= k->to;
+    c.nb = t % k->nblk_n;
+    t /= k->nblk_n;
+    const int tile_x = t % k->tiles_x;
+    t /= k->tiles_x;
+    const int tile_y = t % k->tiles_y;
+    c.nn = t / k->tiles_y;
     c.x0 = tile_x * TW;
     c.y0 = tile_y * TH;
     c.n0 = c.nb * BN;
@@ -139,17 +137,17 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
     c.k0 = c.k1 = c.k2 = c.k3 = 0;
     c.z0 = c.z1 = c.z2 = c.z3 = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxTapsBf16; ++k) {
-      const int z = c.o * a.st + a.delta[k];
-      if (k < a.kt && z >= 0 && z < a.tz) {
-        if (c.nact == 0) { c.k0 = k; c.z0 = z; }
-        else if (c.nact == 1) { c.k1 = k; c.z1 = z; }
-        else if (c.nact == 2) { c.k2 = k; c.z2 = z; }
-        else { c.k3 = k; c.z3 = z; }
+    for (int q = 0; q < kMaxTapsBf16; ++q) {
+      const int z = c.o * k->st + k->delta[q];
+      if (q < k->kt && z >= 0 && z < k->tz) {
+        if (c.nact == 0) { c.k0 = q; c.z0 = z; }
+        else if (c.nact == 1) { c.k1 = q; c.z1 = z; }
+        else if (c.nact == 2) { c.k2 = q; c.z2 = z; }
+        else { c.k3 = q; c.z3 = z; }
         ++c.nact;
       }
     }
-    const int nst = c.nact * (a.cin / CB);
+    const int nst = c.nact * (k->cin / CB);
     c.s0 = c.sp * nst / splits;
     c.s1 = (c.sp + 1) * nst / splits;
     return c;
@@ -214,26 +212,27 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
     return l;
   };
   constexpr int NLOAD = ZIT + WIT;  // load instructions of one stage, per thread
-  // slots are filled 64 at a time (one wave instruction); a wave whose
-  // 64-slot block lies past the tile issues nothing
+  // slots are filled 64 at a time (one wave instruction).  Every wave
+  // issues every instruction, so the waits are one count for all waves: a
+  // wave whose 64-slot block lies past the tile aims it at the sink, with
+  // offsets out of range (slot ids past ZCH / WCH), which the range check
+  // turns into zeros.
   auto issue_piece = [&](const StageLoad& l, int j) {
     uint4* zb = lds + l.buf * STAGE;
     if (j < ZIT) {
-      if (ZSLOTS % NT == 0 || j * NT + wave * 64 < ZSLOTS) {
-        const __amdgpu_buffer_rsrc_t zr =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(l.fp), 0, frame_bytes, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (__attribute__((address_space(3))) void*)(zb + j * NT + wave * 64),
-                                                 16, zoff[j], 0, 0, 0);
-      }
+      const bool in = ZSLOTS % NT == 0 || j * NT + wave * 64 < ZSLOTS;  // wave-uniform
+      const __amdgpu_buffer_rsrc_t zr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(l.fp), 0, frame_bytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          zr, (__attribute__((address_space(3))) void*)(in ? zb + j * NT + wave * 64 : sink), 16, zoff[j], 0, 0, 0);
     } else {
       const int it = j - ZIT;
-      if (WSLOTS % NT == 0 || it * NT + wave * 64 < WSLOTS) {
-        const __amdgpu_buffer_rsrc_t wr =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(l.wp), 0, l.wrec, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr,
-                                                 (__attribute__((address_space(3))) void*)(zb + ZSLOTS + it * NT + wave * 64),
-                                                 16, woff[it], 0, 0, 0);
-      }
+      const bool in = WSLOTS % NT == 0 || it * NT + wave * 64 < WSLOTS;
+      const __amdgpu_buffer_rsrc_t wr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(l.wp), 0, l.wrec, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (__attribute__((address_space(3))) void*)(in ? zb + ZSLOTS + it * NT + wave * 64 : sink), 16,
+          woff[it], 0, 0, 0);
     }
   };
   auto load_stage = [&](const Tile& c, int cc, int ti, int buf) {
@@ -410,21 +409,11 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
 
   // Wait until this wave's loads of all but the NBUF-2 newest stages have
   // landed (vmcnt counts the wave's own outstanding loads, in issue order).
+  constexpr auto vm_imm = [](int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); };
   auto wait_newer_stages = [&]() {
-    if constexpr (NBUF > 2) {
-      switch (wave) {
-        case 0: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(0) * (NBUF - 2)) : "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(1) * (NBUF - 2)) : "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(2) * (NBUF - 2)) : "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(3) * (NBUF - 2)) : "memory"); break;
-        case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(4) * (NBUF - 2)) : "memory"); break;
-        case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(5) * (NBUF - 2)) : "memory"); break;
-        case 6: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(6) * (NBUF - 2)) : "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lps_of(7) * (NBUF - 2)) : "memory"); break;
-      }
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    constexpr int N = LPS * (NBUF - 2);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt(vm_imm(N));  // (the same wait, seen by the compiler's own tracking)
   };
 
   // Workgroup barrier with explicit waits only: the caller has waited for
