@@ -248,6 +248,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   // Epilogue: + bias once (fp32), round to nearest even, bf16 stores.  The
+  // accumulators are read out of their AGPRs one element per store (inline
+  // v_accvgpr_read), so that the compiler does not copy all 192 of them to
+  // VGPRs at once while the next stages' pixels occupy 96 VGPRs.  The
   // lane holding pixel l32 of a 32-pixel block has channels
   // (v/4)*8 + g*4 + (v%4) of each 32-channel block: 4 consecutive channels,
   // one 8-byte store each.  Stores to pixels past the frame fall outside the
@@ -267,8 +270,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int v4 = 0; v4 < 4; ++v4) {
           const int cl = q * 32 + v4 * 8;  // + g*4 in ooff
           const float4 bv = *reinterpret_cast<const float4*>(&bias_lds[par][cl + g * 4]);
-          const unsigned lo = pack_bf16x2(acc[q][rb][v4 * 4 + 0] + bv.x, acc[q][rb][v4 * 4 + 1] + bv.y);
-          const unsigned hi = pack_bf16x2(acc[q][rb][v4 * 4 + 2] + bv.z, acc[q][rb][v4 * 4 + 3] + bv.w);
+          float f[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)  // (read from the accumulator registers one at a time: see above)
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(f[e]) : "a"(acc[q][rb][v4 * 4 + e]));
+          const unsigned lo = pack_bf16x2(f[0] + bv.x, f[1] + bv.y);
+          const unsigned hi = pack_bf16x2(f[2] + bv.z, f[3] + bv.w);
           const u32x2_t v = {lo, hi};
           __builtin_amdgcn_raw_buffer_store_b64(v, orc, ooff, cl * 2, 0);
           // (one store at a time: converting all 96 pairs first would need
