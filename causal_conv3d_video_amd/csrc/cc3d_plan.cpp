@@ -175,9 +175,10 @@ bool variant_for(const cc3d_desc_t& d, const char* name, Variant* v) {
 }
 
 // Default choice.  Large 3x3 maps take the group-staged kernel: the halo
-// staged by 32 channels, one workgroup per compute unit (from three rounds of
-// 256 tiles: 384->384 at 180x320 with 2 frames, 960 tiles, runs 8% faster
-// than the two-workgroup kernel).  Where C_out is a multiple of 64 its
+// staged by 32 channels, one workgroup per compute unit (its 64-wide tile
+// from 1.5 rounds of 256 tiles: 384->384 at 120x208 with 2 frames, 420
+// tiles, 347 vs 383 us on the two-workgroup kernel; 960 tiles at 180x320,
+// 8% faster).  Where C_out is a multiple of 64 its
 // 24x32-pixel x 64-channel tile (three rows per wave) reads 15% fewer LDS
 // bytes per MFMA than the 16x32 x 96 one and runs 1-3% faster.  Small maps
 // keep two smaller workgroups per compute unit so that every unit gets
@@ -194,7 +195,7 @@ const char* default_variant(const cc3d_desc_t& d) {
     if (d.c_out % 64 == 0 && d.c_in % 32 == 0) {
       const int64_t tiles64 =
           int64_t(d.n) * ((d.h + 23) / 24) * ((d.w + 31) / 32) * (d.c_out / 64) * std::max(1, d.t_x);
-      if (tiles64 >= 768) return "bf16_s3_n64_p24x32_g32";
+      if (tiles64 >= 384) return "bf16_s3_n64_p24x32_g32";
     }
     if (d.c_out % 96 == 0) {
       const int64_t big_tiles = int64_t(d.n) * ((d.h + 15) / 16) * ((d.w + 31) / 32) * (d.c_out / 96) *
