@@ -47,8 +47,9 @@ struct ConvArgs {
   // pixel codes instead of bf16 output,
   // code = trunc(clamp(fma(y, px_scale, px_offset) * 255, 0, 255)) in fp32.
   int tile_h;
-  // Few-output-channel kernel: it also writes the cache-out (source frames
-  // co_lo .. tz - 1 into cache_out[n][0 .. tz - co_lo)); co_lo = tz when not.
+  // Few-output-channel and group-staged kernels: they also write the
+  // cache-out (source frames co_lo .. tz - 1 into cache_out[n][0 .. tz -
+  // co_lo)); co_lo = tz when not.
   void* cache_out;
   int co_lo;
   int out_u8;

@@ -5,8 +5,8 @@
 namespace {
 
 // The scheduler counters of every launch of this kernel on the device:
-// cc3d::kSchedSlots slots of kSchedInts ints (a tile counter per XCD, then
-// the count of finished workgroups).  Zero when the code object is loaded;
+// cc3d::kSchedSlots slots of kSchedInts ints (a tile counter per XCD, the
+// count of finished workgroups, then the cache-out chunk counter).  Zero when the code object is loaded;
 // each launch leaves its slot zero when it completes.
 constexpr int kSchedInts = 16;
 __device__ __attribute__((unused)) int g32_sched[cc3d::kSchedSlots * kSchedInts];
@@ -664,13 +664,66 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     }
   }
 
+  // Cache-out: source frames co_lo .. tz - 1 of every batch item go to
+  // cache_out[n][0 .. tz - co_lo) in chunks of U 16-byte pieces per thread,
+  // claimed from the launch's copy counter once a workgroup's tiles have run
+  // out, so the copy runs on the compute units the last tiles leave idle.
+  // The claim of the next chunk is in flight while a chunk is copied; the
+  // buffer range check drops the pieces past the end of a frame.
+  {
+    const KArgs k = kargs();
+    const int co_lo = k->co_lo, tz = k->tz;
+    if (co_lo < tz) {
+      constexpr int U = 16;
+      constexpr int CHUNK = NT * 16 * U;
+      const int L = tz - co_lo;
+      const int cpf = int((int64_t(frame_bytes) + CHUNK - 1) / CHUNK);
+      const int nchunks = k->n * L * cpf;
+      const unsigned char* const xb = static_cast<const unsigned char*>(k->x);
+      const unsigned char* const cb = static_cast<const unsigned char*>(k->cache);
+      unsigned char* const db = static_cast<unsigned char*>(k->cache_out);
+      const int tx = k->tx, tc = k->tc;
+      __shared__ int co_claim[2];
+      if (tid == 0) co_claim[0] = __hip_atomic_fetch_add(sched + 9, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      barrier();
+      int cpar = 0;
+      int c = co_claim[0];
+#pragma unroll 1
+      while (c < nchunks) {
+        int nxt = 0;
+        if (tid == 0) nxt = __hip_atomic_fetch_add(sched + 9, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int f = c / cpf, part = c - f * cpf;
+        const int nn = f / L, j = f - nn * L, zf = co_lo + j;
+        const int64_t off = int64_t(part) * CHUNK;
+        const unsigned char* src = (zf < tc ? cb + (int64_t(nn) * tc + zf) * frame_bytes
+                                            : xb + (int64_t(nn) * tx + (zf - tc)) * frame_bytes) + off;
+        unsigned char* dst = db + int64_t(f) * frame_bytes + off;
+        const int64_t left = frame_bytes - off;
+        const int rec = __builtin_amdgcn_readfirstlane(left < CHUNK ? int(left) : CHUNK);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(src)), 0, rec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rd =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(dst)), 0, rec, 0x00020000);
+        u32x4_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (u * NT + tid) * 16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, (u * NT + tid) * 16, 0, 0);
+        cpar ^= 1;
+        if (tid == 0) co_claim[cpar] = nxt;
+        barrier();
+        c = co_claim[cpar];
+      }
+    }
+  }
+
   // The last workgroup to finish clears the counters for the next launch
   // that uses them (its claims and every other workgroup's are done: each
   // workgroup counts itself after its last claim).
   if (tid == 0) {
     const int done = __hip_atomic_fetch_add(sched + 8, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (done == int(gridDim.x) - 1)
-      for (int x = 0; x < 9; ++x) __hip_atomic_store(sched + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int x = 0; x < 10; ++x) __hip_atomic_store(sched + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #endif
 }

@@ -233,8 +233,8 @@ cc3d_status_t run_plan(cc3d_plan_t plan, const void* x, const void* cache_in, co
     a.w = wsrc;
     a.wpk = nullptr;
   }
-  // the few-output-channel kernel writes the cache-out itself
-  const bool fused_co = in.kernel_id == CC3D_K_BF16_S3_FEW && cache_out && in.t_cache_out > 0;
+  // the few-output-channel and group-staged kernels write the cache-out themselves
+  const bool fused_co = (in.kernel_id == CC3D_K_BF16_S3_FEW || is_g32(in.kernel_id)) && cache_out && in.t_cache_out > 0;
   a.cache_out = fused_co ? cache_out : nullptr;
   a.co_lo = fused_co ? a.tz - in.t_cache_out : a.tz;
   a.splits = split ? in.splits : 1;
