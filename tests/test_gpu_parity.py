@@ -122,6 +122,8 @@ GROUP_STAGED_N64 = [
     (32, 64, 24, 40, 3, 1, (2, 3, 3), 1, 1, 1, True),    # k_t = 2
     (64, 64, 24, 33, 2, 0, (3, 3, 3), 1, 4, 1, True),    # p_base > (k_t-1)*d_t: bias-only frames
     (32, 384, 20, 50, 2, 3, (3, 3, 3), 1, 2, 1, False),  # no bias, |C| > p_base, 6 blocks, one patch row
+    (64, 64, 64, 96, 1, 2, (3, 3, 3), 1, 2, 2, True),    # batch 2, one new frame: each item's cache-out is a
+                                                          # cached and a new frame, 7 copy chunks each (one ragged)
 ]
 
 
