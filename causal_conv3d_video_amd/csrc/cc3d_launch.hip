@@ -21,13 +21,16 @@
 //     dilation 2 ("same") and at spatial stride 2.  One persistent workgroup
 //     per compute unit with a dynamic per-XCD tile schedule; the halo of one
 //     (active tap, 32-channel group) is staged once into LDS and serves 9
-//     spatial taps x 2 sub-stages of 16 channels.
+//     spatial taps x 2 sub-stages of 16 channels.  Workgroups whose tiles
+//     have run out copy the cache-out.
 //   * conv_bf16_mfma (cc3d_k_mfma.hip): smaller 3x3 maps (two workgroups per
 //     compute unit), other C_out, and the 1x1 / (k_t,1,1) convs.
 //   * conv_bf16_few (cc3d_few.inc): C_out <= 5 (the RGB head).  Walks
-//     time per patch, streaming whole halo rows.
+//     time per patch, streaming whole halo rows; stores the cache-out from
+//     the rows it stages.
 //   * conv_bf16_gen, conv_f32_direct, copy_tail_frames (cc3d_k_misc.hip):
-//     any other spatial parameters, the fp32 path, the cache-out.
+//     any other spatial parameters, the fp32 path, the cache-out of the
+//     other kernels.
 // The halo-staged kernels read their weights from a packed, stage-ordered
 // image when the caller supplies one (causal_conv3d_pack_weights), and
 // gather them from W in place otherwise; nothing is kept between calls.
