@@ -55,11 +55,20 @@ __device__ __attribute__((unused)) int g32_sched[cc3d::kSchedSlots * kSchedInts]
 // WPK: the weight sub-stages come from the packed image (a.wpk), one
 // contiguous run each; otherwise each slot's 16-byte piece is gathered from W
 // as the caller stores it, into the same LDS layout.
-template <int BN, int TH, int WM, int DD, int SS, int KSP, bool WPK>
+//
+// SPL: split reduction (maps with so few tiles that most compute units would
+// idle).  Work unit u is split u % a.splits of tile u / a.splits and runs a
+// contiguous share of the tile's group sequence; every unit stores its fp32
+// partial sums in the workspace (device-scope stores), counts itself in the
+// tile's arrival counter, and the last to arrive adds the partials of all
+// splits in split order -- the same sum whichever unit arrives last -- and
+// runs the epilogue.  It leaves the counter zero.
+template <int BN, int TH, int WM, int DD, int SS, int KSP, bool WPK, bool SPL>
 __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4, WM / 4))) void conv_bf16_g32(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using WT = WTile<BN, 3, 16>;
   static_assert(SS == 1 || (SS == 2 && DD == 1), "stride 2 runs undilated");
+  static_assert(!SPL || KSP == 1, "split units on the one-wave-per-row-group schedule");
   constexpr int TW = 32, S = 9;
   constexpr int HP = SS * (TH - 1) + 2 * DD + 1;             // halo rows
   constexpr int WP = SS == 1 ? TW + 2 * DD : 2 * TW + 1;     // halo columns
@@ -148,6 +157,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     int o, nb, nn, x0, y0, n0, nact;
     int k0, k1, k2, k3;
     int z0, z1, z2, z3;
+    int t, sp, g0, g1;  // tile, split, and the split's groups [g0, g1) (SPL only)
   };
   auto act_frame = [&](KArgs k, int j) {  // the j-th output frame with an active tap
     int o = k->act_lo[0] + j;
@@ -162,6 +172,12 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   auto decode = [&](int t) {
     const KArgs k = kargs();
     Tile c;
+    c.t = t;
+    c.sp = 0;
+    if constexpr (SPL) {
+      c.sp = t % k->splits;
+      c.t = t = t / k->splits;
+    }
     c.o = act_frame(k, t % k->ta_n);
     t /= k->ta_n;
     c.nb = t % k->nblk_n;
@@ -186,6 +202,12 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
         else { c.k3 = q; c.z3 = z; }
         ++c.nact;
       }
+    }
+    c.g0 = c.g1 = 0;
+    if constexpr (SPL) {
+      const int g = c.nact * (k->cin / 32);
+      c.g0 = c.sp * g / k->splits;
+      c.g1 = (c.sp + 1) * g / k->splits;
     }
     return c;
   };
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
 
   // A group position: tile, active-tap index, 32-channel group.
   struct Grp {
-    int t, ti, gz;
+    int t, ti, gz, gi;  // (gi: the group's index in its tile's sequence, SPL only)
   };
   auto halo_src = [&](const Tile& c, int ti, int gz) {
     const int z = pick(ti, c.z0, c.z1, c.z2, c.z3);
@@ -393,14 +415,40 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
   // tile is the current one or the next (tnext); the tile after that is the
   // one claimed during the current tile's first group (tnn), which a tile of
   // a single group already needs.  zoff holds the halo offsets of its tile.
-  Grp nx{ctile, 0, 0};
+  Grp nx{ctile, 0, 0, 0};
   Tile nt{};
   bool nx_ok = ctile >= 0;
+  // (a split unit's groups start at g0: group-major, gz = g0 / nact)
+  auto nx_start = [&]() {
+    if constexpr (SPL) {
+      nx.gi = nt.g0;
+      nx.gz = nt.g0 / nt.nact;
+      nx.ti = nt.g0 - nx.gz * nt.nact;
+    }
+  };
   if (nx_ok) {
     nt = decode(ctile);
     halo_offsets(nt);
+    nx_start();
   }
   auto nx_advance = [&]() {
+    if constexpr (SPL) {
+      if (++nx.ti == nt.nact) {
+        nx.ti = 0;
+        ++nx.gz;
+      }
+      if (++nx.gi == nt.g1) {
+        nx.t = nx.t == ctile ? tnext : tnn;
+        if (nx.t < 0) {
+          nx_ok = false;
+          return;
+        }
+        nt = decode(nx.t);
+        halo_offsets(nt);
+        nx_start();
+      }
+      return;
+    }
     if (++nx.ti == nt.nact) {
       nx.ti = 0;
       if (++nx.gz == ngrp) {
@@ -443,6 +491,88 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+  };
+
+  // Split reduction (SPL): this thread's share of a unit's fp32 partial sums
+  // (float4 runs interleaved across the workgroup's threads, so that each
+  // store instruction writes one contiguous block).  The units of a tile may
+  // run on different XCDs, whose L2 caches are not coherent with each
+  // other: the partials are written and read with device-scope (sc1)
+  // accesses, which go to the device's coherence point, and the arrival
+  // count is a device-scope atomic.  Returns (uniformly) whether this unit
+  // arrived last; acc then holds the tile's sum over all splits, added in
+  // split order.
+  __shared__ int last_lds;
+  auto reduce_splits = [&](const Tile& c) {
+    if constexpr (!SPL) {
+      return true;
+    } else {
+      constexpr int NACC = CW * RW * 16;
+      constexpr int kSC1 = 16;  // cache-policy bits of a buffer access: device scope
+      constexpr int part_bytes = (NACC / 4) * NT * 16;
+      const KArgs k = kargs();
+      const int splits = k->splits;
+      int* const arrivals = static_cast<int*>(k->ws);
+      const unsigned char* const tile_parts =
+          static_cast<const unsigned char*>(k->ws) + k->ws_part + int64_t(c.t) * splits * part_bytes;
+      const __amdgpu_buffer_rsrc_t pr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(tile_parts)), 0,
+                                            __builtin_amdgcn_readfirstlane(splits * part_bytes), 0x00020000);
+      const int mine = __builtin_amdgcn_readfirstlane(c.sp * part_bytes);
+#pragma unroll
+      for (int q = 0; q < CW; ++q)
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int e4 = (q * RW + r) * 4 + v4;
+            const u32x4_t v = {__float_as_uint(acc[q][r][v4 * 4]), __float_as_uint(acc[q][r][v4 * 4 + 1]),
+                               __float_as_uint(acc[q][r][v4 * 4 + 2]), __float_as_uint(acc[q][r][v4 * 4 + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, pr, tid * 16, mine + e4 * NT * 16, kSC1);
+          }
+      vm_drain();  // the partials are at the coherence point
+      barrier();
+      if (tid == 0) {
+        const int before = __hip_atomic_fetch_add(arrivals + c.t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = before == splits - 1;
+        if (last) __hip_atomic_store(arrivals + c.t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_lds = last;
+      }
+      barrier();
+      const bool last = __builtin_amdgcn_readfirstlane(last_lds) != 0;
+      if (last) {
+        zero_acc();
+        // per 16-float accumulator run, the loads of up to four units (16
+        // float4) are issued together, then added in split order
+#pragma unroll
+        for (int q = 0; q < CW; ++q)
+#pragma unroll
+          for (int r = 0; r < RW; ++r) {
+            const int run = (q * RW + r) * 4 * NT * 16;
+            for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+              u32x4_t pv[4][4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (sp0 + j < splits) {
+                  const int so = __builtin_amdgcn_readfirstlane((sp0 + j) * part_bytes + run);
+#pragma unroll
+                  for (int v = 0; v < 4; ++v)
+                    pv[j][v] = __builtin_amdgcn_raw_buffer_load_b128(pr, tid * 16, so + v * NT * 16, kSC1);
+                }
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (sp0 + j < splits) {
+#pragma unroll
+                  for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[q][r][v * 4 + e] += __uint_as_float(pv[j][v][e]);
+                }
+            }
+          }
+        vm_drain();
+      }
+      return last;
+    }
   };
 
   if constexpr (KSP == 2) {
@@ -569,14 +699,16 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
         const bool claims = tnext >= 0;  // claim the tile after tnext while this one runs
         const int ngt = ct.nact * ngrp;  // >= 1: only frames with an active tap have tiles
         const bool rows_in = ct.y0 + wr * RW < a.ho;  // wave-uniform
-        for (int gi = 0; gi < ngt; ++gi) {
+        // (a split unit runs groups [g0, g1) of its tile)
+        const int gbeg = SPL ? ct.g0 : 0, gend = SPL ? ct.g1 : ngt;
+        for (int gi = gbeg; gi < gend; ++gi) {
           // group-major order: the active taps of one 32-channel group run back
           // to back, so a source frame's group is reused by the output frames of
           // the neighbouring tiles within a few groups, while it is still in L2
           const int gz = gi / ct.nact, ti = gi - gz * ct.nact;
           const uint4* zb = zl + hpar * ZSLOTS;
           unsigned short bval = 0;
-          if (gi == 0) bval = bias_value(ct);
+          if (gi == gbeg) bval = bias_value(ct);
           const bool more = nx_ok;
           // sub-stage 0: load W[1] <- (this group, second half), H[next] <- next group
           {
@@ -591,7 +723,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
           }
           if (more) wait_halo_in_flight();
           else vm_drain();
-          if (gi == 0 && tid < BN) {
+          if (gi == gbeg && tid < BN) {
             // (the empty asm keeps the use of the bias load -- and so the
             // compiler's wait for it -- here, after the sub-stage, where the
             // load has long landed, instead of right after it is issued)
@@ -605,7 +737,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
           // behind the sub-stage; the claim is published at its barrier).
           const int cx = (xcd + steal) & 7;
           int v = 0;
-          if (gi == 0 && claims && tid == 0) v = claim(cx);
+          if (gi == gbeg && claims && tid == 0) v = claim(cx);
           {
             const WSrc wpn = more ? wsrc(nt, nx.ti, nx.gz * 2) : wnone;
             compute(zb, wbuf(1), rows_in, std::integral_constant<int, 1>{}, std::integral_constant<int, WIT>{},
@@ -614,7 +746,7 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
                     });
           }
           asm volatile("" ::: "memory");  // the claim is read only after the sub-stage
-          if (gi == 0 && claims && tid == 0) {
+          if (gi == gbeg && claims && tid == 0) {
             int t = claimed(cx, v);
             while (t < 0 && steal < 7) {
               ++steal;
@@ -625,12 +757,12 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
           }
           vm_drain();
           barrier();
-          if (gi == 0 && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
+          if (gi == gbeg && claims) tnn = __builtin_amdgcn_readfirstlane(claim_lds);
           if (more) nx_advance();
           hpar ^= 1;
         }
         // (the output stores may stay in flight across this barrier)
-        epilogue(ct, par, hpar ^ 1, 1);
+        if (!SPL || reduce_splits(ct)) epilogue(ct, par, hpar ^ 1, 1);
         barrier();
         par ^= 1;
         ctile = tnext;
@@ -728,15 +860,25 @@ __global__ __launch_bounds__(WM * 64) __attribute__((amdgpu_waves_per_eu(WM / 4,
 #endif
 }
 
-template <int BN, int TH, int WM, int DD, int SS, int KSP, bool WPK>
+template <int BN, int TH, int WM, int DD, int SS, int KSP, bool WPK, bool SPL>
 const void* g32_kernel() {
-  return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM, DD, SS, KSP, WPK>);
+  return reinterpret_cast<const void*>(&conv_bf16_g32<BN, TH, WM, DD, SS, KSP, WPK, SPL>);
 }
 
-template <int BN, int TH, int WM, int DD = 1, int SS = 1, int KSP = 1>
+// (SPL: the split instantiation, for a.splits > 1: its work units are the
+// tiles' splits, a.nat of them)
+template <int BN, int TH, int WM, int DD = 1, int SS = 1, int KSP = 1, bool SPL = false>
 hipError_t launch_g32(const ConvArgs& a, int64_t tiles, int cus, hipStream_t s) {
-  if (a.wpk) return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS, KSP, true>>(a, tiles, cus, WM * 64, s);
-  return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS, KSP, false>>(a, tiles, cus, WM * 64, s);
+  if (a.wpk) return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS, KSP, true, SPL>>(a, tiles, cus, WM * 64, s);
+  return launch_persistent<&g32_kernel<BN, TH, WM, DD, SS, KSP, false, SPL>>(a, tiles, cus, WM * 64, s);
+}
+
+// The split units of a.nat tiles: a.splits per tile.
+template <int BN, int TH, int WM>
+hipError_t launch_g32_split(const ConvArgs& a, int cus, hipStream_t s) {
+  ConvArgs b = a;
+  b.nat = a.nat * a.splits;
+  return launch_g32<BN, TH, WM, 1, 1, 1, true>(b, std::max(b.nat, 1), cus, s);
 }
 
 }  // namespace
@@ -744,6 +886,11 @@ hipError_t launch_g32(const ConvArgs& a, int64_t tiles, int cus, hipStream_t s) 
 namespace cc3d {
 
 hipError_t launch_g32_family(int kernel_id, const ConvArgs& a, int64_t tiles, int cus, hipStream_t s) {
+  if (a.splits > 1) {
+    if (kernel_id == CC3D_K_BF16_S3_N96_G32W8) return launch_g32_split<96, 16, 8>(a, cus, s);
+    if (kernel_id == CC3D_K_BF16_S3_N64_G32W8) return launch_g32_split<64, 24, 8>(a, cus, s);
+    return hipErrorInvalidValue;
+  }
   switch (kernel_id) {
     case CC3D_K_BF16_S3_N96_G32W8: return launch_g32<96, 16, 8>(a, tiles, cus, s);
     case CC3D_K_BF16_S3_N64_G32W8: return launch_g32<64, 24, 8>(a, tiles, cus, s);

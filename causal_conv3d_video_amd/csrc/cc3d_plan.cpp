@@ -355,7 +355,8 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
     }
     if (v.id == CC3D_K_BF16_S3_FEW) in.bytes_cache_out /= 2;  // written from the staged rows, not re-read
     in.weight_layout = layout_fingerprint(p->pack_kind, v.block_n, int32_t(ks), v.cin_chunk, d);
-    // Split reduction (conv_bf16_mfma only; causal_conv3d_forward_packed):
+    // Split reduction (the two-workgroup and 1x1 kernels of conv_bf16_mfma;
+    // causal_conv3d_forward_packed):
     // when a call's tiles would leave three quarters or more of the chip's
     // workgroup slots idle, each tile's K stages are divided among up to 16
     // units (at least 4 stages each) so that the slots fill.  Each unit
@@ -375,6 +376,19 @@ cc3d_status_t plan_impl(const cc3d_desc_t* desc, const char* kernel, cc3d_plan_t
       if (in.tiles * 4 <= slots) {
         const int64_t s = std::min<int64_t>({slots / std::max<int64_t>(in.tiles, 1), stages / 4, 16});
         in.splits = s >= 4 ? int32_t(s) : 1;
+      }
+      if (in.splits > 1)
+        in.workspace_bytes = (in.tiles * 4 + 255) / 256 * 256 +
+                             in.tiles * in.splits * int64_t(in.block_m) * in.block_n * 4;
+    }
+    // The group-staged kernel (one workgroup per compute unit) splits each
+    // tile's group sequence when its tiles would leave half the compute units
+    // or more idle: up to 4 splits, as many as fill the units, each with at
+    // least one 32-channel group of every tile.
+    if (v.id == CC3D_K_BF16_S3_N64_G32W8 || v.id == CC3D_K_BF16_S3_N96_G32W8) {
+      if (in.tiles * 2 <= kComputeUnits) {
+        const int64_t s = std::min<int64_t>({kComputeUnits / std::max<int64_t>(in.tiles, 1), d.c_in / 32, 4});
+        in.splits = s >= 2 ? int32_t(s) : 1;
       }
       if (in.splits > 1)
         in.workspace_bytes = (in.tiles * 4 + 255) / 256 * 256 +

@@ -177,6 +177,9 @@ cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
  *                              (default for large maps)
  *   "bf16_s3_n96_p16x32_g32"  3x3, C_out % 96 == 0, C_in % 32 == 0
  *                              (default for large maps where C_out % 64 != 0)
+ *                              (both: on maps whose tiles leave half the
+ *                              compute units idle, forward_packed splits each
+ *                              tile's channel groups, plan_info.splits)
  *   "bf16_s3_n96_p8x32_x2"    3x3, C_out % 96 == 0
  *   "bf16_s3_n32_p8x32"       3x3, any C_out
  *   "bf16_s3_few_p<R>x128"    3x3, k_t = 3, d_t = 1, s_t = 1, C_out <= 5,

@@ -947,6 +947,11 @@ SPLIT_CASES = [
     ("conv_512_512_24x40", 1, 512, 512, (3, 3, 3), 24, 40, 1, 2, "bf16_s3_n32_p8x32", 5),
     ("temporal_384_768_30x52", 1, 384, 768, (3, 1, 1), 30, 52, 1, 2, "bf16_s1_n192_p8x32", 4),
     ("temporal_384_768_16x64_2f", 1, 384, 768, (3, 1, 1), 16, 64, 2, 2, "bf16_s1_n192_p8x32", 4),
+    # the group-staged kernel's splits of a tile's 32-channel group sequence
+    ("g32_n64_latent_90x160", 1, 384, 384, (3, 3, 3), 90, 160, 1, 2, "bf16_s3_n64_p24x32_g32", 2),
+    ("g32_n96_192_45x80", 1, 384, 192, (3, 3, 3), 45, 80, 1, 2, "bf16_s3_n96_p16x32_g32", 4),
+    ("g32_n64_first_chunk_3f", 1, 64, 64, (3, 3, 3), 48, 64, 3, 0, "bf16_s3_n64_p24x32_g32", 2),
+    ("g32_n64_n2_2f", 2, 128, 128, (3, 3, 3), 40, 70, 2, 2, "bf16_s3_n64_p24x32_g32", 4),
 ]
 
 
