@@ -993,13 +993,16 @@ def test_split_reduction_every_output_and_repeatable(cuda_device, case):
     assert_bf16_close(y1, ref, name + " unsplit", exclude=mask)
 
 
-def test_split_reduction_replays_in_a_graph(cuda_device):
+@pytest.mark.parametrize("variant", [None, "bf16_s3_n64_p24x32_g32"], ids=["default", "group_staged"])
+def test_split_reduction_replays_in_a_graph(cuda_device, variant):
     """A split call captured in a graph: the arrival counters are reset by
-    the last unit of each tile, so every replay starts from zero."""
+    the last unit of each tile, so every replay starts from zero (the
+    group-staged kernel also keeps its captured scheduler slot)."""
     s = next(v for v in synth.DECODER_SIGNATURES_480 if v["name"] == "latent_384_30x52")
     x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"], device=DEV,
                                    seed=synth.SEED_BASE + 610)
-    plan = plan_for(x, s["tc"], w, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    plan = plan_for(x, s["tc"], w, k=s["k"], pad=s["pad"], p_base=s["p_base"], variant=variant)
+    assert plan.info["splits"] > 1
     img = cc3d.causal_conv3d_pack_weights(plan, w)
     ws = workspace_for(plan, DEV)
     ref = nan_like(plan.shapes()["out"], torch.bfloat16, DEV)

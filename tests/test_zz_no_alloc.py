@@ -25,10 +25,10 @@ def _sig(name):
                 if v["name"] == name)
 
 
-def _both(s, seed):
+def _both(s, seed, variant=None):
     x, c, w, b = synth.conv_inputs(1, s["cin"], s["cout"], s["h"], s["w"], s["tx"], s["tc"], s["k"], device=DEV,
                                    seed=seed)
-    plan = plan_for(x, s["tc"], w, k=s["k"], pad=s["pad"], p_base=s["p_base"])
+    plan = plan_for(x, s["tc"], w, k=s["k"], pad=s["pad"], p_base=s["p_base"], variant=variant)
     img = cc3d.causal_conv3d_pack_weights(plan, w)
     ref = nan_like(plan.shapes()["out"], torch.bfloat16, DEV)
     ref_co = nan_like(plan.shapes()["cache_out"], torch.bfloat16, DEV)
@@ -40,12 +40,13 @@ def _both(s, seed):
     return plan, ref, ref_co, got, got_co
 
 
-@pytest.mark.parametrize("first,second", [("latent_384_60x104", "latent_384_30x52"),
-                                          ("latent_384_30x52", "latent_384_12x20")])
-def test_noalloc_matches_the_caller_workspace_call_twice_in_a_row(cuda_device, first, second):
+@pytest.mark.parametrize("first,second,variant", [("latent_384_60x104", "latent_384_30x52", None),
+                                                  ("latent_384_30x52", "latent_384_12x20", None),
+                                                  ("latent_384", "latent_384_30x52", "bf16_s3_n64_p24x32_g32")])
+def test_noalloc_matches_the_caller_workspace_call_twice_in_a_row(cuda_device, first, second, variant):
     big, small = _sig(first), _sig(second)
-    p1, ref1, rco1, got1, gco1 = _both(big, synth.SEED_BASE + 800)
-    p2, ref2, rco2, got2, gco2 = _both(small, synth.SEED_BASE + 801)
+    p1, ref1, rco1, got1, gco1 = _both(big, synth.SEED_BASE + 800, variant)
+    p2, ref2, rco2, got2, gco2 = _both(small, synth.SEED_BASE + 801, variant)
     assert p1.info["splits"] > 1 and p2.info["splits"] > 1
     assert small["h"] * small["w"] * small["cin"] < big["h"] * big["w"] * big["cin"]  # a smaller input second
     assert max(p1.info["workspace_bytes"], p2.info["workspace_bytes"]) <= cc3d.NOALLOC_SCRATCH_BYTES
