@@ -18,7 +18,7 @@ import torch
 import causal_conv3d_video_amd as cc3d
 import oracle
 import synth
-from gpu_util import assert_bf16_close, assert_bias_only_exact, mask_for, run
+from gpu_util import assert_bf16_close, assert_bias_only_exact, mask_for, nan_like, plan_for, run, workspace_for
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -143,3 +143,69 @@ def test_random_shape_on_every_accepting_variant(cuda_device, case):
                 assert_bf16_close(yp, ref, name + " split", exclude=mask)
         keep = min(p_base, z.shape[1])
         assert torch.equal(co, z[:, z.shape[1] - keep:]), plan.info["kernel_name"]
+
+
+def _group_staged_split_cases(count, seed):
+    """Maps small enough that the group-staged kernel splits its tiles'
+    channel groups (or, with one 32-channel group, does not), with temporal
+    taps, dilation, cache depth and batch drawn as above."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        v = str(rng.choice(["bf16_s3_n64_p24x32_g32", "bf16_s3_n96_p16x32_g32"]))
+        cin = int(rng.choice([32, 64, 96, 128, 192]))
+        cout = int(rng.choice([64, 128, 192])) if "n64" in v else int(rng.choice([96, 192, 288]))
+        n = int(rng.choice([1, 1, 2]))
+        h, w = int(rng.integers(1, 60)), int(rng.integers(1, 100))
+        tx, tc = int(rng.integers(1, 5)), int(rng.integers(0, 5))
+        kt, dt = int(rng.choice([1, 2, 3, 3])), int(rng.choice([1, 1, 2]))
+        p_base = dt * (kt - 1) + int(rng.choice([0, 0, 1]))
+        if tx + p_base - dt * (kt - 1) < 1:
+            continue
+        out.append((v, cin, cout, h, w, tx, tc, kt, dt, p_base, n))
+    return out
+
+
+SPLIT_CASES = _group_staged_split_cases(24, 20261203 + 779)
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[str(i) for i in range(len(SPLIT_CASES))])
+def test_group_staged_split_units_packed_with_cache_out(cuda_device, case):
+    """The packed-image forward with a workspace (split units where the
+    planner splits): every output against the oracle, the cache-out copied in
+    the kernel's tail byte for byte, and the arrival counters left zero."""
+    v, cin, cout, h, w_, tx, tc, kt, dt, p_base, n = case
+    k = (kt, 3, 3)
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
+                                   seed=synth.SEED_BASE + 700 + SPLIT_CASES.index(case))
+    plan = plan_for(x, tc, w, k=k, pad=(1, 1), dt=dt, p_base=p_base, variant=v)
+    img = cc3d.causal_conv3d_pack_weights(plan, w)
+    ws = workspace_for(plan, DEV)
+    y = nan_like(plan.shapes()["out"], torch.bfloat16, DEV)
+    co = nan_like(plan.shapes()["cache_out"], torch.bfloat16, DEV)
+    cc3d.causal_conv3d_forward_packed(plan, x, c, img, b, y, co, ws)
+    torch.cuda.synchronize()
+
+    def cpu(t):
+        return None if t is None else t.detach().cpu()
+
+    ref = oracle.conv3d(cpu(x), cpu(c), cpu(w), cpu(b), dilation=(dt, 1, 1), padding=(1, 1), pbase=p_base)
+    name = "%s splits=%d %s" % (v, plan.info["splits"], case)
+    mask = mask_for(plan, x.shape, k=k, pad=(1, 1), dt=dt)
+    assert_bias_only_exact(y, b, mask, name)
+    if not mask.all():
+        assert_bf16_close(y, ref, name, exclude=mask)
+    z = x if c is None else torch.cat([c, x], 1)
+    keep = min(p_base, z.shape[1])
+    assert torch.equal(co, z[:, z.shape[1] - keep:]), name
+    if ws is not None:
+        assert int(ws[: plan.info["tiles"] * 4].view(torch.int32).abs().sum()) == 0, name
+
+
+def test_group_staged_split_cases_do_split():
+    """(host) most of the draws above are split, some are not"""
+    splits = []
+    for v, cin, cout, h, w_, tx, tc, kt, dt, p_base, n in SPLIT_CASES:
+        d = cc3d.make_desc(n, cin, cout, h, w_, tx, tc, k=(kt, 3, 3), dilation=(dt, 1, 1), p_base=p_base)
+        splits.append(cc3d.causal_conv3d_plan_variant(d, v).info["splits"])
+    assert sum(s > 1 for s in splits) >= len(splits) // 2 and min(splits) == 1
