@@ -84,10 +84,41 @@ def metrics(got, ref, exclude=None):
     }
 
 
-def assert_bf16_close(got, ref, what="", exclude=None):
+def bf16_step(r):
+    """The spacing of bf16 numbers at |r| (8 significant bits): 2**(e - 7)
+    for |r| in [2**e, 2**(e + 1)), fp64; the smallest normal spacing below."""
+    a = np.maximum(np.abs(np.asarray(r, dtype=np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 7)
+
+
+def unfaithful(got, ref, rms, exclude=None):
+    """How many outputs lie further from the fp64 value than one bf16 step
+    there (plus 1e-4 x RMS for the fp32 accumulation): an output rounded from
+    an fp32 sum to either bf16 neighbour of the exact value passes."""
+    g = got.detach().float().cpu().numpy().astype(np.float64) if isinstance(got, torch.Tensor) else \
+        np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    g = g.reshape(r.shape)
+    if exclude is not None:
+        keep = ~np.broadcast_to(exclude, r.shape)
+        g, r = g[keep], r[keep]
+    return int(np.sum(np.abs(g - r) > bf16_step(r) + 1e-4 * rms))
+
+
+def assert_bf16_close(got, ref, what="", exclude=None, strict=False):
+    """The bf16 bar: max |gpu - oracle| <= 2e-2 x RMS(oracle).  Where outputs
+    of 4 or more sit beside an RMS under ~0.78, half a bf16 step (1/64 there)
+    exceeds that bar, and no bf16 output can meet it; the bar is then that
+    every output is faithfully rounded (within one bf16 step of its fp64
+    value).  strict: the stated bar alone (the five stated configurations,
+    whose outputs have RMS near 1)."""
     m = metrics(got, ref, exclude)
     assert m["nonfinite_gpu"] == 0 and m["nonfinite_ref"] == 0, (what, m)
-    assert m["max_abs"] <= BF16_REL_TOL * m["rms_ref"], (what, m)
+    if m["max_abs"] <= BF16_REL_TOL * m["rms_ref"]:
+        return m
+    assert not strict, (what, m)
+    m["unfaithful"] = unfaithful(got, ref, m["rms_ref"], exclude)
+    assert m["unfaithful"] == 0, (what, m)
     return m
 
 

@@ -72,3 +72,30 @@ def test_bias_only_mask_marks_exactly_the_unreached_outputs(case):
     assert m.shape == y.shape[:4] + (1,)
     assert np.array_equal(m[..., 0], zero)
     assert zero.any() and not zero.all()
+
+
+def test_bf16_bar_falls_back_to_faithful_rounding_below_the_bf16_step():
+    """An output of 5 rounded to bf16 is 1/64 off at worst; beside an RMS of
+    0.5 the stated bar (2e-2 x RMS = 0.01) is below that step, so the bar
+    becomes faithful rounding: either bf16 neighbour passes, one step and a
+    half off fails, and the strict bar alone fails both."""
+    from gpu_util import assert_bf16_close, bf16_step
+    ref = np.full(128, 0.25)
+    ref[0] = 5.0 + 1.0 / 64  # exactly between two bf16 numbers (5.0 and 5.03125); RMS ~0.51
+    assert bf16_step(5.0) == 1.0 / 32 and bf16_step(0.25) == 1.0 / 512
+    near = ref.copy()
+    near[0] = 5.0  # a bf16 neighbour, 1/64 off
+    m = assert_bf16_close(near, ref)
+    assert m["max_abs"] == pytest.approx(1.0 / 64) and m["unfaithful"] == 0
+    with pytest.raises(AssertionError):
+        assert_bf16_close(near, ref, strict=True)
+    far = ref.copy()
+    far[0] = 5.0 - 1.0 / 32  # the next bf16 number down: 3/64 off, beyond one step
+    with pytest.raises(AssertionError):
+        assert_bf16_close(far, ref)
+    cmp = Comparator("t")
+    cmp.add(near[:64], ref[:64])
+    cmp.add(near[64:], ref[64:])
+    assert cmp.assert_bf16()["beyond_step"] <= 0
+    with pytest.raises(AssertionError):
+        cmp.assert_bf16(strict=True)

@@ -203,7 +203,7 @@ def test_latent_config_full_compare(cuda_device):
     y, co, plan = run(x, c, w, b)
     torch.cuda.synchronize()
     ref = _oracle(x, c, w, b)
-    m = assert_bf16_close(y, ref, "latent")
+    m = assert_bf16_close(y, ref, "latent", strict=True)
     assert m["cos"] > 0.9999
     assert torch.equal(co, torch.cat([c, x], 1)[:, 1:])
 
@@ -227,7 +227,7 @@ def test_full_size_signatures_every_output(cuda_device, sig, packed):
         assert torch.equal(y, y2)
         del y2
         return  # the outputs are those compared below, bit for bit
-    m = compare_full(y, x, c, w, b, s["name"], padding=s["pad"], pbase=s["p_base"])
+    m = compare_full(y, x, c, w, b, s["name"], strict=True, padding=s["pad"], pbase=s["p_base"])
     assert m["count"] == y.numel() and m["cos"] > 0.9999
 
 
@@ -280,8 +280,8 @@ def test_streaming_replay_full_size_every_output(cuda_device, sig):
     y = torch.cat(outs, 1)
     del outs
     whole_x = torch.cat(xs, 1)
-    m = compare_full(y, whole_x, None, wt, bt, sig["name"], dilation=(sig["dt"], 1, 1), padding=sig["pad"],
-                     pbase=sig["p_base"])
+    m = compare_full(y, whole_x, None, wt, bt, sig["name"], strict=True, dilation=(sig["dt"], 1, 1),
+                     padding=sig["pad"], pbase=sig["p_base"])
     assert m["count"] == y.numel()
 
 
