@@ -521,10 +521,14 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(OC
   for (;;) {
     zero_acc();
     if (ct.s1 == ct.s0) {
-      // no stage (no active tap, or fewer stages than splits)
+      // no stage (no active tap, or fewer stages than splits).  The load
+      // cursor has already issued stages pos .. pos+NBUF-2 of the next units
+      // into their buffers; the one buffer they leave free, (pos+NBUF-1) %
+      // NBUF, stages the outputs (its next loads go out only after the
+      // barrier that closes this unit).
       if (tid < BN) bias_lds[par][tid] = bf16_to_f32(bias_value(ct));
       __syncthreads();
-      if (!SPLIT || reduce_splits(ct)) epilogue(ct, par, pos % NBUF);
+      if (!SPLIT || reduce_splits(ct)) epilogue(ct, par, (pos + NBUF - 1) % NBUF);
       __syncthreads();
     } else {
       for (int st = ct.s0; st < ct.s1; ++st, ++pos) {

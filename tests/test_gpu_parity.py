@@ -888,6 +888,63 @@ def test_packed_forwards_of_one_plan_overlap_on_two_streams(cuda_device, cout, v
     assert all(torch.equal(o, ref) for o in outs)
 
 
+# The two-workgroup / LDS-staged kernels when a workgroup's tiles alternate
+# between output frames no tap reaches (bias only, no K stage) and frames
+# with stages: the load cursor runs ahead across tile boundaries, so a
+# bias-only tile must stage its outputs through the one LDS buffer the next
+# tile's prefetched stages leave free.  (variant, n, C_in, C_out, k, H, W,
+# T_x, T_cache, d_t, p_base, bias); T_out is 6 or 7, so the per-XCD tile
+# stride (32 or 64 workgroups) moves a workgroup from a bias-only frame to
+# a frame with stages.
+EMPTY_THEN_STAGED = [
+    ("bf16_s1_n32_p8x32", 3, 64, 192, (3, 1, 1), 11, 69, 5, 0, 2, 5, False),   # d_t = 2: frame 0 bias only
+    ("bf16_s1_n32_p8x32", 1, 64, 64, (3, 1, 1), 40, 320, 4, 0, 1, 5, True),
+    ("bf16_s1_n192_p8x32", 1, 64, 192, (3, 1, 1), 64, 320, 4, 0, 1, 5, True),
+    ("bf16_s3_n32_p8x32", 1, 32, 64, (3, 3, 3), 64, 288, 4, 0, 1, 5, True),
+    ("bf16_s3_n96_p8x32_x2", 1, 32, 96, (3, 3, 3), 96, 416, 4, 0, 1, 5, True),
+]
+
+
+def _empty_then_staged(tiles, to, staged, grid):
+    """Whether, under the persistent schedule (workgroup b on XCD b % 8; each
+    XCD walks its contiguous tile range with a stride of its workgroup
+    count; output frame = tile % T_out), some workgroup runs a tile without
+    stages and then one with stages."""
+    per, rem = divmod(tiles, 8)
+    for xcd in range(8):
+        nblk = grid // 8 + (1 if xcd < grid % 8 else 0)
+        beg = xcd * per + min(xcd, rem)
+        end = beg + per + (1 if xcd < rem else 0)
+        for t in range(beg, min(beg + nblk, end)):
+            if not staged[t % to] and t + nblk < end and any(staged[u % to] for u in range(t + nblk, end, nblk)):
+                return True
+    return False
+
+
+@pytest.mark.parametrize("case", EMPTY_THEN_STAGED, ids=["%s_%d" % (c[0], i) for i, c in enumerate(EMPTY_THEN_STAGED)])
+def test_bias_only_tiles_before_staged_tiles(cuda_device, case):
+    v, n, cin, cout, k, h, w_, tx, tc, dt, p_base, bias = case
+    pad = (0, 0) if k[1] == 1 else (1, 1)
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV, has_bias=bias,
+                                   seed=synth.SEED_BASE + 680 + EMPTY_THEN_STAGED.index(case))
+    y, co, plan = run(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, variant=v)
+    yp, _, _ = run(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base, variant=v, packed=True, want_cache=False)
+    torch.cuda.synchronize()
+    i = plan.info
+    assert i["kernel_name"] == v and i["splits"] == 1
+    to = i["t_out"]
+    staged = [any(0 <= o + tp * dt - i["p_l"] < i["t_z"] for tp in range(k[0])) for o in range(to)]
+    assert not all(staged) and any(staged)
+    # the case walks a bias-only tile into a staged one at one and at two
+    # workgroups per compute unit
+    assert all(_empty_then_staged(i["tiles"], to, staged, min(i["tiles"], 256 * occ)) for occ in (1, 2))
+    assert torch.equal(y, yp)
+    ref = _oracle(x, c, w, b, k=k, pad=pad, dt=dt, p_base=p_base)
+    mask = mask_for(plan, x.shape, k=k, pad=pad, dt=dt)
+    assert_bias_only_exact(y, b, mask, v)
+    assert_bf16_close(y, ref, v, exclude=mask)
+
+
 # The register-direct 1x1 kernel: (n, C_in, C_out, H, W, T_x, T_cache, k_t,
 # d_t, p_base, bias).  Its stage depth follows C_in / 64 (3 for 3, 6 and 12
 # chunks, 4 for 4 and 8, 2 for 2); frames of any pixel count (the last tile
