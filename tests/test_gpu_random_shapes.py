@@ -1,5 +1,6 @@
-"""Seeded random small shapes, each on the default kernel choice and on every
-bf16 variant that accepts it, against the fp64 oracle (every output) and the
+"""Seeded random shapes -- small ones, and maps large enough that every
+kernel runs several tiles per workgroup -- each on the default kernel choice
+and on every bf16 variant that accepts it, against the fp64 oracle (every output) and the
 cache-out against its source frames (byte-exact); each variant also from its
 packed weight image, which must give the same bits as reading W in place
 (unless the packed call splits its K stages, whose sums round differently).
@@ -98,14 +99,52 @@ def _halo_staged_spatial_cases(count, seed):
     return out
 
 
+def _multi_tile_cases(count, seed):
+    """Maps large enough that every kernel runs several tiles per workgroup
+    (its load cursor crossing tile boundaries), with leading output frames
+    that no temporal tap reaches (p_base up to 3 past d_t (k_t - 1)) and
+    frame counts that do not divide the per-XCD tile stride."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        kind = rng.choice(["s3", "s1", "s1", "few"])
+        n = int(rng.choice([1, 1, 2]))
+        h, w = int(rng.integers(40, 73)), int(rng.integers(160, 289))
+        tx, tc = int(rng.integers(2, 6)), int(rng.integers(0, 5))
+        kt = int(rng.choice([2, 3, 3]))
+        dt = int(rng.choice([1, 1, 2]))
+        if kind == "few":
+            cin, cout, kt, dt = int(rng.choice([32, 64, 96])), int(rng.integers(1, 6)), 3, 1
+        else:
+            cin = int(rng.choice([32, 64, 64, 96, 128]))
+            cout = int(rng.choice([32, 64, 96, 192]))
+        k, pad = ((kt, 3, 3), (1, 1)) if kind in ("s3", "few") else ((kt, 1, 1), (0, 0))
+        p_base = dt * (kt - 1) + int(rng.choice([0, 1, 2, 3]))
+        t_out = tx + tc + p_base - tc - dt * (kt - 1)
+        if t_out < 3:
+            continue
+        bias = bool(rng.integers(0, 4) > 0)
+        out.append((cin, cout, h, w, tx, tc, k, pad, (1, 1), (1, 1), 1, dt, p_base, n, bias))
+    return out
+
+
 CASES = _cases(56, 20261203 + 777) + _halo_staged_spatial_cases(12, 20261203 + 778)
+MULTI_TILE_CASES = _multi_tile_cases(10, 20261203 + 780)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
 def test_random_shape_on_every_accepting_variant(cuda_device, case):
+    _every_accepting_variant(case, synth.SEED_BASE + 500 + CASES.index(case))
+
+
+@pytest.mark.parametrize("case", MULTI_TILE_CASES, ids=[str(i) for i in range(len(MULTI_TILE_CASES))])
+def test_random_multi_tile_shape_on_every_accepting_variant(cuda_device, case):
+    _every_accepting_variant(case, synth.SEED_BASE + 900 + MULTI_TILE_CASES.index(case))
+
+
+def _every_accepting_variant(case, seed):
     cin, cout, h, w_, tx, tc, k, pad, sst, sdil, st, dt, p_base, n, bias = case
-    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV,
-                                   seed=synth.SEED_BASE + 500 + CASES.index(case), has_bias=bias)
+    x, c, w, b = synth.conv_inputs(n, cin, cout, h, w_, tx, tc, k, device=DEV, seed=seed, has_bias=bias)
     def cpu(t):
         return None if t is None else t.detach().cpu()
 
