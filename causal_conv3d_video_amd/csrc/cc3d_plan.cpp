@@ -207,6 +207,15 @@ const char* default_variant(const cc3d_desc_t& d) {
       const int64_t x2_tiles = int64_t(d.n) * ((d.h + 7) / 8) * ((d.w + 31) / 32) * (d.c_out / 96) *
                                std::max(1, d.t_x);
       if (x2_tiles < 64) return "bf16_s3_n32_p8x32";
+      // where the 24-row tiles pad the map no more than the 8-row ones and
+      // fill at most half the compute units, the group-staged tile in split
+      // units (packed calls with a workspace; 384->384 at 90x160, 1 frame +
+      // 2 cached: 109 vs 111 us back to back, 118 vs 128 us launched alone)
+      if (d.c_out % 64 == 0 && d.c_in % 32 == 0 && (d.h + 23) / 24 * 24 == (d.h + 7) / 8 * 8) {
+        const int64_t tiles64 =
+            int64_t(d.n) * ((d.h + 23) / 24) * ((d.w + 31) / 32) * (d.c_out / 64) * std::max(1, d.t_x);
+        if (tiles64 * 2 <= kComputeUnits) return "bf16_s3_n64_p24x32_g32";
+      }
       return "bf16_s3_n96_p8x32_x2";
     }
     if (d.c_out <= 5 && d.k_t == 3 && d.d_t == 1 && d.s_t == 1 && d.c_in % 32 == 0 && d.c_in <= 96)

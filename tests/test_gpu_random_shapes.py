@@ -129,7 +129,7 @@ def _multi_tile_cases(count, seed):
 
 
 CASES = _cases(56, 20261203 + 777) + _halo_staged_spatial_cases(12, 20261203 + 778)
-MULTI_TILE_CASES = _multi_tile_cases(10, 20261203 + 780)
+MULTI_TILE_CASES = _multi_tile_cases(24, 20261203 + 780)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])

@@ -405,7 +405,12 @@ def test_default_kernel_choice():
     mid = cc3d.causal_conv3d_plan(_desc(c_in=64, c_out=128, h=360, w=640, t_x=4, t_cache=2))
     assert mid.info["kernel_name"] == "bf16_s3_n64_p24x32_g32"   # C_out % 96 != 0
     lat = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2))
-    assert lat.info["kernel_name"] == "bf16_s3_n96_p8x32_x2"
+    # (120 tiles of 24x32 x 64, no more row padding than 8-row tiles: the
+    # group-staged tile in split units)
+    assert lat.info["kernel_name"] == "bf16_s3_n64_p24x32_g32" and lat.info["splits"] == 2
+    # 60 rows: 24-row tiles pad to 72, 8-row ones to 64
+    lat60 = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=60, w=104, t_x=1, t_cache=2))
+    assert lat60.info["kernel_name"] == "bf16_s3_n96_p8x32_x2"
     odd = cc3d.causal_conv3d_plan(_desc(c_in=48, c_out=96, h=360, w=640, t_x=4, t_cache=2))
     assert odd.info["kernel_name"] == "bf16_s3_n96_p8x32_x2"   # C_in % 32 != 0
     head = cc3d.causal_conv3d_plan(_desc(c_in=96, c_out=3, h=720, w=1280, t_x=4, t_cache=2))
@@ -547,7 +552,7 @@ def test_split_reduction_only_where_tiles_leave_slots_idle():
     assert n32["kernel_name"] == "bf16_s3_n32_p8x32" and n32["tiles"] == 96 and n32["splits"] == 5
     mid = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=60, w=104, t_x=1, t_cache=2))
     assert mid.info["tiles"] == 128 and mid.info["splits"] == 4               # 512 slots / 128 tiles
-    lat = cc3d.causal_conv3d_plan(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2))
+    lat = cc3d.causal_conv3d_plan_variant(_desc(c_in=384, c_out=384, h=90, w=160, t_x=1, t_cache=2), x2)
     assert lat.info["tiles"] == 240 and lat.info["splits"] == 1 and lat.info["workspace_bytes"] == 0  # 2 < 4
     first = cc3d.causal_conv3d_plan_variant(_desc(c_in=384, c_out=384, h=30, w=52, t_x=1, t_cache=0), x2)
     assert first.info["splits"] == 6                                         # one active tap: 24 stages
