@@ -5,14 +5,18 @@
 //
 // Tile: 256 consecutive pixels of one output frame (the frame is flattened:
 // without a spatial halo, rows do not matter) x 192 output channels.  Four
-// waves, each 64 pixels x all 192 channels (2 x 6 MFMA blocks of 32x32, fp32
-// accumulators).  A stage is one active tap x 64 input channels.
+// waves, each 64 pixels x all 192 channels (4 x 12 MFMA blocks of 16x16,
+// fp32 accumulators).  A stage is one active tap x 64 input channels.
 //
-// Operand paths.  The pixel operand of an MFMA lane is 8 consecutive input
-// channels of one pixel -- 16 contiguous bytes of the channels-last frame --
-// so each wave loads its own pixels from memory straight into registers,
-// with no LDS round trip and no barrier on them; the register file is the
-// pipeline buffer (D stages in flight, 32 VGPRs each).  The weights (shared
+// Operand paths.  The pixel operand of a 16x16x32 MFMA lane is 8 consecutive
+// input channels of one pixel -- 16 contiguous bytes of the channels-last
+// frame -- and the four lanes of a pixel hold 32 consecutive channels, so
+// each wave loads its own pixels from memory straight into registers, with
+// no LDS round trip and no barrier on them; the register file is the
+// pipeline buffer (D stages in flight, 32 VGPRs each).  One load instruction
+// covers 16 pixels x 64 contiguous bytes: half a cache line per pixel (the
+// 32x32x16 operand, 32 pixels x 32 bytes, costs the address unit twice the
+// cache-line lookups per byte, and that path is what bounds this kernel).  The weights (shared
 // by the four waves) stream into LDS with direct-to-LDS loads from the
 // stage-ordered packed image (or gathered from W as stored), one 24 KB stage
 // tile per LDS buffer.
@@ -26,9 +30,9 @@ template <bool WPK, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_bf16_s1rd(ConvArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int BN = 192, CB = 64, NT = 256, TP = 256;
-  constexpr int CW = BN / 32;             // 32-channel MFMA blocks (all of them, per wave)
-  constexpr int RB = 2;                   // 32-pixel MFMA blocks per wave
-  constexpr int KK = CB / 16;             // MFMA k-steps per stage
+  constexpr int CW = BN / 16;             // 16-channel MFMA blocks (all of them, per wave)
+  constexpr int RB = 4;                   // 16-pixel MFMA blocks per wave
+  constexpr int KK = CB / 32;             // MFMA k-steps per stage
   using WT = WTile<BN, 1, CB>;            // slot q*PLANE + co: W[co][q*8 .. q*8+8) of the stage
   constexpr int WIT = WT::WSLOTS / NT;    // weight slots per thread per stage
   constexpr int XL = RB * KK;             // pixel loads per lane per stage
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, l16 = lane & 15;  // MFMA lane: k (or row) quarter, column
 
   // Persistent schedule: workgroup b runs on XCD b % 8; each XCD owns one
   // contiguous range of tiles.  Tile order: output frame fastest, then the
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto set_xoff = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int px = lt.p0 + wave * 64 + rb * 32 + l32;
+      const int px = lt.p0 + wave * 64 + rb * 16 + l16;
       xoff[rb] = px < P ? (px * a.cin + g * 8) * 2 : OOB;
     }
   };
@@ -188,8 +192,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  // pixel operand ring: xr[j][rb][kk] = channels kk*16 + g*8 .. +8 of the
-  // stage, for pixel row block rb of this wave
+  // pixel operand ring: xr[j][rb][kk] = channels kk*32 + g*8 .. +8 of the
+  // stage, for 16-pixel block rb of this wave
   u32x4_t xr[D][RB][KK];
   // piece p (0 .. LPS-1) of a stage's loads into buffer J: weight slots
   // first, then pixel loads
@@ -200,49 +204,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                16, woff[p], 0, 0, 0);
     } else {
       const int q = p - WIT, rb = q / KK, kk = q % KK;
-      xr[j][rb][kk] = __builtin_amdgcn_raw_buffer_load_b128(s.xr, xoff[rb], s.xch + kk * 32, 0);
+      xr[j][rb][kk] = __builtin_amdgcn_raw_buffer_load_b128(s.xr, xoff[rb], s.xch + kk * 64, 0);
     }
   };
 
-  f32x16_t acc[CW][RB];
+  f32x4_t acc[CW][RB];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CW; ++c)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[c][rb][v] = 0.f;
+        for (int v = 0; v < 4; ++v) acc[c][rb][v] = 0.f;
   };
 
-  // One stage: KK k-steps of CW x RB MFMAs; the weight fragments of step
-  // kk+1 are read from LDS before step kk's MFMAs issue.  The next loads
-  // (`nxt`, into buffer (J + D - 1) % D) are spread over the k-steps.
+  // One stage: KK k-steps x CW channel blocks = NG groups of RB MFMAs.  The
+  // weight fragment of a group (one ds_read of 16 bytes per lane) is read
+  // from LDS two groups ahead, so its latency hides behind two groups of
+  // MFMAs while only three fragments are live.  The next loads (`nxt`, into
+  // buffer (J + D - 1) % D) are spread over the groups.
   auto compute = [&](auto J, const StageSrc& nxt) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
     constexpr int jn = (j + D - 1) % D;
+    constexpr int NG = KK * CW;
     const uint4* wb = wbuf(J);
-    bf16x8_t wf[2][CW];
-    auto read_w = [&](int kk, bf16x8_t* f) __attribute__((always_inline)) {
-      const int q = kk * 2 + g;
-#pragma unroll
-      for (int c = 0; c < CW; ++c) f[c] = __builtin_bit_cast(bf16x8_t, wb[q * WT::PLANE + c * 32 + l32]);
+    auto read_w = [&](int i) __attribute__((always_inline)) {
+      const int kk = i / CW, c = i % CW;
+      return __builtin_bit_cast(bf16x8_t, wb[(kk * 4 + g) * WT::PLANE + c * 16 + l16]);
     };
-    read_w(0, wf[0]);
+    bf16x8_t wf[3];
+    wf[0] = read_w(0);
+    wf[1] = read_w(1);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) read_w(kk + 1, wf[(kk + 1) & 1]);
+    for (int i = 0; i < NG; ++i) {
+      if (i + 2 < NG) wf[(i + 2) % 3] = read_w(i + 2);
       __builtin_amdgcn_sched_barrier(0);
+      const int kk = i / CW, c = i % CW;
 #pragma unroll
-      for (int c = 0; c < CW; ++c)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          acc[c][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][c],
-                                                               __builtin_bit_cast(bf16x8_t, xr[j][rb][kk]),
-                                                               acc[c][rb], 0, 0, 0);
+      for (int rb = 0; rb < RB; ++rb)
+        acc[c][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i % 3], __builtin_bit_cast(bf16x8_t, xr[j][rb][kk]),
+                                                             acc[c][rb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int p = 0; p < LPS; ++p)
-        if (p * KK / LPS == kk) issue_piece(std::integral_constant<int, jn>{}, nxt, p);
+        if (p * NG / LPS == i) issue_piece(std::integral_constant<int, jn>{}, nxt, p);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -251,9 +256,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // accumulators are read out of their AGPRs one element per store (inline
   // v_accvgpr_read), so that the compiler does not copy all 192 of them to
   // VGPRs at once while the next stages' pixels occupy 96 VGPRs.  The
-  // lane holding pixel l32 of a 32-pixel block has channels
-  // (v/4)*8 + g*4 + (v%4) of each 32-channel block: 4 consecutive channels,
-  // one 8-byte store each.  Stores to pixels past the frame fall outside the
+  // lane holding pixel l16 of a 16-pixel block has channels g*4 .. g*4+3 of
+  // each 16-channel block: 4 consecutive channels, one 8-byte store each.  Stores to pixels past the frame fall outside the
   // buffer's range and are dropped, so every wave issues exactly ST stores.
   auto epilogue = [&](const Tile& c, int par) __attribute__((always_inline)) {
     unsigned short* ob = os + ((int64_t(c.nn) * a.to + c.o) * P) * a.cout + c.n0;
@@ -262,26 +266,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         0x00020000);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int px = c.p0 + wave * 64 + rb * 32 + l32;
+      const int px = c.p0 + wave * 64 + rb * 16 + l16;
       const int ooff = px < P ? (px * a.cout + g * 4) * 2 : OOB;
 #pragma unroll
-      for (int q = 0; q < CW; ++q)
+      for (int q = 0; q < CW; ++q) {
+        const int cl = q * 16;  // + g*4 in ooff
+        const float4 bv = *reinterpret_cast<const float4*>(&bias_lds[par][cl + g * 4]);
+        float f[4];
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int cl = q * 32 + v4 * 8;  // + g*4 in ooff
-          const float4 bv = *reinterpret_cast<const float4*>(&bias_lds[par][cl + g * 4]);
-          float f[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)  // (read from the accumulator registers one at a time: see above)
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(f[e]) : "a"(acc[q][rb][v4 * 4 + e]));
-          const unsigned lo = pack_bf16x2(f[0] + bv.x, f[1] + bv.y);
-          const unsigned hi = pack_bf16x2(f[2] + bv.z, f[3] + bv.w);
-          const u32x2_t v = {lo, hi};
-          __builtin_amdgcn_raw_buffer_store_b64(v, orc, ooff, cl * 2, 0);
-          // (one store at a time: converting all 96 pairs first would need
-          // 192 more VGPRs while the next stages' pixels are in flight)
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int e = 0; e < 4; ++e)  // (read from the accumulator registers one at a time: see above)
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(f[e]) : "a"(acc[q][rb][e]));
+        const unsigned lo = pack_bf16x2(f[0] + bv.x, f[1] + bv.y);
+        const unsigned hi = pack_bf16x2(f[2] + bv.z, f[3] + bv.w);
+        const u32x2_t v = {lo, hi};
+        __builtin_amdgcn_raw_buffer_store_b64(v, orc, ooff, cl * 2, 0);
+        // (one store at a time: converting all 96 pairs first would need
+        // 192 more VGPRs while the next stages' pixels are in flight)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   auto load_bias = [&](const Tile& c, int par) __attribute__((always_inline)) {
