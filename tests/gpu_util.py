@@ -4,7 +4,6 @@ binding, and compare against the oracle with the stated tolerances.
 Outputs and carried caches are filled with NaN before every launch, so a
 tile a kernel never writes shows up as NaN (or as a mismatch) instead of
 passing on memory that an earlier launch left correct."""
-import re
 
 import numpy as np
 import torch
@@ -169,39 +168,6 @@ def mask_for(plan, x_shape, *, k=(3, 3, 3), pad=(1, 1), st=1, sst=(1, 1), dt=1, 
     return bias_only_mask(n, i["t_out"], i["h_out"], i["w_out"], tz=i["t_z"], p_l=i["p_l"], kt=k[0], kh=k[1],
                           kw=k[2], st=st, sh=sst[0], sw=sst[1], dt=dt, dh=sdil[0], dw=sdil[1], ph=pad[0], pw=pad[1],
                           h=h, w=w)
-
-
-def tile_of(plan):
-    """(rows, columns) of the plan's output tile, from its kernel name
-    ("..._p<rows>x<cols>..."); (8, 32) for kernels without one."""
-    m = re.search(r"_p(\d+)x(\d+)", plan.info["kernel_name"])
-    return (int(m.group(1)), int(m.group(2))) if m else (8, 32)
-
-
-def sample_points(n, to, ho, wo, count, seed, tile_h=8, tile_w=32):
-    """Output positions to check: all corners and edge midpoints, positions
-    on both sides of every few workgroup-tile boundaries, and uniform random
-    positions, for every batch item and output frame."""
-    rng = np.random.default_rng(seed)
-    pts = set()
-    for nn in range(n):
-        for o in range(to):
-            for i in (0, 1, ho // 2, ho - 2, ho - 1):
-                for j in (0, 1, wo // 2, wo - 2, wo - 1):
-                    pts.add((nn, o, max(i, 0), max(j, 0)))
-            for t in range(1, min(ho // tile_h, 6) + 1):
-                i = t * tile_h
-                for di in (-1, 0):
-                    if 0 <= i + di < ho:
-                        pts.add((nn, o, i + di, int(rng.integers(wo))))
-            for t in range(1, min(wo // tile_w, 6) + 1):
-                j = t * tile_w
-                for dj in (-1, 0):
-                    if 0 <= j + dj < wo:
-                        pts.add((nn, o, int(rng.integers(ho)), j + dj))
-    while len(pts) < count:
-        pts.add((int(rng.integers(n)), int(rng.integers(to)), int(rng.integers(ho)), int(rng.integers(wo))))
-    return np.array(sorted(pts), dtype=np.int64)
 
 
 def gather(out, pts):

@@ -16,7 +16,7 @@ import oracle
 import synth
 from comparator import compare_full, frame_points
 from gpu_util import (assert_bf16_close, assert_bias_only_exact, assert_f32_close, gather, mask_for, nan_like,
-                      plan_for, run, sample_points, tile_of, workspace_for)
+                      plan_for, run, workspace_for)
 
 pytestmark = pytest.mark.gpu
 
