@@ -166,6 +166,11 @@ typedef struct cc3d_counters {
  *   which have a halo-staged kernel of their own.
  *   CC3D_ERR_INVALID_ARG for a NULL pointer, a size < 1 (t_cache < 0), an
  *   unknown dtype, or an empty output (T_o, H_o or W_o < 1).
+ * Logging: with CC3D_LOG=1 in the environment (read once per process) every
+ * plan built by this call or by causal_conv3d_plan_variant is printed to
+ * stderr -- the descriptor, |Z|, p_l, T_o, each temporal tap's delta, output
+ * interval and source interval, and the kernel with its tile, tile count,
+ * splits and buffer sizes -- and every refused plan with its status.
  */
 cc3d_status_t causal_conv3d_plan(const cc3d_desc_t* desc, cc3d_plan_t* out);
 

@@ -566,3 +566,37 @@ def test_split_reduction_only_where_tiles_leave_slots_idle():
                                          padding=(0, 0)))
     assert full.info["kernel_name"] == "bf16_s1_n192_p256_rd"               # 57 pixel tiles x 4 channel blocks
     assert full.info["tiles"] == 228 and full.info["splits"] == 1          # (this kernel never splits)
+
+
+def test_plan_dump_with_cc3d_log():
+    """With CC3D_LOG=1 each plan built is printed to stderr: the descriptor,
+    one line per temporal tap with its interval, and the kernel.  The two
+    calls of the tiny fp32 workload (4 frames without a cache, then 4 frames
+    behind a 2-frame cache; p_base = 2) print the intervals the lowering
+    section's source-time rule gives: p_l = 2, then 0."""
+    code = ("import torch, causal_conv3d_video_amd as cc3d\n"
+            "for tc in (0, 2):\n"
+            "    cc3d.causal_conv3d_plan(cc3d.make_desc(1, 8, 8, 16, 16, 4, tc, dtype=torch.float32)).close()\n"
+            "try:\n"
+            "    cc3d.causal_conv3d_plan(cc3d.make_desc(1, 8, 8, 16, 16, 4, 0, groups=2))\n"
+            "except cc3d.CC3DError:\n"
+            "    pass\n")
+    env = dict(os.environ, CC3D_LOG="1", PYTHONPATH=ROOT)
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [ln.strip() for ln in r.stderr.splitlines() if ln.startswith(("cc3d", "  "))]
+    plans = [i for i, ln in enumerate(lines) if ln.startswith("cc3d plan:")]
+    assert len(plans) == 2, r.stderr
+    a, b = lines[plans[0]:plans[1]], lines[plans[1]:]
+    assert "T_x=4 T_cache=0" in a[0] and "p_l=2 T_o=4" in a[1] and "cache_out=2 active taps=3" in a[1], a[:2]
+    assert a[2:5] == ["tap 0: delta=-2 out=[2,4) src=[0,2)", "tap 1: delta=-1 out=[1,4) src=[0,3)",
+                      "tap 2: delta=0 out=[0,4) src=[0,4)"], a
+    assert "T_x=4 T_cache=2" in b[0] and "|Z|=6 p_l=0 T_o=4" in b[1], b[:2]
+    assert b[2:5] == ["tap 0: delta=0 out=[0,4) src=[0,4)", "tap 1: delta=1 out=[0,4) src=[1,5)",
+                      "tap 2: delta=2 out=[0,4) src=[2,6)"], b
+    assert a[5].startswith("kernel f32_direct") and b[5].startswith("kernel f32_direct")
+    assert any(ln.startswith("cc3d plan refused") for ln in b[6:]), r.stderr
+    # without the variable nothing is printed
+    env.pop("CC3D_LOG")
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
+    assert r.returncode == 0 and "cc3d plan" not in r.stderr
