@@ -339,6 +339,42 @@ def _cpu_model():
     return None
 
 
+def gpu_clocks_under_load(work, stream, max_seconds=8.0):
+    """Current clock levels (MHz) that rocm-smi reports while the replay step
+    runs back to back: the step is repeated until rocm-smi has answered (at
+    most max_seconds).  None where rocm-smi is missing or fails.  These are
+    the power-management levels, not the effective clock under a power cap
+    (that one comes from the profiler's GRBM_GUI_ACTIVE count)."""
+    import re
+    import shutil
+    import subprocess
+
+    import torch
+    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if exe is None:
+        return None
+    try:
+        p = subprocess.Popen([exe, "--showclocks"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    while p.poll() is None and time.perf_counter() - t0 < max_seconds:
+        run_step(work, stream)
+        torch.cuda.synchronize()
+    try:
+        out, _ = p.communicate(timeout=5)
+    except subprocess.TimeoutExpired:
+        p.kill()
+        p.communicate()
+        return None
+    if p.returncode != 0:
+        return None
+    clocks = {}
+    for m in re.finditer(r"GPU\[0\]\s*:\s*(\w+) clock level:\s*\d+:?\s*\((\d+)\s*Mhz\)", out, flags=re.I):
+        clocks[m.group(1)] = int(m.group(2))
+    return clocks or None
+
+
 def cpu_baseline(work, target_seconds, device):
     """The fp64 CPU oracle as it stands, on the host cores:
       * a bounded sample of the replay workload: random output pixels (all
@@ -557,6 +593,8 @@ def main():
     torch.cuda.synchronize()
     ms_w = e0.elapsed_time(e1) / args.steps
 
+    clocks = gpu_clocks_under_load(work, stream)
+
     kern = time_kernels(work, args.kernel_launches, stream)
     # dominant kernel: the variant with the largest share of a step (each
     # signature makes 5 chunk calls; counted at the steady-state rate)
@@ -626,6 +664,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
+        "gpu_clocks_mhz_under_load": clocks,
         "kernel_source_sha256": _source_hash(),
     }
     print(json.dumps(line))
