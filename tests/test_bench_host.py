@@ -1,4 +1,5 @@
-"""Host-side pieces of bench.py (no GPU): the one-GPU guard and the lookup of
+"""Host-side pieces of bench.py (no GPU): the one-GPU guard, the clock record
+parsed from rocm-smi, and the lookup of
 the committed HBM-traffic summary that fills the roofline's traffic."""
 import os
 import subprocess
@@ -67,3 +68,35 @@ def test_traffic_is_null_for_another_workload_or_kernel(fake_root):
     assert bench.traffic_for(K, "mid_192_dt2") is None
     assert bench.traffic_for("other", "mid_192") is None
 
+
+
+def _fake_smi(tmp_path, body, rc=0):
+    exe = tmp_path / "rocm-smi"
+    exe.write_text("#!/bin/sh\ncat <<'TXT'\n%sTXT\nexit %d\n" % (body, rc))
+    exe.chmod(0o755)
+    return str(exe)
+
+
+def _no_gpu(monkeypatch):
+    import torch
+    monkeypatch.setattr(bench, "run_step", lambda work, stream, packed=True: None)
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+
+
+def test_clock_levels_parsed_from_rocm_smi(tmp_path, monkeypatch):
+    """The clock record reads each clock's current level from rocm-smi's
+    --showclocks text; a failing or missing rocm-smi gives None."""
+    import shutil
+    _no_gpu(monkeypatch)
+    text = ("======== ROCm System Management Interface ========\n"
+            "GPU[0]\t\t: fclk clock level: 0: (1200Mhz)\n"
+            "GPU[0]\t\t: mclk clock level: 3: (1900Mhz)\n"
+            "GPU[0]\t\t: sclk clock level: 1: (2100Mhz)\n")
+    exe = _fake_smi(tmp_path, text)
+    monkeypatch.setattr(shutil, "which", lambda name: exe)
+    assert bench.gpu_clocks_under_load(None, None) == {"fclk": 1200, "mclk": 1900, "sclk": 2100}
+    exe = _fake_smi(tmp_path, text, rc=1)
+    assert bench.gpu_clocks_under_load(None, None) is None
+    monkeypatch.setattr(shutil, "which", lambda name: None)
+    monkeypatch.setattr(bench.os.path, "exists", lambda p: False)
+    assert bench.gpu_clocks_under_load(None, None) is None
